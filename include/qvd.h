@@ -1,0 +1,248 @@
+/*
+ * qvd.h -- C ABI of the MI355X (gfx950) quantized DiT-block forward.
+ *
+ * The hot path of the FastH3 / FastH3 Trim pages: one diffusion-transformer block that denoises
+ * video and audio latents, with
+ *   - AdaLN modulation from a 2,688->16 timestep basis shared by all blocks plus a small per-block
+ *     projection, both stored in fp16 (comfyui-wiki "FastH3 Trim：为 8 GB GPU 打造的剪枝版 8 步
+ *     MiniMax H3", section "Trim 改变了什么", timestep-conditioning bullet);
+ *   - FP8 linear layers with one scale per tensor, the scales applied to the matmul output in the
+ *     same kernel, and query/key quantized to INT8 for the attention scores (same page, section
+ *     "运行速度如何", the note under the timing table);
+ *   - 80% block-sparse attention (same page, "Trim 改变了什么", training bullet);
+ *   - 4-bit weights with calibrated static activation scales (news.farwalk.ai FastH3 story,
+ *     post 6/8; comfyui-wiki page, section "ComfyUI 重打包包含什么").
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library never frees them.
+ *     Scalars that the device produces (scales, amax) stay on the device.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; nothing is synchronised or read back.
+ *   - Return value: QVD_OK or a negative status.  Argument errors are detected on the host before
+ *     anything is enqueued, and leave every buffer untouched.  qvd_last_error() then returns a
+ *     message (per thread).  A failing launch returns QVD_EHIP.  Faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - Tensors must be 16-byte aligned (QVD_EALIGN otherwise); head_dim and tile are 128; d is a
+ *     multiple of 128.
+ *   - Results are deterministic: the same inputs give the same bits on every run.
+ *   - bf16 and fp16 tensors are passed as their 16-bit patterns (uint16_t).  E4M3 codes follow the
+ *     OCP OFP8 E4M3 ("FN") encoding; INT8 codes are symmetric in [-127, 127].
+ *   - Workspaces (`ws`) are caller-allocated device memory of at least the size the matching
+ *     qvd_*_ws_bytes() returns; their contents on entry do not matter.
+ *   - Calls that share a workspace or an output must be ordered on one stream.
+ */
+#ifndef QVD_H
+#define QVD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QVD_ABI_VERSION 1
+
+enum qvd_status {
+    QVD_OK = 0,
+    QVD_EINVAL = -1,       /* null pointer or out-of-range scalar                               */
+    QVD_ESHAPE = -2,       /* unsupported or inconsistent sizes                                 */
+    QVD_EALIGN = -3,       /* a tensor pointer is not 16-byte aligned                           */
+    QVD_EWORKSPACE = -4,   /* workspace missing or smaller than the matching qvd_*_ws_bytes()  */
+    QVD_EUNSUPPORTED = -5, /* the current device is not gfx950                                  */
+    QVD_EHIP = -6          /* a HIP runtime call or kernel launch failed                        */
+};
+
+/* Version of this ABI (QVD_ABI_VERSION). */
+int qvd_abi_version(void);
+
+/* Message describing the last failure on the calling thread ("" if none).  The pointer stays
+ * valid until the next failing call on the same thread. */
+const char* qvd_last_error(void);
+
+/* Checks that the current HIP device is gfx950.  Every other entry point performs the same check
+ * on first use per device; calling it early only reports the result up front.
+ * Returns QVD_OK, QVD_EUNSUPPORTED or QVD_EHIP. */
+int qvd_init(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Per-tensor FP8 (E4M3) quantization -- "运行速度如何" note: one scale per tensor.
+ *   x         : n bf16 values (any shape, contiguous).
+ *   scale_in  : NULL -> dynamic scale: amax = max|x|, s = amax/448 (fp32, correctly rounded),
+ *               q = E4M3(fp32(x * fp32(448/amax))); amax = 0 gives s = 1.
+ *               non-NULL -> static scale read from device memory: s = *scale_in,
+ *               q = E4M3(fp32(x * fp32(1/s))).
+ *   q         : n E4M3 codes (round to nearest even; magnitudes above 448 saturate to 448).
+ *   scale_out : one device fp32 receiving s.
+ *   ws        : qvd_quant_ws_bytes(n) bytes (per-block partial maxima); unused for static scales.
+ * n may be 0 (then only *scale_out is written: s = 1, or *scale_in). */
+size_t qvd_quant_ws_bytes(int64_t n);
+int quant_fp8_per_tensor(const uint16_t* x, int64_t n, const float* scale_in, uint8_t* q,
+                         float* scale_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * INT8 query/key quantization -- "运行速度如何" note: Q and K are quantized to INT8 for the score
+ * computation.  One symmetric scale per (head, tile of 128 tokens):
+ *   a = max |x| over the tile's rows that exist (< L), s = a/127, q = clamp(rint(x * 127/a), +-127)
+ *   (fp32 products, round half to even); a = 0 gives s = 1 and zero codes.
+ *   x     : bf16 [L][H][head_dim] (token-major, heads interleaved; row stride = row_stride
+ *           elements, >= H*head_dim; pass H*head_dim for a dense tensor).
+ *   q     : int8 [L][H][head_dim], dense.
+ *   scale : fp32 [H][ceil(L/tile)].
+ * head_dim and tile must be 128; L >= 0. */
+int quant_int8_qk(const uint16_t* x, int32_t L, int32_t H, int32_t head_dim, int32_t tile,
+                  int64_t row_stride, int8_t* q, float* scale, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * AdaLN projection -- "Trim 改变了什么", timestep-conditioning bullet.
+ *   e(t) = [cos(t f_i), sin(t f_i)], f_i = 10000^(-i/(dt/2)), i < dt/2   (float64)
+ *   c    = B e(t)                (B: fp16 [16][dt], the basis shared by all blocks)
+ *   mod  = P c (+ b)             (P: fp16 [6d][16] per block; b: fp16 [6d] or NULL)
+ * written as fp32 [6][d]: shift1, scale1, gate1, shift2, scale2, gate2.  All arithmetic is
+ * float64, rounded once to fp32.  dt must be even and <= 16384; d a multiple of 128.
+ * The _stack form does n_blocks blocks in one launch: proj [n_blocks][6d][16],
+ * bias [n_blocks][6d] or NULL, mod [n_blocks][6][d]. */
+int qvd_adaln_project(float t, const uint16_t* basis, int32_t dt, const uint16_t* proj,
+                      const uint16_t* bias, int32_t d, float* mod, void* stream);
+int qvd_adaln_project_stack(float t, const uint16_t* basis, int32_t dt, const uint16_t* proj,
+                            const uint16_t* bias, int32_t d, int32_t n_blocks, float* mod,
+                            void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Modulated LayerNorm + per-tensor FP8 -- same bullet (the modulation it applies):
+ *   y = fp32(LN(x) * (1 + scale) + shift), LN without affine parameters, biased variance,
+ *   statistics and the affine map in float64; then the per-tensor E4M3 quantization above
+ *   (dynamic, or static when act_scale_in is non-NULL).
+ *   x   : bf16 [L][d];  mod: fp32 [6][d];  half = 0 uses rows (0 shift1, 1 scale1),
+ *         half = 1 uses rows (3 shift2, 4 scale2).
+ *   q   : E4M3 [L][d];  act_scale_out: one device fp32.
+ *   ws  : qvd_adaln_modulate_ws_bytes(L, d) bytes.
+ * d must be a multiple of 128 and at most 4096. */
+size_t qvd_adaln_modulate_ws_bytes(int32_t L, int32_t d);
+int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                   float eps, const float* act_scale_in, uint8_t* q, float* act_scale_out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Block-sparse attention with INT8 scores -- "Trim 改变了什么" training bullet (80% sparsity)
+ * and the "运行速度如何" note (INT8 Q/K).  For head h and query tile i (128 rows):
+ *   keys   = rows of the key tiles kv_idx[h][i][0 .. kv_cnt[h][i]-1] that exist (< L)
+ *   s      = (Q8 K8^T)[exact int32] * q_scale[h][i] * k_scale[h][j] * sm_scale
+ *   out    = softmax(s) V  (per query row, over the kept keys), written as bf16.
+ *   q, k   : int8 [L][H][head_dim];  q_scale, k_scale: fp32 [H][T], T = ceil(L/128).
+ *   v      : bf16 [L][H][head_dim];  out: bf16 [L][H][head_dim].
+ *   kv_idx : int32 [H][T][kmax]; kv_cnt: int32 [H][T].  Entries outside [0, T) and counts outside
+ *            [0, kmax] are ignored (clamped), so device data can never send the kernel out of
+ *            bounds; a row with no kept key outputs zeros.  Tile lists are expected ascending
+ *            with the diagonal present, but order does not change the result beyond rounding.
+ *   out_amax_partials : NULL, or fp32 [H][T] receiving max|out| of each (h, i) tile (feeds the
+ *            dynamic FP8 quantization of the attention output without another pass).
+ * Arithmetic: INT8 MFMA scores (exact int32), softmax in fp32 with exp2, probabilities and V
+ * rounded to fp16 for an fp16 MFMA P.V with fp32 accumulation.  V must satisfy |v| <= 65504
+ * (larger magnitudes saturate to 65504 in the product). */
+int sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
+                const uint16_t* v, int32_t L, int32_t H, int32_t head_dim,
+                const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
+                uint16_t* out, float* out_amax_partials, void* stream);
+
+/* Exact INT32 accumulators Q8[rows of tile i] . K8[rows of tile j]^T of head h, computed by the
+ * same INT8 MFMA tile routine the attention kernel uses, into out int32 [128][128]
+ * (out[r][c] = query row i*128+r, key row j*128+c; rows/keys >= L are written as 0). */
+int qvd_qk_int32_tile(const int8_t* q, const int8_t* k, int32_t L, int32_t H, int32_t h,
+                      int32_t i, int32_t j, int32_t* out, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * FP8 GEMM with the per-tensor output scale fused into the epilogue -- "运行速度如何" note:
+ *   acc[m][n] = sum_k E4M3(a[m][k]) * E4M3(w[n][k])   (MFMA, fp32 accumulation)
+ *   y[m][n]   = acc * fp32(s_a * s_w) + bias[n]        (bias NULL = 0)
+ * a: E4M3 [M][K], w: E4M3 [N][K] (both K-contiguous); s_a, s_w: device fp32 scalars.
+ * M >= 0, N and K multiples of 128.  The epilogue is chosen by `epi`: */
+enum qvd_epilogue_mode {
+    QVD_EPI_F32 = 0,        /* out_f32[m][n] = y                                               */
+    QVD_EPI_BF16 = 1,       /* out_bf16[m][n] = bf16(y)                                        */
+    QVD_EPI_RESID_GATE = 2, /* out_bf16[m][n] = bf16(resid[m][n] + gate[n] * y); out may alias
+                               resid (in-place residual update)                                 */
+    QVD_EPI_GELU = 3,       /* out_bf16[m][n] = bf16(GELU(y)) (erf form); amax_partials, if
+                               non-NULL, receives per-output-tile max|out| (see below)          */
+    QVD_EPI_QKV = 4         /* N = 3*H*128: columns [Q | K | V].  y is rounded to bf16; the Q and
+                               K parts are then quantized per (head, 128-token tile) exactly as
+                               quant_int8_qk does, into q8/k8 int8 [M][H][128] with scales
+                               q_scale/k_scale [H][ceil(M/128)]; the V part goes to v bf16
+                               [M][H][128]                                                     */
+};
+typedef struct {
+    int32_t mode;               /* qvd_epilogue_mode                                           */
+    int32_t n_heads;            /* QVD_EPI_QKV                                                 */
+    float* out_f32;             /* QVD_EPI_F32                                                 */
+    uint16_t* out_bf16;         /* QVD_EPI_BF16, QVD_EPI_RESID_GATE, QVD_EPI_GELU              */
+    const uint16_t* resid;      /* QVD_EPI_RESID_GATE                                          */
+    const float* gate;          /* QVD_EPI_RESID_GATE: fp32 [N]                                */
+    float* amax_partials;       /* QVD_EPI_GELU (optional): fp32 [qvd_gemm_tiles(M, N)]        */
+    int8_t* q8;                 /* QVD_EPI_QKV                                                 */
+    int8_t* k8;
+    uint16_t* v;
+    float* q_scale;
+    float* k_scale;
+} qvd_epilogue;
+int64_t qvd_gemm_tiles(int32_t M, int32_t N);
+int qvd_gemm_fp8(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
+                 const float* bias, int32_t M, int32_t N, int32_t K, const qvd_epilogue* epi,
+                 void* stream);
+/* The same GEMM with 4-bit weights (news.farwalk.ai FastH3 story, post 6/8, in OCP MX form):
+ *   acc[m][n] = sum_k E4M3(a[m][k]) * E2M1(w[n][k]) * 2^(e8m0[n][k/32] - 127)  (block-scaled MFMA)
+ *   y[m][n]   = acc * s_a + bias[n]
+ * w_packed: uint8 [N][K/2], element 2j in the low nibble of byte j; e8m0: uint8 [N][K/32]. */
+int qvd_gemm_mxfp4(const uint8_t* a, const float* s_a, const uint8_t* w_packed,
+                   const uint8_t* e8m0, const float* bias, int32_t M, int32_t N, int32_t K,
+                   const qvd_epilogue* epi, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * One DiT block forward -- the reading of the block (pre-norm adaLN-Zero DiT block):
+ *   h1 = FP8(LN(x)(1+scale1) + shift1);  [Q|K|V] = bf16(h1 W_qkv^T s s + b)
+ *   Q8, K8 = INT8 per (head, 128-token tile);  O = sparse_attn(Q8, K8, V)
+ *   x1 = bf16(x + gate1 * (FP8(O) W_o^T s s + b))
+ *   h2 = FP8(LN(x1)(1+scale2) + shift2);  g = bf16(GELU(h2 W_up^T s s + b))
+ *   x2 = bf16(x1 + gate2 * (FP8(g) W_down^T s s + b))
+ * Weights are [N][K] (K contiguous).  weight_format QVD_W_FP8: E4M3 codes with per-tensor fp32
+ * scales s_*.  QVD_W_MXFP4: packed E2M1 (element 2j in the low nibble of byte j) with E8M0
+ * scales e8m0_* [N][K/32]; s_* are ignored.  act_scale: NULL (dynamic scales) or fp32 [4] static
+ * scales of the QKV, out, up and down GEMM inputs (required for MXFP4).  Biases may be NULL. */
+enum qvd_weight_format { QVD_W_FP8 = 0, QVD_W_MXFP4 = 1 };
+typedef struct {
+    int32_t version;            /* QVD_ABI_VERSION                                             */
+    int32_t d, n_heads, head_dim, mlp, weight_format;
+    const void *w_qkv, *w_o, *w_up, *w_down;
+    const uint8_t *e8m0_qkv, *e8m0_o, *e8m0_up, *e8m0_down;
+    const float *s_qkv, *s_o, *s_up, *s_down;
+    const float *b_qkv, *b_o, *b_up, *b_down;
+    const float* act_scale;
+    float ln_eps;
+} qvd_block_params;
+
+/* Workspace of dit_block_forward for L tokens. */
+size_t qvd_block_ws_bytes(const qvd_block_params* p, int32_t L);
+/* x: bf16 [L][d], read and overwritten with the block output.  mod: fp32 [6][d] of this block at
+ * this timestep (qvd_adaln_project).  kv_idx/kv_cnt/kmax: the block's sparse mask as in
+ * sparse_attn. */
+int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
+                      const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * MXFP4 weights and static-scale calibration -- farwalk post 6/8 (calibrated 4-bit layers).
+ * qvd_quant_mxfp4: bf16 [N][K] -> packed E2M1 [N][K/2] + E8M0 [N][K/32], per 32 consecutive K:
+ *   X = 2^(floor(log2 amax) - 2) (all-zero block: X = 1), element = E2M1(w / X), RNE, saturating
+ *   at 6.  K must be a multiple of 32.
+ * qvd_amax_update: *amax = max(*amax, max|x|) over n fp32 values (running calibration amax; the
+ *   caller zeroes *amax once before the first batch).
+ * qvd_clip_count: *count += #{ |x| > s*448 } (exact comparison in float64) over n fp32 values,
+ *   s = *scale; *count is a device uint64 the caller zeroes. */
+int qvd_quant_mxfp4(const uint16_t* w, int32_t N, int32_t K, uint8_t* packed, uint8_t* e8m0,
+                    void* stream);
+int qvd_amax_update(const float* x, int64_t n, float* amax, void* stream);
+int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QVD_H */

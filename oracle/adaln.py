@@ -11,7 +11,8 @@ Readings of what the pages leave open:
   vectors are handed on as fp32;
 * the six vectors, in order: shift1, scale1, gate1 (attention branch), shift2, scale2, gate2 (MLP);
 * modulate: LayerNorm over d without affine parameters, biased variance, eps passed as an fp32;
-  y = LN(x) * (1 + scale) + shift, rounded once to fp32 and quantized per tensor to E4M3.
+  y = ((x - mean) * (1/sqrt(var + eps))) * (1 + scale) + shift in float64, rounded once to fp32
+  and quantized per tensor to E4M3.
 """
 from __future__ import annotations
 
@@ -55,7 +56,8 @@ def layernorm_modulate(x_bits, mod_f32, half: int, eps: float) -> np.ndarray:
     mu = x.mean(axis=1, keepdims=True)
     var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
     eps64 = float(np.float32(eps))
-    y = (x - mu) / np.sqrt(var + eps64) * (1.0 + scale) + shift
+    rstd = 1.0 / np.sqrt(var + eps64)
+    y = ((x - mu) * rstd) * (1.0 + scale) + shift
     return f64_to_f32(y)
 
 

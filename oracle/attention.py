@@ -8,11 +8,17 @@ Plain definition, per head h and 128-row query tile i:
   keys(h, i)  = the rows of the kept key tiles kv_idx[h][i][:kv_cnt[h][i]] that exist (< L);
   S[r][c]     = sum_e q[r][h][e] * k[c][h][e]                      (exact integer)
   s[r][c]     = S[r][c] * q_scale[h][i] * k_scale[h][tile(c)] * sm_scale
-  p[r][:]     = softmax over keys(h, i) of s[r][:]                  (row max subtracted)
-  out[r][h][:] = sum_c p[r][c] * v[c][h][:]                         (v is bf16)
+  e[r][c]     = fp16(exp(s[r][c] - max_c' s[r][c']))                (softmax numerator, row max
+                                                                       over every kept key)
+  out[r][h][:] = sum_c e[r][c] * fp16(v[c][h][:]) / sum_c e[r][c]
 Readings: a key tile not in the list weighs zero (it is skipped, not attended with -inf after the
 fact); key rows >= L do not exist; sm_scale = 1/sqrt(head_dim) with the natural exponential.  The
-pages give no precision for softmax.V, so the definition is taken exactly in float64.
+pages give no precision for softmax.V; the reading taken is that the softmax numerators, taken
+against the row maximum, are rounded once to fp16 (round to nearest even) and that V enters the
+product as fp16 (bf16 values convert exactly between 2^-14 and 65,504; larger magnitudes saturate
+at 65,504); the products, sums and the normalisation by the sum of the rounded numerators are
+exact (float64).  Without the rounding of the numerators this is the exact softmax attention;
+each rounded weight is within a relative 2^-11 of the exact one.
 """
 from __future__ import annotations
 
@@ -21,6 +27,13 @@ import numpy as np
 from .codecs import bf16_to_f64
 
 TILE = 128
+F16_MAX = 65504.0
+
+
+def f16_round(x) -> np.ndarray:
+    """float64 -> nearest fp16 value (ties to even, fp16 subnormals kept), as float64.
+    numpy's float64 -> float16 cast rounds once, directly from the float64 value."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
 def kept_keys(kv_idx, kv_cnt, h: int, i: int, L: int) -> tuple[np.ndarray, np.ndarray]:
@@ -44,11 +57,9 @@ def sparse_attn_tile(q, q_scale, k, k_scale, v_bits, kv_idx, kv_cnt, h: int, i: 
     fac = (np.float64(q_scale[h, i]) * np.asarray(k_scale[h], dtype=np.float64)[key_tile]
            * sm_scale)
     s = S * fac[None, :]
-    s = s - s.max(axis=1, keepdims=True)
-    p = np.exp(s)
-    p = p / p.sum(axis=1, keepdims=True)
-    V = bf16_to_f64(v_bits[keys, h, :])
-    return p @ V
+    e = f16_round(np.exp(s - s.max(axis=1, keepdims=True)))
+    V = f16_round(np.clip(bf16_to_f64(v_bits[keys, h, :]), -F16_MAX, F16_MAX))
+    return (e @ V) / e.sum(axis=1, keepdims=True)
 
 
 def sparse_attn(q, q_scale, k, k_scale, v_bits, kv_idx, kv_cnt, sm_scale=None,

@@ -1,0 +1,327 @@
+// AdaLN timestep conditioning: the shared-basis projection and the modulated LayerNorm that feeds
+// the per-tensor FP8 GEMMs.
+//
+// comfyui-wiki "FastH3 Trim：为 8 GB GPU 打造的剪枝版 8 步 MiniMax H3", section "Trim 改变了什么",
+// timestep-conditioning bullet: the time embedding (2,688 wide) is mapped to six modulation vectors
+// per block through a 2,688->16 basis shared by all blocks and a small per-block projection, both
+// stored in fp16.
+//
+// The LayerNorm statistics and the affine map run in float64 and round once to fp32, so the FP8
+// codes do not depend on the summation order of the row statistics (the fp64 sum of bf16 values is
+// exact at these widths).  The kernel is bound by HBM traffic: one wave owns a row, keeps it in
+// registers, and stores its codes as 16-bit pairs.
+#include "common.h"
+#include "kernels.h"
+
+namespace qvd {
+
+constexpr int RANK = 16;
+
+QVD_DEV double fp16_to_f64(uint16_t b) { return (double)__builtin_bit_cast(_Float16, b); }
+
+// ---------------------------------------------------------------------------------------------
+// projection: every workgroup recomputes c = B e(t) (16 x dt MACs, float64) and then produces 256
+// entries of its block's modulation table.
+
+__global__ void __launch_bounds__(256) k_adaln_project(float t, const uint16_t* __restrict__ basis,
+                                                       int dt, const uint16_t* __restrict__ proj,
+                                                       const uint16_t* __restrict__ bias, int d,
+                                                       float* __restrict__ mod) {
+    __shared__ double red[4][RANK];
+    __shared__ double c[RANK];
+    const int half = dt / 2;
+    const double ln1e4 = 9.210340371976184;        // ln(10000), correctly rounded
+    double acc[RANK];
+#pragma unroll
+    for (int r = 0; r < RANK; ++r) acc[r] = 0.0;
+    for (int i = threadIdx.x; i < dt; i += 256) {
+        const int fi = i < half ? i : i - half;
+        const double f = exp((-ln1e4 * (double)fi) / (double)half);
+        const double arg = (double)t * f;
+        const double e = i < half ? cos(arg) : sin(arg);
+#pragma unroll
+        for (int r = 0; r < RANK; ++r) {
+            const double b = fp16_to_f64(basis[r * dt + i]);
+            acc[r] = fma(b, e, acc[r]);
+        }
+    }
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int r = 0; r < RANK; ++r) {
+        const double s = wave_sum_f64(acc[r]);
+        if ((threadIdx.x & 63) == 0) red[w][r] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < RANK)
+        c[threadIdx.x] = (red[0][threadIdx.x] + red[1][threadIdx.x]) +
+                         (red[2][threadIdx.x] + red[3][threadIdx.x]);
+    __syncthreads();
+    const int blk = blockIdx.y;
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= 6 * d) return;
+    const uint16_t* P = proj + ((int64_t)blk * 6 * d + o) * RANK;
+    double m = 0.0;
+#pragma unroll
+    for (int r = 0; r < RANK; ++r) m = fma(fp16_to_f64(P[r]), c[r], m);
+    if (bias) m += fp16_to_f64(bias[(int64_t)blk * 6 * d + o]);
+    mod[(int64_t)blk * 6 * d + o] = (float)m;
+}
+
+// ---------------------------------------------------------------------------------------------
+// modulated LayerNorm.  NW = d/128 32-bit words (bf16 pairs) per lane; lane l owns words
+// l + 64 j, i.e. columns 2(l + 64 j) and 2(l + 64 j) + 1.
+
+template <int NW>
+struct RowRegs {
+    u32 x[NW];
+    float sh[2 * NW], op[2 * NW];   // shift and (1 + scale) source (fp32 scale)
+};
+
+template <int NW>
+QVD_DEV void load_mod(RowRegs<NW>& R, const float* __restrict__ mod, int half, int d, int lane, int nw) {
+    const float* shift = mod + (3 * half) * d;
+    const float* scale = mod + (3 * half + 1) * d;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        if (j < nw) {
+            const int col = 2 * (lane + 64 * j);
+            const float2 a = *reinterpret_cast<const float2*>(shift + col);
+            const float2 b = *reinterpret_cast<const float2*>(scale + col);
+            R.sh[2 * j] = a.x;
+            R.sh[2 * j + 1] = a.y;
+            R.op[2 * j] = b.x;
+            R.op[2 * j + 1] = b.y;
+        }
+    }
+}
+
+// mean and 1/sqrt(var + eps) of one row (float64), all lanes get the result
+template <int NW>
+QVD_DEV void row_stats(const RowRegs<NW>& R, int nw, int d, double eps, double& mu, double& rstd) {
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+        if (j < nw) s += (double)bf16lo(R.x[j]) + (double)bf16hi(R.x[j]);
+    mu = wave_sum_f64(s) / (double)d;
+    double v = 0.0;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        if (j < nw) {
+            const double a = (double)bf16lo(R.x[j]) - mu;
+            const double b = (double)bf16hi(R.x[j]) - mu;
+            v = fma(a, a, v);
+            v = fma(b, b, v);
+        }
+    }
+    const double var = wave_sum_f64(v) / (double)d;
+    rstd = 1.0 / sqrt(var + eps);
+}
+
+// y = fp32(((x - mu) * rstd) * (1 + scale) + shift), each float64 operation rounded separately
+QVD_DEV float modulate_one(float x, double mu, double rstd, float scale, float shift) {
+#pragma clang fp contract(off)
+    const double t = ((double)x - mu) * rstd;
+    const double y = t * (1.0 + (double)scale) + (double)shift;
+    return (float)y;
+}
+
+// pass 1 (dynamic scales): row statistics to ws, per-workgroup max |y| to partials
+template <int NW>
+__global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x, int L, int d,
+                                                  const float* __restrict__ mod, int half, float eps,
+                                                  double2* __restrict__ stats,
+                                                  float* __restrict__ partials) {
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int nw = d >> 7;
+    RowRegs<NW> R;
+    load_mod<NW>(R, mod, half, d, lane, nw);
+    float m = 0.0f;
+    for (int row = blockIdx.x * 4 + wv; row < L; row += gridDim.x * 4) {
+        const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)row * d);
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            if (j < nw) R.x[j] = __builtin_nontemporal_load(xr + lane + 64 * j);
+        double mu, rstd;
+        row_stats<NW>(R, nw, d, (double)eps, mu, rstd);
+        if (lane == 0) stats[row] = make_double2(mu, rstd);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if (j < nw) {
+                m = fmaxf(m, fabsf(modulate_one(bf16lo(R.x[j]), mu, rstd, R.op[2 * j], R.sh[2 * j])));
+                m = fmaxf(m, fabsf(modulate_one(bf16hi(R.x[j]), mu, rstd, R.op[2 * j + 1],
+                                                R.sh[2 * j + 1])));
+            }
+        }
+    }
+    m = block_max_nonneg<4>(m, red);
+    if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// pass 2: codes.  Dynamic: stats from pass 1 and the amax of the partials; static: stats computed
+// here and the scale read from scale_in.
+template <int NW>
+__global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x, int L, int d,
+                                                  const float* __restrict__ mod, int half, float eps,
+                                                  const double2* __restrict__ stats,
+                                                  const float* __restrict__ partials, int np,
+                                                  const float* __restrict__ scale_in,
+                                                  uint8_t* __restrict__ q,
+                                                  float* __restrict__ scale_out) {
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int nw = d >> 7;
+    float s, inv;
+    if (scale_in) {
+        s = *scale_in;
+        inv = __fdiv_rn(1.0f, s);
+    } else {
+        float a = 0.0f;
+        for (int i = threadIdx.x; i < np; i += 256) a = fmaxf(a, partials[i]);
+        a = block_max_nonneg<4>(a, red);
+        if (a == 0.0f) {
+            s = 1.0f;
+            inv = 1.0f;
+        } else {
+            s = __fdiv_rn(a, 448.0f);
+            inv = __fdiv_rn(448.0f, a);
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+    RowRegs<NW> R;
+    load_mod<NW>(R, mod, half, d, lane, nw);
+    for (int row = blockIdx.x * 4 + wv; row < L; row += gridDim.x * 4) {
+        const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)row * d);
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            if (j < nw) R.x[j] = __builtin_nontemporal_load(xr + lane + 64 * j);
+        double mu, rstd;
+        if (scale_in) {
+            row_stats<NW>(R, nw, d, (double)eps, mu, rstd);
+        } else {
+            const double2 st = stats[row];
+            mu = st.x;
+            rstd = st.y;
+        }
+        uint16_t* qr = reinterpret_cast<uint16_t*>(q + (int64_t)row * d);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if (j < nw) {
+                const float y0 = modulate_one(bf16lo(R.x[j]), mu, rstd, R.op[2 * j], R.sh[2 * j]);
+                const float y1 = modulate_one(bf16hi(R.x[j]), mu, rstd, R.op[2 * j + 1], R.sh[2 * j + 1]);
+                qr[lane + 64 * j] = (uint16_t)(e4m3_encode(y0 * inv) | (e4m3_encode(y1 * inv) << 8));
+            }
+        }
+    }
+}
+
+constexpr int LN_GRID_STATS = 1024;
+
+size_t adaln_ws_bytes(int L, int d) {
+    (void)d;
+    return (size_t)L * sizeof(double2) + LN_GRID_STATS * sizeof(float) + 256;
+}
+
+template <int NW>
+static int launch_modulate_nw(const uint16_t* x, int L, int d, const float* mod, int half, float eps,
+                              const float* scale_in, uint8_t* q, float* scale_out, void* ws,
+                              hipStream_t st) {
+    double2* stats = (double2*)ws;
+    float* partials = (float*)((char*)ws + (((size_t)L * sizeof(double2) + 255) & ~(size_t)255));
+    int np = 0;
+    const int rows_per_pass = 4;
+    if (!scale_in) {
+        int g = (L + rows_per_pass - 1) / rows_per_pass;
+        g = g < 1 ? 1 : (g > LN_GRID_STATS ? LN_GRID_STATS : g);
+        hipLaunchKernelGGL(k_ln_stats<NW>, dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, stats,
+                           partials);
+        np = g;
+        int s = launch_status("adaln_modulate stats");
+        if (s) return s;
+    }
+    int g = (L + rows_per_pass - 1) / rows_per_pass;
+    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+    hipLaunchKernelGGL(k_ln_quant<NW>, dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, stats,
+                       partials, np, scale_in, q, scale_out);
+    return launch_status("adaln_modulate quant");
+}
+
+int launch_modulate(const uint16_t* x, int L, int d, const float* mod, int half, float eps,
+                    const float* scale_in, uint8_t* q, float* scale_out, void* ws, hipStream_t st) {
+    switch (d >> 7) {
+        case 2: return launch_modulate_nw<2>(x, L, d, mod, half, eps, scale_in, q, scale_out, ws, st);
+        case 21: return launch_modulate_nw<21>(x, L, d, mod, half, eps, scale_in, q, scale_out, ws, st);
+        default:
+            if ((d >> 7) <= 8)
+                return launch_modulate_nw<8>(x, L, d, mod, half, eps, scale_in, q, scale_out, ws, st);
+            return launch_modulate_nw<32>(x, L, d, mod, half, eps, scale_in, q, scale_out, ws, st);
+    }
+}
+
+int launch_adaln_project(float t, const uint16_t* basis, int dt, const uint16_t* proj,
+                         const uint16_t* bias, int d, int nb, float* mod, hipStream_t st) {
+    hipLaunchKernelGGL(k_adaln_project, dim3((6 * d + 255) / 256, nb), dim3(256), 0, st, t, basis, dt,
+                       proj, bias, d, mod);
+    return launch_status("adaln_project");
+}
+
+}  // namespace qvd
+
+using namespace qvd;
+
+extern "C" {
+
+int qvd_adaln_project_stack(float t, const uint16_t* basis, int32_t dt, const uint16_t* proj,
+                            const uint16_t* bias, int32_t d, int32_t n_blocks, float* mod,
+                            void* stream) {
+    QVD_REQUIRE(dt >= 2 && dt % 2 == 0 && dt <= 16384, QVD_ESHAPE,
+                "qvd_adaln_project: dt = %d (even, 2..16384)", dt);
+    QVD_REQUIRE(d >= 128 && d % 128 == 0 && d <= 65536, QVD_ESHAPE,
+                "qvd_adaln_project: d = %d (multiple of 128)", d);
+    QVD_REQUIRE(n_blocks >= 1 && n_blocks <= 65535, QVD_ESHAPE, "qvd_adaln_project: n_blocks = %d",
+                n_blocks);
+    QVD_REQUIRE(t == t, QVD_EINVAL, "qvd_adaln_project: t is NaN");
+    QVD_PTR(basis);
+    QVD_PTR(proj);
+    QVD_PTR(mod);
+    QVD_ALIGN(mod);
+    QVD_DEVICE_OK();
+    return launch_adaln_project(t, basis, dt, proj, bias, d, n_blocks, mod, (hipStream_t)stream);
+}
+
+int qvd_adaln_project(float t, const uint16_t* basis, int32_t dt, const uint16_t* proj,
+                      const uint16_t* bias, int32_t d, float* mod, void* stream) {
+    return qvd_adaln_project_stack(t, basis, dt, proj, bias, d, 1, mod, stream);
+}
+
+size_t qvd_adaln_modulate_ws_bytes(int32_t L, int32_t d) {
+    return L < 0 ? 0 : adaln_ws_bytes(L, d);
+}
+
+int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                   float eps, const float* act_scale_in, uint8_t* q, float* act_scale_out,
+                   void* ws, size_t ws_bytes, void* stream) {
+    QVD_REQUIRE(L >= 0, QVD_ESHAPE, "adaln_modulate: L = %d", L);
+    QVD_REQUIRE(d >= 128 && d % 128 == 0 && d <= 4096, QVD_ESHAPE,
+                "adaln_modulate: d = %d (multiple of 128, at most 4096)", d);
+    QVD_REQUIRE(half == 0 || half == 1, QVD_EINVAL, "adaln_modulate: half = %d (0 or 1)", half);
+    QVD_REQUIRE(eps >= 0.0f, QVD_EINVAL, "adaln_modulate: eps < 0");
+    QVD_PTR(mod);
+    QVD_PTR(act_scale_out);
+    QVD_ALIGN(mod);
+    if (L > 0) {
+        QVD_PTR(x);
+        QVD_PTR(q);
+        QVD_ALIGN(x);
+        QVD_ALIGN(q);
+    }
+    QVD_PTR(ws);
+    QVD_ALIGN(ws);
+    QVD_REQUIRE(ws_bytes >= adaln_ws_bytes(L, d), QVD_EWORKSPACE,
+                "adaln_modulate: workspace %zu < %zu bytes", ws_bytes, adaln_ws_bytes(L, d));
+    QVD_DEVICE_OK();
+    return launch_modulate(x, L, d, mod, half, eps, act_scale_in, q, act_scale_out, ws,
+                           (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// One DiT block forward: host-side orchestration of the kernels on one stream, with the caller's
+// workspace carved into the block's intermediate tensors.
+//
+// The block (a pre-norm adaLN-Zero DiT block; the pages name its parts, not its wiring):
+//   comfyui-wiki "FastH3 Trim：为 8 GB GPU 打造的剪枝版 8 步 MiniMax H3": section "Trim 改变了什么"
+//   (a transformer that denoises the video and audio latents together; six AdaLN modulation
+//   vectors per block; 80% attention sparsity) and section "运行速度如何", note under the table
+//   (per-tensor FP8 linear layers with the scales applied to the output; INT8 query/key).
+//
+//   adaln_modulate(x, shift1, scale1)             -> h (E4M3) + s_h
+//   GEMM h . W_qkv^T, epilogue: bf16 Q|K|V, INT8 Q/K per (head, 128-token tile)
+//   sparse_attn                                   -> O (bf16) + per-tile max|O|
+//   per-tensor FP8 of O (amax from those partials) -> O8
+//   GEMM O8 . W_o^T, epilogue: x += gate1 * y      (in place)
+//   adaln_modulate(x, shift2, scale2)             -> h
+//   GEMM h . W_up^T, epilogue: g = bf16(GELU(y)) + per-tile max|g|
+//   per-tensor FP8 of g                           -> g8
+//   GEMM g8 . W_down^T, epilogue: x += gate2 * y   (in place)
+// Dynamic scales never leave the device: every amax is reduced from per-workgroup partial maxima
+// written by the producing kernel.
+#include "common.h"
+#include "kernels.h"
+
+namespace qvd {
+
+namespace {
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct BlockWs {
+    uint8_t* h;          // E4M3 [L][d]: modulated LN output, then the FP8 attention output
+    int8_t* q8;          // [L][d]
+    int8_t* k8;          // [L][d]
+    uint16_t* v;         // bf16 [L][d]
+    uint16_t* o;         // bf16 [L][d]
+    uint16_t* g;         // bf16 [L][F]
+    uint8_t* g8;         // E4M3 [L][F]
+    float* qs;           // [H][T]
+    float* ks;           // [H][T]
+    float* attn_part;    // [H][T]
+    float* gelu_part;    // [tiles of the up GEMM]
+    float* scales;       // [4]: s_h1, s_o, s_h2, s_g
+    void* ln_ws;         // adaln_modulate workspace
+    size_t total;
+};
+
+BlockWs carve(const qvd_block_params* p, int L, uint8_t* base) {
+    const size_t Ld = (size_t)L * p->d, LF = (size_t)L * p->mlp;
+    const int T = (L + 127) / 128;
+    const size_t HT = (size_t)p->n_heads * T;
+    BlockWs w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        uint8_t* ptr = base ? base + off : nullptr;
+        off += align256(bytes);
+        return ptr;
+    };
+    w.h = take(Ld);
+    w.q8 = (int8_t*)take(Ld);
+    w.k8 = (int8_t*)take(Ld);
+    w.v = (uint16_t*)take(2 * Ld);
+    w.o = (uint16_t*)take(2 * Ld);
+    w.g = (uint16_t*)take(2 * LF);
+    w.g8 = take(LF);
+    w.qs = (float*)take(4 * HT);
+    w.ks = (float*)take(4 * HT);
+    w.attn_part = (float*)take(4 * HT);
+    w.gelu_part = (float*)take(4 * (size_t)gemm_tiles(L, p->mlp));
+    w.scales = (float*)take(4 * 4);
+    w.ln_ws = take(adaln_ws_bytes(L, p->d));
+    w.total = off;
+    return w;
+}
+
+int validate(const qvd_block_params* p, int L) {
+    QVD_PTR(p);
+    QVD_REQUIRE(p->version == QVD_ABI_VERSION, QVD_EINVAL, "qvd_block_params.version = %d, expected %d",
+                p->version, QVD_ABI_VERSION);
+    QVD_REQUIRE(p->head_dim == 128, QVD_ESHAPE, "block: head_dim = %d (must be 128)", p->head_dim);
+    QVD_REQUIRE(p->n_heads >= 1 && p->d == 128 * p->n_heads, QVD_ESHAPE,
+                "block: d = %d must equal 128 * n_heads (n_heads = %d)", p->d, p->n_heads);
+    QVD_REQUIRE(p->d <= 4096, QVD_ESHAPE, "block: d = %d (at most 4096)", p->d);
+    QVD_REQUIRE(p->mlp >= 128 && p->mlp % 256 == 0, QVD_ESHAPE,
+                "block: mlp = %d (positive multiple of 256)", p->mlp);
+    QVD_REQUIRE(L >= 0, QVD_ESHAPE, "block: L = %d", L);
+    QVD_REQUIRE(p->weight_format == QVD_W_FP8 || p->weight_format == QVD_W_MXFP4, QVD_EINVAL,
+                "block: weight_format = %d", p->weight_format);
+    QVD_REQUIRE(p->ln_eps >= 0.0f, QVD_EINVAL, "block: ln_eps < 0");
+    QVD_PTR(p->w_qkv);
+    QVD_PTR(p->w_o);
+    QVD_PTR(p->w_up);
+    QVD_PTR(p->w_down);
+    QVD_ALIGN(p->w_qkv);
+    QVD_ALIGN(p->w_o);
+    QVD_ALIGN(p->w_up);
+    QVD_ALIGN(p->w_down);
+    if (p->weight_format == QVD_W_FP8) {
+        QVD_PTR(p->s_qkv);
+        QVD_PTR(p->s_o);
+        QVD_PTR(p->s_up);
+        QVD_PTR(p->s_down);
+    } else {
+        QVD_PTR(p->e8m0_qkv);
+        QVD_PTR(p->e8m0_o);
+        QVD_PTR(p->e8m0_up);
+        QVD_PTR(p->e8m0_down);
+        QVD_REQUIRE(p->act_scale != nullptr, QVD_EINVAL,
+                    "block: MXFP4 weights need static activation scales (act_scale)");
+    }
+    const float* b[4] = {p->b_qkv, p->b_o, p->b_up, p->b_down};
+    for (int i = 0; i < 4; ++i)
+        if (b[i]) QVD_ALIGN(b[i]);
+    return QVD_OK;
+}
+
+}  // namespace
+
+}  // namespace qvd
+
+using namespace qvd;
+
+extern "C" {
+
+size_t qvd_block_ws_bytes(const qvd_block_params* p, int32_t L) {
+    if (!p || L < 0 || p->d <= 0 || p->mlp <= 0 || p->n_heads <= 0) return 0;
+    return carve(p, L, nullptr).total;
+}
+
+int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
+                      const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, void* ws,
+                      size_t ws_bytes, void* stream) {
+    int s = validate(p, L);
+    if (s) return s;
+    if (L == 0) return QVD_OK;
+    QVD_PTR(mod);
+    QVD_PTR(x);
+    QVD_PTR(kv_idx);
+    QVD_PTR(kv_cnt);
+    QVD_PTR(ws);
+    QVD_ALIGN(mod);
+    QVD_ALIGN(x);
+    QVD_ALIGN(ws);
+    QVD_REQUIRE(kmax >= 1, QVD_ESHAPE, "dit_block_forward: kmax = %d", kmax);
+    const size_t need = qvd_block_ws_bytes(p, L);
+    QVD_REQUIRE(ws_bytes >= need, QVD_EWORKSPACE, "dit_block_forward: workspace %zu < %zu bytes",
+                ws_bytes, need);
+    QVD_DEVICE_OK();
+
+    hipStream_t st = (hipStream_t)stream;
+    const BlockWs w = carve(p, L, (uint8_t*)ws);
+    const int d = p->d, F = p->mlp, H = p->n_heads;
+    const int T = (L + 127) / 128;
+    const int fmt = p->weight_format;
+    const float* act = p->act_scale;           // NULL: dynamic
+    const float* shift_scale_gate = mod;       // [6][d]
+    const float sm_scale = 0.08838834764831845f;   // 1/sqrt(128)
+
+    // attention branch
+    s = launch_modulate(x, L, d, mod, 0, p->ln_eps, act ? act + 0 : nullptr, w.h, w.scales + 0, w.ln_ws, st);
+    if (s) return s;
+    qvd_epilogue e{};
+    e.mode = QVD_EPI_QKV;
+    e.n_heads = H;
+    e.q8 = w.q8;
+    e.k8 = w.k8;
+    e.v = w.v;
+    e.q_scale = w.qs;
+    e.k_scale = w.ks;
+    s = launch_gemm(w.h, w.scales + 0, p->w_qkv, p->e8m0_qkv, p->s_qkv, fmt, p->b_qkv, L, 3 * d, d, e, st);
+    if (s) return s;
+    s = launch_sparse_attn(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.o,
+                           act ? nullptr : w.attn_part, st);
+    if (s) return s;
+    s = launch_quant_fp8(w.o, (int64_t)L * d, act ? act + 1 : nullptr, w.attn_part, H * T, w.h,
+                         w.scales + 1, st);
+    if (s) return s;
+    e = qvd_epilogue{};
+    e.mode = QVD_EPI_RESID_GATE;
+    e.out_bf16 = x;
+    e.resid = x;
+    e.gate = shift_scale_gate + 2 * d;
+    s = launch_gemm(w.h, w.scales + 1, p->w_o, p->e8m0_o, p->s_o, fmt, p->b_o, L, d, d, e, st);
+    if (s) return s;
+
+    // MLP branch
+    s = launch_modulate(x, L, d, mod, 1, p->ln_eps, act ? act + 2 : nullptr, w.h, w.scales + 2, w.ln_ws, st);
+    if (s) return s;
+    e = qvd_epilogue{};
+    e.mode = QVD_EPI_GELU;
+    e.out_bf16 = w.g;
+    e.amax_partials = act ? nullptr : w.gelu_part;
+    s = launch_gemm(w.h, w.scales + 2, p->w_up, p->e8m0_up, p->s_up, fmt, p->b_up, L, F, d, e, st);
+    if (s) return s;
+    s = launch_quant_fp8(w.g, (int64_t)L * F, act ? act + 3 : nullptr, w.gelu_part,
+                         (int)gemm_tiles(L, F), w.g8, w.scales + 3, st);
+    if (s) return s;
+    e = qvd_epilogue{};
+    e.mode = QVD_EPI_RESID_GATE;
+    e.out_bf16 = x;
+    e.resid = x;
+    e.gate = shift_scale_gate + 5 * d;
+    return launch_gemm(w.g8, w.scales + 3, p->w_down, p->e8m0_down, p->s_down, fmt, p->b_down, L, d, F,
+                       e, st);
+}
+
+}  // extern "C"

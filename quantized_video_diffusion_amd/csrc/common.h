@@ -1,0 +1,129 @@
+// Shared device helpers and host-side argument checking for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/qvd.h"
+
+// ---------------------------------------------------------------------------------------------
+// vector types for MFMA operands
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned int u32;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define QVD_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------------------------------------
+// bf16
+
+QVD_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((u32)b) << 16); }
+QVD_DEV float bf16lo(u32 w) { return __uint_as_float(w << 16); }
+QVD_DEV float bf16hi(u32 w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+QVD_DEV u32 pack_bf16x2(float lo, float hi) {
+    v2bf r;
+    r.x = (__bf16)lo;
+    r.y = (__bf16)hi;
+    return __builtin_bit_cast(u32, r);
+}
+QVD_DEV uint16_t f32_to_bf16(float x) { return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu); }
+
+// ---------------------------------------------------------------------------------------------
+// E4M3 ("FN") encoding, round to nearest even, saturating at 448, NaN -> 0x7F.  Written from the
+// format definition: a normal value keeps 3 fraction bits of the fp32 significand (rounding added
+// at bit 19 with the tie going to the even result), exponent rebased from 127 to 7; below 2^-6
+// the code is the count of 2^-9 quanta.
+QVD_DEV u32 e4m3_encode(float v) {
+    const u32 u = __float_as_uint(v);
+    const u32 sign = (u >> 24) & 0x80u;
+    const u32 a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;                   // NaN
+    const float af = __uint_as_float(a);
+    u32 code;
+    if (af >= 448.0f) {
+        code = 0x7Eu;
+    } else if (af < 0.015625f) {                          // 2^-6
+        code = (u32)__builtin_rintf(af * 512.0f);         // exact scaling, RNE: 0 .. 8
+    } else {
+        const u32 r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);
+        code = code > 0x7Eu ? 0x7Eu : code;
+    }
+    return code | sign;
+}
+
+QVD_DEV int int8_encode(float x, float inv) {
+    float p = x * inv;                                     // one fp32 product (no contraction)
+    float r = __builtin_rintf(p);
+    r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+    return (int)r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// wave / block reductions (wave64)
+
+QVD_DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+QVD_DEV double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// max of non-negative floats over the block; every thread gets the result.  `red` holds one
+// float per wave.
+template <int NWAVES>
+QVD_DEV float block_max_nonneg(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < NWAVES; ++i) m = fmaxf(m, red[i]);
+    return m;
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side
+
+namespace qvd {
+
+void set_error(const char* fmt, ...);
+int fail(int status, const char* fmt, ...);
+int check_device();                       // gfx950 check, cached per device
+int launch_status(const char* what);      // hipGetLastError after a launch -> QVD_OK / QVD_EHIP
+
+inline bool aligned16(const void* p) { return (((uintptr_t)p) & 15u) == 0; }
+
+}  // namespace qvd
+
+#define QVD_REQUIRE(cond, status, ...)                              \
+    do {                                                            \
+        if (!(cond)) return qvd::fail((status), __VA_ARGS__);       \
+    } while (0)
+
+#define QVD_PTR(p) QVD_REQUIRE((p) != nullptr, QVD_EINVAL, "%s: %s is NULL", __func__, #p)
+#define QVD_ALIGN(p) \
+    QVD_REQUIRE(qvd::aligned16(p), QVD_EALIGN, "%s: %s is not 16-byte aligned", __func__, #p)
+#define QVD_DEVICE_OK()                              \
+    do {                                             \
+        int _s = qvd::check_device();                \
+        if (_s != QVD_OK) return _s;                 \
+    } while (0)

@@ -1,0 +1,31 @@
+// Internal launchers shared between the translation units of the library (not part of the ABI).
+#pragma once
+
+#include "common.h"
+
+namespace qvd {
+
+constexpr int AMAX_PARTIALS_MAX = 1024;
+
+int launch_amax_bf16(const uint16_t* x, int64_t n, float* partials, int* np_out, hipStream_t st);
+int launch_quant_fp8(const uint16_t* x, int64_t n, const float* scale_in, const float* partials,
+                     int np, uint8_t* q, float* scale_out, hipStream_t st);
+
+size_t adaln_ws_bytes(int L, int d);
+int launch_modulate(const uint16_t* x, int L, int d, const float* mod, int half, float eps,
+                    const float* scale_in, uint8_t* q, float* scale_out, void* ws, hipStream_t st);
+int launch_adaln_project(float t, const uint16_t* basis, int dt, const uint16_t* proj,
+                         const uint16_t* bias, int d, int nb, float* mod, hipStream_t st);
+
+int64_t gemm_tiles(int M, int N);
+// FP8 x FP8 (w_fmt = QVD_W_FP8, s_w per tensor) or E4M3 x MXFP4 (w_fmt = QVD_W_MXFP4, w packed
+// E2M1 [N][K/2], e8 [N][K/32], s_w ignored).
+int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t* e8, const float* s_w,
+                int w_fmt, const float* bias, int M, int N, int K, const qvd_epilogue& epi,
+                hipStream_t st);
+
+int launch_sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
+                       const uint16_t* v, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt,
+                       int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st);
+
+}  // namespace qvd

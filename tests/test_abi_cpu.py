@@ -1,0 +1,119 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function include/qvd.h
+declares, and rejects bad arguments on the host before anything touches a device."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from quantized_video_diffusion_amd import _lib
+
+LIB = _lib.LIB_PATH
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} is not built")
+    return _lib.lib()
+
+
+def test_exports_every_header_function(lib):
+    names = _lib.header_functions()
+    assert len(names) >= 19
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(lib, n)
+    # every declared function has a ctypes signature in the binding
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_abi_version_and_error_string(lib):
+    assert lib.qvd_abi_version() == _lib.ABI_VERSION
+    assert isinstance(lib.qvd_last_error(), bytes)
+
+
+def _status(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+def test_host_validation_errors(lib):
+    P = C.c_void_p
+    fake = P(0x10000)            # never dereferenced: every call below fails validation first
+    mis = P(0x10001)             # misaligned
+    # quant_fp8_per_tensor
+    assert _status(lib, "quant_fp8_per_tensor", fake, -1, None, fake, fake, fake, 4096, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "quant_fp8_per_tensor", fake, 16, None, fake, None, fake, 4096, None) == _lib.QVD_EINVAL
+    assert b"scale_out" in lib.qvd_last_error()
+    assert _status(lib, "quant_fp8_per_tensor", mis, 16, None, fake, fake, fake, 4096, None) == _lib.QVD_EALIGN
+    assert _status(lib, "quant_fp8_per_tensor", fake, 16, None, fake, fake, fake, 16, None) == _lib.QVD_EWORKSPACE
+    # quant_int8_qk
+    assert _status(lib, "quant_int8_qk", fake, 10, 2, 64, 128, 256, fake, fake, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "quant_int8_qk", fake, 10, 2, 128, 128, 100, fake, fake, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "quant_int8_qk", None, 10, 2, 128, 128, 256, fake, fake, None) == _lib.QVD_EINVAL
+    assert _status(lib, "quant_int8_qk", fake, 0, 2, 128, 128, 256, None, None, None) == _lib.QVD_OK
+    # adaln
+    assert _status(lib, "qvd_adaln_project", C.c_float(1.0), fake, 7, fake, None, 256, fake, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "qvd_adaln_project", C.c_float(1.0), fake, 256, fake, None, 200, fake, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "adaln_modulate", fake, 4, 256, fake, 2, C.c_float(1e-6), None, fake, fake,
+                   fake, 1 << 20, None) == _lib.QVD_EINVAL
+    assert _status(lib, "adaln_modulate", fake, 4, 8192, fake, 0, C.c_float(1e-6), None, fake, fake,
+                   fake, 1 << 20, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "adaln_modulate", fake, 4, 256, fake, 0, C.c_float(1e-6), None, fake, fake,
+                   fake, 8, None) == _lib.QVD_EWORKSPACE
+    # sparse_attn
+    assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 300, 2, 64, fake, fake, 3,
+                   C.c_float(0.1), fake, None, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 300, 2, 128, fake, fake, 0,
+                   C.c_float(0.1), fake, None, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 300, 2, 128, None, fake, 3,
+                   C.c_float(0.1), fake, None, None) == _lib.QVD_EINVAL
+    assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 0, 2, 128, None, None, 3,
+                   C.c_float(0.1), None, None, None) == _lib.QVD_OK
+    assert _status(lib, "qvd_qk_int32_tile", fake, fake, 300, 2, 2, 0, 0, fake, None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_qk_int32_tile", fake, fake, 300, 2, 0, 3, 0, fake, None) == _lib.QVD_EINVAL
+    # GEMM
+    e = _lib.Epilogue()
+    e.mode = _lib.QVD_EPI_F32
+    assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 10, 100, 128, C.byref(e), None) == _lib.QVD_ESHAPE
+    assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 10, 128, 128, C.byref(e), None) == _lib.QVD_EINVAL
+    e.mode = 9
+    e.out_f32 = 0x10000
+    assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 10, 128, 128, C.byref(e), None) == _lib.QVD_EINVAL
+    e.mode = _lib.QVD_EPI_QKV
+    e.n_heads = 2
+    assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 10, 512, 128, C.byref(e), None) == _lib.QVD_ESHAPE
+    assert lib.qvd_gemm_tiles(33784, 8064) == 132 * 32
+    # block
+    p = _lib.BlockParams()
+    p.version = 99
+    assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 10, fake, fake, 1, fake, 1, None) == _lib.QVD_EINVAL
+    p.version, p.d, p.n_heads, p.head_dim, p.mlp = 1, 256, 2, 128, 1024
+    for f in ("w_qkv", "w_o", "w_up", "w_down", "s_qkv", "s_o", "s_up", "s_down"):
+        setattr(p, f, 0x10000)
+    assert lib.qvd_block_ws_bytes(C.byref(p), 256) > 0
+    assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 256, fake, fake, 2, fake, 16, None) == _lib.QVD_EWORKSPACE
+    p.weight_format = _lib.QVD_W_MXFP4
+    assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 256, fake, fake, 2, fake, 1 << 40, None) == _lib.QVD_EINVAL
+    p.weight_format = _lib.QVD_W_FP8
+    p.d = 300
+    assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 256, fake, fake, 2, fake, 1 << 40, None) == _lib.QVD_ESHAPE
+    # MXFP4 / calibration
+    assert _status(lib, "qvd_quant_mxfp4", fake, 4, 33, fake, fake, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "qvd_amax_update", fake, -1, fake, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "qvd_clip_count", fake, 5, None, fake, None) == _lib.QVD_EINVAL
+
+
+def test_workspace_sizes_scale_with_tokens(lib):
+    p = _lib.BlockParams()
+    p.version, p.d, p.n_heads, p.head_dim, p.mlp = 1, 2688, 21, 128, 10752
+    a = lib.qvd_block_ws_bytes(C.byref(p), 4096)
+    b = lib.qvd_block_ws_bytes(C.byref(p), 33784)
+    assert b > 8 * a * 0.95
+    # h, q8, k8 (1 B), v, o (2 B) per L*d; g (2 B) + g8 (1 B) per L*F -> at least 7 L d + 3 L F
+    assert b >= 7 * 33784 * 2688 + 3 * 33784 * 10752
+    assert lib.qvd_quant_ws_bytes(10) >= 4 * 1024

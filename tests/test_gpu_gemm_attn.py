@@ -1,0 +1,228 @@
+"""GPU parity of the FP8 / MXFP4 GEMM epilogues and of the block-sparse INT8-QK attention."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import quantized_video_diffusion_amd as Q
+from quantized_video_diffusion_amd import _lib
+from oracle import codecs as OC, quant as OQ, gemm as OG, attention as OAT
+from _gpu_util import (say, bf16_dev, u8_dev, i32_dev, f32_dev, host, host_bits, bf16_f64,
+                       assert_codes_equal_except_ties, assert_close_rms, assert_bf16_close)
+
+pytestmark = pytest.mark.gpu
+
+
+def _codes(M, K, seed, tensor="codes_a"):
+    return W.random_e4m3_codes((M, K), seed=seed, tensor=tensor)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (391, 384, 256), (33, 2688, 2688), (700, 768, 1024)])
+def test_gemm_fp8_f32_epilogue(M, N, K):
+    say("gemm f32", M, N, K)
+    a, w = _codes(M, K, M), _codes(N, K, N, "codes_b")
+    sa, sw = np.float32(0.0123), np.float32(0.37)
+    bias = (np.arange(N) % 7).astype(np.float32) - 3
+    y = host(Q.gemm_fp8(u8_dev(a), f32_dev([sa]), u8_dev(w), f32_dev([sw]), bias=f32_dev(bias)))
+    want = OG.gemm_fp8(a, sa, w, sw, bias)
+    assert_close_rms(y, want, 1e-3, "gemm f32")
+
+
+def test_gemm_fp8_480p_qkv_shape_sampled():
+    """M = 33,784 (ragged last tile), N = 8,064, K = 2,688; 64 sampled rows checked exactly."""
+    M, N, K = W.TOKENS_480P, 3 * 2688, 2688
+    a, w = _codes(M, K, 1), _codes(N, K, 2, "codes_b")
+    sa, sw = np.float32(1e-2), np.float32(2e-3)
+    y = Q.gemm_fp8(u8_dev(a), f32_dev([sa]), u8_dev(w), f32_dev([sw]))
+    rows = np.r_[np.random.default_rng(0).choice(M, 60, replace=False), [0, M - 1, M - 120, M - 248]]
+    got = host(y[torch.from_numpy(rows).cuda()])
+    want = OG.gemm_fp8(a[rows], sa, w, sw)
+    assert_close_rms(got, want, 1e-3, "gemm 480p rows")
+
+
+def test_gemm_bf16_and_resid_gate_epilogues():
+    M, N, K = 300, 512, 384
+    a, w = _codes(M, K, 3), _codes(N, K, 4, "codes_b")
+    sa, sw = np.float32(0.01), np.float32(0.02)
+    yb = Q.gemm_fp8(u8_dev(a), f32_dev([sa]), u8_dev(w), f32_dev([sw]), mode=_lib.QVD_EPI_BF16)
+    want = OG.gemm_fp8(a, sa, w, sw)
+    assert_bf16_close(host_bits(yb), want, 1e-3, "bf16 epilogue")
+    x = W.normal_bf16((M, N), seed=5)
+    gate = np.linspace(-1, 1, N).astype(np.float32)
+    xd = bf16_dev(x)
+    Q.gemm_fp8(u8_dev(a), f32_dev([sa]), u8_dev(w), f32_dev([sw]), mode=_lib.QVD_EPI_RESID_GATE,
+               out=xd, resid=xd, gate=f32_dev(gate))
+    want_r = OC.bf16_to_f64(x) + gate[None, :].astype(np.float64) * want
+    assert_bf16_close(host_bits(xd), want_r, 1e-3, "resid-gate epilogue (in place)")
+
+
+def test_gemm_gelu_epilogue_and_amax_partials():
+    M, N, K = 333, 1024, 256
+    a, w = _codes(M, K, 6), _codes(N, K, 7, "codes_b")
+    sa, sw = np.float32(0.002), np.float32(0.003)
+    parts = torch.zeros(Q.gemm_tiles(M, N), dtype=torch.float32, device="cuda")
+    g = Q.gemm_fp8(u8_dev(a), f32_dev([sa]), u8_dev(w), f32_dev([sw]), mode=_lib.QVD_EPI_GELU,
+                   amax_partials=parts)
+    want = OG.gelu(OG.gemm_fp8(a, sa, w, sw))
+    assert_bf16_close(host_bits(g), want, 1e-3, "gelu epilogue")
+    assert float(host(parts).max()) == float(np.abs(bf16_f64(g)).max())
+
+
+def _realistic_codes(M, N, K, seed):
+    """Activation codes of N(0,1) data and weight codes of Glorot-uniform weights, both through the
+    oracle's per-tensor quantizer (so the accumulators have a realistic dynamic range)."""
+    a, sa = OQ.quant_fp8_bf16(W.normal_bf16((M, K), seed=seed))
+    wt = W.Workload("t", 80, d=K, n_heads=K // 128, mlp=4 * K, L=M, sparse=False, outliers=False)
+    w, sw = OQ.quant_fp8_bf16(W.f32_to_bf16_bits(W.glorot_uniform(N, K, W.rng_for(seed, 80, 0, "w_qkv"))))
+    return a, sa, w, sw
+
+
+@pytest.mark.parametrize("M,H", [(256, 2), (391, 2), (130, 21)])
+def test_gemm_qkv_epilogue(M, H):
+    d = 128 * H
+    N, K = 3 * d, d
+    a, sa, w, sw = _realistic_codes(M, N, K, 8 + H)
+    q8, k8, v, qs, ks = Q.gemm_fp8(u8_dev(a), f32_dev([sa]), u8_dev(w), f32_dev([sw]),
+                                   mode=_lib.QVD_EPI_QKV, n_heads=H)
+    y = OG.gemm_fp8(a, sa, w, sw)
+    ybits = OC.f64_to_bf16(y)
+    assert_bf16_close(host_bits(v).reshape(M, d), y[:, 2 * d:], 1e-3, "V part")
+    for part, (g8, gs) in enumerate(((q8, qs), (k8, ks))):
+        cw, sw_ = OQ.quant_int8_qk(np.ascontiguousarray(ybits[:, part * d:(part + 1) * d]), M, H)
+        # scales: bf16 rounding of the fp32 accumulators can differ at near-ties only
+        np.testing.assert_allclose(host(gs), sw_, rtol=2 ** -7)
+        xv = OC.bf16_to_f64(ybits[:, part * d:(part + 1) * d]).reshape(M, H, 128).astype(np.float32)
+        T = (M + 127) // 128
+        pre = np.empty_like(xv)
+        for h in range(H):
+            for i in range(T):
+                r = slice(i * 128, min(M, (i + 1) * 128))
+                a_ = np.float32(np.abs(xv[r, h]).max())
+                pre[r, h] = xv[r, h] * (np.float32(127) / a_)
+        n = assert_codes_equal_except_ties(host(g8), cw, pre, "int8", max_frac=1e-3,
+                                           name=f"qkv part {part}",
+                                           upstream=y[:, part * d:(part + 1) * d].reshape(M, H, 128))
+        say(f"qkv part {part}: {n} tie flips")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (391, 384, 256), (300, 2688, 2688)])
+def test_gemm_mxfp4_f32_and_bf16(M, N, K):
+    say("gemm mxfp4", M, N, K)
+    a = _codes(M, K, M + 1)
+    wb = W.normal_bf16((N, K), seed=N + K, scale=0.03)
+    pw, ew = OQ.quant_mxfp4_weight(wb)
+    sa = np.float32(0.05)
+    bias = np.linspace(-1, 1, N).astype(np.float32)
+    want = OG.gemm_mxfp4(a, sa, pw, ew, bias)
+    y = host(Q.gemm_mxfp4(u8_dev(a), f32_dev([sa]), u8_dev(pw), u8_dev(ew), bias=f32_dev(bias)))
+    assert_close_rms(y, want, 1e-3, "mxfp4 f32")
+    yb = Q.gemm_mxfp4(u8_dev(a), f32_dev([sa]), u8_dev(pw), u8_dev(ew), bias=f32_dev(bias),
+                      mode=_lib.QVD_EPI_BF16)
+    assert_bf16_close(host_bits(yb), want, 1e-3, "mxfp4 bf16")
+
+
+# --- attention ---------------------------------------------------------------------------------
+
+def _attn_inputs(L, H, seed, sparse, w=None):
+    qb, kb, vb = W.qkv_heads(L, H, seed=seed)
+    wl = W.Workload("t", 90 + H, d=128 * H, n_heads=H, mlp=512 * H, L=L, sparse=sparse,
+                    outliers=False) if w is None else w
+    idx, cnt = W.block_mask(wl, seed=seed, L=L)
+    return qb, kb, vb, idx, cnt
+
+
+def _quantize_both(qb, kb, L, H):
+    q8, qs = Q.quant_int8_qk(bf16_dev(qb.reshape(L, H * 128)), H)
+    k8, ks = Q.quant_int8_qk(bf16_dev(kb.reshape(L, H * 128)), H)
+    oq, oqs = OQ.quant_int8_qk(qb, L, H)
+    ok, oks = OQ.quant_int8_qk(kb, L, H)
+    np.testing.assert_array_equal(host(q8), oq)       # identical inputs to both attentions
+    np.testing.assert_array_equal(host(k8), ok)
+    return (q8, qs, k8, ks), (oq, oqs, ok, oks)
+
+
+@pytest.mark.parametrize("L,i,j", [(256, 0, 1), (391, 3, 3), (391, 1, 3), (1000, 7, 2)])
+def test_qk_int32_accumulators_bit_exact(L, i, j):
+    H = 2
+    qb, kb, _, _, _ = _attn_inputs(L, H, 3, False)
+    (q8, _, k8, _), (oq, _, ok, _) = _quantize_both(qb, kb, L, H)
+    for h in range(H):
+        got = host(Q.qk_int32_tile(q8, k8, h, i, j))
+        want = np.zeros((128, 128), np.int64)
+        r = np.arange(i * 128, min(L, (i + 1) * 128))
+        c = np.arange(j * 128, min(L, (j + 1) * 128))
+        want[: len(r), : len(c)] = oq[r, h].astype(np.int64) @ ok[c, h].astype(np.int64).T
+        np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("L,H,sparse", [(256, 2, False), (391, 2, False), (1290, 2, True),
+                                        (2000, 3, True), (128, 1, False)])
+def test_sparse_attn_vs_oracle(L, H, sparse):
+    say("attn", L, H, sparse)
+    qb, kb, vb, idx, cnt = _attn_inputs(L, H, L, sparse)
+    (q8, qs, k8, ks), (oq, oqs, ok, oks) = _quantize_both(qb, kb, L, H)
+    out, part = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt), want_amax=True)
+    want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx, cnt)
+    got = bf16_f64(out)
+    assert_bf16_close(host_bits(out), want, 1e-2, f"attn L={L}")
+    T = (L + 127) // 128
+    gp = host(part)
+    for h in range(H):
+        for i in range(T):
+            rr = slice(i * 128, min(L, (i + 1) * 128))
+            assert gp[h, i] == np.abs(got[rr, h]).max()
+
+
+def test_sparse_attn_diag_only_and_out_of_range_entries():
+    L, H = 391, 2
+    qb, kb, vb, _, _ = _attn_inputs(L, H, 9, False)
+    (q8, qs, k8, ks), (oq, oqs, ok, oks) = _quantize_both(qb, kb, L, H)
+    T = 4
+    idx = np.full((H, T, 3), -1, np.int32)
+    idx[:, :, 0] = np.arange(T)
+    idx[:, :, 1] = 99                   # out of range: ignored by the kernel
+    cnt = np.full((H, T), 2, np.int32)
+    out = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt))
+    want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx[:, :, :1].copy(), np.ones((H, T), np.int32))
+    assert_bf16_close(host_bits(out), want, 1e-2, "diag only")
+    # a row with no kept key outputs zeros
+    cnt0 = np.zeros((H, T), np.int32)
+    out0 = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt0))
+    assert not host_bits(out0).any()
+
+
+def test_sparse_attn_480p_sampled_tiles():
+    """The attention-only 480p workload: 21 heads, 264 tiles, 53 kept per row; sampled tiles."""
+    w = W.WORKLOADS["attn_480p"]
+    L, H = w.L, w.n_heads
+    qb, kb, vb = W.qkv_heads(L, H, seed=0, tag=w.tag)
+    idx, cnt = W.block_mask(w, seed=0)
+    q8, qs = Q.quant_int8_qk(bf16_dev(qb.reshape(L, -1)), H)
+    k8, ks = Q.quant_int8_qk(bf16_dev(kb.reshape(L, -1)), H)
+    out = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt))
+    T = w.n_tiles
+    tiles = [(0, 0), (20, T - 1), (5, 131), (17, 263), (11, 7)]
+    # oracle inputs come from the oracle's own quantizer, for the query tiles sampled and every key
+    # tile they read; the GPU's codes for the same tiles are compared to them separately
+    gq, gk = host(q8), host(k8)
+    qq = np.zeros((L, H, 128), np.int8)
+    kq = np.zeros((L, H, 128), np.int8)
+    qsc = np.ones((H, T), np.float32)
+    ksc = np.ones((H, T), np.float32)
+    for h, i in tiles:
+        rows = slice(i * 128, min(L, (i + 1) * 128))
+        cw, sw = OQ.quant_int8_qk(np.ascontiguousarray(qb[rows, h:h + 1]), rows.stop - rows.start, 1)
+        qq[rows, h], qsc[h, i] = cw[:, 0], sw[0, 0]
+        np.testing.assert_array_equal(gq[rows, h], cw[:, 0])
+        for j in idx[h, i, : cnt[h, i]]:
+            rk = slice(j * 128, min(L, (j + 1) * 128))
+            cw, sw = OQ.quant_int8_qk(np.ascontiguousarray(kb[rk, h:h + 1]), rk.stop - rk.start, 1)
+            kq[rk, h], ksc[h, j] = cw[:, 0], sw[0, 0]
+            np.testing.assert_array_equal(gk[rk, h], cw[:, 0])
+    got = bf16_f64(out)
+    for h, i in tiles:
+        rows = slice(i * 128, min(L, (i + 1) * 128))
+        want = OAT.sparse_attn_tile(qq, qsc, kq, ksc, vb, idx, cnt, h, i, 1 / math.sqrt(128))
+        assert_bf16_close(host_bits(out)[rows, h], want, 1e-2, f"480p tile {(h, i)}")
