@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark: one denoising step of the 42-block FastH3-Trim-shaped DiT stack at the 480p token count
+on one MI355X, through the C ABI (dit_block_forward per block, AdaLN projection once per step).
+
+A step is the whole hot path over one batch: the AdaLN projection of all 42 blocks at the step's
+timestep (shared 2,688->16 basis, per-block fp16 projection), then 42 block forwards, each with the
+modulated LayerNorm + FP8 quantizers, the FP8 QKV GEMM with its fused INT8 Q/K epilogue, 80% block-
+sparse attention with INT8 scores, the FP8 out-projection with the gated residual, and the FP8 GELU
+MLP.  Inputs are synthetic and seeded (workloads.py): 33,784 tokens (21 latent frames x 30 x 52
+video + 1,024 audio), d = 2,688, 21 heads x 128, MLP 10,752, one independent weight set and mask per
+block; the same input enters every step and step k runs at sampler timestep k mod 8.
+
+Prints one JSON line.  `value` is the block forward's algorithmic throughput (TFLOP/s: FP8 GEMM
+flops + INT8 QK ops + fp16 PV flops over the kept tiles, per second of the timed steps).
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DiT-block forward ms & TFLOPS at 480p token count; % of FP8/INT8 MFMA peak"
+PEAK_TFLOPS = {"fp8": 5000.0, "int8": 5000.0, "fp16": 2500.0, "bf16": 2500.0}
+HBM_GBS = 8000.0
+
+
+def kept_scores(kv_idx, kv_cnt, L):
+    """Number of (query, key) pairs the sparse attention evaluates (ragged tiles counted exactly)."""
+    import numpy as np
+    H, T, _ = kv_idx.shape
+    rows = np.minimum(128, L - 128 * np.arange(T))               # rows of each tile
+    total = 0
+    for h in range(H):
+        for i in range(T):
+            tiles = kv_idx[h, i, : kv_cnt[h, i]]
+            total += int(rows[i]) * int(rows[tiles].sum())
+    return total
+
+
+def gemm_shapes(w, L):
+    d, F = w.d, w.mlp
+    return {"qkv": (L, 3 * d, d), "o": (L, d, d), "up": (L, F, d), "down": (L, d, F)}
+
+
+def make_stack(w, n_blocks, seed, threads=8):
+    """Generate and quantize the weights, AdaLN projections and masks of every block on the GPU."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import quantized_video_diffusion_amd as Q
+
+    def gen(b):
+        return b, W.block_weights(w, seed, b), W.adaln_proj(w, seed, b), W.block_mask(w, seed, b)
+
+    blocks, projs, masks, kept = [None] * n_blocks, [None] * n_blocks, [None] * n_blocks, 0
+    host_block0 = None
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for b, wb, pb, (idx, cnt) in ex.map(gen, range(n_blocks)):
+            dev = {k: Q.from_bits(v) for k, v in wb.items()}
+            blocks[b] = Q.quantize_block_weights(dev, w.d, w.n_heads, w.mlp)
+            del dev
+            projs[b] = Q.from_bits(pb, torch.float16)
+            masks[b] = (torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda())
+            kept += kept_scores(idx, cnt, w.L)
+            if b == 0:
+                host_block0 = (wb, pb, idx, cnt)
+    torch.cuda.synchronize()
+    proj_all = torch.stack(projs).contiguous()
+    return blocks, proj_all, masks, kept, host_block0
+
+
+def cpu_baseline(w, seed, host_block0, sample_tokens=4096):
+    """The oracle (as it stands) on a bounded sample of the workload: one block of the stack on the
+    first `sample_tokens` tokens of the 480p input, with the block's weights and an 80%-sparse mask
+    drawn for that token count; reported in the metric's unit (algorithmic TFLOP/s)."""
+    import numpy as np
+    import workloads as W
+    from oracle import adaln as OA, block as OB
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    wb, pb, _, _ = host_block0
+    L = sample_tokens
+    x = W.activations(w, seed, L=L)
+    idx, cnt = W.block_mask(w, seed, 0, L=L)
+    t0 = time.perf_counter()
+    qw = OB.quantize_block_weights(wb)
+    t_wq = time.perf_counter() - t0
+    mod = OA.adaln_project(999.0, W.adaln_basis(w, seed), pb)
+    t0 = time.perf_counter()
+    OB.dit_block(x, mod, qw, idx, cnt, w.n_heads)
+    dt = time.perf_counter() - t0
+    d, F = w.d, w.mlp
+    ops = 2.0 * L * (3 * d * d + d * d + d * F + F * d) + 4.0 * 128 * kept_scores(idx, cnt, L)
+    return {"value": ops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one block, first {L} tokens of the 480p input (d=2688, 21 heads, MLP 10752, "
+                      f"{int(cnt[0, 0])}/{idx.shape[1]} key tiles kept per row), weights pre-quantized "
+                      f"({t_wq:.1f} s, not counted); {dt:.2f} s for {ops / 1e12:.3f} TFLOP",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--blocks", type=int, default=42)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="time the steps without the per-kernel HIP events")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path's sharding is described, not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import quantized_video_diffusion_amd as Q
+
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS["trim_stack42_480p"]
+    L, d = w.L, w.d
+    nb = args.blocks
+    t_setup = time.perf_counter()
+    x0 = Q.from_bits(W.activations(w, args.seed))
+    basis = Q.from_bits(W.adaln_basis(w, args.seed), torch.float16)
+    blocks, proj_all, masks, kept, host_block0 = make_stack(w, nb, args.seed)
+    ws = torch.empty(Q.block_ws_bytes(blocks[0], L), dtype=torch.uint8, device="cuda")
+    x = torch.empty_like(x0)
+    setup_s = time.perf_counter() - t_setup
+    print(f"[bench] setup {setup_s:.1f} s: {nb} blocks, L={L}, ws {ws.numel() / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
+
+    ts = W.SAMPLER_TIMESTEPS
+    step_ms = []
+
+    def step(k):
+        x.copy_(x0)                                   # the same input enters every step
+        mods = Q.adaln_project(float(ts[k % len(ts)]), basis, proj_all)
+        for b in range(nb):
+            Q.dit_block_forward(blocks[b], mods[b], x, masks[b][0], masks[b][1], ws)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    if not args.no_kernel_timing:
+        Q.timing_enable(True)
+        Q.timing_report()                             # drop the warm-up records
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for k in range(args.steps):
+        step(k)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    kernels = {}
+    if not args.no_kernel_timing:
+        kernels = Q.timing_report()
+        Q.timing_enable(False)
+
+    # ---- derived numbers --------------------------------------------------------------------------
+    gemm_flops = 2.0 * L * (3 * d * d + d * d + d * w.mlp + w.mlp * d)
+    qk_ops = 2.0 * 128 * kept / nb                   # per block (mean over the blocks' masks)
+    pv_flops = qk_ops
+    block_ops_total = gemm_flops + qk_ops + pv_flops
+    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_block = ms_per_step / nb
+    tflops = block_ops_total * nb / (ms_per_step * 1e-3) / 1e12
+    t_bound_ms = (gemm_flops / PEAK_TFLOPS["fp8"] + qk_ops / PEAK_TFLOPS["int8"]
+                  + pv_flops / PEAK_TFLOPS["fp16"]) / 1e9
+    per_ts = {}
+    for k, ms in enumerate(step_ms):
+        per_ts.setdefault(str(ts[k % len(ts)]), []).append(round(ms, 3))
+
+    roofline = None
+    breakdown = {}
+    if kernels:
+        steps = args.steps
+        shapes = gemm_shapes(w, L)
+        work = {}
+        for key, v in kernels.items():
+            avg_ms = v["total_ms"] / v["count"]
+            breakdown[key] = {"launches_per_step": v["count"] / steps,
+                              "ms_per_step": round(v["total_ms"] / steps, 4),
+                              "avg_ms": round(avg_ms, 5)}
+            if key.startswith("gemm_fp8"):
+                M, N, K = (int(s) for s in key.rsplit("_", 1)[1].split("x"))
+                work[key] = ("mfma", 2.0 * M * N * K, PEAK_TFLOPS["fp8"], avg_ms)
+            elif key == "sparse_attn":
+                ops = qk_ops + pv_flops
+                peak = ops / (qk_ops / PEAK_TFLOPS["int8"] + pv_flops / PEAK_TFLOPS["fp16"])
+                work[key] = ("mfma", ops, peak, avg_ms)
+        dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
+        if dom in work:
+            bound, ops, peak, avg_ms = work[dom]
+            ach = ops / (avg_ms * 1e-3) / 1e12
+            roofline = {"kernel": dom, "bound": bound, "achieved": round(ach, 1), "peak": round(peak, 1),
+                        "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                        "avg_launch_ms": round(avg_ms, 5), "algorithmic_per_launch": ops}
+        for key, (bound, ops, peak, avg_ms) in work.items():
+            ach = ops / (avg_ms * 1e-3) / 1e12
+            breakdown[key].update({"TFLOP/s": round(ach, 1), "frac_of_peak": round(ach / peak, 4)})
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "trim_stack42_480p", "tokens": L, "d": d, "heads": w.n_heads,
+                   "head_dim": 128, "mlp": w.mlp, "blocks": nb, "kept_key_tiles_per_row": w.kmax,
+                   "key_tiles": w.n_tiles, "timesteps": list(ts), "parallelism": "none (1 GPU)"},
+        "ms_per_block": round(ms_per_block, 4),
+        "block_tflop": round(block_ops_total / 1e12, 4),
+        "pct_of_fp8_int8_peak": round(100 * tflops / PEAK_TFLOPS["fp8"], 2),
+        "pct_of_block_roofline": round(100 * t_bound_ms / ms_per_block, 2),
+        "step_ms_by_timestep": per_ts,
+        "roofline": roofline,
+        "kernels": breakdown,
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a bounded sample ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.seed, host_block0)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -242,6 +242,16 @@ int qvd_quant_mxfp4(const uint16_t* w, int32_t N, int32_t K, uint8_t* packed, ui
 int qvd_amax_update(const float* x, int64_t n, float* amax, void* stream);
 int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* count, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Per-kernel timing (off by default).  While enabled, each kernel launch the library makes is
+ * bracketed by a pair of HIP events recorded on the launch's own stream.  qvd_timing_report waits
+ * for the recorded work, writes {"<kernel key>": {"count": n, "total_ms": t}, ...} (NUL-terminated
+ * JSON) into buf and clears the records.  Keys: "sparse_attn", "adaln_modulate", "adaln_project",
+ * "quant_fp8", "amax_bf16", "quant_int8_qk", "gemm_<fp8|mxfp4>_<epilogue>_<M>x<N>x<K>".
+ * Returns QVD_EINVAL if len is too small (the records are then lost), QVD_EHIP on event errors. */
+int qvd_timing_enable(int on);
+int qvd_timing_report(char* buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@
 // registers, and stores its codes as 16-bit pairs.
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace qvd {
 
@@ -230,6 +231,7 @@ static int launch_modulate_nw(const uint16_t* x, int L, int d, const float* mod,
     float* partials = (float*)((char*)ws + (((size_t)L * sizeof(double2) + 255) & ~(size_t)255));
     int np = 0;
     const int rows_per_pass = 4;
+    TimingScope ts("adaln_modulate", st);
     if (!scale_in) {
         int g = (L + rows_per_pass - 1) / rows_per_pass;
         g = g < 1 ? 1 : (g > LN_GRID_STATS ? LN_GRID_STATS : g);
@@ -260,6 +262,7 @@ int launch_modulate(const uint16_t* x, int L, int d, const float* mod, int half,
 
 int launch_adaln_project(float t, const uint16_t* basis, int dt, const uint16_t* proj,
                          const uint16_t* bias, int d, int nb, float* mod, hipStream_t st) {
+    TimingScope ts("adaln_project", st);
     hipLaunchKernelGGL(k_adaln_project, dim3((6 * d + 255) / 256, nb), dim3(256), 0, st, t, basis, dt,
                        proj, bias, d, mod);
     return launch_status("adaln_project");

@@ -22,6 +22,7 @@
 // Masked key tiles are never loaded or multiplied.
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace qvd {
 
@@ -295,6 +296,7 @@ int launch_sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, c
     if (L == 0) return QVD_OK;
     const int T = (L + 127) / 128;
     const float c = sm_scale * LOG2E;
+    TimingScope ts("sparse_attn", st);
     if (amax_partials)
         hipLaunchKernelGGL(k_sparse_attn<true>, dim3(T, H), dim3(256), 0, st, q, q_scale, k, k_scale, v,
                            L, H, kv_idx, kv_cnt, kmax, c, out, amax_partials);

@@ -17,6 +17,7 @@
 //   tiles sweeping the output tiles, so an XCD's L2 holds the operands its tiles share.
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace qvd {
 
@@ -375,6 +376,11 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
     g.tiles_m = (M + BM - 1) / BM;
     g.tiles_n = (N + BN - 1) / BN;
     g.epi = epi;
+    static const char* epi_name[] = {"f32", "bf16", "resid_gate", "gelu", "qkv"};
+    char key[96];
+    snprintf(key, sizeof(key), "gemm_%s_%s_%dx%dx%d", w_fmt == QVD_W_MXFP4 ? "mxfp4" : "fp8",
+             (epi.mode >= 0 && epi.mode < 5) ? epi_name[epi.mode] : "?", M, N, K);
+    TimingScope ts(key, st);
     return w_fmt == QVD_W_MXFP4 ? launch_fmt<QVD_W_MXFP4>(g, st) : launch_fmt<QVD_W_FP8>(g, st);
 }
 

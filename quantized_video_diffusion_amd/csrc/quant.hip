@@ -9,6 +9,7 @@
 // loops sized to a few workgroups per CU, and reduce in registers and LDS.
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace qvd {
 
@@ -104,6 +105,7 @@ static int grid_for(int64_t nvec, int cap) {
 int launch_quant_fp8(const uint16_t* x, int64_t n, const float* scale_in, const float* partials,
                      int np, uint8_t* q, float* scale_out, hipStream_t st) {
     const int g = grid_for(n >> 3, 2048);
+    TimingScope ts("quant_fp8", st);
     hipLaunchKernelGGL(k_quant_fp8_bf16, dim3(g), dim3(QBLOCK), 0, st, x, n, scale_in, partials, np,
                        q, scale_out);
     return launch_status("quant_fp8 kernel");
@@ -111,6 +113,7 @@ int launch_quant_fp8(const uint16_t* x, int64_t n, const float* scale_in, const 
 
 int launch_amax_bf16(const uint16_t* x, int64_t n, float* partials, int* np_out, hipStream_t st) {
     const int g = grid_for(n >> 3, AMAX_PARTIALS);
+    TimingScope ts("amax_bf16", st);
     hipLaunchKernelGGL(k_amax_bf16, dim3(g), dim3(QBLOCK), 0, st, x, n, partials);
     *np_out = g;
     return launch_status("amax kernel");
@@ -295,6 +298,7 @@ int quant_int8_qk(const uint16_t* x, int32_t L, int32_t H, int32_t head_dim, int
     QVD_ALIGN(q);
     QVD_DEVICE_OK();
     const int T = (L + 127) / 128;
+    TimingScope ts("quant_int8_qk", (hipStream_t)stream);
     hipLaunchKernelGGL(k_quant_int8_qk, dim3(T, H), dim3(256), 0, (hipStream_t)stream, x, L, H,
                        row_stride, q, scale);
     return launch_status("quant_int8_qk");

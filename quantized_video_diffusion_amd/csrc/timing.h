@@ -1,0 +1,26 @@
+// Per-kernel event timing hooks (see timing.hip).
+#pragma once
+
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+namespace qvd {
+
+bool timing_enabled();
+
+// Records an event pair around the launches made during its lifetime, when timing is enabled.
+class TimingScope {
+public:
+    TimingScope(const char* key, hipStream_t st);
+    ~TimingScope();
+    TimingScope(const TimingScope&) = delete;
+    TimingScope& operator=(const TimingScope&) = delete;
+
+private:
+    hipStream_t st_;
+    hipEvent_t start_ = nullptr, stop_ = nullptr;
+    std::string key_;
+};
+
+}  // namespace qvd

@@ -284,3 +284,18 @@ def dit_block_forward(bw: BlockWeights, mod: torch.Tensor, x: torch.Tensor, kv_i
     call("dit_block_forward", C.byref(p), _ptr(mod), _ptr(x), L, _ptr(kv_idx), _ptr(kv_cnt),
          kv_idx.shape[-1], _ptr(ws), ws.numel(), _stream())
     return x
+
+
+# ----------------------------------------------------------------------------------------------
+# per-kernel event timing
+
+def timing_enable(on: bool = True):
+    call("qvd_timing_enable", 1 if on else 0)
+
+
+def timing_report() -> dict:
+    """{kernel key: {"count": n, "total_ms": t}} for the launches since the last report."""
+    import json
+    buf = C.create_string_buffer(1 << 20)
+    call("qvd_timing_report", buf, len(buf))
+    return json.loads(buf.value.decode())
