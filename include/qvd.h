@@ -128,22 +128,32 @@ int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, in
  * and the "运行速度如何" note (INT8 Q/K).  For head h and query tile i (128 rows):
  *   keys   = rows of the key tiles kv_idx[h][i][0 .. kv_cnt[h][i]-1] that exist (< L)
  *   s      = (Q8 K8^T)[exact int32] * q_scale[h][i] * k_scale[h][j] * sm_scale
- *   out    = softmax(s) V  (per query row, over the kept keys), written as bf16.
+ *   e      = fp16(exp(s - max over all kept keys of the row))     (softmax numerators)
+ *   out    = sum e * fp16(V) / sum e  per query row, written as bf16.
  *   q, k   : int8 [L][H][head_dim];  q_scale, k_scale: fp32 [H][T], T = ceil(L/128).
  *   v      : bf16 [L][H][head_dim];  out: bf16 [L][H][head_dim].
  *   kv_idx : int32 [H][T][kmax]; kv_cnt: int32 [H][T].  Entries outside [0, T) and counts outside
  *            [0, kmax] are ignored (clamped), so device data can never send the kernel out of
  *            bounds; a row with no kept key outputs zeros.  Tile lists are expected ascending
- *            with the diagonal present, but order does not change the result beyond rounding.
+ *            with the diagonal present, but their order does not change the result.
  *   out_amax_partials : NULL, or fp32 [H][T] receiving max|out| of each (h, i) tile (feeds the
  *            dynamic FP8 quantization of the attention output without another pass).
- * Arithmetic: INT8 MFMA scores (exact int32), softmax in fp32 with exp2, probabilities and V
- * rounded to fp16 for an fp16 MFMA P.V with fp32 accumulation.  V must satisfy |v| <= 65504
- * (larger magnitudes saturate to 65504 in the product). */
+ *   ws     : qvd_sparse_attn_ws_bytes(L, H) bytes: V transposed to fp16 [H][128][T*128].
+ * Arithmetic: INT8 MFMA scores (exact int32); pass 1 finds each row's maximum over the kept keys,
+ * pass 2 rounds the numerators exp2((s - max) * log2 e) to fp16 and runs the fp16 MFMA P.V and the
+ * numerator sum with fp32 accumulation.  |V| above 65504 saturates to 65504 in the product. */
+size_t qvd_sparse_attn_ws_bytes(int32_t L, int32_t H);
 int sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                 const uint16_t* v, int32_t L, int32_t H, int32_t head_dim,
                 const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
-                uint16_t* out, float* out_amax_partials, void* stream);
+                uint16_t* out, float* out_amax_partials, void* ws, size_t ws_bytes, void* stream);
+/* The same attention with V already transposed to fp16: vt [H][128][T*128] (keys contiguous per
+ * (head, dim) row; columns L .. T*128-1 must hold finite values, e.g. zeros).  This is the layout
+ * the QKV GEMM epilogue writes. */
+int qvd_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k,
+                       const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                       const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
+                       uint16_t* out, float* out_amax_partials, void* stream);
 
 /* Exact INT32 accumulators Q8[rows of tile i] . K8[rows of tile j]^T of head h, computed by the
  * same INT8 MFMA tile routine the attention kernel uses, into out int32 [128][128]
@@ -167,8 +177,10 @@ enum qvd_epilogue_mode {
     QVD_EPI_QKV = 4         /* N = 3*H*128: columns [Q | K | V].  y is rounded to bf16; the Q and
                                K parts are then quantized per (head, 128-token tile) exactly as
                                quant_int8_qk does, into q8/k8 int8 [M][H][128] with scales
-                               q_scale/k_scale [H][ceil(M/128)]; the V part goes to v bf16
-                               [M][H][128]                                                     */
+                               q_scale/k_scale [H][ceil(M/128)]; the V part (bf16 values) is
+                               written transposed and converted to fp16 into v as
+                               [H][128][ceil(M/128)*128], columns M.. of the last tile zeroed
+                               (the layout qvd_sparse_attn_vt reads)                            */
 };
 typedef struct {
     int32_t mode;               /* qvd_epilogue_mode                                           */
@@ -180,7 +192,7 @@ typedef struct {
     float* amax_partials;       /* QVD_EPI_GELU (optional): fp32 [qvd_gemm_tiles(M, N)]        */
     int8_t* q8;                 /* QVD_EPI_QKV                                                 */
     int8_t* k8;
-    uint16_t* v;
+    uint16_t* v;                /* QVD_EPI_QKV: fp16 V^T [H][128][ceil(M/128)*128]               */
     float* q_scale;
     float* k_scale;
 } qvd_epilogue;

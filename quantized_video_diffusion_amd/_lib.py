@@ -57,7 +57,10 @@ SIGNATURES = {
     "qvd_adaln_project_stack": (C.c_int, [_f32, _p, _i32, _p, _p, _i32, _i32, _p, _p]),
     "qvd_adaln_modulate_ws_bytes": (_sz, [_i32, _i32]),
     "adaln_modulate": (C.c_int, [_p, _i32, _i32, _p, _i32, _f32, _p, _p, _p, _p, _sz, _p]),
-    "sparse_attn": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _f32, _p, _p, _p]),
+    "qvd_sparse_attn_ws_bytes": (_sz, [_i32, _i32]),
+    "sparse_attn": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _f32, _p, _p, _p, _sz,
+                              _p]),
+    "qvd_sparse_attn_vt": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p, _p]),
     "qvd_qk_int32_tile": (C.c_int, [_p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "qvd_gemm_tiles": (_i64, [_i32, _i32]),
     "qvd_gemm_fp8": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(Epilogue), _p]),

@@ -8,7 +8,7 @@
 //   (per-tensor FP8 linear layers with the scales applied to the output; INT8 query/key).
 //
 //   adaln_modulate(x, shift1, scale1)             -> h (E4M3) + s_h
-//   GEMM h . W_qkv^T, epilogue: bf16 Q|K|V, INT8 Q/K per (head, 128-token tile)
+//   GEMM h . W_qkv^T, epilogue: bf16 Q|K|V, INT8 Q/K per (head, 128-token tile), V^T in fp16
 //   sparse_attn                                   -> O (bf16) + per-tile max|O|
 //   per-tensor FP8 of O (amax from those partials) -> O8
 //   GEMM O8 . W_o^T, epilogue: x += gate1 * y      (in place)
@@ -31,7 +31,7 @@ struct BlockWs {
     uint8_t* h;          // E4M3 [L][d]: modulated LN output, then the FP8 attention output
     int8_t* q8;          // [L][d]
     int8_t* k8;          // [L][d]
-    uint16_t* v;         // bf16 [L][d]
+    uint16_t* v;         // fp16 V^T [H][128][T*128]
     uint16_t* o;         // bf16 [L][d]
     uint16_t* g;         // bf16 [L][F]
     uint8_t* g8;         // E4M3 [L][F]
@@ -58,7 +58,7 @@ BlockWs carve(const qvd_block_params* p, int L, uint8_t* base) {
     w.h = take(Ld);
     w.q8 = (int8_t*)take(Ld);
     w.k8 = (int8_t*)take(Ld);
-    w.v = (uint16_t*)take(2 * Ld);
+    w.v = (uint16_t*)take(vt_bytes(L, p->n_heads));
     w.o = (uint16_t*)take(2 * Ld);
     w.g = (uint16_t*)take(2 * LF);
     w.g8 = take(LF);
@@ -168,8 +168,8 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     e.k_scale = w.ks;
     s = launch_gemm(w.h, w.scales + 0, p->w_qkv, p->e8m0_qkv, p->s_qkv, fmt, p->b_qkv, L, 3 * d, d, e, st);
     if (s) return s;
-    s = launch_sparse_attn(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.o,
-                           act ? nullptr : w.attn_part, st);
+    s = launch_sparse_attn_vt(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.o,
+                              act ? nullptr : w.attn_part, st);
     if (s) return s;
     s = launch_quant_fp8(w.o, (int64_t)L * d, act ? act + 1 : nullptr, w.attn_part, H * T, w.h,
                          w.scales + 1, st);

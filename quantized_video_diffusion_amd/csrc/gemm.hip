@@ -252,19 +252,28 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
         const int head = (nw0 - part * dm) >> 7;
         const int Tm = (M + 127) >> 7;
         if (part == 2) {
+            // V: bf16 rounding, then fp16 (exact for 2^-14 <= |v| <= 65504; larger saturate),
+            // stored transposed as V^T[head][dim][token] with tokens M .. Lp-1 zeroed
+            const int64_t Lp = (int64_t)Tm * 128;
+            uint16_t* vt = ep.v + (int64_t)head * 128 * Lp;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 const int n = nw0 + 16 * nb + 4 * fg;
                 float4 b = g.bias ? *reinterpret_cast<const float4*>(g.bias + n)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int dd = 16 * nb + 4 * fg;
 #pragma unroll
                 for (int mb = 0; mb < 8; ++mb) {
                     const int m = mw0 + 16 * mb + fr;
-                    if (m < M) {
-                        const v4f c = acc[nb][mb];
-                        *reinterpret_cast<uint2*>(ep.v + (int64_t)m * dm + (n - 2 * dm)) =
-                            make_uint2(pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y),
-                                       pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w));
+                    const v4f c = acc[nb][mb];
+                    float y[4] = {c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z,
+                                  c[3] * alpha + b.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float vb = bf16lo(pack_bf16x2(y[r], 0.0f));
+                        const float vc = fminf(fmaxf(vb, -65504.0f), 65504.0f);
+                        const uint16_t h16 = m < M ? __builtin_bit_cast(uint16_t, (_Float16)vc) : (uint16_t)0;
+                        vt[(int64_t)(dd + r) * Lp + m] = h16;
                     }
                 }
             }

@@ -24,8 +24,10 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
                 int w_fmt, const float* bias, int M, int N, int K, const qvd_epilogue& epi,
                 hipStream_t st);
 
-int launch_sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
-                       const uint16_t* v, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt,
-                       int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st);
+// attention over fp16 V^T [H][128][ceil(L/128)*128]
+int launch_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
+                          const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt,
+                          int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st);
+size_t vt_bytes(int L, int H);
 
 }  // namespace qvd

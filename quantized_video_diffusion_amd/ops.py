@@ -121,7 +121,21 @@ def sparse_attn(q8, q_scale, k8, k_scale, v, kv_idx, kv_cnt, sm_scale: float = S
     _check(kv_cnt, torch.int32, "kv_cnt")
     out = torch.empty((L, H, D), dtype=torch.bfloat16, device=q8.device)
     part = torch.empty(q_scale.shape, dtype=torch.float32, device=q8.device) if want_amax else None
+    ws = torch.empty((_lib.lib().qvd_sparse_attn_ws_bytes(L, H),), dtype=torch.uint8, device=q8.device)
     call("sparse_attn", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), L, H, D,
+         _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(out), _ptr(part),
+         _ptr(ws), ws.numel(), _stream())
+    return (out, part) if want_amax else out
+
+
+def sparse_attn_vt(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, sm_scale: float = SM_SCALE,
+                   want_amax: bool = False):
+    """As sparse_attn, with V given as fp16 V^T [H][128][ceil(L/128)*128]."""
+    L, H, D = q8.shape
+    _check(vt, torch.float16, "vt")
+    out = torch.empty((L, H, D), dtype=torch.bfloat16, device=q8.device)
+    part = torch.empty(q_scale.shape, dtype=torch.float32, device=q8.device) if want_amax else None
+    call("qvd_sparse_attn_vt", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt), L, H,
          _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(out), _ptr(part),
          _stream())
     return (out, part) if want_amax else out
@@ -184,7 +198,7 @@ def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, 
         T = (M + 127) // 128
         q8 = torch.empty((M, H, 128), dtype=torch.int8, device=a.device)
         k8 = torch.empty_like(q8)
-        v = torch.empty((M, H, 128), dtype=torch.bfloat16, device=a.device)
+        v = torch.empty((H, 128, T * 128), dtype=torch.float16, device=a.device)   # V^T, fp16
         qs = torch.empty((H, T), dtype=torch.float32, device=a.device)
         ks = torch.empty_like(qs)
         e.n_heads = H

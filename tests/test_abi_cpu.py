@@ -66,14 +66,20 @@ def test_host_validation_errors(lib):
     assert _status(lib, "adaln_modulate", fake, 4, 256, fake, 0, C.c_float(1e-6), None, fake, fake,
                    fake, 8, None) == _lib.QVD_EWORKSPACE
     # sparse_attn
+    big = 1 << 30
     assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 300, 2, 64, fake, fake, 3,
-                   C.c_float(0.1), fake, None, None) == _lib.QVD_ESHAPE
+                   C.c_float(0.1), fake, None, fake, big, None) == _lib.QVD_ESHAPE
     assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 300, 2, 128, fake, fake, 0,
-                   C.c_float(0.1), fake, None, None) == _lib.QVD_ESHAPE
+                   C.c_float(0.1), fake, None, fake, big, None) == _lib.QVD_ESHAPE
     assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 300, 2, 128, None, fake, 3,
-                   C.c_float(0.1), fake, None, None) == _lib.QVD_EINVAL
+                   C.c_float(0.1), fake, None, fake, big, None) == _lib.QVD_EINVAL
+    assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 300, 2, 128, fake, fake, 3,
+                   C.c_float(0.1), fake, None, fake, 16, None) == _lib.QVD_EWORKSPACE
     assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 0, 2, 128, None, None, 3,
-                   C.c_float(0.1), None, None, None) == _lib.QVD_OK
+                   C.c_float(0.1), None, None, None, 0, None) == _lib.QVD_OK
+    assert lib.qvd_sparse_attn_ws_bytes(300, 2) == 2 * 128 * 384 * 2
+    assert _status(lib, "qvd_sparse_attn_vt", fake, fake, fake, fake, mis, 300, 2, fake, fake, 3,
+                   C.c_float(0.1), fake, None, None) == _lib.QVD_EALIGN
     assert _status(lib, "qvd_qk_int32_tile", fake, fake, 300, 2, 2, 0, 0, fake, None) == _lib.QVD_EINVAL
     assert _status(lib, "qvd_qk_int32_tile", fake, fake, 300, 2, 0, 3, 0, fake, None) == _lib.QVD_EINVAL
     # GEMM

@@ -88,7 +88,15 @@ def test_gemm_qkv_epilogue(M, H):
                                    mode=_lib.QVD_EPI_QKV, n_heads=H)
     y = OG.gemm_fp8(a, sa, w, sw)
     ybits = OC.f64_to_bf16(y)
-    assert_bf16_close(host_bits(v).reshape(M, d), y[:, 2 * d:], 1e-3, "V part")
+    # V part: V^T [H][128][Lp] in fp16 holding the bf16-rounded values, zeros past M
+    T = (M + 127) // 128
+    vt = host(v.view(torch.float16)).astype(np.float64)
+    assert vt.shape == (H, 128, T * 128)
+    assert not vt[:, :, M:].any()
+    v_got = vt[:, :, :M].transpose(2, 0, 1).reshape(M, d)
+    v_bits = OC.f64_to_bf16(v_got)           # fp16 holding a bf16 value converts back exactly
+    np.testing.assert_array_equal(OC.bf16_to_f64(v_bits), v_got)
+    assert_bf16_close(v_bits, y[:, 2 * d:], 1e-3, "V part")
     for part, (g8, gs) in enumerate(((q8, qs), (k8, ks))):
         cw, sw_ = OQ.quant_int8_qk(np.ascontiguousarray(ybits[:, part * d:(part + 1) * d]), M, H)
         # scales: bf16 rounding of the fp32 accumulators can differ at near-ties only
@@ -173,6 +181,19 @@ def test_sparse_attn_vs_oracle(L, H, sparse):
         for i in range(T):
             rr = slice(i * 128, min(L, (i + 1) * 128))
             assert gp[h, i] == np.abs(got[rr, h]).max()
+
+
+def test_sparse_attn_vt_entry_matches_bf16_entry():
+    """The fp16 V^T entry point on a host-transposed V gives the same bits as the bf16 entry."""
+    L, H = 1290, 2
+    qb, kb, vb, idx, cnt = _attn_inputs(L, H, 12, True)
+    (q8, qs, k8, ks), _ = _quantize_both(qb, kb, L, H)
+    T = (L + 127) // 128
+    vt = np.zeros((H, 128, T * 128), np.float16)
+    vt[:, :, :L] = OC.bf16_to_f64(vb).transpose(1, 2, 0).astype(np.float16)
+    a = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt))
+    b = Q.sparse_attn_vt(q8, qs, k8, ks, torch.from_numpy(vt).cuda(), i32_dev(idx), i32_dev(cnt))
+    np.testing.assert_array_equal(host_bits(a), host_bits(b))
 
 
 def test_sparse_attn_diag_only_and_out_of_range_entries():
