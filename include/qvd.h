@@ -132,7 +132,7 @@ int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, in
  *   out    = sum e * fp16(V) / sum e  per query row, written as bf16.
  *   q, k   : int8 [L][H][head_dim];  q_scale, k_scale: fp32 [H][T], T = ceil(L/128).
  *   v      : bf16 [L][H][head_dim];  out: bf16 [L][H][head_dim].
- *   kv_idx : int32 [H][T][kmax]; kv_cnt: int32 [H][T].  Entries outside [0, T) and counts outside
+ *   kv_idx : int32 [H][T][kmax], 1 <= kmax <= 1024; kv_cnt: int32 [H][T].  Entries outside [0, T) and counts outside
  *            [0, kmax] are ignored (clamped), so device data can never send the kernel out of
  *            bounds; a row with no kept key outputs zeros.  Tile lists are expected ascending
  *            with the diagonal present, but their order does not change the result.

@@ -29,9 +29,13 @@ namespace qvd {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+constexpr int MAX_KEPT = 1024;      // longest kept-tile list a workgroup takes (kmax bound)
+
 struct AttnSmem {
-    int8_t k[128 * 128];            // 16 KB
+    int8_t k[2][128 * 128];         // 2 x 16 KB: double-buffered K tiles
     uint16_t vt[128 * 128];         // 32 KB, fp16 bit patterns
+    int tiles[MAX_KEPT];            // the valid entries of this row's kept-tile list, in order
+    int wcount[4];
 };
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -50,6 +54,8 @@ QVD_DEV void dma16(const void* g, void* lds_slot_base) {
 }
 
 QVD_DEV void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most 4 DMA/vector loads are outstanding (the 4 K-tile loads issued last)
+QVD_DEV void dma_wait_but_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
 // Q fragments of this wave (B operand): qf[qb][ks] = Q[q0 + 16 qb + fr][h][64 ks + 16 fg .. +15]
 QVD_DEV void load_q_frags(const int8_t* __restrict__ q, int L, int H, int h, int q0, int fr, int fg,
@@ -66,7 +72,7 @@ QVD_DEV void load_q_frags(const int8_t* __restrict__ q, int L, int H, int h, int
 
 // K tile j -> LDS.  Wave w, instruction u fills LDS rows (4w + u)*8 .. +7; lane l lands in row
 // r = (4w+u)*8 + l/8, slot l%8, and fetches chunk (l%8) ^ (r & 7) of key row j*128 + r (clamped).
-QVD_DEV void stage_k(AttnSmem& sm, const int8_t* __restrict__ k, int L, int H, int h, int j,
+QVD_DEV void stage_k(int8_t* kbuf, const int8_t* __restrict__ k, int L, int H, int h, int j,
                      int wv, int lane) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -75,32 +81,36 @@ QVD_DEV void stage_k(AttnSmem& sm, const int8_t* __restrict__ k, int L, int H, i
         const int c = (lane & 7) ^ (r & 7);
         int kr = j * 128 + r;
         kr = kr < L ? kr : L - 1;
-        dma16(k + ((int64_t)kr * H + h) * 128 + 16 * c, sm.k + blk * 1024);
+        const uint32_t off = ((uint32_t)kr * (uint32_t)H + (uint32_t)h) * 128u + (uint32_t)(16 * c);
+        dma16(k + off, kbuf + blk * 1024);
     }
 }
 
 // V^T tile j -> LDS.  vt rows are (head, dim), Lp keys each.  Wave w, instruction u fills LDS rows
 // (8w + u)*4 .. +3 (256 B each); lane l lands in row d = (8w+u)*4 + l/16, slot l%16, and fetches
 // chunk (l%16) ^ (d & 15) of keys j*128 .. j*128+127.
-QVD_DEV void stage_vt(AttnSmem& sm, const uint16_t* __restrict__ vt, int64_t Lp, int h, int j,
+// (32-bit offsets: H*128*Lp*2 bytes stays far below 2^32 for every L the launcher accepts)
+QVD_DEV void stage_vt(AttnSmem& sm, const uint16_t* __restrict__ vt, int Lp, int h, int j,
                       int wv, int lane) {
+    const char* base = reinterpret_cast<const char*>(vt) + (size_t)j * 256u;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int blk = 8 * wv + u;
         const int d = blk * 4 + (lane >> 4);
         const int c = (lane & 15) ^ (d & 15);
-        dma16(vt + ((int64_t)h * 128 + d) * Lp + j * 128 + 8 * c, sm.vt + blk * 512);
+        const uint32_t off = ((uint32_t)(h * 128 + d) * (uint32_t)Lp + (uint32_t)(8 * c)) * 2u;
+        dma16(base + off, sm.vt + blk * 512);
     }
 }
 
 // S^T = K . Q^T for this wave: s[qb][kb][r] = score(query q0 + 16 qb + fr, key 16 kb + 4 fg + r)
-QVD_DEV void qk_scores(const AttnSmem& sm, const v4i qf[2][2], int fr, int fg, v4i s[2][8]) {
+QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v4i s[2][8]) {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
         const int row = 16 * kb + fr;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const v4i kf = *reinterpret_cast<const v4i*>(sm.k + row * 128 + (((4 * ks + fg) ^ (row & 7)) << 4));
+            const v4i kf = *reinterpret_cast<const v4i*>(kbuf + row * 128 + (((4 * ks + fg) ^ (row & 7)) << 4));
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const v4i c = ks == 0 ? (v4i){0, 0, 0, 0} : s[qb][kb];
@@ -154,6 +164,29 @@ QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int k
     }
 }
 
+// The valid entries (0 <= j < T) of the first `cnt` list elements, in list order, into sm.tiles;
+// returns their number.  Ballot-based prefix sums keep the order deterministic.
+QVD_DEV int compact_tiles(AttnSmem& sm, const int32_t* __restrict__ list, int cnt, int T, int tid,
+                          int lane, int wv) {
+    int total = 0;
+    for (int base = 0; base < cnt; base += 256) {
+        const int t = base + tid;
+        const int j = t < cnt ? list[t] : -1;
+        const bool ok = j >= 0 && j < T;
+        const unsigned long long mask = __ballot(ok);
+        const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+        __syncthreads();
+        if (lane == 0) sm.wcount[wv] = __popcll(mask);
+        __syncthreads();
+        int off = total;
+        for (int w = 0; w < wv; ++w) off += sm.wcount[w];
+        if (ok) sm.tiles[off + pos] = j;
+        total += sm.wcount[0] + sm.wcount[1] + sm.wcount[2] + sm.wcount[3];
+    }
+    __syncthreads();
+    return total;
+}
+
 template <bool WRITE_AMAX>
 __global__ void __launch_bounds__(256, 2) k_sparse_attn(
     const int8_t* __restrict__ q, const float* __restrict__ q_scale, const int8_t* __restrict__ k,
@@ -166,7 +199,7 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int fr = lane & 15, fg = lane >> 4;
     const int q0 = i * 128 + 32 * wv;
-    const int64_t Lp = (int64_t)T * 128;
+    const int Lp = T * 128;
     const bool ragged_L = (L & 127) != 0;
 
     v4i qf[2][2];
@@ -175,18 +208,19 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
     int cnt = kv_cnt[h * T + i];
     cnt = cnt < 0 ? 0 : (cnt > kmax ? kmax : cnt);
     const int32_t* list = kv_idx + ((int64_t)h * T + i) * kmax;
+    const int n = compact_tiles(sm, list, cnt, T, tid, lane, wv);
 
-    // pass 1: the maximum of every query row over all kept keys
+    // pass 1: the maximum of every query row over all kept keys; K double-buffered, the next tile
+    // loading while this one is multiplied
     float m[2] = {-INFINITY, -INFINITY};
-    for (int t = 0; t < cnt; ++t) {
-        const int j = list[t];
-        if (j < 0 || j >= T) continue;
-        __syncthreads();                       // the previous tile's LDS reads are done
-        stage_k(sm, k, L, H, h, j, wv, lane);
+    if (n > 0) stage_k(sm.k[0], k, L, H, h, sm.tiles[0], wv, lane);
+    for (int t = 0; t < n; ++t) {
+        const int j = sm.tiles[t];
         dma_wait();
-        __syncthreads();
+        __syncthreads();                       // K(t) is in LDS; everyone is done with K(t-1)
+        if (t + 1 < n) stage_k(sm.k[(t + 1) & 1], k, L, H, h, sm.tiles[t + 1], wv, lane);
         v4i s[2][8];
-        qk_scores(sm, qf, fr, fg, s);
+        qk_scores(sm.k[t & 1], qf, fr, fg, s);
         const float c = qsc * k_scale[h * T + j];
         if (ragged_L && j == T - 1) tile_max<true>(s, c, j * 128, L, fg, m);
         else tile_max<false>(s, c, j * 128, L, fg, m);
@@ -197,7 +231,8 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
         m[qb] = fmaxf(m[qb], __shfl_xor(m[qb], 32, 64));
     }
 
-    // pass 2: fp16 numerators, their sum (ones . P^T) and P.V
+    // pass 2: fp16 numerators, their sum (ones . P^T) and P.V.  V^T(t) loads under QK(t) and the
+    // numerators; K(t+1) loads under P.V(t).
     v4f o[2][8], lacc[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -207,17 +242,18 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
     }
     const v8h ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
-    for (int t = 0; t < cnt; ++t) {
-        const int j = list[t];
-        if (j < 0 || j >= T) continue;
-        __syncthreads();
-        stage_k(sm, k, L, H, h, j, wv, lane);
-        stage_vt(sm, vt, Lp, h, j, wv, lane);
+    __syncthreads();                           // pass 1's last reads of sm.k are done
+    if (n > 0) stage_k(sm.k[0], k, L, H, h, sm.tiles[0], wv, lane);
+    for (int t = 0; t < n; ++t) {
+        const int j = sm.tiles[t];
         dma_wait();
-        __syncthreads();
+        __syncthreads();                       // K(t) in LDS; P.V(t-1) and QK(t-1) are done
+        stage_vt(sm, vt, Lp, h, j, wv, lane);
+        const bool more = t + 1 < n;
+        if (more) stage_k(sm.k[(t + 1) & 1], k, L, H, h, sm.tiles[t + 1], wv, lane);
 
         v4i s[2][8];
-        qk_scores(sm, qf, fr, fg, s);
+        qk_scores(sm.k[t & 1], qf, fr, fg, s);
         const float c = qsc * k_scale[h * T + j];
         v8h pb[2][4];
         if (ragged_L && j == T - 1) tile_numerators<true>(s, c, m, j * 128, L, fg, pb);
@@ -228,6 +264,9 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
                 lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[qb][kp], lacc[qb], 0, 0, 0);
+        if (more) dma_wait_but_4();            // V^T(t) landed (K(t+1) may still be in flight)
+        else dma_wait();
+        __syncthreads();                       // every wave's part of V^T(t) is in LDS
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             const int d = 16 * db + fr;
@@ -243,6 +282,9 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
                 for (int qb = 0; qb < 2; ++qb)
                     o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[qb][kp], o[qb][db], 0, 0, 0);
             }
+            // keep the V fragment reads of one 16-dim block next to their MFMAs (bounds the
+            // registers the scheduler may spend on reads hoisted ahead)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -314,11 +356,11 @@ __global__ void __launch_bounds__(256) k_qk_tile(const int8_t* __restrict__ q, c
     const int q0 = i * 128 + 32 * wv;
     v4i qf[2][2];
     load_q_frags(q, L, H, h, q0, fr, fg, qf);
-    stage_k(sm, k, L, H, h, j, wv, lane);
+    stage_k(sm.k[0], k, L, H, h, j, wv, lane);
     dma_wait();
     __syncthreads();
     v4i s[2][8];
-    qk_scores(sm, qf, fr, fg, s);
+    qk_scores(sm.k[0], qf, fr, fg, s);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -359,8 +401,9 @@ int validate_attn(const char* fn, const int8_t* q, const float* q_scale, const i
                   const float* k_scale, const void* v, int32_t L, int32_t H, const int32_t* kv_idx,
                   const int32_t* kv_cnt, int32_t kmax, float sm_scale, uint16_t* out) {
     QVD_REQUIRE(L >= 0 && H >= 1 && H <= 65535, QVD_ESHAPE, "%s: L = %d, H = %d", fn, L, H);
-    QVD_REQUIRE(L <= (1 << 24), QVD_ESHAPE, "%s: L = %d too large", fn, L);
-    QVD_REQUIRE(kmax >= 1, QVD_ESHAPE, "%s: kmax = %d", fn, kmax);
+    QVD_REQUIRE((double)H * 128.0 * ((L + 127) / 128) * 128.0 * 2.0 < 4294967296.0, QVD_ESHAPE,
+                "%s: L = %d, H = %d too large (V^T must stay below 4 GiB)", fn, L, H);
+    QVD_REQUIRE(kmax >= 1 && kmax <= MAX_KEPT, QVD_ESHAPE, "%s: kmax = %d (1 .. %d)", fn, kmax, MAX_KEPT);
     QVD_REQUIRE(sm_scale > 0.0f && sm_scale < 1e30f, QVD_EINVAL, "%s: sm_scale out of range", fn);
     if (L == 0) return QVD_OK;
     QVD_REQUIRE(q && q_scale && k && k_scale && v && kv_idx && kv_cnt && out, QVD_EINVAL,

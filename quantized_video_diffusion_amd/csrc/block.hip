@@ -140,7 +140,7 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     QVD_ALIGN(mod);
     QVD_ALIGN(x);
     QVD_ALIGN(ws);
-    QVD_REQUIRE(kmax >= 1, QVD_ESHAPE, "dit_block_forward: kmax = %d", kmax);
+    QVD_REQUIRE(kmax >= 1 && kmax <= 1024, QVD_ESHAPE, "dit_block_forward: kmax = %d (1 .. 1024)", kmax);
     const size_t need = qvd_block_ws_bytes(p, L);
     QVD_REQUIRE(ws_bytes >= need, QVD_EWORKSPACE, "dit_block_forward: workspace %zu < %zu bytes",
                 ws_bytes, need);

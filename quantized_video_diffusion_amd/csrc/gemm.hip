@@ -11,8 +11,9 @@
 // ends up holding four consecutive output columns of one token row -- the shape every epilogue
 // wants (8-byte bf16 stores, per-column bias/gate vectors, per-head INT8 quantization).
 //   workgroup tile 256 (tokens) x 256 (outputs) x 128 (K), four waves of 128 x 128;
-//   both operands K-contiguous, staged through LDS (double buffered, 16-byte chunks XOR-swizzled by
-//   row so the 16-row MFMA fragment reads are bank-conflict free);
+//   both operands K-contiguous, moved HBM/L2 -> LDS by global_load_lds_dwordx4 into a double buffer
+//   (the next K-step lands while this one is multiplied), 16-byte chunks XOR-swizzled by row so the
+//   16-row MFMA fragment reads are bank-conflict free;
 //   tile order: contiguous tile ranges per XCD (workgroup b runs on XCD b % 8) and groups of 8 token
 //   tiles sweeping the output tiles, so an XCD's L2 holds the operands its tiles share.
 #include "common.h"
@@ -82,12 +83,36 @@ QVD_DEV v8i frag_fp4(const uint8_t* tile, int r, int g) {
     return __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int WFMT>
 struct TileCfg {
     static constexpr int W_BYTES = WFMT == QVD_W_MXFP4 ? BN * BK / 2 : BN * BK;
     static constexpr int E_BYTES = WFMT == QVD_W_MXFP4 ? BN * 4 : 0;
     static constexpr int STAGE = BM * BK + W_BYTES + E_BYTES;
 };
+
+// One K-step of both operands -> LDS stage `buf` (see the staging comment in k_gemm).
+template <int WFMT>
+QVD_DEV void stage_tiles(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv,
+                         const uint32_t* a_off, const uint32_t* w_off, uint32_t e_off) {
+    using Cfg = TileCfg<WFMT>;
+    constexpr int WINST = WFMT == QVD_W_MXFP4 ? 4 : 8;
+    uint8_t* As_ = smem + buf * Cfg::STAGE;
+    uint8_t* Ws_ = As_ + BM * BK;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        __builtin_amdgcn_global_load_lds(g.a + a_off[u] + k0, (lds_void*)(As_ + (8 * wv + u) * 1024), 16, 0, 0);
+    const uint32_t wk = WFMT == QVD_W_MXFP4 ? (uint32_t)k0 / 2 : (uint32_t)k0;
+#pragma unroll
+    for (int u = 0; u < WINST; ++u) {
+        const int blk = WFMT == QVD_W_MXFP4 ? 4 * wv + u : 8 * wv + u;
+        __builtin_amdgcn_global_load_lds(g.w + w_off[u] + wk, (lds_void*)(Ws_ + blk * 1024), 16, 0, 0);
+    }
+    if (WFMT == QVD_W_MXFP4)
+        __builtin_amdgcn_global_load_lds(g.e8 + e_off + k0 / 32, (lds_void*)(Ws_ + Cfg::W_BYTES + 256 * wv),
+                                         4, 0, 0);
+}
 
 template <int EPI, int WFMT>
 __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
@@ -101,113 +126,102 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
 
-    // ---- global -> register staging -------------------------------------------------------------
-    // A (and FP8 W): thread t moves 16-byte chunk (t & 7) of rows (t >> 3) + 32 j, j < 8.
-    // MXFP4 W (64-byte rows): chunk (t & 3) of rows (t >> 2) + 64 j, j < 4; E8M0: row t, 4 bytes.
-    const int ld_row = tid >> 3, ld_ch = tid & 7;
-    constexpr int WJ = WFMT == QVD_W_MXFP4 ? 4 : 8;
-    constexpr int WSTEP = WFMT == QVD_W_MXFP4 ? 64 : 32;
-    const int wld_row = WFMT == QVD_W_MXFP4 ? (tid >> 2) : ld_row;
-    const int wld_ch = WFMT == QVD_W_MXFP4 ? (tid & 3) : ld_ch;
-    const int64_t w_row_bytes = WFMT == QVD_W_MXFP4 ? K / 2 : K;
-    const uint8_t* a_base = g.a + ld_ch * 16;
-    const uint8_t* w_base = g.w + wld_ch * 16;
-    int a_off[8], w_off[WJ];          // row offsets (bytes / 16) of the clamped rows
+    // ---- HBM/L2 -> LDS staging with global_load_lds (no register round trip) ---------------------
+    // FP8 operands (128-byte rows): wave w's instruction u fills LDS rows (8w+u)*8 .. +7; lane l
+    // lands in row r = (8w+u)*8 + l/8, slot l%8, and fetches chunk (l%8) ^ (r&7) of its row.
+    // MXFP4 W (64-byte rows): instruction u fills rows (4w+u)*16 .. +15; lane l: row (4w+u)*16 + l/4,
+    // slot l%4, chunk (l%4) ^ ((row>>2)&3).  E8M0 scales: 4 bytes per row, row 64w + l.
+    // Rows past M (N) repeat the last row; their results are never stored.
+    constexpr int WINST = WFMT == QVD_W_MXFP4 ? 4 : 8;
+    const uint32_t w_row_bytes = WFMT == QVD_W_MXFP4 ? (uint32_t)K / 2 : (uint32_t)K;
+    uint32_t a_off[8], w_off[WINST];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        int r = m0 + ld_row + 32 * j;
-        r = r < M ? r : M - 1;
-        a_off[j] = r;
+    for (int u = 0; u < 8; ++u) {
+        const int r = (8 * wv + u) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const int row = m0 + r < M ? m0 + r : M - 1;
+        a_off[u] = (uint32_t)row * (uint32_t)K + 16u * c;
     }
 #pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-        int r = n0 + wld_row + WSTEP * j;
-        r = r < N ? r : N - 1;
-        w_off[j] = r;
+    for (int u = 0; u < WINST; ++u) {
+        int r, c;
+        if (WFMT == QVD_W_MXFP4) {
+            r = (4 * wv + u) * 16 + (lane >> 2);
+            c = (lane & 3) ^ ((r >> 2) & 3);
+        } else {
+            r = (8 * wv + u) * 8 + (lane >> 3);
+            c = (lane & 7) ^ (r & 7);
+        }
+        const int row = n0 + r < N ? n0 + r : N - 1;
+        w_off[u] = (uint32_t)row * w_row_bytes + 16u * c;
     }
-    const uint8_t* e_src = nullptr;
+    uint32_t e_off = 0;
     if (WFMT == QVD_W_MXFP4) {
-        int r = n0 + tid;
-        r = r < N ? r : N - 1;
-        e_src = g.e8 + (int64_t)r * (K / 32);
+        const int r = 64 * wv + lane;
+        const int row = n0 + r < N ? n0 + r : N - 1;
+        e_off = (uint32_t)row * (uint32_t)(K / 32);
     }
-
     v4f acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    u32x4 ra[8], rw[WJ];
-    u32 re = 0;
-#define QVD_GLOAD(k0)                                                                              \
-    do {                                                                                           \
-        _Pragma("unroll") for (int j = 0; j < 8; ++j) ra[j] =                                      \
-            *reinterpret_cast<const u32x4*>(a_base + (int64_t)a_off[j] * K + (k0));                \
-        _Pragma("unroll") for (int j = 0; j < WJ; ++j) rw[j] = *reinterpret_cast<const u32x4*>(    \
-            w_base + (int64_t)w_off[j] * w_row_bytes + (WFMT == QVD_W_MXFP4 ? (k0) / 2 : (k0)));    \
-        if (WFMT == QVD_W_MXFP4) re = *reinterpret_cast<const u32*>(e_src + (k0) / 32);            \
-    } while (0)
-#define QVD_LSTORE(buf)                                                                            \
-    do {                                                                                           \
-        uint8_t* As_ = smem + (buf) * Cfg::STAGE;                                                  \
-        uint8_t* Ws_ = As_ + BM * BK;                                                              \
-        _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                            \
-            const int r = ld_row + 32 * j;                                                         \
-            *reinterpret_cast<u32x4*>(As_ + r * 128 + ((ld_ch ^ (r & 7)) << 4)) = ra[j];           \
-        }                                                                                          \
-        if (WFMT == QVD_W_MXFP4) {                                                                 \
-            _Pragma("unroll") for (int j = 0; j < WJ; ++j) {                                       \
-                const int r = wld_row + WSTEP * j;                                                 \
-                *reinterpret_cast<u32x4*>(Ws_ + r * 64 + ((wld_ch ^ ((r >> 2) & 3)) << 4)) = rw[j]; \
-            }                                                                                      \
-            reinterpret_cast<u32*>(Ws_ + Cfg::W_BYTES)[tid] = re;                                  \
-        } else {                                                                                   \
-            _Pragma("unroll") for (int j = 0; j < WJ; ++j) {                                       \
-                const int r = ld_row + 32 * j;                                                     \
-                *reinterpret_cast<u32x4*>(Ws_ + r * 128 + ((ld_ch ^ (r & 7)) << 4)) = rw[j];       \
-            }                                                                                      \
-        }                                                                                          \
-    } while (0)
-
     const int KT = K / BK;
-    QVD_GLOAD(0);
-    QVD_LSTORE(0);
-    __syncthreads();
+    stage_tiles<WFMT>(g, smem, 0, 0, wv, a_off, w_off, e_off);
     const int fr = lane & 15, fg = lane >> 4;
     for (int kt = 0; kt < KT; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < KT) QVD_GLOAD((kt + 1) * BK);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                       // tile kt is in LDS; every wave is done with kt-1
+        if (kt + 1 < KT) stage_tiles<WFMT>(g, smem, buf ^ 1, (kt + 1) * BK, wv, a_off, w_off, e_off);
         const uint8_t* As = smem + buf * Cfg::STAGE;
         const uint8_t* Ws = As + BM * BK;
+        // Software-pipelined fragment reads: every fragment is read one MFMA group ahead of its
+        // use and sched_barrier pins that order (left alone, the scheduler hoists all the reads
+        // and waits for every one of them before the first MFMA).
         v8i bfr[8];
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-            bfr[mb] = WFMT == QVD_W_MXFP4 ? frag_fp8_for_fp4(As, 128 * wm + 16 * mb + fr, fg)
-                                          : frag_fp8(As, 128 * wm + 16 * mb + fr, fg);
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
+        v8i af, af_next;
+        int sc = 0, sc_next = 0;
+        auto wfrag = [&](int nb, v8i& f, int& scale) {
             const int r = 128 * wn + 16 * nb + fr;
             if (WFMT == QVD_W_MXFP4) {
-                const v8i af = frag_fp4(Ws, r, fg);
-                const int sc = (int)(reinterpret_cast<const u32*>(Ws + Cfg::W_BYTES)[r] >> (8 * fg));
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af, bfr[mb], acc[nb][mb], 4, 0, 0, sc, 0, 127);
+                f = frag_fp4(Ws, r, fg);
+                scale = (int)(reinterpret_cast<const u32*>(Ws + Cfg::W_BYTES)[r] >> (8 * fg));
             } else {
-                const v8i af = frag_fp8(Ws, r, fg);
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af, bfr[mb], acc[nb][mb], 0, 0, 0, 0, 0, 0);
+                f = frag_fp8(Ws, r, fg);
             }
+        };
+        auto afrag = [&](int mb) {
+            return WFMT == QVD_W_MXFP4 ? frag_fp8_for_fp4(As, 128 * wm + 16 * mb + fr, fg)
+                                       : frag_fp8(As, 128 * wm + 16 * mb + fr, fg);
+        };
+        auto mfma = [&](const v8i& a, const v8i& b, v4f c, int scale) {
+            return WFMT == QVD_W_MXFP4
+                ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale, 0, 127)
+                : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+        };
+        wfrag(0, af, sc);
+        bfr[0] = afrag(0);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            if (mb + 1 < 8) bfr[mb + 1] = afrag(mb + 1);
+            else wfrag(1, af_next, sc_next);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[0][mb] = mfma(af, bfr[mb], acc[0][mb], sc);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < KT) QVD_LSTORE(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int nb = 1; nb < 8; ++nb) {
+            af = af_next;
+            sc = sc_next;
+            if (nb + 1 < 8) wfrag(nb + 1, af_next, sc_next);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = mfma(af, bfr[mb], acc[nb][mb], sc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-#undef QVD_GLOAD
-#undef QVD_LSTORE
 
     // ---- epilogue: lane holds C[m][n .. n+3], m = mrow(mb), n = ncol(nb) ----------------------------
     const float alpha = WFMT == QVD_W_MXFP4 ? *g.s_a : (*g.s_a) * (*g.s_w);
@@ -403,6 +417,8 @@ static int validate_gemm(const char* fn, const uint8_t* a, const float* s_a, con
     QVD_REQUIRE(M >= 0 && N >= 128 && N % 128 == 0 && K >= 128 && K % 128 == 0, QVD_ESHAPE,
                 "%s: M = %d, N = %d, K = %d (N, K: positive multiples of 128)", fn, M, N, K);
     QVD_REQUIRE(gemm_tiles(M, N) < (1ll << 31), QVD_ESHAPE, "%s: too many tiles", fn);
+    QVD_REQUIRE((double)M * K < 4294967296.0 && (double)N * K < 4294967296.0, QVD_ESHAPE,
+                "%s: operands must stay below 4 GiB (M = %d, N = %d, K = %d)", fn, M, N, K);
     QVD_REQUIRE(s_a != nullptr && w != nullptr, QVD_EINVAL, "%s: s_a or w is NULL", fn);
     QVD_REQUIRE(aligned16(w) && (!bias || aligned16(bias)), QVD_EALIGN, "%s: w/bias not 16-byte aligned", fn);
     if (M > 0) QVD_REQUIRE(a && aligned16(a), QVD_EINVAL, "%s: a is NULL or misaligned", fn);
@@ -456,6 +472,7 @@ int qvd_gemm_mxfp4(const uint8_t* a, const float* s_a, const uint8_t* w_packed,
     int s = validate_gemm("qvd_gemm_mxfp4", a, s_a, w_packed, bias, M, N, K, epi);
     if (s) return s;
     QVD_PTR(e8m0);
+    QVD_REQUIRE(((uintptr_t)e8m0 & 3u) == 0, QVD_EALIGN, "qvd_gemm_mxfp4: e8m0 must be 4-byte aligned");
     QVD_DEVICE_OK();
     return launch_gemm(a, s_a, w_packed, e8m0, nullptr, QVD_W_MXFP4, bias, M, N, K, *epi,
                        (hipStream_t)stream);

@@ -32,6 +32,14 @@ def test_exports_every_header_function(lib):
     assert sorted(_lib.SIGNATURES) == names
 
 
+def test_no_unresolved_library_symbols(lib):
+    """Every kernel stub and helper is defined inside the library (a template instantiation the
+    host pass drops shows up as an undefined qvd:: symbol)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", LIB], capture_output=True, text=True).stdout
+    bad = [l for l in out.splitlines() if "qvd" in l]
+    assert not bad, bad
+
+
 def test_abi_version_and_error_string(lib):
     assert lib.qvd_abi_version() == _lib.ABI_VERSION
     assert isinstance(lib.qvd_last_error(), bytes)
