@@ -36,6 +36,7 @@ struct AttnSmem {
     uint16_t vt[128 * 128];         // 32 KB, fp16 bit patterns
     int tiles[MAX_KEPT];            // the valid entries of this row's kept-tile list, in order
     int wcount[4];
+    float red[4];                   // block reduction of max|O|
 };
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -193,8 +194,9 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
     const float* __restrict__ k_scale, const uint16_t* __restrict__ vt, int L, int H,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int kmax, float c_log2,
     uint16_t* __restrict__ out, float* __restrict__ amax_partials) {
+    // a single LDS object: with a second __shared__ array the compiler waits for every DMA before
+    // each LDS read
     __shared__ __attribute__((aligned(16))) AttnSmem sm;
-    __shared__ float red[4];
     const int i = blockIdx.x, h = blockIdx.y, T = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int fr = lane & 15, fg = lane >> 4;
@@ -308,7 +310,7 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
         }
     }
     if (WRITE_AMAX) {
-        amax = block_max_nonneg<4>(amax, red);
+        amax = block_max_nonneg<4>(amax, sm.red);
         if (tid == 0) amax_partials[h * T + i] = amax;
     }
 }

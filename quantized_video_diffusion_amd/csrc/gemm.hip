@@ -16,6 +16,8 @@
 //   16-row MFMA fragment reads are bank-conflict free;
 //   tile order: contiguous tile ranges per XCD (workgroup b runs on XCD b % 8) and groups of 8 token
 //   tiles sweeping the output tiles, so an XCD's L2 holds the operands its tiles share.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -55,7 +57,22 @@ QVD_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
     tn = in / gm;
 }
 
-QVD_DEV float gelu_erf(float y) { return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f)); }
+// GELU(y) = y/2 (1 + erf(y/sqrt 2)).  erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26: erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1/(1 + p z), z >= 0, with
+// |error| <= 1.5e-7; odd extension for z < 0.  Two transcendental and about ten plain instructions,
+// far below the error of the bf16 rounding that follows.
+QVD_DEV float gelu_erf(float y) {
+    const float z = fabsf(y) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float p = fmaf(1.061405429f, t, -1.453152027f);
+    p = fmaf(p, t, 1.421413741f);
+    p = fmaf(p, t, -0.284496736f);
+    p = fmaf(p, t, 0.254829592f);
+    p *= t;
+    const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
+    const float erf_abs = fmaf(-p, e, 1.0f);
+    return 0.5f * y * (1.0f + __builtin_copysignf(erf_abs, y));
+}
 
 // 32-byte MFMA fragment of row r (16-byte chunks 2g and 2g+1 of a 128-byte, XOR-swizzled row)
 QVD_DEV v8i frag_fp8(const uint8_t* tile, int r, int g) {
@@ -114,135 +131,60 @@ QVD_DEV void stage_tiles(const GemmArgs& g, uint8_t* smem, int buf, int k0, int 
                                          4, 0, 0);
 }
 
-template <int EPI, int WFMT>
-__global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
-    using Cfg = TileCfg<WFMT>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg::STAGE];
+// ---- accumulator layouts -------------------------------------------------------------------------
+// Both MFMA shapes below compute C^T = W . A^T, so a lane holds runs of 4 consecutive output
+// columns (n) of one token row (m).  A layout enumerates them as NCG column groups x MR row blocks.
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv & 1, wn = wv >> 1;
-    int tm, tn;
-    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int M = g.M, N = g.N, K = g.K;
+// v_mfma_f32_16x16x128: acc[nb][mb], lane l holds C[16 mb + l%16][16 nb + 4 (l/16) .. +3]
+struct Layout16 {
+    static constexpr int NCG = 8, MR = 8;
+    typedef v4f Acc[8][8];
+    QVD_DEV static int ncol(int cg, int lane) { return 16 * cg + 4 * (lane >> 4); }
+    QVD_DEV static int mrow(int r, int lane) { return 16 * r + (lane & 15); }
+    QVD_DEV static v4f get(const Acc& a, int cg, int r) { return a[cg][r]; }
+};
 
-    // ---- HBM/L2 -> LDS staging with global_load_lds (no register round trip) ---------------------
-    // FP8 operands (128-byte rows): wave w's instruction u fills LDS rows (8w+u)*8 .. +7; lane l
-    // lands in row r = (8w+u)*8 + l/8, slot l%8, and fetches chunk (l%8) ^ (r&7) of its row.
-    // MXFP4 W (64-byte rows): instruction u fills rows (4w+u)*16 .. +15; lane l: row (4w+u)*16 + l/4,
-    // slot l%4, chunk (l%4) ^ ((row>>2)&3).  E8M0 scales: 4 bytes per row, row 64w + l.
-    // Rows past M (N) repeat the last row; their results are never stored.
-    constexpr int WINST = WFMT == QVD_W_MXFP4 ? 4 : 8;
-    const uint32_t w_row_bytes = WFMT == QVD_W_MXFP4 ? (uint32_t)K / 2 : (uint32_t)K;
-    uint32_t a_off[8], w_off[WINST];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int r = (8 * wv + u) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
-        const int row = m0 + r < M ? m0 + r : M - 1;
-        a_off[u] = (uint32_t)row * (uint32_t)K + 16u * c;
+// v_mfma_f32_32x32x64: acc[nb][mb] (16 values), value 4g + i of lane l is
+// C[32 mb + l%32][32 nb + 8 g + 4 (l/32) + i]
+struct Layout32 {
+    static constexpr int NCG = 16, MR = 4;
+    typedef v16f Acc[4][4];
+    QVD_DEV static int ncol(int cg, int lane) { return 32 * (cg >> 2) + 8 * (cg & 3) + 4 * (lane >> 5); }
+    QVD_DEV static int mrow(int r, int lane) { return 32 * r + (lane & 31); }
+    QVD_DEV static v4f get(const Acc& a, int cg, int r) {
+        const v16f& v = a[cg >> 2][r];
+        const int b = 4 * (cg & 3);
+        return (v4f){v[b], v[b + 1], v[b + 2], v[b + 3]};
     }
-#pragma unroll
-    for (int u = 0; u < WINST; ++u) {
-        int r, c;
-        if (WFMT == QVD_W_MXFP4) {
-            r = (4 * wv + u) * 16 + (lane >> 2);
-            c = (lane & 3) ^ ((r >> 2) & 3);
-        } else {
-            r = (8 * wv + u) * 8 + (lane >> 3);
-            c = (lane & 7) ^ (r & 7);
-        }
-        const int row = n0 + r < N ? n0 + r : N - 1;
-        w_off[u] = (uint32_t)row * w_row_bytes + 16u * c;
-    }
-    uint32_t e_off = 0;
-    if (WFMT == QVD_W_MXFP4) {
-        const int r = 64 * wv + lane;
-        const int row = n0 + r < N ? n0 + r : N - 1;
-        e_off = (uint32_t)row * (uint32_t)(K / 32);
-    }
-    v4f acc[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+};
 
-    const int KT = K / BK;
-    stage_tiles<WFMT>(g, smem, 0, 0, wv, a_off, w_off, e_off);
-    const int fr = lane & 15, fg = lane >> 4;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                       // tile kt is in LDS; every wave is done with kt-1
-        if (kt + 1 < KT) stage_tiles<WFMT>(g, smem, buf ^ 1, (kt + 1) * BK, wv, a_off, w_off, e_off);
-        const uint8_t* As = smem + buf * Cfg::STAGE;
-        const uint8_t* Ws = As + BM * BK;
-        // Software-pipelined fragment reads: every fragment is read one MFMA group ahead of its
-        // use and sched_barrier pins that order (left alone, the scheduler hoists all the reads
-        // and waits for every one of them before the first MFMA).
-        v8i bfr[8];
-        v8i af, af_next;
-        int sc = 0, sc_next = 0;
-        auto wfrag = [&](int nb, v8i& f, int& scale) {
-            const int r = 128 * wn + 16 * nb + fr;
-            if (WFMT == QVD_W_MXFP4) {
-                f = frag_fp4(Ws, r, fg);
-                scale = (int)(reinterpret_cast<const u32*>(Ws + Cfg::W_BYTES)[r] >> (8 * fg));
-            } else {
-                f = frag_fp8(Ws, r, fg);
-            }
-        };
-        auto afrag = [&](int mb) {
-            return WFMT == QVD_W_MXFP4 ? frag_fp8_for_fp4(As, 128 * wm + 16 * mb + fr, fg)
-                                       : frag_fp8(As, 128 * wm + 16 * mb + fr, fg);
-        };
-        auto mfma = [&](const v8i& a, const v8i& b, v4f c, int scale) {
-            return WFMT == QVD_W_MXFP4
-                ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale, 0, 127)
-                : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-        };
-        wfrag(0, af, sc);
-        bfr[0] = afrag(0);
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-            if (mb + 1 < 8) bfr[mb + 1] = afrag(mb + 1);
-            else wfrag(1, af_next, sc_next);
-            __builtin_amdgcn_sched_barrier(0);
-            acc[0][mb] = mfma(af, bfr[mb], acc[0][mb], sc);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int nb = 1; nb < 8; ++nb) {
-            af = af_next;
-            sc = sc_next;
-            if (nb + 1 < 8) wfrag(nb + 1, af_next, sc_next);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = mfma(af, bfr[mb], acc[nb][mb], sc);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
+QVD_DEV float4 load_bias4(const float* bias, int n) {
+    return bias ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
 
-    // ---- epilogue: lane holds C[m][n .. n+3], m = mrow(mb), n = ncol(nb) ----------------------------
-    const float alpha = WFMT == QVD_W_MXFP4 ? *g.s_a : (*g.s_a) * (*g.s_w);
+// ---- fused epilogues: y = acc * alpha + bias, then the mode's output ---------------------------------
+// The wave owns the 128 x 128 block at (mw0, nw0) = (m0 + 128 wm, n0 + 128 wn).
+template <int EPI, class LY>
+QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float alpha, int m0, int n0,
+                           int wm, int wn, float* red) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int M = g.M, N = g.N;
     const int mw0 = m0 + 128 * wm, nw0 = n0 + 128 * wn;
     const bool wave_live = nw0 < N && mw0 < M;
     const qvd_epilogue& ep = g.epi;
 
     if (EPI == QVD_EPI_GELU) {
-        __shared__ float red[4];
         float amax = 0.0f;
         if (wave_live) {
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int n = nw0 + 16 * nb + 4 * fg;
-                float4 b = g.bias ? *reinterpret_cast<const float4*>(g.bias + n)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int cg = 0; cg < LY::NCG; ++cg) {
+                const int n = nw0 + LY::ncol(cg, lane);
+                const float4 b = load_bias4(g.bias, n);
 #pragma unroll
-                for (int mb = 0; mb < 8; ++mb) {
-                    const int m = mw0 + 16 * mb + fr;
+                for (int r = 0; r < LY::MR; ++r) {
+                    const int m = mw0 + LY::mrow(r, lane);
                     if (m < M) {
-                        const v4f c = acc[nb][mb];
+                        const v4f c = LY::get(acc, cg, r);
                         const u32 p0 = pack_bf16x2(gelu_erf(c[0] * alpha + b.x), gelu_erf(c[1] * alpha + b.y));
                         const u32 p1 = pack_bf16x2(gelu_erf(c[2] * alpha + b.z), gelu_erf(c[3] * alpha + b.w));
                         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(p0)), fabsf(bf16hi(p0))),
@@ -271,23 +213,21 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
             const int64_t Lp = (int64_t)Tm * 128;
             uint16_t* vt = ep.v + (int64_t)head * 128 * Lp;
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int n = nw0 + 16 * nb + 4 * fg;
-                float4 b = g.bias ? *reinterpret_cast<const float4*>(g.bias + n)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-                const int dd = 16 * nb + 4 * fg;
+            for (int cg = 0; cg < LY::NCG; ++cg) {
+                const int dd = LY::ncol(cg, lane);
+                const float4 b = load_bias4(g.bias, nw0 + dd);
 #pragma unroll
-                for (int mb = 0; mb < 8; ++mb) {
-                    const int m = mw0 + 16 * mb + fr;
-                    const v4f c = acc[nb][mb];
-                    float y[4] = {c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z,
-                                  c[3] * alpha + b.w};
+                for (int r = 0; r < LY::MR; ++r) {
+                    const int m = mw0 + LY::mrow(r, lane);
+                    const v4f c = LY::get(acc, cg, r);
+                    const float y[4] = {c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z,
+                                        c[3] * alpha + b.w};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float vb = bf16lo(pack_bf16x2(y[r], 0.0f));
+                    for (int i = 0; i < 4; ++i) {
+                        const float vb = bf16lo(pack_bf16x2(y[i], 0.0f));
                         const float vc = fminf(fmaxf(vb, -65504.0f), 65504.0f);
                         const uint16_t h16 = m < M ? __builtin_bit_cast(uint16_t, (_Float16)vc) : (uint16_t)0;
-                        vt[(int64_t)(dd + r) * Lp + m] = h16;
+                        vt[(int64_t)(dd + i) * Lp + m] = h16;
                     }
                 }
             }
@@ -296,13 +236,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
         // Q or K: round to bf16, then one symmetric INT8 scale over this (128-token tile, head)
         float amax = 0.0f;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int n = nw0 + 16 * nb + 4 * fg;
-            float4 b = g.bias ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int cg = 0; cg < LY::NCG; ++cg) {
+            const float4 b = load_bias4(g.bias, nw0 + LY::ncol(cg, lane));
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-                const int m = mw0 + 16 * mb + fr;
-                const v4f c = acc[nb][mb];
+            for (int r = 0; r < LY::MR; ++r) {
+                const int m = mw0 + LY::mrow(r, lane);
+                const v4f c = LY::get(acc, cg, r);
                 const u32 p0 = pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y);
                 const u32 p1 = pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w);
                 if (m < M)
@@ -316,14 +255,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
         float* sdst = part == 0 ? ep.q_scale : ep.k_scale;
         if (lane == 0) sdst[head * Tm + (mw0 >> 7)] = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 127.0f);
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int n = nw0 + 16 * nb + 4 * fg;
-            float4 b = g.bias ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int cg = 0; cg < LY::NCG; ++cg) {
+            const int n = nw0 + LY::ncol(cg, lane);
+            const float4 b = load_bias4(g.bias, n);
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-                const int m = mw0 + 16 * mb + fr;
+            for (int r = 0; r < LY::MR; ++r) {
+                const int m = mw0 + LY::mrow(r, lane);
                 if (m < M) {
-                    const v4f c = acc[nb][mb];
+                    const v4f c = LY::get(acc, cg, r);
                     const u32 p0 = pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y);
                     const u32 p1 = pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w);
                     const u32 q = (u32)(int8_encode(bf16lo(p0), inv) & 0xFF) |
@@ -338,16 +277,16 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
     }
 
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-        const int n = nw0 + 16 * nb + 4 * fg;
-        float4 b = g.bias ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int cg = 0; cg < LY::NCG; ++cg) {
+        const int n = nw0 + LY::ncol(cg, lane);
+        const float4 b = load_bias4(g.bias, n);
         float4 gt = make_float4(0.f, 0.f, 0.f, 0.f);
         if (EPI == QVD_EPI_RESID_GATE) gt = *reinterpret_cast<const float4*>(ep.gate + n);
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-            const int m = mw0 + 16 * mb + fr;
+        for (int r = 0; r < LY::MR; ++r) {
+            const int m = mw0 + LY::mrow(r, lane);
             if (m >= M) continue;
-            const v4f c = acc[nb][mb];
+            const v4f c = LY::get(acc, cg, r);
             const float y0 = c[0] * alpha + b.x, y1 = c[1] * alpha + b.y;
             const float y2 = c[2] * alpha + b.z, y3 = c[3] * alpha + b.w;
             const int64_t off = (int64_t)m * N + n;
@@ -366,21 +305,243 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs g) {
     }
 }
 
-template <int WFMT>
-static int launch_fmt(const GemmArgs& g, hipStream_t st) {
+// ================================================================================================
+// E4M3 x MXFP4: 256 x 256 x 128 tiles, two LDS stages, v_mfma_scale_f32_16x16x128_f8f6f4 with the
+// E2M1 operand's E8M0 scale per lane.
+template <int EPI>
+__global__ void __launch_bounds__(256, 1) k_gemm_mx(GemmArgs g) {
+    using Cfg = TileCfg<QVD_W_MXFP4>;
+    constexpr int WFMT = QVD_W_MXFP4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg::STAGE];
+    __shared__ float red[4];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv & 1, wn = wv >> 1;
+    int tm, tn;
+    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+
+    // ---- HBM/L2 -> LDS staging with global_load_lds (no register round trip) ---------------------
+    // A (128-byte rows): wave w's instruction u fills LDS rows (8w+u)*8 .. +7; lane l lands in row
+    // r = (8w+u)*8 + l/8, slot l%8, and fetches chunk (l%8) ^ (r&7) of its row.
+    // W (64-byte rows): instruction u fills rows (4w+u)*16 .. +15; lane l: row (4w+u)*16 + l/4,
+    // slot l%4, chunk (l%4) ^ ((row>>2)&3).  E8M0 scales: 4 bytes per row, row 64w + l.
+    // Rows past M (N) repeat the last row; their results are never stored.
+    uint32_t a_off[8], w_off[4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int r = (8 * wv + u) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const int row = m0 + r < M ? m0 + r : M - 1;
+        a_off[u] = (uint32_t)row * (uint32_t)K + 16u * c;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = (4 * wv + u) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        const int row = n0 + r < N ? n0 + r : N - 1;
+        w_off[u] = (uint32_t)row * (uint32_t)(K / 2) + 16u * c;
+    }
+    uint32_t e_off;
+    {
+        const int r = 64 * wv + lane;
+        const int row = n0 + r < N ? n0 + r : N - 1;
+        e_off = (uint32_t)row * (uint32_t)(K / 32);
+    }
+    Layout16::Acc acc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    const int KT = K / BK;
+    stage_tiles<WFMT>(g, smem, 0, 0, wv, a_off, w_off, e_off);
+    const int fr = lane & 15, fg = lane >> 4;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                       // tile kt is in LDS; every wave is done with kt-1
+        if (kt + 1 < KT) stage_tiles<WFMT>(g, smem, buf ^ 1, (kt + 1) * BK, wv, a_off, w_off, e_off);
+        const uint8_t* As = smem + buf * Cfg::STAGE;
+        const uint8_t* Ws = As + BM * BK;
+        v8i bfr[8];
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) bfr[mb] = frag_fp8_for_fp4(As, 128 * wm + 16 * mb + fr, fg);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int r = 128 * wn + 16 * nb + fr;
+            const v8i af = frag_fp4(Ws, r, fg);
+            const int sc = (int)(reinterpret_cast<const u32*>(Ws + Cfg::W_BYTES)[r] >> (8 * fg));
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[mb], acc[nb][mb], 4, 0, 0,
+                                                                              sc, 0, 127);
+        }
+    }
+    gemm_epilogue<EPI, Layout16>(g, acc, *g.s_a, m0, n0, wm, wn, red);
+}
+
+// ================================================================================================
+// E4M3 x E4M3: 256 x 256 x 64 K-steps through a ring of four LDS stages, v_mfma_f32_32x32x64_f8f6f4.
+//
+// Per K-step each wave issues the DMA of the stage three steps ahead, then runs its 16 MFMAs on
+// fragments already in registers while it reads the next step's fragments from LDS, one 16-byte
+// read per MFMA.  A single s_barrier per step (after the wave's own DMA for the next stage has landed
+// and its fragment reads have completed) both publishes the next stage and frees the stage just read.
+// Stage layout: A rows and W rows of 64 bytes; 16-byte chunk c of row r sits at chunk c ^ ((r>>2)&3).
+// The 64 LDS banks (256 bytes) serve a 16-lane group of a 16-byte read per cycle: rows r .. r+15 at one
+// logical chunk then land on 16 distinct bank quads.  DMA writes are 1 KB contiguous per instruction.
+constexpr int BK8 = 64;
+constexpr int NSTAGE8 = 4;
+constexpr int STAGE8 = (BM + BN) * BK8;          // 32 KB
+
+// DMA instruction u (0..3: A rows, 4..7: W rows) of this wave's share of one stage
+QVD_DEV void dma_f8(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
+                    const uint32_t* w_off, int u) {
+    uint8_t* dst = smem + buf * STAGE8 + (u < 4 ? 0 : BM * BK8) + (4 * wv + (u & 3)) * 1024;
+    const uint8_t* src = u < 4 ? g.a + a_off[u] + k0 : g.w + w_off[u & 3] + k0;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+QVD_DEV void stage_f8(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
+                      const uint32_t* w_off) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dma_f8(g, smem, buf, k0, wv, a_off, w_off, u);
+}
+
+// 32-byte MFMA operand of rows 32 b .. 32 b + 31 of a 64-byte-row tile: lane l reads row l%32,
+// bytes 32 (l/32) .. +31 (offsets precomputed in lo/hi)
+QVD_DEV v8i frag32(const uint8_t* tile, int b, uint32_t lo, uint32_t hi) {
+    const v4i x = *reinterpret_cast<const v4i*>(tile + b * 2048 + lo);
+    const v4i y = *reinterpret_cast<const v4i*>(tile + b * 2048 + hi);
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// wait until at most N of this wave's vector-memory operations are outstanding (whole stages of 8
+// DMA instructions), drain its LDS reads, and meet the other waves
+template <int N>
+QVD_DEV void wait_stage_barrier() {
+    static_assert(N == 0 || N == 8 || N == 16 || N == 24, "vmcnt in whole stages");
+    if (N == 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int V> using IC = std::integral_constant<int, V>;
+
+template <int EPI>
+__global__ void __launch_bounds__(256, 1) k_gemm_f8(GemmArgs g) {
+    // one LDS object: the stage ring and, past it, the epilogue's reduction slots (a second __shared__
+    // array makes the compiler wait for every DMA before each LDS read)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE8 * STAGE8 + 16];
+    float* red = reinterpret_cast<float*>(smem + NSTAGE8 * STAGE8);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv & 1, wn = wv >> 1;
+    int tm, tn;
+    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+
+    // DMA: wave w's instruction u fills rows (4w+u)*16 .. +15 of a tile; lane l lands in row
+    // r = (4w+u)*16 + l/4, slot l%4, and fetches chunk (l%4) ^ ((r>>2)&3) of its row.
+    // Rows past M (N) repeat the last row; their results are never stored.
+    uint32_t a_off[4], w_off[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = (4 * wv + u) * 16 + (lane >> 2);
+        const uint32_t c = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+        const int ra = m0 + r < M ? m0 + r : M - 1;
+        const int rw = n0 + r < N ? n0 + r : N - 1;
+        a_off[u] = (uint32_t)ra * (uint32_t)K + 16u * c;
+        w_off[u] = (uint32_t)rw * (uint32_t)K + 16u * c;
+    }
+    // fragment reads: row l%32 of a 32-row block, logical chunks 2 (l/32) and 2 (l/32) + 1
+    const uint32_t fs = (uint32_t)(((lane & 31) >> 2) & 3);
+    const uint32_t flo = (uint32_t)(lane & 31) * 64u + 16u * ((2u * (uint32_t)(lane >> 5)) ^ fs);
+    const uint32_t fhi = (uint32_t)(lane & 31) * 64u + 16u * ((2u * (uint32_t)(lane >> 5) + 1u) ^ fs);
+    const int a_blk = 4 * wm, w_blk = 4 * wn;    // first 32-row block of this wave's rows
+
+    Layout32::Acc acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // K is a multiple of 128, so the step count KT is even and the register sets alternate in pairs
+    const int KT = K / BK8;
+    if (KT >= NSTAGE8) {
+        for (int s = 0; s < NSTAGE8; ++s) stage_f8(g, smem, s, s * BK8, wv, a_off, w_off);
+        wait_stage_barrier<24>();                // stage 0 has landed for every wave
+    } else {
+        for (int s = 0; s < KT; ++s) stage_f8(g, smem, s, s * BK8, wv, a_off, w_off);
+        wait_stage_barrier<8>();
+    }
+
+    v8i fr[2][8];                                // [set][W blocks 0..3, A blocks 4..7]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fr[0][i] = frag32(smem + BM * BK8, w_blk + i, flo, fhi);
+        fr[0][4 + i] = frag32(smem, a_blk + i, flo, fhi);
+    }
+
+    // One K-step on register set P.  WAIT >= 0: first wait for stage kt+1 with WAIT DMA
+    // instructions (later stages) left in flight.  REFILL: issue stage kt+4 into the stage of kt.
+    // Issue order: the refill DMA and the 16 fragment reads of step kt+1 go out during the first 8
+    // MFMAs, so their latency is covered by the other 8 before the next barrier.
+    auto kstep = [&](auto P, auto WAIT, auto REFILL, int kt) {
+        constexpr int p = decltype(P)::value;
+        constexpr int wait = decltype(WAIT)::value;
+        constexpr bool refill = decltype(REFILL)::value != 0;
+        if (wait >= 0) wait_stage_barrier<(wait < 0 ? 0 : wait)>();
+        const uint8_t* As = smem + ((kt + 1) & 3) * STAGE8;
+        const uint8_t* Ws = As + BM * BK8;
+        // the last step's reads fetch a stale stage and are never used
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fr[p][q >> 2], fr[p][4 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0, 0, 0, 0);
+            if (q < 8) {
+                if (refill) dma_f8(g, smem, kt & 3, (kt + NSTAGE8) * BK8, wv, a_off, w_off, q);
+                fr[p ^ 1][q] = q < 4 ? frag32(Ws, w_blk + q, flo, fhi) : frag32(As, a_blk + q - 4, flo, fhi);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    int kt = 0;
+    for (; kt + NSTAGE8 < KT; kt += 2) {
+        kstep(IC<0>{}, IC<16>{}, IC<1>{}, kt);
+        kstep(IC<1>{}, IC<16>{}, IC<1>{}, kt + 1);
+    }
+    if (KT >= NSTAGE8) {                         // kt = KT - 4
+        kstep(IC<0>{}, IC<16>{}, IC<0>{}, kt);
+        kstep(IC<1>{}, IC<8>{}, IC<0>{}, kt + 1);
+        kt += 2;
+    }
+    kstep(IC<0>{}, IC<0>{}, IC<0>{}, kt);        // kt = KT - 2
+    kstep(IC<1>{}, IC<-1>{}, IC<0>{}, kt + 1);   // kt = KT - 1
+    gemm_epilogue<EPI, Layout32>(g, acc, (*g.s_a) * (*g.s_w), m0, n0, wm, wn, red);
+}
+
+template <template <int> class KERN>
+static int launch_epi(const GemmArgs& g, hipStream_t st) {
     const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), blk(256);
     switch (g.epi.mode) {
-        case QVD_EPI_F32: hipLaunchKernelGGL((k_gemm<QVD_EPI_F32, WFMT>), grid, blk, 0, st, g); break;
-        case QVD_EPI_BF16: hipLaunchKernelGGL((k_gemm<QVD_EPI_BF16, WFMT>), grid, blk, 0, st, g); break;
-        case QVD_EPI_RESID_GATE:
-            hipLaunchKernelGGL((k_gemm<QVD_EPI_RESID_GATE, WFMT>), grid, blk, 0, st, g);
-            break;
-        case QVD_EPI_GELU: hipLaunchKernelGGL((k_gemm<QVD_EPI_GELU, WFMT>), grid, blk, 0, st, g); break;
-        case QVD_EPI_QKV: hipLaunchKernelGGL((k_gemm<QVD_EPI_QKV, WFMT>), grid, blk, 0, st, g); break;
+        case QVD_EPI_F32: hipLaunchKernelGGL(KERN<QVD_EPI_F32>::fn, grid, blk, 0, st, g); break;
+        case QVD_EPI_BF16: hipLaunchKernelGGL(KERN<QVD_EPI_BF16>::fn, grid, blk, 0, st, g); break;
+        case QVD_EPI_RESID_GATE: hipLaunchKernelGGL(KERN<QVD_EPI_RESID_GATE>::fn, grid, blk, 0, st, g); break;
+        case QVD_EPI_GELU: hipLaunchKernelGGL(KERN<QVD_EPI_GELU>::fn, grid, blk, 0, st, g); break;
+        case QVD_EPI_QKV: hipLaunchKernelGGL(KERN<QVD_EPI_QKV>::fn, grid, blk, 0, st, g); break;
         default: return fail(QVD_EINVAL, "gemm: epilogue mode %d", g.epi.mode);
     }
     return launch_status("gemm");
 }
+template <int EPI> struct KF8 { static constexpr auto fn = k_gemm_f8<EPI>; };
+template <int EPI> struct KMX { static constexpr auto fn = k_gemm_mx<EPI>; };
 
 int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t* e8, const float* s_w,
                 int w_fmt, const float* bias, int M, int N, int K, const qvd_epilogue& epi,
@@ -404,7 +565,7 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
     snprintf(key, sizeof(key), "gemm_%s_%s_%dx%dx%d", w_fmt == QVD_W_MXFP4 ? "mxfp4" : "fp8",
              (epi.mode >= 0 && epi.mode < 5) ? epi_name[epi.mode] : "?", M, N, K);
     TimingScope ts(key, st);
-    return w_fmt == QVD_W_MXFP4 ? launch_fmt<QVD_W_MXFP4>(g, st) : launch_fmt<QVD_W_FP8>(g, st);
+    return w_fmt == QVD_W_MXFP4 ? launch_epi<KMX>(g, st) : launch_epi<KF8>(g, st);
 }
 
 }  // namespace qvd
