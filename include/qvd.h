@@ -135,13 +135,15 @@ int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, in
  *   kv_idx : int32 [H][T][kmax], 1 <= kmax <= 1024; kv_cnt: int32 [H][T].  Entries outside [0, T) and counts outside
  *            [0, kmax] are ignored (clamped), so device data can never send the kernel out of
  *            bounds; a row with no kept key outputs zeros.  Tile lists are expected ascending
- *            with the diagonal present, but their order does not change the result.
+ *            with the diagonal present; another order changes the result only at the level of
+ *            fp16/fp32 rounding.
  *   out_amax_partials : NULL, or fp32 [H][T] receiving max|out| of each (h, i) tile (feeds the
  *            dynamic FP8 quantization of the attention output without another pass).
  *   ws     : qvd_sparse_attn_ws_bytes(L, H) bytes: V transposed to fp16 [H][128][T*128].
- * Arithmetic: INT8 MFMA scores (exact int32); pass 1 finds each row's maximum over the kept keys,
- * pass 2 rounds the numerators exp2((s - max) * log2 e) to fp16 and runs the fp16 MFMA P.V and the
- * numerator sum with fp32 accumulation.  |V| above 65504 saturates to 65504 in the product. */
+ * Arithmetic: INT8 MFMA scores (exact int32); one pass over the kept tiles with each row's running
+ * maximum m: numerators exp2((s - m) log2 e) rounded to fp16, the fp32 sums rescaled whenever m
+ * grows, fp16 MFMA P.V and numerator sums with fp32 accumulation.  Each weight is within one fp16
+ * rounding of the numerator taken against the final maximum.  |V| above 65504 saturates to 65504. */
 size_t qvd_sparse_attn_ws_bytes(int32_t L, int32_t H);
 int sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                 const uint16_t* v, int32_t L, int32_t H, int32_t head_dim,

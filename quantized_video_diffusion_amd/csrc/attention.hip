@@ -4,19 +4,20 @@
 // training bullet (the model runs with 80% attention sparsity) and section "运行速度如何", note under
 // the table (query and key are quantized to INT8 for the score computation).
 //
-// One workgroup per (query tile of 128 rows, head); four waves of 32 query rows.  Two passes over
-// the kept key tiles (masked tiles are never loaded or multiplied):
-//   pass 1: K tile -> LDS; S^T = K . Q^T with v_mfma_i32_16x16x64_i8 (exact int32, Q fragments in
-//           registers); each query row keeps its maximum of S * sQ*sK*sm_scale*log2(e);
-//   pass 2: K and V^T tiles -> LDS; S^T again; numerators exp2(s - max) rounded to fp16 against the
-//           final row maximum; O^T += V^T . P^T with v_mfma_f32_16x16x32_f16 and the numerator
-//           sum as ones . P^T on the same unit (fp32 accumulation).
-// Rounding against the final maximum makes every rounding decision a function of the scores alone:
-// the result is the oracle's reading (fp16 numerators, exact normalisation by their sum) up to the
-// fp32 accumulation order.
+// One workgroup per (query tile of 128 rows, head); four waves of 32 query rows; two workgroups per
+// CU.  One pass over the kept key tiles (masked tiles are never loaded or multiplied):
+//   S^T = K . Q^T with v_mfma_i32_16x16x64_i8 (exact int32, Q fragments in registers);
+//   running row maxima m of S * sQ*sK*sm_scale*log2(e); numerators exp2(s - m) rounded to fp16;
+//   the fp32 sums so far are multiplied by exp2(m_old - m_new) (every tile, branch-free);
+//   numerator sums (ones . P^T) and O^T += V^T . P^T with v_mfma_f32_16x16x32_f16, fp32 accumulation.
+// A numerator rounded against the running maximum and later rescaled differs from the one rounded
+// against the final maximum by at most one fp16 rounding (relative 2^-11); the output is normalised by
+// the sum of the numerators actually used.
 //
-// Staging: tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no register round trip).  Each
-// lane picks the global 16-byte chunk that belongs at its LDS slot, which applies an XOR swizzle:
+// Staging: tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no register round trip).  The K
+// tile's rows are permuted (key_of_row) so that each lane's 8 numerators of a 32-key block are 8
+// consecutive keys, read from V^T in one 16-byte access.  Each lane picks the global 16-byte chunk
+// that belongs at its LDS slot, which applies an XOR swizzle:
 // K rows (128 B) swizzle chunks by row & 7, V^T rows (256 B, fp16, keys contiguous) by row & 15,
 // so the 16-row MFMA fragment reads hit distinct banks.  V arrives transposed and in fp16 from the
 // QKV GEMM epilogue (or from a conversion pass for bf16 callers).  Computing the transposed products
@@ -54,9 +55,20 @@ QVD_DEV void dma16(const void* g, void* lds_slot_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_slot_base, 16, 0, 0);
 }
 
-QVD_DEV void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// wait until at most 4 DMA/vector loads are outstanding (the 4 K-tile loads issued last)
-QVD_DEV void dma_wait_but_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+// Barriers with explicit waits: this wave's DMA (all of it, or all but the 4 K-tile instructions
+// issued last) has landed and its LDS reads are done, then every wave meets.  (__syncthreads() would
+// also wait for the K prefetch, which is meant to stay in flight.)
+QVD_DEV void dma_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+QVD_DEV void dma_barrier_but_4() { asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Key (0..127 within its tile) held by row rho of the LDS K tile.  Row rho = 16 kb + 4 g + r is the
+// score-block row that lane group g receives as element r of block kb; the map gives lane group g the
+// keys 32 (kb/2) + 8 g + 4 (kb%2) + r, i.e. 8 consecutive keys across blocks 2 kp and 2 kp + 1, which
+// one 16-byte read of a V^T row then matches.
+QVD_DEV int key_of_row(int rho) {
+    const int kb = rho >> 4, g = (rho >> 2) & 3, r = rho & 3;
+    return 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
+}
 
 // Q fragments of this wave (B operand): qf[qb][ks] = Q[q0 + 16 qb + fr][h][64 ks + 16 fg .. +15]
 QVD_DEV void load_q_frags(const int8_t* __restrict__ q, int L, int H, int h, int q0, int fr, int fg,
@@ -72,7 +84,8 @@ QVD_DEV void load_q_frags(const int8_t* __restrict__ q, int L, int H, int h, int
 }
 
 // K tile j -> LDS.  Wave w, instruction u fills LDS rows (4w + u)*8 .. +7; lane l lands in row
-// r = (4w+u)*8 + l/8, slot l%8, and fetches chunk (l%8) ^ (r & 7) of key row j*128 + r (clamped).
+// r = (4w+u)*8 + l/8, slot l%8, and fetches chunk (l%8) ^ (r & 7) of key row j*128 + key_of_row(r)
+// (clamped to L-1).
 QVD_DEV void stage_k(int8_t* kbuf, const int8_t* __restrict__ k, int L, int H, int h, int j,
                      int wv, int lane) {
 #pragma unroll
@@ -80,7 +93,7 @@ QVD_DEV void stage_k(int8_t* kbuf, const int8_t* __restrict__ k, int L, int H, i
         const int blk = 4 * wv + u;
         const int r = blk * 8 + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
-        int kr = j * 128 + r;
+        int kr = j * 128 + key_of_row(r);
         kr = kr < L ? kr : L - 1;
         const uint32_t off = ((uint32_t)kr * (uint32_t)H + (uint32_t)h) * 128u + (uint32_t)(16 * c);
         dma16(k + off, kbuf + blk * 1024);
@@ -104,24 +117,39 @@ QVD_DEV void stage_vt(AttnSmem& sm, const uint16_t* __restrict__ vt, int Lp, int
     }
 }
 
-// S^T = K . Q^T for this wave: s[qb][kb][r] = score(query q0 + 16 qb + fr, key 16 kb + 4 fg + r)
+// S^T = K . Q^T for this wave: s[qb][kb][r] = score(query q0 + 16 qb + fr, key key_of_row(16 kb + 4 fg + r))
 QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v4i s[2][8]) {
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
+    // steps (ks, half): 4 key blocks x 2 query blocks; an accumulator's next MFMA comes 16 later, and
+    // the next step's K fragments are read while this step multiplies
+    auto kfrag = [&](int kb, int ks) {
         const int row = 16 * kb + fr;
+        return *reinterpret_cast<const v4i*>(kbuf + row * 128 + (((4 * ks + fg) ^ (row & 7)) << 4));
+    };
+    v4i kcur[4], knext[4];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const v4i kf = *reinterpret_cast<const v4i*>(kbuf + row * 128 + (((4 * ks + fg) ^ (row & 7)) << 4));
+    for (int b = 0; b < 4; ++b) kcur[b] = kfrag(b, 0);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int ks = st >> 1, hf = st & 1;
+        if (st + 1 < 4) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) knext[b] = kfrag(4 * ((st + 1) & 1) + b, (st + 1) >> 1);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
+                const int kb = 4 * hf + b;
                 const v4i c = ks == 0 ? (v4i){0, 0, 0, 0} : s[qb][kb];
-                s[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf, qf[qb][ks], c, 0, 0, 0);
+                s[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kcur[b], qf[qb][ks], c, 0, 0, 0);
             }
-        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) kcur[b] = knext[b];
     }
 }
 
-// pass-1 body: running row maxima (in log2 units) of this tile's scores
+// running row maxima (in log2 units) of this tile's scores, this lane's share
 template <bool RAGGED>
 QVD_DEV void tile_max(const v4i s[2][8], float c, int key0, int L, int fg, float m[2]) {
 #pragma unroll
@@ -131,14 +159,14 @@ QVD_DEV void tile_max(const v4i s[2][8], float c, int key0, int L, int fg, float
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if (RAGGED && key0 + 16 * kb + 4 * fg + r >= L) continue;
+                if (RAGGED && key0 + key_of_row(16 * kb + 4 * fg + r) >= L) continue;
                 mx = max(mx, s[qb][kb][r]);
             }
         if (!RAGGED || mx != INT_MIN) m[qb] = fmaxf(m[qb], (float)mx * c);
     }
 }
 
-// pass-2 body: fp16 numerators of this tile as the B operand of the P.V MFMA
+// fp16 numerators of this tile against the running maxima, as the B operand of the P.V MFMA
 template <bool RAGGED>
 QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int key0, int L, int fg,
                              v8h pb[2][4]) {
@@ -154,7 +182,7 @@ QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int k
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     p[r] = __builtin_amdgcn_exp2f(fmaf((float)s[qb][kb][r], c, -m[qb]));
-                    if (RAGGED && key0 + 16 * kb + 4 * fg + r >= L) p[r] = 0.0f;
+                    if (RAGGED && key0 + key_of_row(16 * kb + 4 * fg + r) >= L) p[r] = 0.0f;
                 }
                 w[2 * hlf] = pack_f16x2(p[0], p[1]);
                 w[2 * hlf + 1] = pack_f16x2(p[2], p[3]);
@@ -212,29 +240,10 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
     const int32_t* list = kv_idx + ((int64_t)h * T + i) * kmax;
     const int n = compact_tiles(sm, list, cnt, T, tid, lane, wv);
 
-    // pass 1: the maximum of every query row over all kept keys; K double-buffered, the next tile
-    // loading while this one is multiplied
+    // running row maxima (log2 units) of the tiles seen so far
     float m[2] = {-INFINITY, -INFINITY};
-    if (n > 0) stage_k(sm.k[0], k, L, H, h, sm.tiles[0], wv, lane);
-    for (int t = 0; t < n; ++t) {
-        const int j = sm.tiles[t];
-        dma_wait();
-        __syncthreads();                       // K(t) is in LDS; everyone is done with K(t-1)
-        if (t + 1 < n) stage_k(sm.k[(t + 1) & 1], k, L, H, h, sm.tiles[t + 1], wv, lane);
-        v4i s[2][8];
-        qk_scores(sm.k[t & 1], qf, fr, fg, s);
-        const float c = qsc * k_scale[h * T + j];
-        if (ragged_L && j == T - 1) tile_max<true>(s, c, j * 128, L, fg, m);
-        else tile_max<false>(s, c, j * 128, L, fg, m);
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        m[qb] = fmaxf(m[qb], __shfl_xor(m[qb], 16, 64));
-        m[qb] = fmaxf(m[qb], __shfl_xor(m[qb], 32, 64));
-    }
 
-    // pass 2: fp16 numerators, their sum (ones . P^T) and P.V.  V^T(t) loads under QK(t) and the
-    // numerators; K(t+1) loads under P.V(t).
+    // per tile: V^T(t) loads under QK(t) and the numerators; K(t+1) loads under P.V(t)
     v4f o[2][8], lacc[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -244,12 +253,10 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
     }
     const v8h ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
-    __syncthreads();                           // pass 1's last reads of sm.k are done
     if (n > 0) stage_k(sm.k[0], k, L, H, h, sm.tiles[0], wv, lane);
     for (int t = 0; t < n; ++t) {
         const int j = sm.tiles[t];
-        dma_wait();
-        __syncthreads();                       // K(t) in LDS; P.V(t-1) and QK(t-1) are done
+        dma_barrier();                         // K(t) in LDS; P.V(t-1) and QK(t-1) are done
         stage_vt(sm, vt, Lp, h, j, wv, lane);
         const bool more = t + 1 < n;
         if (more) stage_k(sm.k[(t + 1) & 1], k, L, H, h, sm.tiles[t + 1], wv, lane);
@@ -257,36 +264,62 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
         v4i s[2][8];
         qk_scores(sm.k[t & 1], qf, fr, fg, s);
         const float c = qsc * k_scale[h * T + j];
+        // new running maxima; the sums so far are rescaled to them (every tile, without a branch)
+        float tmax[2] = {-INFINITY, -INFINITY};
+        if (ragged_L && j == T - 1) tile_max<true>(s, c, j * 128, L, fg, tmax);
+        else tile_max<false>(s, c, j * 128, L, fg, tmax);
+        float alpha[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            tmax[qb] = fmaxf(tmax[qb], __shfl_xor(tmax[qb], 16, 64));
+            tmax[qb] = fmaxf(tmax[qb], __shfl_xor(tmax[qb], 32, 64));
+            const float mnew = fmaxf(m[qb], tmax[qb]);
+            alpha[qb] = m[qb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[qb] - mnew);
+            m[qb] = mnew;
+        }
         v8h pb[2][4];
         if (ragged_L && j == T - 1) tile_numerators<true>(s, c, m, j * 128, L, fg, pb);
         else tile_numerators<false>(s, c, m, j * 128, L, fg, pb);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            lacc[qb] *= alpha[qb];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[qb][db] *= alpha[qb];
+        }
 
-#pragma unroll
-        for (int kp = 0; kp < 4; ++kp)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-                lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[qb][kp], lacc[qb], 0, 0, 0);
-        if (more) dma_wait_but_4();            // V^T(t) landed (K(t+1) may still be in flight)
-        else dma_wait();
-        __syncthreads();                       // every wave's part of V^T(t) is in LDS
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
+        if (more) dma_barrier_but_4();         // every wave's V^T(t) landed; K(t+1) may be in flight
+        else dma_barrier();
+        // O^T += V^T . P^T; lane group g's 8 numerators meet keys 32 kp + 8 g .. +7 of V^T row d,
+        // one 16-byte chunk.  Steps (kp, half of the 16-dim blocks): an accumulator's next MFMA comes
+        // 16 later, and the next step's fragments are read while this step multiplies.
+        auto vfrag = [&](int db, int kp) {
             const int d = 16 * db + fr;
-            const uint16_t* vrow = sm.vt + d * 128;
+            return *reinterpret_cast<const v8h*>(sm.vt + d * 128 + 8 * ((4 * kp + fg) ^ (d & 15)));
+        };
+        v8h vcur[4], vnext[4];
 #pragma unroll
-            for (int kp = 0; kp < 4; ++kp) {
-                const int c0 = (4 * kp + (fg >> 1)) ^ (d & 15);
-                const int c1 = (4 * kp + 2 + (fg >> 1)) ^ (d & 15);
-                const v2i lo = *reinterpret_cast<const v2i*>(vrow + 8 * c0 + 4 * (fg & 1));
-                const v2i hi = *reinterpret_cast<const v2i*>(vrow + 8 * c1 + 4 * (fg & 1));
-                const v8h vf = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+        for (int b = 0; b < 4; ++b) vcur[b] = vfrag(b, 0);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const int kp = st >> 1, hf = st & 1;
+            if (st + 1 < 8) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) vnext[b] = vfrag(4 * ((st + 1) & 1) + b, (st + 1) >> 1);
+            }
+            if (hf == 0) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[qb][kp], o[qb][db], 0, 0, 0);
+                    lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[qb][kp], lacc[qb], 0, 0, 0);
             }
-            // keep the V fragment reads of one 16-dim block next to their MFMAs (bounds the
-            // registers the scheduler may spend on reads hoisted ahead)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    o[qb][4 * hf + b] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vcur[b], pb[qb][kp], o[qb][4 * hf + b], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) vcur[b] = vnext[b];
         }
     }
 
@@ -359,8 +392,7 @@ __global__ void __launch_bounds__(256) k_qk_tile(const int8_t* __restrict__ q, c
     v4i qf[2][2];
     load_q_frags(q, L, H, h, q0, fr, fg, qf);
     stage_k(sm.k[0], k, L, H, h, j, wv, lane);
-    dma_wait();
-    __syncthreads();
+    dma_barrier();
     v4i s[2][8];
     qk_scores(sm.k[0], qf, fr, fg, s);
 #pragma unroll
@@ -369,7 +401,7 @@ __global__ void __launch_bounds__(256) k_qk_tile(const int8_t* __restrict__ q, c
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int rr = 32 * wv + 16 * qb + fr, cc = 16 * kb + 4 * fg + r;
+                const int rr = 32 * wv + 16 * qb + fr, cc = key_of_row(16 * kb + 4 * fg + r);
                 const bool ok = (i * 128 + rr) < L && (j * 128 + cc) < L;
                 out[rr * 128 + cc] = ok ? s[qb][kb][r] : 0;
             }
