@@ -69,41 +69,32 @@ __global__ void __launch_bounds__(256) k_adaln_project(float t, const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------------------------
-// modulated LayerNorm.  NW = d/128 32-bit words (bf16 pairs) per lane; lane l owns words
-// l + 64 j, i.e. columns 2(l + 64 j) and 2(l + 64 j) + 1.
+// modulated LayerNorm.  One wave per row; NW = d/128 32-bit words (bf16 pairs) per lane, lane l owns
+// words l + 64 j, i.e. columns 2(l + 64 j) and 2(l + 64 j) + 1.  The per-column modulation sits in
+// LDS as float4 (a0, b0, a1, b1) per column pair, so registers hold the row and little else.
 
 template <int NW>
-struct RowRegs {
+struct Row {
     u32 x[NW];
-    float sh[2 * NW], op[2 * NW];   // shift and (1 + scale) source (fp32 scale)
 };
 
+// The compiler may not reuse values derived from the row across this point (it would otherwise keep
+// float64 copies of every element live between the loops and run out of registers).
 template <int NW>
-QVD_DEV void load_mod(RowRegs<NW>& R, const float* __restrict__ mod, int half, int d, int lane, int nw) {
-    const float* shift = mod + (3 * half) * d;
-    const float* scale = mod + (3 * half + 1) * d;
+QVD_DEV void row_fence(Row<NW>& R) {
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-        if (j < nw) {
-            const int col = 2 * (lane + 64 * j);
-            const float2 a = *reinterpret_cast<const float2*>(shift + col);
-            const float2 b = *reinterpret_cast<const float2*>(scale + col);
-            R.sh[2 * j] = a.x;
-            R.sh[2 * j + 1] = a.y;
-            R.op[2 * j] = b.x;
-            R.op[2 * j + 1] = b.y;
-        }
-    }
+    for (int j = 0; j < NW; ++j) asm volatile("" : "+v"(R.x[j]));
 }
 
 // mean and 1/sqrt(var + eps) of one row (float64), all lanes get the result
 template <int NW>
-QVD_DEV void row_stats(const RowRegs<NW>& R, int nw, int d, double eps, double& mu, double& rstd) {
+QVD_DEV void row_stats(Row<NW>& R, int nw, int d, double eps, double& mu, double& rstd) {
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < NW; ++j)
         if (j < nw) s += (double)bf16lo(R.x[j]) + (double)bf16hi(R.x[j]);
     mu = wave_sum_f64(s) / (double)d;
+    row_fence<NW>(R);
     double v = 0.0;
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
@@ -116,6 +107,7 @@ QVD_DEV void row_stats(const RowRegs<NW>& R, int nw, int d, double eps, double& 
     }
     const double var = wave_sum_f64(v) / (double)d;
     rstd = 1.0 / sqrt(var + eps);
+    row_fence<NW>(R);
 }
 
 // y = fp32(((x - mu) * rstd) * (1 + scale) + shift), each float64 operation rounded separately
@@ -126,18 +118,41 @@ QVD_DEV float modulate_one(float x, double mu, double rstd, float scale, float s
     return (float)y;
 }
 
-// pass 1 (dynamic scales): row statistics to ws, per-workgroup max |y| to partials
+// LDS table of the modulation: tab[p] = (a(2p), b(2p), a(2p+1), b(2p+1)) with a = scale, b = shift
+// (raw), or, with inv given, a = (1 + scale) inv and b = shift inv
+QVD_DEV void load_mod_table(float4* tab, const float* __restrict__ mod, int half, int d, bool fold, float inv) {
+    const float* shift = mod + (3 * half) * d;
+    const float* scale = mod + (3 * half + 1) * d;
+    for (int p = threadIdx.x; p < d / 2; p += blockDim.x) {
+        const float2 sh = *reinterpret_cast<const float2*>(shift + 2 * p);
+        const float2 sc = *reinterpret_cast<const float2*>(scale + 2 * p);
+        tab[p] = fold ? make_float4((1.0f + sc.x) * inv, sh.x * inv, (1.0f + sc.y) * inv, sh.y * inv)
+                      : make_float4(sc.x, sh.x, sc.y, sh.y);
+    }
+    __syncthreads();
+}
+
+// pass 1 (dynamic scales): row statistics to ws, per-workgroup max |y| to partials.
+// max |y| is the float64 modulation's, rounded to fp32, exactly: every element is first evaluated in
+// fp32 as fma(fp32(x - mu), fp32(rstd) fp32(1 + scale), shift), which is within 2^-21 (|y| + |shift|)
+// of it; only elements within 2^-19 (max + max|shift|) of the row's fp32 maximum can hold the exact
+// maximum, and those (usually one) are evaluated in float64.
 template <int NW>
 __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x, int L, int d,
                                                   const float* __restrict__ mod, int half, float eps,
                                                   double2* __restrict__ stats,
                                                   float* __restrict__ partials) {
+    __shared__ float4 tab[4096 / 2];
     __shared__ float red[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int nw = d >> 7;
-    RowRegs<NW> R;
-    load_mod<NW>(R, mod, half, d, lane, nw);
+    load_mod_table(tab, mod, half, d, false, 1.0f);
+    float shmax = 0.0f;
+    for (int p = threadIdx.x; p < d / 2; p += 256)
+        shmax = fmaxf(shmax, fmaxf(fabsf(tab[p].y), fabsf(tab[p].w)));
+    shmax = block_max_nonneg<4>(shmax, red);
     float m = 0.0f;
+    Row<NW> R;
     for (int row = blockIdx.x * 4 + wv; row < L; row += gridDim.x * 4) {
         const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)row * d);
 #pragma unroll
@@ -146,12 +161,27 @@ __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x
         double mu, rstd;
         row_stats<NW>(R, nw, d, (double)eps, mu, rstd);
         if (lane == 0) stats[row] = make_double2(mu, rstd);
+        const float rs = (float)rstd;
+        float ay[2 * NW];
+        float m32 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             if (j < nw) {
-                m = fmaxf(m, fabsf(modulate_one(bf16lo(R.x[j]), mu, rstd, R.op[2 * j], R.sh[2 * j])));
-                m = fmaxf(m, fabsf(modulate_one(bf16hi(R.x[j]), mu, rstd, R.op[2 * j + 1],
-                                                R.sh[2 * j + 1])));
+                const float4 c = tab[lane + 64 * j];
+                ay[2 * j] = fabsf(fmaf((float)((double)bf16lo(R.x[j]) - mu), rs * (1.0f + c.x), c.y));
+                ay[2 * j + 1] = fabsf(fmaf((float)((double)bf16hi(R.x[j]) - mu), rs * (1.0f + c.z), c.w));
+                m32 = fmaxf(m32, fmaxf(ay[2 * j], ay[2 * j + 1]));
+            }
+        }
+        m32 = wave_max(m32);
+        row_fence<NW>(R);
+        const float thr = m32 - 0x1p-19f * (m32 + shmax);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if (j < nw && fmaxf(ay[2 * j], ay[2 * j + 1]) >= thr) {
+                const float4 c = tab[lane + 64 * j];
+                if (ay[2 * j] >= thr) m = fmaxf(m, fabsf(modulate_one(bf16lo(R.x[j]), mu, rstd, c.x, c.y)));
+                if (ay[2 * j + 1] >= thr) m = fmaxf(m, fabsf(modulate_one(bf16hi(R.x[j]), mu, rstd, c.z, c.w)));
             }
         }
     }
@@ -160,7 +190,10 @@ __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x
 }
 
 // pass 2: codes.  Dynamic: stats from pass 1 and the amax of the partials; static: stats computed
-// here and the scale read from scale_in.
+// here and the scale read from scale_in.  The codes are E4M3(y * inv) with y * inv formed in fp32 as
+// fma(x - mu, rstd (1 + scale) inv, shift inv): x - mu is taken in float64 and rounded once, so
+// cancellation cannot cost accuracy; the result is within a few fp32 ulps of the float64 modulation,
+// which moves a code only where the value lies that close to a rounding midpoint.
 template <int NW>
 __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x, int L, int d,
                                                   const float* __restrict__ mod, int half, float eps,
@@ -169,6 +202,7 @@ __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x
                                                   const float* __restrict__ scale_in,
                                                   uint8_t* __restrict__ q,
                                                   float* __restrict__ scale_out) {
+    __shared__ float4 tab[4096 / 2];
     __shared__ float red[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int nw = d >> 7;
@@ -189,8 +223,8 @@ __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x
         }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-    RowRegs<NW> R;
-    load_mod<NW>(R, mod, half, d, lane, nw);
+    load_mod_table(tab, mod, half, d, true, inv);
+    Row<NW> R;
     for (int row = blockIdx.x * 4 + wv; row < L; row += gridDim.x * 4) {
         const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)row * d);
 #pragma unroll
@@ -204,13 +238,15 @@ __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x
             mu = st.x;
             rstd = st.y;
         }
+        const float rs = (float)rstd;
         uint16_t* qr = reinterpret_cast<uint16_t*>(q + (int64_t)row * d);
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             if (j < nw) {
-                const float y0 = modulate_one(bf16lo(R.x[j]), mu, rstd, R.op[2 * j], R.sh[2 * j]);
-                const float y1 = modulate_one(bf16hi(R.x[j]), mu, rstd, R.op[2 * j + 1], R.sh[2 * j + 1]);
-                qr[lane + 64 * j] = (uint16_t)(e4m3_encode(y0 * inv) | (e4m3_encode(y1 * inv) << 8));
+                const float4 c = tab[lane + 64 * j];
+                const float v0 = fmaf((float)((double)bf16lo(R.x[j]) - mu), rs * c.x, c.y);
+                const float v1 = fmaf((float)((double)bf16hi(R.x[j]) - mu), rs * c.z, c.w);
+                qr[lane + 64 * j] = (uint16_t)e4m3_encode2(v0, v1);
             }
         }
     }

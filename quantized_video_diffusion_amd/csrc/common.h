@@ -46,24 +46,19 @@ QVD_DEV uint16_t f32_to_bf16(float x) { return (uint16_t)(pack_bf16x2(x, 0.0f) &
 // format definition: a normal value keeps 3 fraction bits of the fp32 significand (rounding added
 // at bit 19 with the tie going to the even result), exponent rebased from 127 to 7; below 2^-6
 // the code is the count of 2^-9 quanta.
-QVD_DEV u32 e4m3_encode(float v) {
-    const u32 u = __float_as_uint(v);
-    const u32 sign = (u >> 24) & 0x80u;
-    const u32 a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return 0x7Fu;                   // NaN
-    const float af = __uint_as_float(a);
-    u32 code;
-    if (af >= 448.0f) {
-        code = 0x7Eu;
-    } else if (af < 0.015625f) {                          // 2^-6
-        code = (u32)__builtin_rintf(af * 512.0f);         // exact scaling, RNE: 0 .. 8
-    } else {
-        const u32 r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        code = (r >> 20) - (120u << 3);
-        code = code > 0x7Eu ? 0x7Eu : code;
-    }
-    return code | sign;
+// fp32 -> E4M3 (OCP "FN"): round to nearest even, finite values beyond 448 saturate to +-448, NaN -> 0x7F.
+// The gfx950 converter rounds to nearest even; clamping to +-448 first makes it saturate (the pair
+// agrees with a direct implementation of the rule on all 2^32 fp32 inputs, checked on the device).
+QVD_DEV u32 e4m3_encode2(float a, float b) {
+    const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    u32 r = (u32)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+    if (a != a) r = (r & 0xFF00u) | 0x7Fu;
+    if (b != b) r = (r & 0x00FFu) | 0x7F00u;
+    return r;
 }
+
+QVD_DEV u32 e4m3_encode(float v) { return e4m3_encode2(v, v) & 0xFFu; }
 
 QVD_DEV int int8_encode(float x, float inv) {
     float p = x * inv;                                     // one fp32 product (no contraction)
