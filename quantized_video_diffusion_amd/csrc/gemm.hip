@@ -137,7 +137,7 @@ QVD_DEV void stage_tiles(const GemmArgs& g, uint8_t* smem, int buf, int k0, int 
 
 // v_mfma_f32_16x16x128: acc[nb][mb], lane l holds C[16 mb + l%16][16 nb + 4 (l/16) .. +3]
 struct Layout16 {
-    static constexpr int NCG = 8, MR = 8;
+    static constexpr int NCG = 8, MR = 8, RB = 16;
     typedef v4f Acc[8][8];
     QVD_DEV static int ncol(int cg, int lane) { return 16 * cg + 4 * (lane >> 4); }
     QVD_DEV static int mrow(int r, int lane) { return 16 * r + (lane & 15); }
@@ -147,7 +147,7 @@ struct Layout16 {
 // v_mfma_f32_32x32x64: acc[nb][mb] (16 values), value 4g + i of lane l is
 // C[32 mb + l%32][32 nb + 8 g + 4 (l/32) + i]
 struct Layout32 {
-    static constexpr int NCG = 16, MR = 4;
+    static constexpr int NCG = 16, MR = 4, RB = 32;
     typedef v16f Acc[4][4];
     QVD_DEV static int ncol(int cg, int lane) { return 32 * (cg >> 2) + 8 * (cg & 3) + 4 * (lane >> 5); }
     QVD_DEV static int mrow(int r, int lane) { return 32 * r + (lane & 31); }
@@ -163,37 +163,64 @@ QVD_DEV float4 load_bias4(const float* bias, int n) {
 }
 
 // ---- fused epilogues: y = acc * alpha + bias, then the mode's output ---------------------------------
-// The wave owns the 128 x 128 block at (mw0, nw0) = (m0 + 128 wm, n0 + 128 wn).
+// The wave owns the 128 x 128 block at (mw0, nw0) = (m0 + 128 wm, n0 + 128 wn).  Results go through a
+// 16 KB LDS region of the wave (stage), in rounds of rows, so that every global store is 16 bytes per
+// lane over whole rows: bf16 rows of 256 B, fp32 rows of 512 B, INT8 rows of 128 B, and V^T rows
+// (one head dimension, 64 tokens per round) of 128 B.  16-byte chunks are XOR-swizzled by row.
+QVD_DEV void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <int EPI, class LY>
 QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float alpha, int m0, int n0,
-                           int wm, int wn, float* red) {
+                           int wm, int wn, float* red, uint8_t* stage) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int M = g.M, N = g.N;
     const int mw0 = m0 + 128 * wm, nw0 = n0 + 128 * wn;
     const bool wave_live = nw0 < N && mw0 < M;
     const qvd_epilogue& ep = g.epi;
 
-    if (EPI == QVD_EPI_GELU) {
-        float amax = 0.0f;
-        if (wave_live) {
+    // bf16 outputs (plain or GELU): rounds of 64 rows, LDS rows of 256 B (16 chunks)
+    auto bf16_rounds = [&](auto gelu, float& amax) {
+        constexpr bool GELU = decltype(gelu)::value != 0;
+        constexpr int RPR = 64 / LY::RB;                     // r blocks per round
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
 #pragma unroll
             for (int cg = 0; cg < LY::NCG; ++cg) {
-                const int n = nw0 + LY::ncol(cg, lane);
-                const float4 b = load_bias4(g.bias, n);
+                const int nl = LY::ncol(cg, lane);
+                const float4 b = load_bias4(g.bias, nw0 + nl);
 #pragma unroll
-                for (int r = 0; r < LY::MR; ++r) {
-                    const int m = mw0 + LY::mrow(r, lane);
-                    if (m < M) {
-                        const v4f c = LY::get(acc, cg, r);
-                        const u32 p0 = pack_bf16x2(gelu_erf(c[0] * alpha + b.x), gelu_erf(c[1] * alpha + b.y));
-                        const u32 p1 = pack_bf16x2(gelu_erf(c[2] * alpha + b.z), gelu_erf(c[3] * alpha + b.w));
+                for (int rr = 0; rr < RPR; ++rr) {
+                    const int r = rd * RPR + rr;
+                    const int ml = LY::mrow(r, lane) - 64 * rd;
+                    const v4f c = LY::get(acc, cg, r);
+                    float y[4] = {c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z, c[3] * alpha + b.w};
+                    if (GELU) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) y[i] = gelu_erf(y[i]);
+                    }
+                    const u32 p0 = pack_bf16x2(y[0], y[1]), p1 = pack_bf16x2(y[2], y[3]);
+                    if (GELU && mw0 + 64 * rd + ml < M)
                         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(p0)), fabsf(bf16hi(p0))),
                                                  fmaxf(fabsf(bf16lo(p1)), fabsf(bf16hi(p1)))));
-                        *reinterpret_cast<uint2*>(ep.out_bf16 + (int64_t)m * N + n) = make_uint2(p0, p1);
-                    }
+                    const int ch = (nl >> 3) ^ (ml & 15);
+                    *reinterpret_cast<u32x2*>(stage + ml * 256 + ch * 16 + ((nl >> 2) & 1) * 8) = (u32x2){p0, p1};
                 }
             }
+            lds_wait();
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int idx = 64 * it + lane, ml = idx >> 4, c = idx & 15;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) << 4));
+                const int m = mw0 + 64 * rd + ml;
+                if (m < M) *reinterpret_cast<u32x4*>(ep.out_bf16 + (int64_t)m * N + nw0 + 8 * c) = v;
+            }
+            lds_wait();
         }
+    };
+
+    if (EPI == QVD_EPI_GELU) {
+        float amax = 0.0f;
+        if (wave_live) bf16_rounds(std::integral_constant<int, 1>{}, amax);
         if (ep.amax_partials) {
             amax = block_max_nonneg<4>(amax, red);
             if (tid == 0) ep.amax_partials[blockIdx.x] = amax;
@@ -201,6 +228,11 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
         return;
     }
     if (!wave_live) return;
+    if (EPI == QVD_EPI_BF16) {
+        float unused = 0.0f;
+        bf16_rounds(std::integral_constant<int, 0>{}, unused);
+        return;
+    }
 
     if (EPI == QVD_EPI_QKV) {
         const int dm = N / 3;
@@ -208,32 +240,50 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
         const int head = (nw0 - part * dm) >> 7;
         const int Tm = (M + 127) >> 7;
         if (part == 2) {
-            // V: bf16 rounding, then fp16 (exact for 2^-14 <= |v| <= 65504; larger saturate),
-            // stored transposed as V^T[head][dim][token] with tokens M .. Lp-1 zeroed
+            // V: bf16 rounding, then fp16 (exact for 2^-14 <= |v| <= 65504; larger saturate), stored
+            // transposed as V^T[head][dim][token] with tokens M .. Lp-1 zeroed.  LDS: 128 dimension
+            // rows of 64 tokens (128 B, 8 chunks) per round.
             const int64_t Lp = (int64_t)Tm * 128;
             uint16_t* vt = ep.v + (int64_t)head * 128 * Lp;
+            constexpr int RPR = 64 / LY::RB;
 #pragma unroll
-            for (int cg = 0; cg < LY::NCG; ++cg) {
-                const int dd = LY::ncol(cg, lane);
-                const float4 b = load_bias4(g.bias, nw0 + dd);
+            for (int rd = 0; rd < 2; ++rd) {
 #pragma unroll
-                for (int r = 0; r < LY::MR; ++r) {
-                    const int m = mw0 + LY::mrow(r, lane);
-                    const v4f c = LY::get(acc, cg, r);
-                    const float y[4] = {c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z,
-                                        c[3] * alpha + b.w};
+                for (int cg = 0; cg < LY::NCG; ++cg) {
+                    const int dd = LY::ncol(cg, lane);
+                    const float4 b = load_bias4(g.bias, nw0 + dd);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float vb = bf16lo(pack_bf16x2(y[i], 0.0f));
-                        const float vc = fminf(fmaxf(vb, -65504.0f), 65504.0f);
-                        const uint16_t h16 = m < M ? __builtin_bit_cast(uint16_t, (_Float16)vc) : (uint16_t)0;
-                        vt[(int64_t)(dd + i) * Lp + m] = h16;
+                    for (int rr = 0; rr < RPR; ++rr) {
+                        const int r = rd * RPR + rr;
+                        const int ml = LY::mrow(r, lane) - 64 * rd;
+                        const bool ok = mw0 + 64 * rd + ml < M;
+                        const v4f c = LY::get(acc, cg, r);
+                        const float y[4] = {c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z,
+                                            c[3] * alpha + b.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float vb = bf16lo(pack_bf16x2(y[i], 0.0f));
+                            const float vc = fminf(fmaxf(vb, -65504.0f), 65504.0f);
+                            const uint16_t h16 = ok ? __builtin_bit_cast(uint16_t, (_Float16)vc) : (uint16_t)0;
+                            const int row = dd + i;
+                            *reinterpret_cast<uint16_t*>(stage + row * 128 + (((ml >> 3) ^ (row & 7)) << 4) +
+                                                         (ml & 7) * 2) = h16;
+                        }
                     }
                 }
+                lds_wait();
+#pragma unroll
+                for (int it = 0; it < 16; ++it) {
+                    const int idx = 64 * it + lane, row = idx >> 3, c = idx & 7;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * 128 + ((c ^ (row & 7)) << 4));
+                    *reinterpret_cast<u32x4*>(vt + (int64_t)row * Lp + mw0 + 64 * rd + 8 * c) = v;
+                }
+                lds_wait();
             }
             return;
         }
-        // Q or K: round to bf16, then one symmetric INT8 scale over this (128-token tile, head)
+        // Q or K: round to bf16, then one symmetric INT8 scale over this (128-token tile, head).
+        // LDS: 128 token rows of 128 codes (8 chunks).
         float amax = 0.0f;
 #pragma unroll
         for (int cg = 0; cg < LY::NCG; ++cg) {
@@ -256,52 +306,107 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
         if (lane == 0) sdst[head * Tm + (mw0 >> 7)] = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 127.0f);
 #pragma unroll
         for (int cg = 0; cg < LY::NCG; ++cg) {
-            const int n = nw0 + LY::ncol(cg, lane);
-            const float4 b = load_bias4(g.bias, n);
+            const int nl = LY::ncol(cg, lane);
+            const float4 b = load_bias4(g.bias, nw0 + nl);
 #pragma unroll
             for (int r = 0; r < LY::MR; ++r) {
-                const int m = mw0 + LY::mrow(r, lane);
-                if (m < M) {
-                    const v4f c = LY::get(acc, cg, r);
-                    const u32 p0 = pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y);
-                    const u32 p1 = pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w);
-                    const u32 q = (u32)(int8_encode(bf16lo(p0), inv) & 0xFF) |
-                                  ((u32)(int8_encode(bf16hi(p0), inv) & 0xFF) << 8) |
-                                  ((u32)(int8_encode(bf16lo(p1), inv) & 0xFF) << 16) |
-                                  ((u32)(int8_encode(bf16hi(p1), inv) & 0xFF) << 24);
-                    *reinterpret_cast<u32*>(dst + (int64_t)m * dm + (n - part * dm)) = q;
-                }
+                const int ml = LY::mrow(r, lane);
+                const v4f c = LY::get(acc, cg, r);
+                const u32 p0 = pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y);
+                const u32 p1 = pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w);
+                const u32 q = (u32)(int8_encode(bf16lo(p0), inv) & 0xFF) |
+                              ((u32)(int8_encode(bf16hi(p0), inv) & 0xFF) << 8) |
+                              ((u32)(int8_encode(bf16lo(p1), inv) & 0xFF) << 16) |
+                              ((u32)(int8_encode(bf16hi(p1), inv) & 0xFF) << 24);
+                *reinterpret_cast<u32*>(stage + ml * 128 + (((nl >> 4) ^ (ml & 7)) << 4) + (nl & 15)) = q;
             }
+        }
+        lds_wait();
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int idx = 64 * it + lane, ml = idx >> 3, c = idx & 7;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * 128 + ((c ^ (ml & 7)) << 4));
+            const int m = mw0 + ml;
+            if (m < M) *reinterpret_cast<u32x4*>(dst + (int64_t)m * dm + (nw0 - part * dm) + 16 * c) = v;
         }
         return;
     }
 
+    if (EPI == QVD_EPI_RESID_GATE) {
+        // x += gate * y in place: rounds of 64 rows; the x rows come into LDS with 16-byte loads, are
+        // updated there in the accumulator layout, and leave with 16-byte stores
+        constexpr int RPR = 64 / LY::RB;
 #pragma unroll
-    for (int cg = 0; cg < LY::NCG; ++cg) {
-        const int n = nw0 + LY::ncol(cg, lane);
-        const float4 b = load_bias4(g.bias, n);
-        float4 gt = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (EPI == QVD_EPI_RESID_GATE) gt = *reinterpret_cast<const float4*>(ep.gate + n);
+        for (int rd = 0; rd < 2; ++rd) {
 #pragma unroll
-        for (int r = 0; r < LY::MR; ++r) {
-            const int m = mw0 + LY::mrow(r, lane);
-            if (m >= M) continue;
-            const v4f c = LY::get(acc, cg, r);
-            const float y0 = c[0] * alpha + b.x, y1 = c[1] * alpha + b.y;
-            const float y2 = c[2] * alpha + b.z, y3 = c[3] * alpha + b.w;
-            const int64_t off = (int64_t)m * N + n;
-            if (EPI == QVD_EPI_F32) {
-                *reinterpret_cast<float4*>(ep.out_f32 + off) = make_float4(y0, y1, y2, y3);
-            } else if (EPI == QVD_EPI_BF16) {
-                *reinterpret_cast<uint2*>(ep.out_bf16 + off) =
-                    make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
-            } else if (EPI == QVD_EPI_RESID_GATE) {
-                const uint2 xr = *reinterpret_cast<const uint2*>(ep.resid + off);
-                *reinterpret_cast<uint2*>(ep.out_bf16 + off) =
-                    make_uint2(pack_bf16x2(bf16lo(xr.x) + gt.x * y0, bf16hi(xr.x) + gt.y * y1),
-                               pack_bf16x2(bf16lo(xr.y) + gt.z * y2, bf16hi(xr.y) + gt.w * y3));
+            for (int it = 0; it < 16; ++it) {
+                const int idx = 64 * it + lane, ml = idx >> 4, c = idx & 15;
+                const int m = mw0 + 64 * rd + ml;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (m < M) v = *reinterpret_cast<const u32x4*>(ep.resid + (int64_t)m * N + nw0 + 8 * c);
+                *reinterpret_cast<u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) << 4)) = v;
+            }
+            lds_wait();
+#pragma unroll
+            for (int cg = 0; cg < LY::NCG; ++cg) {
+                const int nl = LY::ncol(cg, lane);
+                const float4 b = load_bias4(g.bias, nw0 + nl);
+                const float4 gt = *reinterpret_cast<const float4*>(ep.gate + nw0 + nl);
+#pragma unroll
+                for (int rr = 0; rr < RPR; ++rr) {
+                    const int r = rd * RPR + rr;
+                    const int ml = LY::mrow(r, lane) - 64 * rd;
+                    const v4f c = LY::get(acc, cg, r);
+                    u32x2* slot = reinterpret_cast<u32x2*>(stage + ml * 256 + (((nl >> 3) ^ (ml & 15)) << 4) +
+                                                           ((nl >> 2) & 1) * 8);
+                    const u32x2 xr = *slot;
+                    *slot = (u32x2){pack_bf16x2(bf16lo(xr[0]) + gt.x * (c[0] * alpha + b.x),
+                                                bf16hi(xr[0]) + gt.y * (c[1] * alpha + b.y)),
+                                    pack_bf16x2(bf16lo(xr[1]) + gt.z * (c[2] * alpha + b.z),
+                                                bf16hi(xr[1]) + gt.w * (c[3] * alpha + b.w))};
+                }
+            }
+            lds_wait();
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int idx = 64 * it + lane, ml = idx >> 4, c = idx & 15;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) << 4));
+                const int m = mw0 + 64 * rd + ml;
+                if (m < M) *reinterpret_cast<u32x4*>(ep.out_bf16 + (int64_t)m * N + nw0 + 8 * c) = v;
+            }
+            lds_wait();
+        }
+        return;
+    }
+
+    // fp32 output: rounds of 32 rows, LDS rows of 512 B (32 chunks)
+    constexpr int RPR = 32 / LY::RB > 0 ? 32 / LY::RB : 1;
+#pragma unroll
+    for (int rd = 0; rd < 4; ++rd) {
+#pragma unroll
+        for (int cg = 0; cg < LY::NCG; ++cg) {
+            const int nl = LY::ncol(cg, lane);
+            const float4 b = load_bias4(g.bias, nw0 + nl);
+#pragma unroll
+            for (int rr = 0; rr < RPR; ++rr) {
+                const int r = rd * RPR + rr;
+                const int ml = LY::mrow(r, lane) - 32 * rd;
+                const v4f c = LY::get(acc, cg, r);
+                const float4 y = make_float4(c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z,
+                                             c[3] * alpha + b.w);
+                *reinterpret_cast<float4*>(stage + ml * 512 + (((nl >> 2) ^ (ml & 31)) << 4)) = y;
             }
         }
+        lds_wait();
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int idx = 64 * it + lane, ml = idx >> 5, c = idx & 31;
+            const float4 y = *reinterpret_cast<const float4*>(stage + ml * 512 + ((c ^ (ml & 31)) << 4));
+            const int m = mw0 + 32 * rd + ml;
+            const int n = nw0 + 4 * c;
+            if (m < M) *reinterpret_cast<float4*>(ep.out_f32 + (int64_t)m * N + n) = y;
+        }
+        lds_wait();
     }
 }
 
@@ -379,7 +484,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_mx(GemmArgs g) {
                                                                               sc, 0, 127);
         }
     }
-    gemm_epilogue<EPI, Layout16>(g, acc, *g.s_a, m0, n0, wm, wn, red);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages are free
+    gemm_epilogue<EPI, Layout16>(g, acc, *g.s_a, m0, n0, wm, wn, red, smem + wv * 16384);
 }
 
 // ================================================================================================
@@ -524,7 +630,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_f8(GemmArgs g) {
     }
     kstep(IC<0>{}, IC<0>{}, IC<0>{}, kt);        // kt = KT - 2
     kstep(IC<1>{}, IC<-1>{}, IC<0>{}, kt + 1);   // kt = KT - 1
-    gemm_epilogue<EPI, Layout32>(g, acc, (*g.s_a) * (*g.s_w), m0, n0, wm, wn, red);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages are free
+    gemm_epilogue<EPI, Layout32>(g, acc, (*g.s_a) * (*g.s_w), m0, n0, wm, wn, red, smem + wv * 16384);
 }
 
 template <template <int> class KERN>
