@@ -10,6 +10,7 @@ import ctypes as C
 import math
 from dataclasses import dataclass, field
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -231,6 +232,19 @@ def clip_count(x: torch.Tensor, scale: torch.Tensor, count: torch.Tensor):
 
 # ----------------------------------------------------------------------------------------------
 # block
+
+def calibrated_scale(amax: float) -> np.float32:
+    """Static per-tensor FP8 scale from a calibration amax: fp32(amax / 448), moved up by one fp32 ulp
+    when 448 s (exact) would fall below amax, so that no calibration value exceeds the E4M3 range.
+    amax = 0 gives 1."""
+    a = np.float32(amax)
+    if a == 0:
+        return np.float32(1.0)
+    s = np.float32(a / np.float32(448.0))
+    while float(s) * 448.0 < float(a):
+        s = np.nextafter(s, np.float32(np.inf))
+    return s
+
 
 @dataclass
 class BlockWeights:

@@ -262,6 +262,31 @@ def outlier_spec(d_in: int, ratio: float, seed: int = 0, tag: int = 5, site: int
     return ch, np.float32(ratio * base / ch_max), base
 
 
+def _device_seed(*key) -> int:
+    return int(np.random.SeedSequence(list(key)).generate_state(1)[0])
+
+
+def calibration_batch_device(d_in: int, b: int, seed: int = 0, tag: int = 5, site: int = 0,
+                             tokens: int = 1024, device: str = "cuda"):
+    """Batch ``b`` of heavy-tailed activations drawn on the GPU (full-size calibration runs): Student-t
+    with nu = 3 built from its definition, Z / sqrt((Z1^2 + Z2^2 + Z3^2) / 3), from torch's seeded
+    normal generator; fp32 [tokens][d_in].  A different stream from ``calibration_batch``."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_device_seed(seed, tag, site, _TENSOR_IDS["calib"], b, 1))
+    z = torch.randn((4, tokens, d_in), generator=g, device=device)
+    return z[0] / torch.sqrt((z[1] * z[1] + z[2] * z[2] + z[3] * z[3]) / 3.0)
+
+
+def outlier_channels_device(d_in: int, seed: int = 0, tag: int = 5, site: int = 0, device: str = "cuda"):
+    """round(0.001 d_in) (at least one) distinct channels of a site, drawn on the GPU, ascending."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_device_seed(seed, tag, site, _TENSOR_IDS["outlier_ch"], 1))
+    n_ch = max(1, int(round(0.001 * d_in)))
+    return torch.sort(torch.randperm(d_in, generator=g, device=device)[:n_ch]).values
+
+
 def apply_outliers(batch: np.ndarray, channels: np.ndarray, factor: np.float32) -> np.ndarray:
     out = batch.copy()
     out[:, channels] *= factor
