@@ -131,6 +131,23 @@ def test_gemm_mxfp4_f32_and_bf16(M, N, K):
     assert_bf16_close(host_bits(yb), want, 1e-3, "mxfp4 bf16")
 
 
+def test_gemm_mxfp4_768p_qkv_shape_sampled():
+    """The 768p QKV shape with MXFP4 weights: M = 85,696 (ragged last tile), N = 8,064, K = 2,688;
+    64 sampled rows against the oracle."""
+    M, N, K = W.TOKENS_768P, 3 * 2688, 2688
+    say("gemm mxfp4 768p", M, N, K)
+    a = _codes(M, K, 11)
+    wb = W.normal_bf16((N, K), seed=12, scale=0.03)
+    pw, ew = OQ.quant_mxfp4_weight(wb)
+    sa = np.float32(0.02)
+    y = Q.gemm_mxfp4(u8_dev(a), f32_dev([sa]), u8_dev(pw), u8_dev(ew))
+    rows = np.r_[np.random.default_rng(1).choice(M, 60, replace=False), [0, M - 1, M - 64, M - 200]]
+    got = host(y[torch.from_numpy(rows).cuda()])
+    del y
+    want = OG.gemm_mxfp4(a[rows], sa, pw, ew)
+    assert_close_rms(got, want, 1e-3, "mxfp4 768p rows")
+
+
 # --- attention ---------------------------------------------------------------------------------
 
 def _attn_inputs(L, H, seed, sparse, w=None):
@@ -212,6 +229,37 @@ def test_sparse_attn_diag_only_and_out_of_range_entries():
     cnt0 = np.zeros((H, T), np.int32)
     out0 = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt0))
     assert not host_bits(out0).any()
+
+
+def test_sparse_attn_768p_sampled_tiles():
+    """The 768p token count (85,696 tokens: 670 tiles, last one of 64 rows; 135 kept per row), three
+    heads of the 768p mask; sampled query tiles against the oracle."""
+    w = W.WORKLOADS["block_768p_mxfp4"]
+    L, H = w.L, 3
+    T = w.n_tiles
+    say("attn 768p", L, T)
+    qb, kb, vb = W.qkv_heads(L, H, seed=3, tag=w.tag)
+    idx, cnt = W.block_mask(w, seed=0)
+    idx, cnt = np.ascontiguousarray(idx[:H]), np.ascontiguousarray(cnt[:H])
+    q8, qs = Q.quant_int8_qk(bf16_dev(qb.reshape(L, -1)), H)
+    k8, ks = Q.quant_int8_qk(bf16_dev(kb.reshape(L, -1)), H)
+    out = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt))
+    tiles = [(0, 0), (1, T - 1), (2, 335), (0, 669), (1, 2)]
+    qq, kq = np.zeros((L, H, 128), np.int8), np.zeros((L, H, 128), np.int8)
+    qsc, ksc = np.ones((H, T), np.float32), np.ones((H, T), np.float32)
+    for h, i in tiles:
+        rows = slice(i * 128, min(L, (i + 1) * 128))
+        cw, sw = OQ.quant_int8_qk(np.ascontiguousarray(qb[rows, h:h + 1]), rows.stop - rows.start, 1)
+        qq[rows, h], qsc[h, i] = cw[:, 0], sw[0, 0]
+        for j in idx[h, i, : cnt[h, i]]:
+            rk = slice(j * 128, min(L, (j + 1) * 128))
+            cw, sw = OQ.quant_int8_qk(np.ascontiguousarray(kb[rk, h:h + 1]), rk.stop - rk.start, 1)
+            kq[rk, h], ksc[h, j] = cw[:, 0], sw[0, 0]
+    ob = host_bits(out)
+    for h, i in tiles:
+        rows = slice(i * 128, min(L, (i + 1) * 128))
+        want = OAT.sparse_attn_tile(qq, qsc, kq, ksc, vb, idx, cnt, h, i, 1 / math.sqrt(128))
+        assert_bf16_close(ob[rows, h], want, 1e-2, f"768p tile {(h, i)}")
 
 
 def test_sparse_attn_480p_sampled_tiles():
