@@ -158,60 +158,98 @@ struct Layout32 {
     }
 };
 
+// v_mfma_f32_32x32x64 over a 128 x 64 wave tile: acc[nb][mb], nb in 0..1
+struct Layout32N64 {
+    static constexpr int NCG = 8, MR = 4, RB = 32;
+    typedef v16f Acc[2][4];
+    QVD_DEV static int ncol(int cg, int lane) { return 32 * (cg >> 2) + 8 * (cg & 3) + 4 * (lane >> 5); }
+    QVD_DEV static int mrow(int r, int lane) { return 32 * r + (lane & 31); }
+    QVD_DEV static v4f get(const Acc& a, int cg, int r) {
+        const v16f& v = a[cg >> 2][r];
+        const int b = 4 * (cg & 3);
+        return (v4f){v[b], v[b + 1], v[b + 2], v[b + 3]};
+    }
+};
+
 QVD_DEV float4 load_bias4(const float* bias, int n) {
     return bias ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ---- fused epilogues: y = acc * alpha + bias, then the mode's output ---------------------------------
-// The wave owns the 128 x 128 block at (mw0, nw0) = (m0 + 128 wm, n0 + 128 wn).  Results go through a
-// 16 KB LDS region of the wave (stage), in rounds of rows, so that every global store is 16 bytes per
-// lane over whole rows: bf16 rows of 256 B, fp32 rows of 512 B, INT8 rows of 128 B, and V^T rows
-// (one head dimension, 64 tokens per round) of 128 B.  16-byte chunks are XOR-swizzled by row.
+// The wave owns the 128 x WN block at (mw0, nw0) = (m0 + 128 wm, n0 + WN wn) of a workgroup of NWV
+// waves.  Results go through a 16 KB LDS region of the wave (stage), in rounds of rows, so that every
+// global store is 16 bytes per lane over whole rows (bf16, fp32 and INT8 token rows; V^T head-
+// dimension rows).  16-byte chunks are XOR-swizzled by row.  red: NWV floats of LDS.
 QVD_DEV void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int EPI, class LY>
+template <int EPI, class LY, int WN, int NWV>
 QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float alpha, int m0, int n0,
                            int wm, int wn, float* red, uint8_t* stage) {
-    const int tid = threadIdx.x, lane = tid & 63;
+    static_assert(WN == 64 || WN == 128, "wave tile width");
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int M = g.M, N = g.N;
-    const int mw0 = m0 + 128 * wm, nw0 = n0 + 128 * wn;
+    const int mw0 = m0 + 128 * wm, nw0 = n0 + WN * wn;
     const bool wave_live = nw0 < N && mw0 < M;
     const qvd_epilogue& ep = g.epi;
 
-    // bf16 outputs (plain or GELU): rounds of 64 rows, LDS rows of 256 B (16 chunks)
-    auto bf16_rounds = [&](auto gelu, float& amax) {
-        constexpr bool GELU = decltype(gelu)::value != 0;
-        constexpr int RPR = 64 / LY::RB;                     // r blocks per round
+    // bf16 token rows of 2 WN bytes, R rows per round; RESID first brings the x rows in
+    constexpr int BC = WN / 8;                           // 16-byte chunks per row
+    constexpr int BR = 16384 / (2 * WN);                 // rows per round
+    auto bslot = [&](int ml, int c) { return stage + ml * (2 * WN) + ((c ^ (ml & (BC - 1))) << 4); };
+    auto bf16_rounds = [&](auto mode, float& amax) {
+        constexpr int MODE = decltype(mode)::value;      // 0 plain, 1 GELU, 2 x += gate y
+        constexpr int RPR = BR / LY::RB;
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
+        for (int rd = 0; rd < 128 / BR; ++rd) {
+            if (MODE == 2) {
+#pragma unroll
+                for (int it = 0; it < 16; ++it) {
+                    const int idx = 64 * it + lane, ml = idx / BC, c = idx % BC;
+                    const int m = mw0 + BR * rd + ml;
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (m < M) v = *reinterpret_cast<const u32x4*>(ep.resid + (int64_t)m * N + nw0 + 8 * c);
+                    *reinterpret_cast<u32x4*>(bslot(ml, c)) = v;
+                }
+                lds_wait();
+            }
 #pragma unroll
             for (int cg = 0; cg < LY::NCG; ++cg) {
                 const int nl = LY::ncol(cg, lane);
                 const float4 b = load_bias4(g.bias, nw0 + nl);
+                float4 gt = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (MODE == 2) gt = *reinterpret_cast<const float4*>(ep.gate + nw0 + nl);
 #pragma unroll
                 for (int rr = 0; rr < RPR; ++rr) {
                     const int r = rd * RPR + rr;
-                    const int ml = LY::mrow(r, lane) - 64 * rd;
+                    const int ml = LY::mrow(r, lane) - BR * rd;
                     const v4f c = LY::get(acc, cg, r);
                     float y[4] = {c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z, c[3] * alpha + b.w};
-                    if (GELU) {
+                    u32x2* slot = reinterpret_cast<u32x2*>(bslot(ml, nl >> 3) + ((nl >> 2) & 1) * 8);
+                    u32 p0, p1;
+                    if (MODE == 2) {
+                        const u32x2 xr = *slot;
+                        p0 = pack_bf16x2(bf16lo(xr[0]) + gt.x * y[0], bf16hi(xr[0]) + gt.y * y[1]);
+                        p1 = pack_bf16x2(bf16lo(xr[1]) + gt.z * y[2], bf16hi(xr[1]) + gt.w * y[3]);
+                    } else {
+                        if (MODE == 1) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) y[i] = gelu_erf(y[i]);
+                            for (int i = 0; i < 4; ++i) y[i] = gelu_erf(y[i]);
+                        }
+                        p0 = pack_bf16x2(y[0], y[1]);
+                        p1 = pack_bf16x2(y[2], y[3]);
+                        if (MODE == 1 && mw0 + BR * rd + ml < M)
+                            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(p0)), fabsf(bf16hi(p0))),
+                                                     fmaxf(fabsf(bf16lo(p1)), fabsf(bf16hi(p1)))));
                     }
-                    const u32 p0 = pack_bf16x2(y[0], y[1]), p1 = pack_bf16x2(y[2], y[3]);
-                    if (GELU && mw0 + 64 * rd + ml < M)
-                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(p0)), fabsf(bf16hi(p0))),
-                                                 fmaxf(fabsf(bf16lo(p1)), fabsf(bf16hi(p1)))));
-                    const int ch = (nl >> 3) ^ (ml & 15);
-                    *reinterpret_cast<u32x2*>(stage + ml * 256 + ch * 16 + ((nl >> 2) & 1) * 8) = (u32x2){p0, p1};
+                    *slot = (u32x2){p0, p1};
                 }
             }
             lds_wait();
 #pragma unroll
             for (int it = 0; it < 16; ++it) {
-                const int idx = 64 * it + lane, ml = idx >> 4, c = idx & 15;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) << 4));
-                const int m = mw0 + 64 * rd + ml;
+                const int idx = 64 * it + lane, ml = idx / BC, c = idx % BC;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(bslot(ml, c));
+                const int m = mw0 + BR * rd + ml;
                 if (m < M) *reinterpret_cast<u32x4*>(ep.out_bf16 + (int64_t)m * N + nw0 + 8 * c) = v;
             }
             lds_wait();
@@ -222,32 +260,33 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
         float amax = 0.0f;
         if (wave_live) bf16_rounds(std::integral_constant<int, 1>{}, amax);
         if (ep.amax_partials) {
-            amax = block_max_nonneg<4>(amax, red);
+            amax = block_max_nonneg<NWV>(amax, red);
             if (tid == 0) ep.amax_partials[blockIdx.x] = amax;
         }
-        return;
-    }
-    if (!wave_live) return;
-    if (EPI == QVD_EPI_BF16) {
-        float unused = 0.0f;
-        bf16_rounds(std::integral_constant<int, 0>{}, unused);
         return;
     }
 
     if (EPI == QVD_EPI_QKV) {
         const int dm = N / 3;
-        const int part = nw0 / dm;                     // 0 Q, 1 K, 2 V
-        const int head = (nw0 - part * dm) >> 7;
+        // The V columns start at 2 dm = 256 H, a tile boundary, so a workgroup's waves are either all
+        // in Q|K or all in V (the exchange barrier below is taken by all of them or by none).
+        const bool v_tile = n0 >= 2 * dm;
+        const int part = v_tile ? 2 : nw0 / dm;        // 0 Q, 1 K, 2 V
+        const int hc = nw0 - part * dm;                // column of this wave inside its part
+        const int head = hc >> 7;
         const int Tm = (M + 127) >> 7;
-        if (part == 2) {
+        if (v_tile) {
+            if (!wave_live) return;
             // V: bf16 rounding, then fp16 (exact for 2^-14 <= |v| <= 65504; larger saturate), stored
-            // transposed as V^T[head][dim][token] with tokens M .. Lp-1 zeroed.  LDS: 128 dimension
-            // rows of 64 tokens (128 B, 8 chunks) per round.
+            // transposed as V^T[head][dim][token] with tokens M .. Lp-1 zeroed.  LDS: WN dimension rows
+            // of TR tokens per round.
+            constexpr int TR = 16384 / (2 * WN);
+            constexpr int CT = TR / 8;
+            constexpr int RPR = TR / LY::RB;
             const int64_t Lp = (int64_t)Tm * 128;
-            uint16_t* vt = ep.v + (int64_t)head * 128 * Lp;
-            constexpr int RPR = 64 / LY::RB;
+            uint16_t* vt = ep.v + ((int64_t)head * 128 + (hc & 127)) * Lp;
 #pragma unroll
-            for (int rd = 0; rd < 2; ++rd) {
+            for (int rd = 0; rd < 128 / TR; ++rd) {
 #pragma unroll
                 for (int cg = 0; cg < LY::NCG; ++cg) {
                     const int dd = LY::ncol(cg, lane);
@@ -255,8 +294,8 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
 #pragma unroll
                     for (int rr = 0; rr < RPR; ++rr) {
                         const int r = rd * RPR + rr;
-                        const int ml = LY::mrow(r, lane) - 64 * rd;
-                        const bool ok = mw0 + 64 * rd + ml < M;
+                        const int ml = LY::mrow(r, lane) - TR * rd;
+                        const bool ok = mw0 + TR * rd + ml < M;
                         const v4f c = LY::get(acc, cg, r);
                         const float y[4] = {c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z,
                                             c[3] * alpha + b.w};
@@ -266,7 +305,7 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
                             const float vc = fminf(fmaxf(vb, -65504.0f), 65504.0f);
                             const uint16_t h16 = ok ? __builtin_bit_cast(uint16_t, (_Float16)vc) : (uint16_t)0;
                             const int row = dd + i;
-                            *reinterpret_cast<uint16_t*>(stage + row * 128 + (((ml >> 3) ^ (row & 7)) << 4) +
+                            *reinterpret_cast<uint16_t*>(stage + row * (2 * TR) + (((ml >> 3) ^ (row & (CT - 1))) << 4) +
                                                          (ml & 7) * 2) = h16;
                         }
                     }
@@ -274,36 +313,46 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
                 lds_wait();
 #pragma unroll
                 for (int it = 0; it < 16; ++it) {
-                    const int idx = 64 * it + lane, row = idx >> 3, c = idx & 7;
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * 128 + ((c ^ (row & 7)) << 4));
-                    *reinterpret_cast<u32x4*>(vt + (int64_t)row * Lp + mw0 + 64 * rd + 8 * c) = v;
+                    const int idx = 64 * it + lane, row = idx / CT, c = idx % CT;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * (2 * TR) + ((c ^ (row & (CT - 1))) << 4));
+                    *reinterpret_cast<u32x4*>(vt + (int64_t)row * Lp + mw0 + TR * rd + 8 * c) = v;
                 }
                 lds_wait();
             }
             return;
         }
-        // Q or K: round to bf16, then one symmetric INT8 scale over this (128-token tile, head).
-        // LDS: 128 token rows of 128 codes (8 chunks).
+        // Q or K: round to bf16, then one symmetric INT8 scale over this (128-token tile, head); a
+        // 64-wide wave shares the head with its neighbour (wn ^ 1) and their maxima meet in LDS.
+        // LDS: 128 token rows of WN codes.
         float amax = 0.0f;
+        if (wave_live) {
 #pragma unroll
-        for (int cg = 0; cg < LY::NCG; ++cg) {
-            const float4 b = load_bias4(g.bias, nw0 + LY::ncol(cg, lane));
+            for (int cg = 0; cg < LY::NCG; ++cg) {
+                const float4 b = load_bias4(g.bias, nw0 + LY::ncol(cg, lane));
 #pragma unroll
-            for (int r = 0; r < LY::MR; ++r) {
-                const int m = mw0 + LY::mrow(r, lane);
-                const v4f c = LY::get(acc, cg, r);
-                const u32 p0 = pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y);
-                const u32 p1 = pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w);
-                if (m < M)
-                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(p0)), fabsf(bf16hi(p0))),
-                                             fmaxf(fabsf(bf16lo(p1)), fabsf(bf16hi(p1)))));
+                for (int r = 0; r < LY::MR; ++r) {
+                    const int m = mw0 + LY::mrow(r, lane);
+                    const v4f c = LY::get(acc, cg, r);
+                    const u32 p0 = pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y);
+                    const u32 p1 = pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w);
+                    if (m < M)
+                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(p0)), fabsf(bf16hi(p0))),
+                                                 fmaxf(fabsf(bf16lo(p1)), fabsf(bf16hi(p1)))));
+                }
             }
         }
         amax = wave_max(amax);
+        if (WN == 64) {                                // every wave takes part: the barrier is shared
+            if (lane == 0) red[wv] = amax;
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            amax = fmaxf(amax, red[wv ^ 2]);
+        }
+        if (!wave_live) return;
         const float inv = amax == 0.0f ? 1.0f : __fdiv_rn(127.0f, amax);
         int8_t* dst = part == 0 ? ep.q8 : ep.k8;
         float* sdst = part == 0 ? ep.q_scale : ep.k_scale;
-        if (lane == 0) sdst[head * Tm + (mw0 >> 7)] = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 127.0f);
+        if (lane == 0 && (hc & 127) == 0) sdst[head * Tm + (mw0 >> 7)] = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 127.0f);
+        constexpr int QC = WN / 16;                    // 16-byte chunks per token row
 #pragma unroll
         for (int cg = 0; cg < LY::NCG; ++cg) {
             const int nl = LY::ncol(cg, lane);
@@ -318,71 +367,33 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
                               ((u32)(int8_encode(bf16hi(p0), inv) & 0xFF) << 8) |
                               ((u32)(int8_encode(bf16lo(p1), inv) & 0xFF) << 16) |
                               ((u32)(int8_encode(bf16hi(p1), inv) & 0xFF) << 24);
-                *reinterpret_cast<u32*>(stage + ml * 128 + (((nl >> 4) ^ (ml & 7)) << 4) + (nl & 15)) = q;
+                *reinterpret_cast<u32*>(stage + ml * WN + (((nl >> 4) ^ (ml & (QC - 1))) << 4) + (nl & 15)) = q;
             }
         }
         lds_wait();
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
-            const int idx = 64 * it + lane, ml = idx >> 3, c = idx & 7;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * 128 + ((c ^ (ml & 7)) << 4));
+        for (int it = 0; it < 2 * QC; ++it) {
+            const int idx = 64 * it + lane, ml = idx / QC, c = idx % QC;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * WN + ((c ^ (ml & (QC - 1))) << 4));
             const int m = mw0 + ml;
-            if (m < M) *reinterpret_cast<u32x4*>(dst + (int64_t)m * dm + (nw0 - part * dm) + 16 * c) = v;
+            if (m < M) *reinterpret_cast<u32x4*>(dst + (int64_t)m * dm + hc + 16 * c) = v;
         }
         return;
     }
 
-    if (EPI == QVD_EPI_RESID_GATE) {
-        // x += gate * y in place: rounds of 64 rows; the x rows come into LDS with 16-byte loads, are
-        // updated there in the accumulator layout, and leave with 16-byte stores
-        constexpr int RPR = 64 / LY::RB;
-#pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
-#pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const int idx = 64 * it + lane, ml = idx >> 4, c = idx & 15;
-                const int m = mw0 + 64 * rd + ml;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (m < M) v = *reinterpret_cast<const u32x4*>(ep.resid + (int64_t)m * N + nw0 + 8 * c);
-                *reinterpret_cast<u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) << 4)) = v;
-            }
-            lds_wait();
-#pragma unroll
-            for (int cg = 0; cg < LY::NCG; ++cg) {
-                const int nl = LY::ncol(cg, lane);
-                const float4 b = load_bias4(g.bias, nw0 + nl);
-                const float4 gt = *reinterpret_cast<const float4*>(ep.gate + nw0 + nl);
-#pragma unroll
-                for (int rr = 0; rr < RPR; ++rr) {
-                    const int r = rd * RPR + rr;
-                    const int ml = LY::mrow(r, lane) - 64 * rd;
-                    const v4f c = LY::get(acc, cg, r);
-                    u32x2* slot = reinterpret_cast<u32x2*>(stage + ml * 256 + (((nl >> 3) ^ (ml & 15)) << 4) +
-                                                           ((nl >> 2) & 1) * 8);
-                    const u32x2 xr = *slot;
-                    *slot = (u32x2){pack_bf16x2(bf16lo(xr[0]) + gt.x * (c[0] * alpha + b.x),
-                                                bf16hi(xr[0]) + gt.y * (c[1] * alpha + b.y)),
-                                    pack_bf16x2(bf16lo(xr[1]) + gt.z * (c[2] * alpha + b.z),
-                                                bf16hi(xr[1]) + gt.w * (c[3] * alpha + b.w))};
-                }
-            }
-            lds_wait();
-#pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const int idx = 64 * it + lane, ml = idx >> 4, c = idx & 15;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) << 4));
-                const int m = mw0 + 64 * rd + ml;
-                if (m < M) *reinterpret_cast<u32x4*>(ep.out_bf16 + (int64_t)m * N + nw0 + 8 * c) = v;
-            }
-            lds_wait();
-        }
+    if (!wave_live) return;
+    if (EPI == QVD_EPI_BF16 || EPI == QVD_EPI_RESID_GATE) {
+        float unused = 0.0f;
+        bf16_rounds(std::integral_constant<int, EPI == QVD_EPI_RESID_GATE ? 2 : 0>{}, unused);
         return;
     }
 
-    // fp32 output: rounds of 32 rows, LDS rows of 512 B (32 chunks)
-    constexpr int RPR = 32 / LY::RB > 0 ? 32 / LY::RB : 1;
+    // fp32 output: token rows of 4 WN bytes
+    constexpr int FC = WN / 4;
+    constexpr int FR = 16384 / (4 * WN);
+    constexpr int RPR = FR / LY::RB > 0 ? FR / LY::RB : 1;
 #pragma unroll
-    for (int rd = 0; rd < 4; ++rd) {
+    for (int rd = 0; rd < 128 / FR; ++rd) {
 #pragma unroll
         for (int cg = 0; cg < LY::NCG; ++cg) {
             const int nl = LY::ncol(cg, lane);
@@ -390,21 +401,20 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
 #pragma unroll
             for (int rr = 0; rr < RPR; ++rr) {
                 const int r = rd * RPR + rr;
-                const int ml = LY::mrow(r, lane) - 32 * rd;
+                const int ml = LY::mrow(r, lane) - FR * rd;
                 const v4f c = LY::get(acc, cg, r);
                 const float4 y = make_float4(c[0] * alpha + b.x, c[1] * alpha + b.y, c[2] * alpha + b.z,
                                              c[3] * alpha + b.w);
-                *reinterpret_cast<float4*>(stage + ml * 512 + (((nl >> 2) ^ (ml & 31)) << 4)) = y;
+                *reinterpret_cast<float4*>(stage + ml * (4 * WN) + (((nl >> 2) ^ (ml & (FC - 1))) << 4)) = y;
             }
         }
         lds_wait();
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
-            const int idx = 64 * it + lane, ml = idx >> 5, c = idx & 31;
-            const float4 y = *reinterpret_cast<const float4*>(stage + ml * 512 + ((c ^ (ml & 31)) << 4));
-            const int m = mw0 + 32 * rd + ml;
-            const int n = nw0 + 4 * c;
-            if (m < M) *reinterpret_cast<float4*>(ep.out_f32 + (int64_t)m * N + n) = y;
+            const int idx = 64 * it + lane, ml = idx / FC, c = idx % FC;
+            const float4 y = *reinterpret_cast<const float4*>(stage + ml * (4 * WN) + ((c ^ (ml & (FC - 1))) << 4));
+            const int m = mw0 + FR * rd + ml;
+            if (m < M) *reinterpret_cast<float4*>(ep.out_f32 + (int64_t)m * N + nw0 + 4 * c) = y;
         }
         lds_wait();
     }
@@ -485,28 +495,34 @@ __global__ void __launch_bounds__(256, 1) k_gemm_mx(GemmArgs g) {
         }
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages are free
-    gemm_epilogue<EPI, Layout16>(g, acc, *g.s_a, m0, n0, wm, wn, red, smem + wv * 16384);
+    gemm_epilogue<EPI, Layout16, 128, 4>(g, acc, *g.s_a, m0, n0, wm, wn, red, smem + wv * 16384);
 }
 
 // ================================================================================================
-// E4M3 x E4M3: 256 x 256 x 64 K-steps through a ring of four LDS stages, v_mfma_f32_32x32x64_f8f6f4.
+// E4M3 x E4M3: 256 x 256 tiles, v_mfma_f32_32x32x64_f8f6f4, eight waves (two per SIMD) of 128 x 64
+// outputs each.
 //
-// Per K-step each wave issues the DMA of the stage three steps ahead, then runs its 16 MFMAs on
-// fragments already in registers while it reads the next step's fragments from LDS, one 16-byte
-// read per MFMA.  A single s_barrier per step (after the wave's own DMA for the next stage has landed
-// and its fragment reads have completed) both publishes the next stage and frees the stage just read.
-// Stage layout: A rows and W rows of 64 bytes; 16-byte chunk c of row r sits at chunk c ^ ((r>>2)&3).
-// The 64 LDS banks (256 bytes) serve a 16-lane group of a 16-byte read per cycle: rows r .. r+15 at one
-// logical chunk then land on 16 distinct bank quads.  DMA writes are 1 KB contiguous per instruction.
-constexpr int BK8 = 64;
-constexpr int NSTAGE8 = 4;
-constexpr int STAGE8 = (BM + BN) * BK8;          // 32 KB
+// Operands move HBM/L2 -> LDS by global_load_lds_dwordx4 in stages of 128 K (two LDS buffers of
+// 64 KB): one DMA instruction fills 8 whole 128-byte rows, so every request is a full cache line.
+// The MFMAs run in K-steps of 64 (half a stage) on fragments already in registers while the next
+// step's 6 fragments are read from LDS.  One s_barrier per stage, at the start of the stage's second
+// step: stage s+1 has landed (its first fragments are read during that step) and every wave is done
+// with stage s-1, whose buffer then receives stage s+2 -- two steps of lead for the DMA.
+// Two waves per SIMD matter here: a single wave draws fragments from LDS at about half the rate that
+// two do, and the MFMA work of one wave covers the other's waits.
+// Stage layout: A rows and W rows of 128 bytes; 16-byte chunk c of row r sits at chunk c ^ ((r>>1)&7),
+// so rows r .. r+15 at one logical chunk land on 16 distinct bank quads of the 64 LDS banks.
+constexpr int BKS = 128;                          // K per stage
+constexpr int NBUF8 = 2;
+constexpr int STAGE8 = (BM + BN) * BKS;           // 64 KB
+constexpr int NWAVE8 = 8;
 
-// DMA instruction u (0..3: A rows, 4..7: W rows) of this wave's share of one stage
+// DMA instruction u of wave w's share of a stage (0..3: A row blocks 4w+u; 4..7: W row blocks
+// 4w+u-4; 8 rows each)
 QVD_DEV void dma_f8(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
                     const uint32_t* w_off, int u) {
-    uint8_t* dst = smem + buf * STAGE8 + (u < 4 ? 0 : BM * BK8) + (4 * wv + (u & 3)) * 1024;
-    const uint8_t* src = u < 4 ? g.a + a_off[u] + k0 : g.w + w_off[u & 3] + k0;
+    uint8_t* dst = smem + buf * STAGE8 + (u < 4 ? 0 : BM * BKS) + (4 * wv + (u & 3)) * 1024;
+    const uint8_t* src = u < 4 ? g.a + a_off[u & 3] + k0 : g.w + w_off[u & 3] + k0;
     __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
@@ -516,33 +532,22 @@ QVD_DEV void stage_f8(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv,
     for (int u = 0; u < 8; ++u) dma_f8(g, smem, buf, k0, wv, a_off, w_off, u);
 }
 
-// 32-byte MFMA operand of rows 32 b .. 32 b + 31 of a 64-byte-row tile: lane l reads row l%32,
-// bytes 32 (l/32) .. +31 (offsets precomputed in lo/hi)
+// 32-byte MFMA operand of rows 32 b .. 32 b + 31 of a 128-byte-row tile, K half h: lane l reads row
+// l%32, logical chunks 4h + 2(l/32) and 4h + 2(l/32) + 1 (row offsets precomputed in lo/hi per half)
 QVD_DEV v8i frag32(const uint8_t* tile, int b, uint32_t lo, uint32_t hi) {
-    const v4i x = *reinterpret_cast<const v4i*>(tile + b * 2048 + lo);
-    const v4i y = *reinterpret_cast<const v4i*>(tile + b * 2048 + hi);
+    const v4i x = *reinterpret_cast<const v4i*>(tile + b * 4096 + lo);
+    const v4i y = *reinterpret_cast<const v4i*>(tile + b * 4096 + hi);
     return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// wait until at most N of this wave's vector-memory operations are outstanding (whole stages of 8
-// DMA instructions), drain its LDS reads, and meet the other waves
-template <int N>
-QVD_DEV void wait_stage_barrier() {
-    static_assert(N == 0 || N == 8 || N == 16 || N == 24, "vmcnt in whole stages");
-    if (N == 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int V> using IC = std::integral_constant<int, V>;
 
 template <int EPI>
-__global__ void __launch_bounds__(256, 1) k_gemm_f8(GemmArgs g) {
-    // one LDS object: the stage ring and, past it, the epilogue's reduction slots (a second __shared__
-    // array makes the compiler wait for every DMA before each LDS read)
-    __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE8 * STAGE8 + 16];
-    float* red = reinterpret_cast<float*>(smem + NSTAGE8 * STAGE8);
+__global__ void __launch_bounds__(512, 1) k_gemm_f8(GemmArgs g) {
+    // one LDS object: the two stage buffers and, past them, the epilogue's reduction slots (a second
+    // __shared__ array makes the compiler wait for every DMA before each LDS read)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF8 * STAGE8 + 4 * NWAVE8];
+    float* red = reinterpret_cast<float*>(smem + NBUF8 * STAGE8);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv & 1, wn = wv >> 1;
@@ -551,92 +556,80 @@ __global__ void __launch_bounds__(256, 1) k_gemm_f8(GemmArgs g) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
 
-    // DMA: wave w's instruction u fills rows (4w+u)*16 .. +15 of a tile; lane l lands in row
-    // r = (4w+u)*16 + l/4, slot l%4, and fetches chunk (l%4) ^ ((r>>2)&3) of its row.
+    // DMA: wave w's A (W) instruction u fills rows (4w+u)*8 .. +7 of the tile; lane l lands in row
+    // r = (4w+u)*8 + l/8, slot l%8, and fetches chunk (l%8) ^ ((r>>1)&7) of its row.
     // Rows past M (N) repeat the last row; their results are never stored.
     uint32_t a_off[4], w_off[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int r = (4 * wv + u) * 16 + (lane >> 2);
-        const uint32_t c = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+        const int r = (4 * wv + u) * 8 + (lane >> 3);
+        const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
         const int ra = m0 + r < M ? m0 + r : M - 1;
         const int rw = n0 + r < N ? n0 + r : N - 1;
         a_off[u] = (uint32_t)ra * (uint32_t)K + 16u * c;
         w_off[u] = (uint32_t)rw * (uint32_t)K + 16u * c;
     }
-    // fragment reads: row l%32 of a 32-row block, logical chunks 2 (l/32) and 2 (l/32) + 1
-    const uint32_t fs = (uint32_t)(((lane & 31) >> 2) & 3);
-    const uint32_t flo = (uint32_t)(lane & 31) * 64u + 16u * ((2u * (uint32_t)(lane >> 5)) ^ fs);
-    const uint32_t fhi = (uint32_t)(lane & 31) * 64u + 16u * ((2u * (uint32_t)(lane >> 5) + 1u) ^ fs);
-    const int a_blk = 4 * wm, w_blk = 4 * wn;    // first 32-row block of this wave's rows
+    // fragment reads, per K half h: row l%32 of a 32-row block, logical chunks 4h + 2(l/32) (+1)
+    const uint32_t fs = (uint32_t)(((lane & 31) >> 1) & 7);
+    const uint32_t rb = (uint32_t)(lane & 31) * 128u, cg0 = 2u * (uint32_t)(lane >> 5);
+    const uint32_t flo0 = rb + 16u * (cg0 ^ fs), fhi0 = rb + 16u * ((cg0 + 1u) ^ fs);
+    const uint32_t flo1 = rb + 16u * ((cg0 + 4u) ^ fs), fhi1 = rb + 16u * ((cg0 + 5u) ^ fs);
+    const int a_blk = 4 * wm, w_blk = 2 * wn;    // first 32-row block of this wave's A / W rows
 
-    Layout32::Acc acc;
+    Layout32N64::Acc acc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // K is a multiple of 128, so the step count KT is even and the register sets alternate in pairs
-    const int KT = K / BK8;
-    if (KT >= NSTAGE8) {
-        for (int s = 0; s < NSTAGE8; ++s) stage_f8(g, smem, s, s * BK8, wv, a_off, w_off);
-        wait_stage_barrier<24>();                // stage 0 has landed for every wave
-    } else {
-        for (int s = 0; s < KT; ++s) stage_f8(g, smem, s, s * BK8, wv, a_off, w_off);
-        wait_stage_barrier<8>();
-    }
+    // K is a multiple of 128: S stages, 2 S steps (an even count, so the register sets alternate in
+    // pairs: even steps use set 0, odd steps set 1)
+    const int S = K / BKS;
+    stage_f8(g, smem, 0, 0, wv, a_off, w_off);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (S > 1) stage_f8(g, smem, 1, BKS, wv, a_off, w_off);
 
-    v8i fr[2][8];                                // [set][W blocks 0..3, A blocks 4..7]
+    v8i fr[2][6];                                // [set][W blocks 0..1, A blocks 2..5]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        fr[0][i] = frag32(smem + BM * BK8, w_blk + i, flo, fhi);
-        fr[0][4 + i] = frag32(smem, a_blk + i, flo, fhi);
-    }
+    for (int i = 0; i < 2; ++i) fr[0][i] = frag32(smem + BM * BKS, w_blk + i, flo0, fhi0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fr[0][2 + i] = frag32(smem, a_blk + i, flo0, fhi0);
 
-    // One K-step on register set P.  WAIT >= 0: first wait for stage kt+1 with WAIT DMA
-    // instructions (later stages) left in flight.  REFILL: issue stage kt+4 into the stage of kt.
-    // Issue order: the refill DMA and the 16 fragment reads of step kt+1 go out during the first 8
-    // MFMAs, so their latency is covered by the other 8 before the next barrier.
-    auto kstep = [&](auto P, auto WAIT, auto REFILL, int kt) {
-        constexpr int p = decltype(P)::value;
-        constexpr int wait = decltype(WAIT)::value;
-        constexpr bool refill = decltype(REFILL)::value != 0;
-        if (wait >= 0) wait_stage_barrier<(wait < 0 ? 0 : wait)>();
-        const uint8_t* As = smem + ((kt + 1) & 3) * STAGE8;
-        const uint8_t* Ws = As + BM * BK8;
-        // the last step's reads fetch a stale stage and are never used
+    // Stage s, half h, on register set h.  Half 0 reads the fragments of half 1 (same buffer).  Half 1
+    // first waits for stage s+1 (bar): after that barrier every wave has also finished reading stage s
+    // (its halves were read during the two previous steps), so stage s's buffer takes stage s+2
+    // (refill) while the fragments of stage s+1, half 0 are read from the other buffer.
+    auto kstep = [&](auto H, int s, bool bar, bool refill) {
+        constexpr int h = decltype(H)::value;
+        if (h == 1 && bar) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // fragments of the next step: stage s half 1, or stage s+1 half 0 (a stale buffer after the
+        // last step, never used)
+        const uint8_t* As = smem + ((h == 0 ? s : s + 1) & 1) * STAGE8;
+        const uint8_t* Ws = As + BM * BKS;
+        const uint32_t lo = h == 0 ? flo1 : flo0, hi = h == 0 ? fhi1 : fhi0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < 8; ++q) {
             acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fr[p][q >> 2], fr[p][4 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0, 0, 0, 0);
-            if (q < 8) {
-                if (refill) dma_f8(g, smem, kt & 3, (kt + NSTAGE8) * BK8, wv, a_off, w_off, q);
-                fr[p ^ 1][q] = q < 4 ? frag32(Ws, w_blk + q, flo, fhi) : frag32(As, a_blk + q - 4, flo, fhi);
-            }
+                fr[h][q >> 2], fr[h][2 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0, 0, 0, 0);
+            if (h == 1 && refill) dma_f8(g, smem, s & 1, (s + 2) * BKS, wv, a_off, w_off, q);
+            if (q < 6) fr[h ^ 1][q] = q < 2 ? frag32(Ws, w_blk + q, lo, hi) : frag32(As, a_blk + q - 2, lo, hi);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    int kt = 0;
-    for (; kt + NSTAGE8 < KT; kt += 2) {
-        kstep(IC<0>{}, IC<16>{}, IC<1>{}, kt);
-        kstep(IC<1>{}, IC<16>{}, IC<1>{}, kt + 1);
+    for (int s = 0; s < S; ++s) {
+        kstep(IC<0>{}, s, false, false);
+        kstep(IC<1>{}, s, s + 1 < S, s + 2 < S);
     }
-    if (KT >= NSTAGE8) {                         // kt = KT - 4
-        kstep(IC<0>{}, IC<16>{}, IC<0>{}, kt);
-        kstep(IC<1>{}, IC<8>{}, IC<0>{}, kt + 1);
-        kt += 2;
-    }
-    kstep(IC<0>{}, IC<0>{}, IC<0>{}, kt);        // kt = KT - 2
-    kstep(IC<1>{}, IC<-1>{}, IC<0>{}, kt + 1);   // kt = KT - 1
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages are free
-    gemm_epilogue<EPI, Layout32>(g, acc, (*g.s_a) * (*g.s_w), m0, n0, wm, wn, red, smem + wv * 16384);
+    gemm_epilogue<EPI, Layout32N64, 64, NWAVE8>(g, acc, (*g.s_a) * (*g.s_w), m0, n0, wm, wn, red,
+                                                smem + wv * 16384);
 }
 
 template <template <int> class KERN>
 static int launch_epi(const GemmArgs& g, hipStream_t st) {
-    const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), blk(256);
+    const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), blk(KERN<QVD_EPI_F32>::threads);
     switch (g.epi.mode) {
         case QVD_EPI_F32: hipLaunchKernelGGL(KERN<QVD_EPI_F32>::fn, grid, blk, 0, st, g); break;
         case QVD_EPI_BF16: hipLaunchKernelGGL(KERN<QVD_EPI_BF16>::fn, grid, blk, 0, st, g); break;
@@ -647,8 +640,8 @@ static int launch_epi(const GemmArgs& g, hipStream_t st) {
     }
     return launch_status("gemm");
 }
-template <int EPI> struct KF8 { static constexpr auto fn = k_gemm_f8<EPI>; };
-template <int EPI> struct KMX { static constexpr auto fn = k_gemm_mx<EPI>; };
+template <int EPI> struct KF8 { static constexpr auto fn = k_gemm_f8<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
+template <int EPI> struct KMX { static constexpr auto fn = k_gemm_mx<EPI>; static constexpr unsigned threads = 256; };
 
 int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t* e8, const float* s_w,
                 int w_fmt, const float* bias, int M, int N, int K, const qvd_epilogue& epi,
