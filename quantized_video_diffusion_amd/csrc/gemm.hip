@@ -24,7 +24,7 @@
 
 namespace qvd {
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BM = 256, BN = 256;
 
 struct GemmArgs {
     const uint8_t* a;
@@ -74,91 +74,13 @@ QVD_DEV float gelu_erf(float y) {
     return 0.5f * y * (1.0f + __builtin_copysignf(erf_abs, y));
 }
 
-// 32-byte MFMA fragment of row r (16-byte chunks 2g and 2g+1 of a 128-byte, XOR-swizzled row)
-QVD_DEV v8i frag_fp8(const uint8_t* tile, int r, int g) {
-    const int p0 = (2 * g) ^ (r & 7);
-    const v4i lo = *reinterpret_cast<const v4i*>(tile + r * 128 + (p0 << 4));
-    const v4i hi = *reinterpret_cast<const v4i*>(tile + r * 128 + ((p0 ^ 1) << 4));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// FP8 fragment that pairs with an FP4 fragment in the mixed-format MFMA: for 16x16x128 with an E2M1
-// operand, lane group g's 32 FP4 elements meet the FP8 bytes of 16-byte chunks g and g + 4 of the
-// other operand (measured on gfx950 with identity operands), so the FP8 side gathers those chunks
-// and every 32-element E2M1 block keeps its own E8M0 scale.
-QVD_DEV v8i frag_fp8_for_fp4(const uint8_t* tile, int r, int g) {
-    const v4i lo = *reinterpret_cast<const v4i*>(tile + r * 128 + ((g ^ (r & 7)) << 4));
-    const v4i hi = *reinterpret_cast<const v4i*>(tile + r * 128 + (((g + 4) ^ (r & 7)) << 4));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// 16-byte FP4 fragment (32 elements) of row r of a 64-byte row; chunks swizzled by (r >> 2) & 3
-QVD_DEV v8i frag_fp4(const uint8_t* tile, int r, int g) {
-    const int p = g ^ ((r >> 2) & 3);
-    const v4i v = *reinterpret_cast<const v4i*>(tile + r * 64 + (p << 4));
-    const v4i z = {0, 0, 0, 0};
-    return __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int WFMT>
-struct TileCfg {
-    static constexpr int W_BYTES = WFMT == QVD_W_MXFP4 ? BN * BK / 2 : BN * BK;
-    static constexpr int E_BYTES = WFMT == QVD_W_MXFP4 ? BN * 4 : 0;
-    static constexpr int STAGE = BM * BK + W_BYTES + E_BYTES;
-};
-
-// One K-step of both operands -> LDS stage `buf` (see the staging comment in k_gemm).
-template <int WFMT>
-QVD_DEV void stage_tiles(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv,
-                         const uint32_t* a_off, const uint32_t* w_off, uint32_t e_off) {
-    using Cfg = TileCfg<WFMT>;
-    constexpr int WINST = WFMT == QVD_W_MXFP4 ? 4 : 8;
-    uint8_t* As_ = smem + buf * Cfg::STAGE;
-    uint8_t* Ws_ = As_ + BM * BK;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-        __builtin_amdgcn_global_load_lds(g.a + a_off[u] + k0, (lds_void*)(As_ + (8 * wv + u) * 1024), 16, 0, 0);
-    const uint32_t wk = WFMT == QVD_W_MXFP4 ? (uint32_t)k0 / 2 : (uint32_t)k0;
-#pragma unroll
-    for (int u = 0; u < WINST; ++u) {
-        const int blk = WFMT == QVD_W_MXFP4 ? 4 * wv + u : 8 * wv + u;
-        __builtin_amdgcn_global_load_lds(g.w + w_off[u] + wk, (lds_void*)(Ws_ + blk * 1024), 16, 0, 0);
-    }
-    if (WFMT == QVD_W_MXFP4)
-        __builtin_amdgcn_global_load_lds(g.e8 + e_off + k0 / 32, (lds_void*)(Ws_ + Cfg::W_BYTES + 256 * wv),
-                                         4, 0, 0);
-}
-
-// ---- accumulator layouts -------------------------------------------------------------------------
-// Both MFMA shapes below compute C^T = W . A^T, so a lane holds runs of 4 consecutive output
-// columns (n) of one token row (m).  A layout enumerates them as NCG column groups x MR row blocks.
-
-// v_mfma_f32_16x16x128: acc[nb][mb], lane l holds C[16 mb + l%16][16 nb + 4 (l/16) .. +3]
-struct Layout16 {
-    static constexpr int NCG = 8, MR = 8, RB = 16;
-    typedef v4f Acc[8][8];
-    QVD_DEV static int ncol(int cg, int lane) { return 16 * cg + 4 * (lane >> 4); }
-    QVD_DEV static int mrow(int r, int lane) { return 16 * r + (lane & 15); }
-    QVD_DEV static v4f get(const Acc& a, int cg, int r) { return a[cg][r]; }
-};
-
-// v_mfma_f32_32x32x64: acc[nb][mb] (16 values), value 4g + i of lane l is
-// C[32 mb + l%32][32 nb + 8 g + 4 (l/32) + i]
-struct Layout32 {
-    static constexpr int NCG = 16, MR = 4, RB = 32;
-    typedef v16f Acc[4][4];
-    QVD_DEV static int ncol(int cg, int lane) { return 32 * (cg >> 2) + 8 * (cg & 3) + 4 * (lane >> 5); }
-    QVD_DEV static int mrow(int r, int lane) { return 32 * r + (lane & 31); }
-    QVD_DEV static v4f get(const Acc& a, int cg, int r) {
-        const v16f& v = a[cg >> 2][r];
-        const int b = 4 * (cg & 3);
-        return (v4f){v[b], v[b + 1], v[b + 2], v[b + 3]};
-    }
-};
-
-// v_mfma_f32_32x32x64 over a 128 x 64 wave tile: acc[nb][mb], nb in 0..1
+// ---- accumulator layout ----------------------------------------------------------------------------
+// The MFMAs compute C^T = W . A^T, so a lane holds runs of 4 consecutive output columns (n) of one token
+// row (m).  v_mfma_f32_32x32x64 over a 128 x 64 wave tile: acc[nb][mb] (nb in 0..1, mb in 0..3, 16
+// values each); value 4g + i of lane l is C[32 mb + l%32][32 nb + 8 g + 4 (l/32) + i].  The epilogue
+// walks it as NCG column groups of 4 x MR row blocks of RB rows.
 struct Layout32N64 {
     static constexpr int NCG = 8, MR = 4, RB = 32;
     typedef v16f Acc[2][4];
@@ -421,84 +343,6 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
 }
 
 // ================================================================================================
-// E4M3 x MXFP4: 256 x 256 x 128 tiles, two LDS stages, v_mfma_scale_f32_16x16x128_f8f6f4 with the
-// E2M1 operand's E8M0 scale per lane.
-template <int EPI>
-__global__ void __launch_bounds__(256, 1) k_gemm_mx(GemmArgs g) {
-    using Cfg = TileCfg<QVD_W_MXFP4>;
-    constexpr int WFMT = QVD_W_MXFP4;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg::STAGE];
-    __shared__ float red[4];
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv & 1, wn = wv >> 1;
-    int tm, tn;
-    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int M = g.M, N = g.N, K = g.K;
-
-    // ---- HBM/L2 -> LDS staging with global_load_lds (no register round trip) ---------------------
-    // A (128-byte rows): wave w's instruction u fills LDS rows (8w+u)*8 .. +7; lane l lands in row
-    // r = (8w+u)*8 + l/8, slot l%8, and fetches chunk (l%8) ^ (r&7) of its row.
-    // W (64-byte rows): instruction u fills rows (4w+u)*16 .. +15; lane l: row (4w+u)*16 + l/4,
-    // slot l%4, chunk (l%4) ^ ((row>>2)&3).  E8M0 scales: 4 bytes per row, row 64w + l.
-    // Rows past M (N) repeat the last row; their results are never stored.
-    uint32_t a_off[8], w_off[4];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int r = (8 * wv + u) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
-        const int row = m0 + r < M ? m0 + r : M - 1;
-        a_off[u] = (uint32_t)row * (uint32_t)K + 16u * c;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = (4 * wv + u) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
-        const int row = n0 + r < N ? n0 + r : N - 1;
-        w_off[u] = (uint32_t)row * (uint32_t)(K / 2) + 16u * c;
-    }
-    uint32_t e_off;
-    {
-        const int r = 64 * wv + lane;
-        const int row = n0 + r < N ? n0 + r : N - 1;
-        e_off = (uint32_t)row * (uint32_t)(K / 32);
-    }
-    Layout16::Acc acc;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-    const int KT = K / BK;
-    stage_tiles<WFMT>(g, smem, 0, 0, wv, a_off, w_off, e_off);
-    const int fr = lane & 15, fg = lane >> 4;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                       // tile kt is in LDS; every wave is done with kt-1
-        if (kt + 1 < KT) stage_tiles<WFMT>(g, smem, buf ^ 1, (kt + 1) * BK, wv, a_off, w_off, e_off);
-        const uint8_t* As = smem + buf * Cfg::STAGE;
-        const uint8_t* Ws = As + BM * BK;
-        v8i bfr[8];
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) bfr[mb] = frag_fp8_for_fp4(As, 128 * wm + 16 * mb + fr, fg);
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int r = 128 * wn + 16 * nb + fr;
-            const v8i af = frag_fp4(Ws, r, fg);
-            const int sc = (int)(reinterpret_cast<const u32*>(Ws + Cfg::W_BYTES)[r] >> (8 * fg));
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
-                acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[mb], acc[nb][mb], 4, 0, 0,
-                                                                              sc, 0, 127);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages are free
-    gemm_epilogue<EPI, Layout16, 128, 4>(g, acc, *g.s_a, m0, n0, wm, wn, red, smem + wv * 16384);
-}
-
-// ================================================================================================
 // E4M3 x E4M3: 256 x 256 tiles, v_mfma_f32_32x32x64_f8f6f4, eight waves (two per SIMD) of 128 x 64
 // outputs each.
 //
@@ -627,6 +471,167 @@ __global__ void __launch_bounds__(512, 1) k_gemm_f8(GemmArgs g) {
                                                 smem + wv * 16384);
 }
 
+// ================================================================================================
+// E4M3 activations x MXFP4 weights: the tiles, eight waves, 128-K stages and barrier schedule of the
+// E4M3 x E4M3 kernel, with v_mfma_scale_f32_32x32x64_f8f6f4 taking the E2M1 operand (cbsz = 4) and
+// one E8M0 scale per lane.
+// Operand pairing of that MFMA with E2M1 x E4M3 (measured on gfx950 with one-hot operands): lane half h
+// of the E2M1 operand holds k = 32h .. 32h+31 of its row in order -- 16 bytes, exactly one 32-element
+// block, whose scale the lane supplies -- and lane half h of the E4M3 operand holds k = 16h .. 16h+15
+// in its first 16 bytes and k = 32+16h .. 32+16h+15 in its last 16.
+// Stage layout (49 KB): A rows of 128 bytes as in the E4M3 kernel; W rows of 64 bytes (128 packed E2M1
+// values), 16-byte chunk c of row r at c ^ ((r>>2)&3), so rows r .. r+15 at one logical chunk cover
+// 16 distinct bank quads; then the 4 E8M0 bytes of each W row (blocks k0/32 .. k0/32+3).
+constexpr int W4_OFF = BM * BKS;                  // W rows of a stage
+constexpr int E8_OFF = W4_OFF + BN * BKS / 2;     // E8M0 words of a stage
+constexpr int STAGE_MX = E8_OFF + BN * 4;
+constexpr int SMEM_MX = 2 * STAGE_MX > NWAVE8 * 16384 ? 2 * STAGE_MX : NWAVE8 * 16384;
+
+// DMA instruction u of wave w's share of a stage: 0..3 A row blocks 4w+u (8 rows of 128 bytes each),
+// 4..5 W row blocks 2w+u-4 (16 rows of 64 bytes each), 6 the E8M0 words of W rows 64(w%4) .. +63
+// (4 bytes per lane; waves w and w+4 write the same words, which keeps the code free of branches).
+QVD_DEV void dma_mx(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
+                    const uint32_t* w_off, uint32_t e_off, int u) {
+    uint8_t* st = smem + buf * STAGE_MX;
+    if (u < 4)
+        __builtin_amdgcn_global_load_lds(g.a + a_off[u] + k0, (lds_void*)(st + (4 * wv + u) * 1024), 16, 0, 0);
+    else if (u < 6)
+        __builtin_amdgcn_global_load_lds(g.w + w_off[u - 4] + k0 / 2,
+                                         (lds_void*)(st + W4_OFF + (2 * wv + u - 4) * 1024), 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(g.e8 + e_off + k0 / 32, (lds_void*)(st + E8_OFF + 256 * (wv & 3)),
+                                         4, 0, 0);
+}
+
+QVD_DEV void stage_mx(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
+                      const uint32_t* w_off, uint32_t e_off) {
+#pragma unroll
+    for (int u = 0; u < 7; ++u) dma_mx(g, smem, buf, k0, wv, a_off, w_off, e_off, u);
+}
+
+// 16-byte E2M1 operand (32 elements) of rows 32 b .. 32 b + 31 of a 64-byte-row tile; the MFMA reads
+// only the low four registers
+QVD_DEV v8i frag_e2m1(const uint8_t* tile, int b, uint32_t off) {
+    const v4i x = *reinterpret_cast<const v4i*>(tile + b * 2048 + off);
+    const v4i z = {0, 0, 0, 0};
+    return __builtin_shufflevector(x, z, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
+    // one LDS object (see k_gemm_f8): stage buffers, which the epilogue then reuses as 16 KB per wave,
+    // and the reduction slots
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_MX + 4 * NWAVE8];
+    float* red = reinterpret_cast<float*>(smem + SMEM_MX);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv & 1, wn = wv >> 1;
+    int tm, tn;
+    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+
+    // DMA sources.  A as in k_gemm_f8.  W instruction u: lane l lands in row r = (2w+u)*16 + l/4, slot
+    // l%4, and fetches chunk (l%4) ^ ((r>>2)&3) of the row's 64 stage bytes.  E8M0: lane l brings row
+    // 64(w%4) + l.  Rows past M (N) repeat the last row; their results are never stored.
+    uint32_t a_off[4], w_off[2], e_off;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = (4 * wv + u) * 8 + (lane >> 3);
+        const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+        const int ra = m0 + r < M ? m0 + r : M - 1;
+        a_off[u] = (uint32_t)ra * (uint32_t)K + 16u * c;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r = (2 * wv + u) * 16 + (lane >> 2);
+        const uint32_t c = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+        const int rw = n0 + r < N ? n0 + r : N - 1;
+        w_off[u] = (uint32_t)rw * (uint32_t)(K / 2) + 16u * c;
+    }
+    {
+        const int r = 64 * (wv & 3) + lane;
+        const int rw = n0 + r < N ? n0 + r : N - 1;
+        e_off = (uint32_t)rw * (uint32_t)(K / 32);
+    }
+    // fragment offsets per K step j of a stage.  A (E4M3): row l%32, logical chunks 4j + h and
+    // 4j + 2 + h for lane half h.  W (E2M1): row l%32, logical chunk 2j + h.  Scale word: row l%32.
+    const int lr = lane & 31, hl = lane >> 5;
+    const uint32_t fs = (uint32_t)((lr >> 1) & 7), rb = (uint32_t)lr * 128u;
+    const uint32_t alo0 = rb + 16u * ((uint32_t)hl ^ fs), ahi0 = rb + 16u * ((2u + hl) ^ fs);
+    const uint32_t alo1 = rb + 16u * ((4u + hl) ^ fs), ahi1 = rb + 16u * ((6u + hl) ^ fs);
+    const uint32_t ws = (uint32_t)((lr >> 2) & 3), rw64 = (uint32_t)lr * 64u;
+    const uint32_t wo0 = rw64 + 16u * ((uint32_t)hl ^ ws), wo1 = rw64 + 16u * ((2u + hl) ^ ws);
+    const int a_blk = 4 * wm, w_blk = 2 * wn;
+    const uint32_t* e_row = reinterpret_cast<const uint32_t*>(smem + E8_OFF) + 32 * w_blk + lr;
+
+    Layout32N64::Acc acc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // K is a multiple of 128: S stages, 2 S steps
+    const int S = K / BKS;
+    stage_mx(g, smem, 0, 0, wv, a_off, w_off, e_off);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    stage_mx(g, smem, 1, S > 1 ? BKS : 0, wv, a_off, w_off, e_off);
+
+    v8i fw[2][2], fa[2][4];                      // [set][W blocks] / [set][A blocks]
+    uint32_t sc[2], sc_next[2];                  // E8M0 words of this stage, shifted to the lane half's block
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fw[0][i] = frag_e2m1(smem + W4_OFF, w_blk + i, wo0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = frag32(smem, a_blk + i, alo0, ahi0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sc[i] = e_row[32 * i] >> (8 * hl);
+
+    // The step schedule of k_gemm_f8, kept free of branches: the compiler moves MFMAs across branches
+    // (out of their interleave with the fragment reads), so step 1 always waits at the barrier and
+    // always refills, in the last two stages with a copy of stage S-1 (the buffer it lands in is not
+    // read again before the epilogue's barrier).  Step 0 of a stage uses blocks h of the stage (byte h
+    // of the shifted words), step 1 blocks 2 + h (byte 2); the words of stage s+1 are read at the start
+    // of step 1 of stage s.
+    const int k_last = K - BKS;
+    auto kstep = [&](auto H, int s) {
+        constexpr int h = decltype(H)::value;
+        if (h == 1) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int k_refill = (s + 2) * BKS < k_last ? (s + 2) * BKS : k_last;
+        const int nbuf = (h == 0 ? s : s + 1) & 1;
+        const uint8_t* As = smem + nbuf * STAGE_MX;
+        const uint8_t* Ws = As + W4_OFF;
+        const uint32_t lo = h == 0 ? alo1 : alo0, hi = h == 0 ? ahi1 : ahi0, wo = h == 0 ? wo1 : wo0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int sw = (int)(h == 0 ? sc[q >> 2] : sc[q >> 2] >> 16);
+            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fw[h][q >> 2], fa[h][q & 3], acc[q >> 2][q & 3], 4, 0, 0, sw, 0, 127);
+            if (h == 1 && q < 7) dma_mx(g, smem, s & 1, k_refill, wv, a_off, w_off, e_off, q);
+            if (h == 1 && q == 0) {             // first, so that LDS (which answers in order) has
+#pragma unroll                                  // them back before the fragments
+                for (int i = 0; i < 2; ++i) sc_next[i] = e_row[nbuf * (STAGE_MX / 4) + 32 * i] >> (8 * hl);
+            }
+            if (q < 2)
+                fw[h ^ 1][q] = frag_e2m1(Ws, w_blk + q, wo);
+            else if (q < 6)
+                fa[h ^ 1][q - 2] = frag32(As, a_blk + q - 2, lo, hi);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (h == 1) {
+            sc[0] = sc_next[0];
+            sc[1] = sc_next[1];
+        }
+    };
+    for (int s = 0; s < S; ++s) {
+        kstep(IC<0>{}, s);
+        kstep(IC<1>{}, s);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages are free
+    gemm_epilogue<EPI, Layout32N64, 64, NWAVE8>(g, acc, *g.s_a, m0, n0, wm, wn, red, smem + wv * 16384);
+}
+
 template <template <int> class KERN>
 static int launch_epi(const GemmArgs& g, hipStream_t st) {
     const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), blk(KERN<QVD_EPI_F32>::threads);
@@ -641,7 +646,7 @@ static int launch_epi(const GemmArgs& g, hipStream_t st) {
     return launch_status("gemm");
 }
 template <int EPI> struct KF8 { static constexpr auto fn = k_gemm_f8<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
-template <int EPI> struct KMX { static constexpr auto fn = k_gemm_mx<EPI>; static constexpr unsigned threads = 256; };
+template <int EPI> struct KMX { static constexpr auto fn = k_gemm_mx<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
 
 int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t* e8, const float* s_w,
                 int w_fmt, const float* bias, int M, int N, int K, const qvd_epilogue& epi,
