@@ -442,9 +442,9 @@ __global__ void __launch_bounds__(512, 1) k_gemm_f8(GemmArgs g) {
     for (int i = 0; i < 4; ++i) fr[0][2 + i] = frag32(smem, a_blk + i, flo0, fhi0);
 
     // Stage s, half h, on register set h.  Half 0 reads the fragments of half 1 (same buffer).  Half 1
-    // first waits for stage s+1 (bar): after that barrier every wave has also finished reading stage s
-    // (its halves were read during the two previous steps), so stage s's buffer takes stage s+2
-    // (refill) while the fragments of stage s+1, half 0 are read from the other buffer.
+    // first waits for stage s+1: after that barrier every wave has also finished reading stage s (its
+    // halves were read during the two previous steps), so stage s's buffer takes stage s+2 while the
+    // fragments of stage s+1, half 0 are read from the other buffer.
     auto kstep = [&](auto H, int s, bool bar, bool refill) {
         constexpr int h = decltype(H)::value;
         if (h == 1 && bar) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -588,17 +588,17 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) sc[i] = e_row[32 * i] >> (8 * hl);
 
-    // The step schedule of k_gemm_f8, kept free of branches: the compiler moves MFMAs across branches
-    // (out of their interleave with the fragment reads), so step 1 always waits at the barrier and
-    // always refills, in the last two stages with a copy of stage S-1 (the buffer it lands in is not
-    // read again before the epilogue's barrier).  Step 0 of a stage uses blocks h of the stage (byte h
-    // of the shifted words), step 1 blocks 2 + h (byte 2); the words of stage s+1 are read at the start
-    // of step 1 of stage s.
-    const int k_last = K - BKS;
-    auto kstep = [&](auto H, int s) {
+    // The step schedule of k_gemm_f8, with step bodies free of branches: with the refill and the E8M0
+    // loads of waves 0..3 behind branches, the compiler moved every MFMA of the loop behind the last
+    // of them (out of its interleave with the fragment reads) and spilled.  So the main loop always
+    // refills, the last two stages never do, step 1 always waits at the barrier (once more than
+    // needed, in the last stage), and all eight waves load E8M0 words.  Step 0 of a stage uses blocks
+    // h of the stage (byte h of the shifted words), step 1 blocks 2 + h (byte 2); the words of stage
+    // s+1 are read at the start of step 1 of stage s.
+    auto kstep = [&](auto H, auto REFILL, int s) {
         constexpr int h = decltype(H)::value;
+        constexpr bool refill = decltype(REFILL)::value == 1;
         if (h == 1) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        const int k_refill = (s + 2) * BKS < k_last ? (s + 2) * BKS : k_last;
         const int nbuf = (h == 0 ? s : s + 1) & 1;
         const uint8_t* As = smem + nbuf * STAGE_MX;
         const uint8_t* Ws = As + W4_OFF;
@@ -608,7 +608,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
             const int sw = (int)(h == 0 ? sc[q >> 2] : sc[q >> 2] >> 16);
             acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 fw[h][q >> 2], fa[h][q & 3], acc[q >> 2][q & 3], 4, 0, 0, sw, 0, 127);
-            if (h == 1 && q < 7) dma_mx(g, smem, s & 1, k_refill, wv, a_off, w_off, e_off, q);
+            if (h == 1 && refill && q < 7) dma_mx(g, smem, s & 1, (s + 2) * BKS, wv, a_off, w_off, e_off, q);
             if (h == 1 && q == 0) {             // first, so that LDS (which answers in order) has
 #pragma unroll                                  // them back before the fragments
                 for (int i = 0; i < 2; ++i) sc_next[i] = e_row[nbuf * (STAGE_MX / 4) + 32 * i] >> (8 * hl);
@@ -624,9 +624,14 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
             sc[1] = sc_next[1];
         }
     };
-    for (int s = 0; s < S; ++s) {
-        kstep(IC<0>{}, s);
-        kstep(IC<1>{}, s);
+    int s = 0;
+    for (; s < S - 2; ++s) {
+        kstep(IC<0>{}, IC<0>{}, s);
+        kstep(IC<1>{}, IC<1>{}, s);
+    }
+    for (; s < S; ++s) {
+        kstep(IC<0>{}, IC<0>{}, s);
+        kstep(IC<1>{}, IC<0>{}, s);
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages are free
     gemm_epilogue<EPI, Layout32N64, 64, NWAVE8>(g, acc, *g.s_a, m0, n0, wm, wn, red, smem + wv * 16384);
