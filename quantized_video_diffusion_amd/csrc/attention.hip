@@ -4,15 +4,23 @@
 // training bullet (the model runs with 80% attention sparsity) and section "运行速度如何", note under
 // the table (query and key are quantized to INT8 for the score computation).
 //
-// One workgroup per (query tile of 128 rows, head); four waves of 32 query rows; two workgroups per
-// CU.  One pass over the kept key tiles (masked tiles are never loaded or multiplied):
-//   S^T = K . Q^T with v_mfma_i32_16x16x64_i8 (exact int32, Q fragments in registers);
-//   running row maxima m of S * sQ*sK*sm_scale*log2(e); numerators exp2(s - m) rounded to fp16;
-//   the fp32 sums so far are multiplied by exp2(m_old - m_new) (every tile, branch-free);
-//   numerator sums (ones . P^T) and O^T += V^T . P^T with v_mfma_f32_16x16x32_f16, fp32 accumulation.
-// A numerator rounded against the running maximum and later rescaled differs from the one rounded
-// against the final maximum by at most one fp16 rounding (relative 2^-11); the output is normalised by
-// the sum of the numerators actually used.
+// Work item: one (query tile of 128 rows, head); four waves of 32 query rows each.  A workgroup of
+// eight waves (one per CU, two per SIMD) holds two work items, one per group of four waves, and runs
+// them in alternating phases separated by workgroup barriers: while one group multiplies (MFMA) the
+// other computes its softmax numerators (VALU), so the matrix cores and the vector ALUs of each SIMD
+// work at the same time.  Per item, over the kept key tiles t (masked tiles are never loaded or
+// multiplied):
+//   MFMA phase t:  O^T += V^T(t-1) . P^T(t-1) and the numerator sums (ones . P^T) with
+//                  v_mfma_f32_16x16x32_f16, fp32 accumulation; then S^T = K(t) . Q^T with
+//                  v_mfma_i32_16x16x64_i8 (exact int32, Q fragments in registers);
+//   VALU phase t:  row maxima of S * sQ*sK*sm_scale*log2(e); numerators P = exp2(s - m) rounded to
+//                  fp16 against a reference maximum m per row (scores biased into float patterns,
+//                  see SCORE_BIAS).
+// The reference m moves only when a tile's row maximum exceeds it by more than 8 (log2 units), and
+// then the fp32 sums so far are multiplied by exp2(m_old - m_new); otherwise the numerators stay
+// below 2^8.  A numerator rounded against such a reference and rescaled differs from the one rounded
+// against the final maximum by at most one fp16 rounding (relative 2^-11), and the output is
+// normalised by the sum of the numerators actually used.
 //
 // Staging: tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no register round trip).  The K
 // tile's rows are permuted (key_of_row) so that each lane's 8 numerators of a 32-key block are 8
@@ -32,12 +40,18 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 constexpr int MAX_KEPT = 1024;      // longest kept-tile list a workgroup takes (kmax bound)
 
-struct AttnSmem {
+// LDS of one work item (group of four waves)
+struct GroupSmem {
     int8_t k[2][128 * 128];         // 2 x 16 KB: double-buffered K tiles
     uint16_t vt[128 * 128];         // 32 KB, fp16 bit patterns
-    int tiles[MAX_KEPT];            // the valid entries of this row's kept-tile list, in order
-    int wcount[4];
-    float red[4];                   // block reduction of max|O|
+    int tiles[MAX_KEPT];            // the valid entries of the item's kept-tile list, in order
+};
+
+struct AttnSmem {
+    GroupSmem grp[2];
+    int wcount[2][4];
+    int n[2];                       // kept tiles per group
+    float red[8];                   // per-group reductions of max|O|
 };
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -55,11 +69,11 @@ QVD_DEV void dma16(const void* g, void* lds_slot_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_slot_base, 16, 0, 0);
 }
 
-// Barriers with explicit waits: this wave's DMA (all of it, or all but the 4 K-tile instructions
-// issued last) has landed and its LDS reads are done, then every wave meets.  (__syncthreads() would
-// also wait for the K prefetch, which is meant to stay in flight.)
+// Barriers with explicit waits: this wave's LDS reads are done (and with dma_barrier its DMA has
+// landed), then every wave meets.  (__syncthreads() would also wait for DMA that is meant to stay in
+// flight across the barrier.)
 QVD_DEV void dma_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-QVD_DEV void dma_barrier_but_4() { asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+QVD_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Key (0..127 within its tile) held by row rho of the LDS K tile.  Row rho = 16 kb + 4 g + r is the
 // score-block row that lane group g receives as element r of block kb; the map gives lane group g the
@@ -104,7 +118,7 @@ QVD_DEV void stage_k(int8_t* kbuf, const int8_t* __restrict__ k, int L, int H, i
 // (8w + u)*4 .. +3 (256 B each); lane l lands in row d = (8w+u)*4 + l/16, slot l%16, and fetches
 // chunk (l%16) ^ (d & 15) of keys j*128 .. j*128+127.
 // (32-bit offsets: H*128*Lp*2 bytes stays far below 2^32 for every L the launcher accepts)
-QVD_DEV void stage_vt(AttnSmem& sm, const uint16_t* __restrict__ vt, int Lp, int h, int j,
+QVD_DEV void stage_vt(uint16_t* vbuf, const uint16_t* __restrict__ vt, int Lp, int h, int j,
                       int wv, int lane) {
     const char* base = reinterpret_cast<const char*>(vt) + (size_t)j * 256u;
 #pragma unroll
@@ -113,12 +127,13 @@ QVD_DEV void stage_vt(AttnSmem& sm, const uint16_t* __restrict__ vt, int Lp, int
         const int d = blk * 4 + (lane >> 4);
         const int c = (lane & 15) ^ (d & 15);
         const uint32_t off = ((uint32_t)(h * 128 + d) * (uint32_t)Lp + (uint32_t)(8 * c)) * 2u;
-        dma16(base + off, sm.vt + blk * 512);
+        dma16(base + off, vbuf + blk * 512);
     }
 }
 
-// S^T = K . Q^T for this wave: s[qb][kb][r] = score(query q0 + 16 qb + fr, key key_of_row(16 kb + 4 fg + r))
-QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v4i s[2][8]) {
+// S^T = K . Q^T for this wave: s[qb][kb][r] = s0 + score(query q0 + 16 qb + fr,
+// key key_of_row(16 kb + 4 fg + r)) (exact int32 sums)
+QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v4i s[2][8], int s0) {
     // steps (ks, half): 4 key blocks x 2 query blocks; an accumulator's next MFMA comes 16 later, and
     // the next step's K fragments are read while this step multiplies
     auto kfrag = [&](int kb, int ks) {
@@ -140,7 +155,7 @@ QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const int kb = 4 * hf + b;
-                const v4i c = ks == 0 ? (v4i){0, 0, 0, 0} : s[qb][kb];
+                const v4i c = ks == 0 ? (v4i){s0, s0, s0, s0} : s[qb][kb];
                 s[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kcur[b], qf[qb][ks], c, 0, 0, 0);
             }
         __builtin_amdgcn_sched_barrier(0);
@@ -149,9 +164,35 @@ QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v
     }
 }
 
-// running row maxima (in log2 units) of this tile's scores, this lane's share
+// Scores arrive biased: the QK accumulators start at the bit pattern of SCORE_BIAS = 1.5 * 2^23, so
+// the int32 result is the bit pattern of the float SCORE_BIAS + s, exactly (|s| <= 128^3 = 2^21 <
+// 2^22 keeps it in the binade of SCORE_BIAS, where the float spacing is 1).  The row maximum is then
+// an integer maximum of the patterns (positive floats order as their patterns), and the numerator
+// argument s c - m is a single fma, fma(SCORE_BIAS + s, c, -(m + SCORE_BIAS c)), with no int -> float
+// conversion; the folded constant is rounded once, an absolute error of at most
+// 2^-24 (SCORE_BIAS c + |m|) in log2 units, far below the fp16 rounding of the numerator.
+constexpr int SCORE_BIAS_BITS = 0x4B400000;
+constexpr float SCORE_BIAS = 12582912.0f;
+
+// Vector elements reach a bit_cast through this by-value helper: a bit_cast applied to a vector
+// element lvalue reads element 0.
+QVD_DEV float as_float(u32 x) { return __builtin_bit_cast(float, x); }
+
+QVD_DEV float unbias(int bits) { return as_float((u32)bits) - SCORE_BIAS; }
+
+// max over lanes l, l^16, l^32, l^48 with the gfx950 lane swaps (pure VALU: v_permlane16_swap pairs
+// lane l with l^16, v_permlane32_swap with l^32), so the softmax phase issues no LDS instruction
+QVD_DEV int max_over_lane_groups(int x) {
+    const auto a = __builtin_amdgcn_permlane16_swap((u32)x, (u32)x, false, false);
+    const int y = max((int)a[0], (int)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((u32)y, (u32)y, false, false);
+    return max((int)b[0], (int)b[1]);
+}
+
+// row maxima (log2 units) of this tile's scores: integer maxima of the biased patterns over this
+// lane's keys, then over the row's four lane groups
 template <bool RAGGED>
-QVD_DEV void tile_max(const v4i s[2][8], float c, int key0, int L, int fg, float m[2]) {
+QVD_DEV void tile_max(const v4i s[2][8], float c, int key0, int L, int fg, float tmax[2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         int mx = INT_MIN;
@@ -162,16 +203,18 @@ QVD_DEV void tile_max(const v4i s[2][8], float c, int key0, int L, int fg, float
                 if (RAGGED && key0 + key_of_row(16 * kb + 4 * fg + r) >= L) continue;
                 mx = max(mx, s[qb][kb][r]);
             }
-        if (!RAGGED || mx != INT_MIN) m[qb] = fmaxf(m[qb], (float)mx * c);
+        mx = max_over_lane_groups(mx);         // every row keeps at least one key of a ragged tile
+        tmax[qb] = unbias(mx) * c;
     }
 }
 
-// fp16 numerators of this tile against the running maxima, as the B operand of the P.V MFMA
+// fp16 numerators of this tile against the reference maxima, as the B operand of the P.V MFMA
 template <bool RAGGED>
 QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int key0, int L, int fg,
                              v8h pb[2][4]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+        const float mb = fmaf(SCORE_BIAS, c, m[qb]);
 #pragma unroll
         for (int kp = 0; kp < 4; ++kp) {
             u32 w[4];
@@ -181,7 +224,7 @@ QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int k
                 float p[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    p[r] = __builtin_amdgcn_exp2f(fmaf((float)s[qb][kb][r], c, -m[qb]));
+                    p[r] = __builtin_amdgcn_exp2f(fmaf(as_float((u32)s[qb][kb][r]), c, -mb));
                     if (RAGGED && key0 + key_of_row(16 * kb + 4 * fg + r) >= L) p[r] = 0.0f;
                 }
                 w[2 * hlf] = pack_f16x2(p[0], p[1]);
@@ -193,31 +236,103 @@ QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int k
     }
 }
 
-// The valid entries (0 <= j < T) of the first `cnt` list elements, in list order, into sm.tiles;
-// returns their number.  Ballot-based prefix sums keep the order deterministic.
-QVD_DEV int compact_tiles(AttnSmem& sm, const int32_t* __restrict__ list, int cnt, int T, int tid,
-                          int lane, int wv) {
+// The valid entries (0 <= j < T) of the first `cnt` list elements, in list order, into tiles; their
+// number into *n_out.  Run by both groups of the workgroup at once (gtid: thread index in the group,
+// wg: wave in the group): the iteration count depends on kmax only, so every wave meets the same
+// barriers.  Ballot-based prefix sums keep the order deterministic.
+QVD_DEV void compact_tiles(int* tiles, int* wcount, int* n_out, const int32_t* __restrict__ list, int cnt,
+                           int kmax, int T, int gtid, int lane, int wg) {
     int total = 0;
-    for (int base = 0; base < cnt; base += 256) {
-        const int t = base + tid;
+    for (int base = 0; base < kmax; base += 256) {
+        const int t = base + gtid;
         const int j = t < cnt ? list[t] : -1;
         const bool ok = j >= 0 && j < T;
         const unsigned long long mask = __ballot(ok);
         const int pos = __popcll(mask & ((1ull << lane) - 1ull));
         __syncthreads();
-        if (lane == 0) sm.wcount[wv] = __popcll(mask);
+        if (lane == 0) wcount[wg] = __popcll(mask);
         __syncthreads();
         int off = total;
-        for (int w = 0; w < wv; ++w) off += sm.wcount[w];
-        if (ok) sm.tiles[off + pos] = j;
-        total += sm.wcount[0] + sm.wcount[1] + sm.wcount[2] + sm.wcount[3];
+        for (int w = 0; w < wg; ++w) off += wcount[w];
+        if (ok) tiles[off + pos] = j;
+        total += wcount[0] + wcount[1] + wcount[2] + wcount[3];
     }
+    if (gtid == 0) *n_out = total;
     __syncthreads();
-    return total;
+}
+
+// O^T += V^T . P^T and the numerator sums, this wave's share, from the V^T tile in LDS.  Lane group
+// g's 8 numerators meet keys 32 kp + 8 g .. +7 of V^T row d, one 16-byte chunk.  Steps (kp, half of
+// the 16-dim blocks): an accumulator's next MFMA comes 16 later, and the next step's fragments are
+// read while this step multiplies.
+QVD_DEV void pv_tile(const uint16_t* vbuf, const v8h pb[2][4], int fr, int fg, v4f o[2][8], v4f lacc[2]) {
+    const v8h ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    auto vfrag = [&](int db, int kp) {
+        const int d = 16 * db + fr;
+        return *reinterpret_cast<const v8h*>(vbuf + d * 128 + 8 * ((4 * kp + fg) ^ (d & 15)));
+    };
+    v8h vcur[4], vnext[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) vcur[b] = vfrag(b, 0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        const int kp = st >> 1, hf = st & 1;
+        if (st + 1 < 8) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) vnext[b] = vfrag(4 * ((st + 1) & 1) + b, (st + 1) >> 1);
+        }
+        if (hf == 0) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[qb][kp], lacc[qb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                o[qb][4 * hf + b] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(vcur[b], pb[qb][kp], o[qb][4 * hf + b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) vcur[b] = vnext[b];
+    }
+}
+
+constexpr float RESCALE_SLACK = 8.0f;   // log2 units a tile maximum may exceed the reference by
+
+
+// Numerators of one tile against the reference maxima m (moved, and the sums rescaled, when a row's
+// tile maximum exceeds its reference by more than RESCALE_SLACK; the wave takes or skips the rescale
+// as a whole).
+QVD_DEV void softmax_tile(const v4i s[2][8], float c, bool ragged, int key0, int L, int fg, float m[2],
+                          v4f o[2][8], v4f lacc[2], v8h pb[2][4]) {
+    float tmax[2];
+    if (ragged) tile_max<true>(s, c, key0, L, fg, tmax);
+    else tile_max<false>(s, c, key0, L, fg, tmax);
+    float alpha[2];
+    bool up = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const bool u = tmax[qb] > m[qb] + RESCALE_SLACK;
+        const float mnew = u ? tmax[qb] : m[qb];
+        alpha[qb] = m[qb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[qb] - mnew);
+        m[qb] = mnew;
+        up = up || u;
+    }
+    if (__ballot(up) != 0ull) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            lacc[qb] *= alpha[qb];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[qb][db] *= alpha[qb];
+        }
+    }
+    if (ragged) tile_numerators<true>(s, c, m, key0, L, fg, pb);
+    else tile_numerators<false>(s, c, m, key0, L, fg, pb);
 }
 
 template <bool WRITE_AMAX>
-__global__ void __launch_bounds__(256, 2) k_sparse_attn(
+__global__ void __launch_bounds__(512, 1) k_sparse_attn(
     const int8_t* __restrict__ q, const float* __restrict__ q_scale, const int8_t* __restrict__ k,
     const float* __restrict__ k_scale, const uint16_t* __restrict__ vt, int L, int H,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int kmax, float c_log2,
@@ -225,25 +340,41 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
     // a single LDS object: with a second __shared__ array the compiler waits for every DMA before
     // each LDS read
     __shared__ __attribute__((aligned(16))) AttnSmem sm;
-    const int i = blockIdx.x, h = blockIdx.y, T = gridDim.x;
+    const int T = (L + 127) >> 7, total = T * H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = wv >> 2, wg = wv & 3;
     const int fr = lane & 15, fg = lane >> 4;
-    const int q0 = i * 128 + 32 * wv;
+
+    // Workgroup b -> pair index -> work items 2 pair + g, head-major (h = id / T, i = id % T).
+    // Workgroups are handed to the 8 XCDs round-robin (b % 8), so each XCD is given one contiguous
+    // range of pairs: the workgroups resident on an XCD at a time hold neighbouring query tiles of one
+    // head, whose ascending tile lists sweep the same K and V^T tiles through the XCD's L2 at about
+    // the same time.
+    int id;
+    {
+        const int pairs = (total + 1) >> 1, b = blockIdx.x;
+        const int xcd = b & 7, per = pairs >> 3, rem = pairs & 7;
+        id = 2 * (xcd * per + (xcd < rem ? xcd : rem) + (b >> 3)) + g;
+    }
+    const bool valid = id < total;               // an odd item count leaves the last group idle
+    const int h = valid ? id / T : 0;
+    const int i = valid ? id - h * T : 0;
+    const int q0 = i * 128 + 32 * wg;
     const int Lp = T * 128;
     const bool ragged_L = (L & 127) != 0;
+    GroupSmem& gs = sm.grp[g];
 
     v4i qf[2][2];
     load_q_frags(q, L, H, h, q0, fr, fg, qf);
     const float qsc = q_scale[h * T + i] * c_log2;
-    int cnt = kv_cnt[h * T + i];
+    int cnt = valid ? kv_cnt[h * T + i] : 0;
     cnt = cnt < 0 ? 0 : (cnt > kmax ? kmax : cnt);
     const int32_t* list = kv_idx + ((int64_t)h * T + i) * kmax;
-    const int n = compact_tiles(sm, list, cnt, T, tid, lane, wv);
+    compact_tiles(gs.tiles, sm.wcount[g], &sm.n[g], list, cnt, kmax, T, tid & 255, lane, wg);
+    const int n = sm.n[g];
+    const int n_other = sm.n[g ^ 1];
 
-    // running row maxima (log2 units) of the tiles seen so far
-    float m[2] = {-INFINITY, -INFINITY};
-
-    // per tile: V^T(t) loads under QK(t) and the numerators; K(t+1) loads under P.V(t)
+    float m[2] = {-INFINITY, -INFINITY};         // reference row maxima (log2 units)
     v4f o[2][8], lacc[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -251,77 +382,57 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
 #pragma unroll
         for (int b = 0; b < 8; ++b) o[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
-    const v8h ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    v4i s[2][8];                                  // scores of tile t: MFMA phase t -> VALU phase t
+    v8h pb[2][4];                                 // numerators of tile t: VALU phase t -> MFMA phase t+1
+    float ksc = 0.0f;                             // K scale of the tile the next VALU phase takes
 
-    if (n > 0) stage_k(sm.k[0], k, L, H, h, sm.tiles[0], wv, lane);
-    for (int t = 0; t < n; ++t) {
-        const int j = sm.tiles[t];
-        dma_barrier();                         // K(t) in LDS; P.V(t-1) and QK(t-1) are done
-        stage_vt(sm, vt, Lp, h, j, wv, lane);
-        const bool more = t + 1 < n;
-        if (more) stage_k(sm.k[(t + 1) & 1], k, L, H, h, sm.tiles[t + 1], wv, lane);
+    // Phases p = 0, 1, ... end at workgroup barriers B_p (B_-1 before phase 0).  Group 0 runs MFMA
+    // phase t in phase 2t and VALU phase t in phase 2t+1; group 1 one phase later.  Each group runs
+    // its own loop, so its scores and numerators are live only where it uses them; the loops meet
+    // the same barriers (s_barrier counts waves, not program locations), P + 1 of them in all.
+    // Before a group's MFMA phase its waves wait for their DMA (K(t) and V^T(t-1)).
+    //   MFMA phase t: index and K scale of tile t; K(t+1) -> LDS (its buffer was last read in MFMA phase t-1);
+    //                 P.V(t-1); S(t).  (The last one, t = n, multiplies a stale K buffer into unused
+    //                 scores, which keeps the loop free of register merges.)
+    //   VALU phase t: V^T(t) -> LDS (its buffer was last read in MFMA phase t); numerators of tile t.
+    //                 No LDS reads: the tile index and its K scale are read in the MFMA phase before,
+    //                 so the other group's fragment reads never hold this phase up.
+    const int n0 = g == 0 ? n : n_other, n1 = g == 0 ? n_other : n;
+    const int P = 2 * n0 + 1 > 2 * n1 + 2 ? 2 * n0 + 1 : 2 * n1 + 2;
+    auto mfma_qk = [&](int t) {                   // the QK part of MFMA phase t and its DMA
+        if (t + 1 < n) stage_k(gs.k[(t + 1) & 1], k, L, H, h, gs.tiles[t + 1], wg, lane);
+        qk_scores(gs.k[t & 1], qf, fr, fg, s, SCORE_BIAS_BITS);
+    };
+    int j = 0;                                    // tile of the next VALU phase (read in the MFMA phase)
+    auto valu_phase = [&]() {
+        stage_vt(gs.vt, vt, Lp, h, j, wg, lane);
+        softmax_tile(s, qsc * ksc, ragged_L && j == T - 1, j * 128, L, fg, m, o, lacc, pb);
+    };
 
-        v4i s[2][8];
-        qk_scores(sm.k[t & 1], qf, fr, fg, s);
-        const float c = qsc * k_scale[h * T + j];
-        // new running maxima; the sums so far are rescaled to them (every tile, without a branch)
-        float tmax[2] = {-INFINITY, -INFINITY};
-        if (ragged_L && j == T - 1) tile_max<true>(s, c, j * 128, L, fg, tmax);
-        else tile_max<false>(s, c, j * 128, L, fg, tmax);
-        float alpha[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            tmax[qb] = fmaxf(tmax[qb], __shfl_xor(tmax[qb], 16, 64));
-            tmax[qb] = fmaxf(tmax[qb], __shfl_xor(tmax[qb], 32, 64));
-            const float mnew = fmaxf(m[qb], tmax[qb]);
-            alpha[qb] = m[qb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[qb] - mnew);
-            m[qb] = mnew;
-        }
-        v8h pb[2][4];
-        if (ragged_L && j == T - 1) tile_numerators<true>(s, c, m, j * 128, L, fg, pb);
-        else tile_numerators<false>(s, c, m, j * 128, L, fg, pb);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            lacc[qb] *= alpha[qb];
-#pragma unroll
-            for (int db = 0; db < 8; ++db) o[qb][db] *= alpha[qb];
-        }
-
-        if (more) dma_barrier_but_4();         // every wave's V^T(t) landed; K(t+1) may be in flight
-        else dma_barrier();
-        // O^T += V^T . P^T; lane group g's 8 numerators meet keys 32 kp + 8 g .. +7 of V^T row d,
-        // one 16-byte chunk.  Steps (kp, half of the 16-dim blocks): an accumulator's next MFMA comes
-        // 16 later, and the next step's fragments are read while this step multiplies.
-        auto vfrag = [&](int db, int kp) {
-            const int d = 16 * db + fr;
-            return *reinterpret_cast<const v8h*>(sm.vt + d * 128 + 8 * ((4 * kp + fg) ^ (d & 15)));
-        };
-        v8h vcur[4], vnext[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) vcur[b] = vfrag(b, 0);
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const int kp = st >> 1, hf = st & 1;
-            if (st + 1 < 8) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) vnext[b] = vfrag(4 * ((st + 1) & 1) + b, (st + 1) >> 1);
+    if (n > 0) stage_k(gs.k[0], k, L, H, h, gs.tiles[0], wg, lane);
+    if (g == 1) lds_barrier();                   // group 1: B_-1 (its phase 0 is idle)
+    dma_barrier();                                // group 0: B_-1; group 1: B_0
+    int passed = 1 + g;                           // barriers passed
+    if (n > 0) {
+        j = gs.tiles[0];
+        ksc = k_scale[h * T + j];
+        mfma_qk(0);
+        lds_barrier();
+        ++passed;
+        for (int t = 0; t < n; ++t) {
+            valu_phase();
+            dma_barrier();
+            if (t + 1 < n) {
+                j = gs.tiles[t + 1];
+                ksc = k_scale[h * T + j];
             }
-            if (hf == 0) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[qb][kp], lacc[qb], 0, 0, 0);
-            }
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    o[qb][4 * hf + b] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vcur[b], pb[qb][kp], o[qb][4 * hf + b], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) vcur[b] = vnext[b];
+            pv_tile(gs.vt, pb, fr, fg, o, lacc);
+            mfma_qk(t + 1);
+            lds_barrier();
+            passed += 2;
         }
     }
+    for (; passed < P + 1; ++passed) lds_barrier();
 
     float amax = 0.0f;
 #pragma unroll
@@ -329,7 +440,7 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
         const float lt = lacc[qb][0];
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
         const int row = q0 + 16 * qb + fr;
-        if (row < L) {
+        if (valid && row < L) {
             uint16_t* orow = out + ((int64_t)row * H + h) * 128;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
@@ -343,8 +454,13 @@ __global__ void __launch_bounds__(256, 2) k_sparse_attn(
         }
     }
     if (WRITE_AMAX) {
-        amax = block_max_nonneg<4>(amax, sm.red);
-        if (tid == 0) amax_partials[h * T + i] = amax;
+        // max over the group's four waves (both groups reduce at once)
+        amax = wave_max(amax);
+        if (lane == 0) sm.red[wv] = amax;
+        __syncthreads();
+        if ((tid & 255) == 0 && valid)
+            amax_partials[h * T + i] = fmaxf(fmaxf(sm.red[4 * g], sm.red[4 * g + 1]),
+                                             fmaxf(sm.red[4 * g + 2], sm.red[4 * g + 3]));
     }
 }
 
@@ -385,16 +501,16 @@ __global__ void __launch_bounds__(256) k_vt_from_bf16(const uint16_t* __restrict
 __global__ void __launch_bounds__(256) k_qk_tile(const int8_t* __restrict__ q, const int8_t* __restrict__ k,
                                                  int L, int H, int h, int i, int j,
                                                  int32_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) AttnSmem sm;
+    __shared__ __attribute__((aligned(16))) int8_t ktile[128 * 128];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int fr = lane & 15, fg = lane >> 4;
     const int q0 = i * 128 + 32 * wv;
     v4i qf[2][2];
     load_q_frags(q, L, H, h, q0, fr, fg, qf);
-    stage_k(sm.k[0], k, L, H, h, j, wv, lane);
+    stage_k(ktile, k, L, H, h, j, wv, lane);
     dma_barrier();
     v4i s[2][8];
-    qk_scores(sm.k[0], qf, fr, fg, s);
+    qk_scores(ktile, qf, fr, fg, s, SCORE_BIAS_BITS);      // as the attention kernel, bias removed below
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -403,7 +519,7 @@ __global__ void __launch_bounds__(256) k_qk_tile(const int8_t* __restrict__ q, c
             for (int r = 0; r < 4; ++r) {
                 const int rr = 32 * wv + 16 * qb + fr, cc = key_of_row(16 * kb + 4 * fg + r);
                 const bool ok = (i * 128 + rr) < L && (j * 128 + cc) < L;
-                out[rr * 128 + cc] = ok ? s[qb][kb][r] : 0;
+                out[rr * 128 + cc] = ok ? s[qb][kb][r] - SCORE_BIAS_BITS : 0;
             }
 }
 
@@ -412,13 +528,14 @@ int launch_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k
                           int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st) {
     if (L == 0) return QVD_OK;
     const int T = (L + 127) / 128;
+    const unsigned pairs = (unsigned)((T * H + 1) / 2);
     const float c = sm_scale * LOG2E;
     TimingScope ts("sparse_attn", st);
     if (amax_partials)
-        hipLaunchKernelGGL(k_sparse_attn<true>, dim3(T, H), dim3(256), 0, st, q, q_scale, k, k_scale, vt,
+        hipLaunchKernelGGL(k_sparse_attn<true>, dim3(pairs), dim3(512), 0, st, q, q_scale, k, k_scale, vt,
                            L, H, kv_idx, kv_cnt, kmax, c, out, amax_partials);
     else
-        hipLaunchKernelGGL(k_sparse_attn<false>, dim3(T, H), dim3(256), 0, st, q, q_scale, k, k_scale, vt,
+        hipLaunchKernelGGL(k_sparse_attn<false>, dim3(pairs), dim3(512), 0, st, q, q_scale, k, k_scale, vt,
                            L, H, kv_idx, kv_cnt, kmax, c, out, amax_partials);
     return launch_status("sparse_attn");
 }

@@ -200,6 +200,26 @@ def test_sparse_attn_vs_oracle(L, H, sparse):
             assert gp[h, i] == np.abs(got[rr, h]).max()
 
 
+def test_sparse_attn_peaked_rows_large_logit_gap():
+    """Every query row has one dominant key (the same unit direction in Q and K, |.| = 20 against
+    0.05-scaled noise), about 50 log2 units above the other scores.  For three rows in four that key
+    lies outside the first 8 keys of its 32-key block, so a row maximum taken over part of a tile
+    would leave numerators far above one (beyond fp16 range): the result must stay finite and equal
+    the oracle's, which is the mean of the V rows of the dominant keys."""
+    L, H = 256, 2
+    qb, kb, vb, idx, cnt = _attn_inputs(L, H, 5, False)
+    hot = np.zeros((L, H, 128), np.float32)
+    rows = np.arange(L)
+    hot[rows, :, rows % 128] = 20.0
+    qb2 = W.f32_to_bf16_bits(0.05 * W.bf16_bits_to_f32(qb) + hot)
+    kb2 = W.f32_to_bf16_bits(0.05 * W.bf16_bits_to_f32(kb) + hot)
+    (q8, qs, k8, ks), (oq, oqs, ok, oks) = _quantize_both(qb2, kb2, L, H)
+    out = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt))
+    want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx, cnt)
+    assert np.isfinite(bf16_f64(out)).all()
+    assert_bf16_close(host_bits(out), want, 1e-2, "peaked rows")
+
+
 def test_sparse_attn_vt_entry_matches_bf16_entry():
     """The fp16 V^T entry point on a host-transposed V gives the same bits as the bf16 entry."""
     L, H = 1290, 2
