@@ -140,10 +140,11 @@ int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, in
  *   out_amax_partials : NULL, or fp32 [H][T] receiving max|out| of each (h, i) tile (feeds the
  *            dynamic FP8 quantization of the attention output without another pass).
  *   ws     : qvd_sparse_attn_ws_bytes(L, H) bytes: V transposed to fp16 [H][128][T*128].
- * Arithmetic: INT8 MFMA scores (exact int32); one pass over the kept tiles with each row's running
- * maximum m: numerators exp2((s - m) log2 e) rounded to fp16, the fp32 sums rescaled whenever m
- * grows, fp16 MFMA P.V and numerator sums with fp32 accumulation.  Each weight is within one fp16
- * rounding of the numerator taken against the final maximum.  |V| above 65504 saturates to 65504. */
+ * Arithmetic: INT8 MFMA scores (exact int32); one pass over the kept tiles with a reference
+ * maximum m per row, moved (and the fp32 sums rescaled) only when a tile's row maximum exceeds it
+ * by more than 8 in log2 units: numerators exp2((s - m) log2 e) <= 2^8 rounded to fp16, fp16 MFMA
+ * P.V and numerator sums with fp32 accumulation.  Each weight is within one fp16 rounding of the
+ * numerator taken against the final maximum.  |V| above 65504 saturates to 65504. */
 size_t qvd_sparse_attn_ws_bytes(int32_t L, int32_t H);
 int sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                 const uint16_t* v, int32_t L, int32_t H, int32_t head_dim,
@@ -156,6 +157,16 @@ int qvd_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k,
                        const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
                        const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
                        uint16_t* out, float* out_amax_partials, void* stream);
+
+/* The same attention over fp16 V^T writing, instead of bf16 O, the E4M3 codes
+ *   out_q[l][h][d] = E4M3(bf16(O[l][h][d]) * fp32(1 / *out_scale))
+ * that quant_fp8_per_tensor computes from bf16 O with scale_in = out_scale (a static, calibrated
+ * per-tensor scale > 0), without writing O: the attention output enters the out-projection GEMM
+ * directly.  out_q: uint8 [L][H][128], 16-byte aligned. */
+int qvd_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
+                            const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                            const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
+                            const float* out_scale, uint8_t* out_q, void* stream);
 
 /* Exact INT32 accumulators Q8[rows of tile i] . K8[rows of tile j]^T of head h, computed by the
  * same INT8 MFMA tile routine the attention kernel uses, into out int32 [128][128]
@@ -176,13 +187,17 @@ enum qvd_epilogue_mode {
                                resid (in-place residual update)                                 */
     QVD_EPI_GELU = 3,       /* out_bf16[m][n] = bf16(GELU(y)) (erf form); amax_partials, if
                                non-NULL, receives per-output-tile max|out| (see below)          */
-    QVD_EPI_QKV = 4         /* N = 3*H*128: columns [Q | K | V].  y is rounded to bf16; the Q and
+    QVD_EPI_QKV = 4,        /* N = 3*H*128: columns [Q | K | V].  y is rounded to bf16; the Q and
                                K parts are then quantized per (head, 128-token tile) exactly as
                                quant_int8_qk does, into q8/k8 int8 [M][H][128] with scales
                                q_scale/k_scale [H][ceil(M/128)]; the V part (bf16 values) is
                                written transposed and converted to fp16 into v as
                                [H][128][ceil(M/128)*128], columns M.. of the last tile zeroed
                                (the layout qvd_sparse_attn_vt reads)                            */
+    QVD_EPI_GELU_E4M3 = 5   /* out_e4m3[m][n] = E4M3(bf16(GELU(y)) * fp32(1 / *out_scale)): the
+                               GELU output quantized with a static per-tensor scale exactly as
+                               quant_fp8_per_tensor does with scale_in = out_scale, without the
+                               bf16 tensor (static scales: the calibrated path)                 */
 };
 typedef struct {
     int32_t mode;               /* qvd_epilogue_mode                                           */
@@ -197,6 +212,8 @@ typedef struct {
     uint16_t* v;                /* QVD_EPI_QKV: fp16 V^T [H][128][ceil(M/128)*128]               */
     float* q_scale;
     float* k_scale;
+    uint8_t* out_e4m3;          /* QVD_EPI_GELU_E4M3: E4M3 codes [M][N]                          */
+    const float* out_scale;     /* QVD_EPI_GELU_E4M3: device fp32 static scale s (> 0)           */
 } qvd_epilogue;
 int64_t qvd_gemm_tiles(int32_t M, int32_t N);
 int qvd_gemm_fp8(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,

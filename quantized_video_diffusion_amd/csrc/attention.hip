@@ -331,12 +331,16 @@ QVD_DEV void softmax_tile(const v4i s[2][8], float c, bool ragged, int key0, int
     else tile_numerators<false>(s, c, m, key0, L, fg, pb);
 }
 
-template <bool WRITE_AMAX>
+// Output of the attention kernel: bf16 O; bf16 O and the per-(head, tile) max|O|; or the E4M3 codes
+// of bf16 O under a static per-tensor scale, as the standalone static quantizer computes them.
+enum AttnOut { OUT_BF16 = 0, OUT_BF16_AMAX = 1, OUT_E4M3 = 2 };
+
+template <int OUT>
 __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     const int8_t* __restrict__ q, const float* __restrict__ q_scale, const int8_t* __restrict__ k,
     const float* __restrict__ k_scale, const uint16_t* __restrict__ vt, int L, int H,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int kmax, float c_log2,
-    uint16_t* __restrict__ out, float* __restrict__ amax_partials) {
+    void* __restrict__ out, float* __restrict__ amax_partials, const float* __restrict__ out_scale) {
     // a single LDS object: with a second __shared__ array the compiler waits for every DMA before
     // each LDS read
     __shared__ __attribute__((aligned(16))) AttnSmem sm;
@@ -435,25 +439,33 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     for (; passed < P + 1; ++passed) lds_barrier();
 
     float amax = 0.0f;
+    const float inv_s = OUT == OUT_E4M3 ? __fdiv_rn(1.0f, *out_scale) : 0.0f;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const float lt = lacc[qb][0];
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
         const int row = q0 + 16 * qb + fr;
         if (valid && row < L) {
-            uint16_t* orow = out + ((int64_t)row * H + h) * 128;
+            const int64_t orow = ((int64_t)row * H + h) * 128;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
                 const v4f cc = o[qb][db];
                 const u32 w0 = pack_bf16x2(cc[0] * inv, cc[1] * inv);
                 const u32 w1 = pack_bf16x2(cc[2] * inv, cc[3] * inv);
-                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(w0)), fabsf(bf16hi(w0))),
-                                         fmaxf(fabsf(bf16lo(w1)), fabsf(bf16hi(w1)))));
-                *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * fg) = (u32x2){w0, w1};
+                if (OUT == OUT_E4M3) {
+                    const u32 c4 = e4m3_encode2(bf16lo(w0) * inv_s, bf16hi(w0) * inv_s) |
+                                   (e4m3_encode2(bf16lo(w1) * inv_s, bf16hi(w1) * inv_s) << 16);
+                    *reinterpret_cast<u32*>(static_cast<uint8_t*>(out) + orow + 16 * db + 4 * fg) = c4;
+                } else {
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(w0)), fabsf(bf16hi(w0))),
+                                             fmaxf(fabsf(bf16lo(w1)), fabsf(bf16hi(w1)))));
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + 16 * db + 4 * fg) =
+                        (u32x2){w0, w1};
+                }
             }
         }
     }
-    if (WRITE_AMAX) {
+    if (OUT == OUT_BF16_AMAX) {
         // max over the group's four waves (both groups reduce at once)
         amax = wave_max(amax);
         if (lane == 0) sm.red[wv] = amax;
@@ -523,21 +535,38 @@ __global__ void __launch_bounds__(256) k_qk_tile(const int8_t* __restrict__ q, c
             }
 }
 
-int launch_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
-                          const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt,
-                          int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st) {
+namespace {
+template <int OUT>
+int launch_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
+                const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt, int kmax,
+                float sm_scale, void* out, float* amax_partials, const float* out_scale, hipStream_t st) {
     if (L == 0) return QVD_OK;
     const int T = (L + 127) / 128;
     const unsigned pairs = (unsigned)((T * H + 1) / 2);
     const float c = sm_scale * LOG2E;
     TimingScope ts("sparse_attn", st);
-    if (amax_partials)
-        hipLaunchKernelGGL(k_sparse_attn<true>, dim3(pairs), dim3(512), 0, st, q, q_scale, k, k_scale, vt,
-                           L, H, kv_idx, kv_cnt, kmax, c, out, amax_partials);
-    else
-        hipLaunchKernelGGL(k_sparse_attn<false>, dim3(pairs), dim3(512), 0, st, q, q_scale, k, k_scale, vt,
-                           L, H, kv_idx, kv_cnt, kmax, c, out, amax_partials);
+    hipLaunchKernelGGL(k_sparse_attn<OUT>, dim3(pairs), dim3(512), 0, st, q, q_scale, k, k_scale, vt, L, H,
+                       kv_idx, kv_cnt, kmax, c, out, amax_partials, out_scale);
     return launch_status("sparse_attn");
+}
+}  // namespace
+
+int launch_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
+                          const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt,
+                          int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st) {
+    if (amax_partials)
+        return launch_attn<OUT_BF16_AMAX>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+                                          out, amax_partials, nullptr, st);
+    return launch_attn<OUT_BF16>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out,
+                                 nullptr, nullptr, st);
+}
+
+int launch_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
+                               const float* k_scale, const uint16_t* vt, int L, int H,
+                               const int32_t* kv_idx, const int32_t* kv_cnt, int kmax, float sm_scale,
+                               const float* out_scale, uint8_t* out_q, hipStream_t st) {
+    return launch_attn<OUT_E4M3>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out_q,
+                                 nullptr, out_scale, st);
 }
 
 size_t vt_bytes(int L, int H) { return (size_t)H * 128 * (size_t)((L + 127) / 128) * 128 * 2; }
@@ -607,6 +636,19 @@ int sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const fl
     }
     return launch_sparse_attn_vt(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out,
                                  out_amax_partials, st);
+}
+
+int qvd_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
+                            const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                            const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
+                            const float* out_scale, uint8_t* out_q, void* stream) {
+    int s = validate_attn("qvd_sparse_attn_vt_e4m3", q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt,
+                          kmax, sm_scale, reinterpret_cast<uint16_t*>(out_q));
+    if (s || L == 0) return s;
+    QVD_PTR(out_scale);
+    QVD_DEVICE_OK();
+    return launch_sparse_attn_vt_e4m3(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+                                      out_scale, out_q, (hipStream_t)stream);
 }
 
 int qvd_qk_int32_tile(const int8_t* q, const int8_t* k, int32_t L, int32_t H, int32_t h,

@@ -17,7 +17,10 @@
 //   per-tensor FP8 of g                           -> g8
 //   GEMM g8 . W_down^T, epilogue: x += gate2 * y   (in place)
 // Dynamic scales never leave the device: every amax is reduced from per-workgroup partial maxima
-// written by the producing kernel.
+// written by the producing kernel.  With static (calibrated) scales the two per-tensor FP8 steps
+// are fused into their producers: the attention writes the E4M3 codes of O and the up-projection's
+// epilogue the E4M3 codes of g, with the same arithmetic as the standalone quantizer, so neither
+// bf16 tensor is written or read back.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,8 +35,8 @@ struct BlockWs {
     int8_t* q8;          // [L][d]
     int8_t* k8;          // [L][d]
     uint16_t* v;         // fp16 V^T [H][128][T*128]
-    uint16_t* o;         // bf16 [L][d]
-    uint16_t* g;         // bf16 [L][F]
+    uint16_t* o;         // bf16 [L][d] (dynamic scales only)
+    uint16_t* g;         // bf16 [L][F] (dynamic scales only)
     uint8_t* g8;         // E4M3 [L][F]
     float* qs;           // [H][T]
     float* ks;           // [H][T]
@@ -59,8 +62,9 @@ BlockWs carve(const qvd_block_params* p, int L, uint8_t* base) {
     w.q8 = (int8_t*)take(Ld);
     w.k8 = (int8_t*)take(Ld);
     w.v = (uint16_t*)take(vt_bytes(L, p->n_heads));
-    w.o = (uint16_t*)take(2 * Ld);
-    w.g = (uint16_t*)take(2 * LF);
+    const bool stat = p->act_scale != nullptr;   // static scales: O and g exist only as E4M3 codes
+    w.o = (uint16_t*)take(stat ? 0 : 2 * Ld);
+    w.g = (uint16_t*)take(stat ? 0 : 2 * LF);
     w.g8 = take(LF);
     w.qs = (float*)take(4 * HT);
     w.ks = (float*)take(4 * HT);
@@ -168,39 +172,52 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     e.k_scale = w.ks;
     s = launch_gemm(w.h, w.scales + 0, p->w_qkv, p->e8m0_qkv, p->s_qkv, fmt, p->b_qkv, L, 3 * d, d, e, st);
     if (s) return s;
-    s = launch_sparse_attn_vt(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.o,
-                              act ? nullptr : w.attn_part, st);
-    if (s) return s;
-    s = launch_quant_fp8(w.o, (int64_t)L * d, act ? act + 1 : nullptr, w.attn_part, H * T, w.h,
-                         w.scales + 1, st);
+    if (act) {
+        s = launch_sparse_attn_vt_e4m3(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+                                       act + 1, w.h, st);
+    } else {
+        s = launch_sparse_attn_vt(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.o,
+                                  w.attn_part, st);
+        if (s) return s;
+        s = launch_quant_fp8(w.o, (int64_t)L * d, nullptr, w.attn_part, H * T, w.h, w.scales + 1, st);
+    }
     if (s) return s;
     e = qvd_epilogue{};
     e.mode = QVD_EPI_RESID_GATE;
     e.out_bf16 = x;
     e.resid = x;
     e.gate = shift_scale_gate + 2 * d;
-    s = launch_gemm(w.h, w.scales + 1, p->w_o, p->e8m0_o, p->s_o, fmt, p->b_o, L, d, d, e, st);
+    s = launch_gemm(w.h, act ? act + 1 : w.scales + 1, p->w_o, p->e8m0_o, p->s_o, fmt, p->b_o, L, d, d, e,
+                    st);
     if (s) return s;
 
     // MLP branch
     s = launch_modulate(x, L, d, mod, 1, p->ln_eps, act ? act + 2 : nullptr, w.h, w.scales + 2, w.ln_ws, st);
     if (s) return s;
     e = qvd_epilogue{};
-    e.mode = QVD_EPI_GELU;
-    e.out_bf16 = w.g;
-    e.amax_partials = act ? nullptr : w.gelu_part;
+    if (act) {
+        e.mode = QVD_EPI_GELU_E4M3;
+        e.out_e4m3 = w.g8;
+        e.out_scale = act + 3;
+    } else {
+        e.mode = QVD_EPI_GELU;
+        e.out_bf16 = w.g;
+        e.amax_partials = w.gelu_part;
+    }
     s = launch_gemm(w.h, w.scales + 2, p->w_up, p->e8m0_up, p->s_up, fmt, p->b_up, L, F, d, e, st);
     if (s) return s;
-    s = launch_quant_fp8(w.g, (int64_t)L * F, act ? act + 3 : nullptr, w.gelu_part,
-                         (int)gemm_tiles(L, F), w.g8, w.scales + 3, st);
-    if (s) return s;
+    if (!act) {
+        s = launch_quant_fp8(w.g, (int64_t)L * F, nullptr, w.gelu_part, (int)gemm_tiles(L, F), w.g8,
+                             w.scales + 3, st);
+        if (s) return s;
+    }
     e = qvd_epilogue{};
     e.mode = QVD_EPI_RESID_GATE;
     e.out_bf16 = x;
     e.resid = x;
     e.gate = shift_scale_gate + 5 * d;
-    return launch_gemm(w.g8, w.scales + 3, p->w_down, p->e8m0_down, p->s_down, fmt, p->b_down, L, d, F,
-                       e, st);
+    return launch_gemm(w.g8, act ? act + 3 : w.scales + 3, p->w_down, p->e8m0_down, p->s_down, fmt,
+                       p->b_down, L, d, F, e, st);
 }
 
 }  // extern "C"

@@ -57,21 +57,27 @@ QVD_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
     tn = in / gm;
 }
 
-// GELU(y) = y/2 (1 + erf(y/sqrt 2)).  erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26: erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1/(1 + p z), z >= 0, with
-// |error| <= 1.5e-7; odd extension for z < 0.  Two transcendental and about ten plain instructions,
-// far below the error of the bf16 rounding that follows.
+// GELU(y) = y/2 (1 + erf(y/sqrt 2)) = y/2 erfc(|y|/sqrt 2) for y < 0, y/2 (2 - erfc(y/sqrt 2)) for
+// y >= 0.  erfc from the Chebyshev fit of W. H. Press et al., Numerical Recipes, section 6.2
+// (function erfcc): erfc(z) = t exp(-z^2 - 1.26551223 + t (1.00002368 + ... + 0.17087277 t^8)),
+// t = 1/(1 + z/2), with fractional error below 1.2e-7 for every z >= 0 -- also in the tail, where
+// a form built on 1 - erf would lose the small values that a static E4M3 scale can still resolve.
+// The exponent is evaluated in log2 units (coefficients times log2 e) for exp2.
 QVD_DEV float gelu_erf(float y) {
     const float z = fabsf(y) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-    float p = fmaf(1.061405429f, t, -1.453152027f);
-    p = fmaf(p, t, 1.421413741f);
-    p = fmaf(p, t, -0.284496736f);
-    p = fmaf(p, t, 0.254829592f);
-    p *= t;
-    const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
-    const float erf_abs = fmaf(-p, e, 1.0f);
-    return 0.5f * y * (1.0f + __builtin_copysignf(erf_abs, y));
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+    float p = fmaf(0.2465173f, t, -1.1861149f);
+    p = fmaf(p, t, 2.1474745f);
+    p = fmaf(p, t, -1.6377531f);
+    p = fmaf(p, t, 0.40232158f);
+    p = fmaf(p, t, -0.26875687f);
+    p = fmaf(p, t, 0.13963005f);
+    p = fmaf(p, t, 0.5397006f);
+    p = fmaf(p, t, 1.4427292f);
+    p = fmaf(p, t, -1.8257482f);
+    const float arg = fmaf(-(z * 1.4426950408889634f), z, p);
+    const float ec = t * __builtin_amdgcn_exp2f(arg);            // erfc(z)
+    return 0.5f * y * (y < 0.0f ? ec : 2.0f - ec);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -184,6 +190,39 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
         if (ep.amax_partials) {
             amax = block_max_nonneg<NWV>(amax, red);
             if (tid == 0) ep.amax_partials[blockIdx.x] = amax;
+        }
+        return;
+    }
+
+    if (EPI == QVD_EPI_GELU_E4M3) {
+        // GELU, bf16 rounding, then E4M3 with the static scale: the standalone static quantizer's
+        // arithmetic (one fp32 product by the correctly rounded 1/s, saturating encode).  LDS: 128
+        // token rows of WN codes, stored as whole 16-byte chunks of the rows.
+        if (!wave_live) return;
+        const float inv_s = __fdiv_rn(1.0f, *ep.out_scale);
+        constexpr int QC = WN / 16;
+#pragma unroll
+        for (int cg = 0; cg < LY::NCG; ++cg) {
+            const int nl = LY::ncol(cg, lane);
+            const float4 b = load_bias4(g.bias, nw0 + nl);
+#pragma unroll
+            for (int r = 0; r < LY::MR; ++r) {
+                const int ml = LY::mrow(r, lane);
+                const v4f c = LY::get(acc, cg, r);
+                const u32 p0 = pack_bf16x2(gelu_erf(c[0] * alpha + b.x), gelu_erf(c[1] * alpha + b.y));
+                const u32 p1 = pack_bf16x2(gelu_erf(c[2] * alpha + b.z), gelu_erf(c[3] * alpha + b.w));
+                const u32 q = e4m3_encode2(bf16lo(p0) * inv_s, bf16hi(p0) * inv_s) |
+                              (e4m3_encode2(bf16lo(p1) * inv_s, bf16hi(p1) * inv_s) << 16);
+                *reinterpret_cast<u32*>(stage + ml * WN + (((nl >> 4) ^ (ml & (QC - 1))) << 4) + (nl & 15)) = q;
+            }
+        }
+        lds_wait();
+#pragma unroll
+        for (int it = 0; it < 2 * QC; ++it) {
+            const int idx = 64 * it + lane, ml = idx / QC, c = idx % QC;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * WN + ((c ^ (ml & (QC - 1))) << 4));
+            const int m = mw0 + ml;
+            if (m < M) *reinterpret_cast<u32x4*>(ep.out_e4m3 + (int64_t)m * N + nw0 + 16 * c) = v;
         }
         return;
     }
@@ -646,6 +685,7 @@ static int launch_epi(const GemmArgs& g, hipStream_t st) {
         case QVD_EPI_RESID_GATE: hipLaunchKernelGGL(KERN<QVD_EPI_RESID_GATE>::fn, grid, blk, 0, st, g); break;
         case QVD_EPI_GELU: hipLaunchKernelGGL(KERN<QVD_EPI_GELU>::fn, grid, blk, 0, st, g); break;
         case QVD_EPI_QKV: hipLaunchKernelGGL(KERN<QVD_EPI_QKV>::fn, grid, blk, 0, st, g); break;
+        case QVD_EPI_GELU_E4M3: hipLaunchKernelGGL(KERN<QVD_EPI_GELU_E4M3>::fn, grid, blk, 0, st, g); break;
         default: return fail(QVD_EINVAL, "gemm: epilogue mode %d", g.epi.mode);
     }
     return launch_status("gemm");
@@ -670,10 +710,10 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
     g.tiles_m = (M + BM - 1) / BM;
     g.tiles_n = (N + BN - 1) / BN;
     g.epi = epi;
-    static const char* epi_name[] = {"f32", "bf16", "resid_gate", "gelu", "qkv"};
+    static const char* epi_name[] = {"f32", "bf16", "resid_gate", "gelu", "qkv", "gelu_e4m3"};
     char key[96];
     snprintf(key, sizeof(key), "gemm_%s_%s_%dx%dx%d", w_fmt == QVD_W_MXFP4 ? "mxfp4" : "fp8",
-             (epi.mode >= 0 && epi.mode < 5) ? epi_name[epi.mode] : "?", M, N, K);
+             (epi.mode >= 0 && epi.mode < 6) ? epi_name[epi.mode] : "?", M, N, K);
     TimingScope ts(key, st);
     return w_fmt == QVD_W_MXFP4 ? launch_epi<KMX>(g, st) : launch_epi<KF8>(g, st);
 }
@@ -705,6 +745,10 @@ static int validate_gemm(const char* fn, const uint8_t* a, const float* s_a, con
             QVD_REQUIRE(epi->out_bf16 && epi->resid && epi->gate, QVD_EINVAL, "%s: out/resid/gate NULL", fn);
             QVD_REQUIRE(aligned16(epi->out_bf16) && aligned16(epi->resid) && aligned16(epi->gate),
                         QVD_EALIGN, "%s: out/resid/gate not 16-byte aligned", fn);
+            break;
+        case QVD_EPI_GELU_E4M3:
+            QVD_REQUIRE(epi->out_e4m3 && aligned16(epi->out_e4m3) && epi->out_scale, QVD_EINVAL,
+                        "%s: out_e4m3 NULL/misaligned or out_scale NULL", fn);
             break;
         case QVD_EPI_QKV:
             QVD_REQUIRE(epi->n_heads >= 1 && N == 3 * 128 * epi->n_heads, QVD_ESHAPE,

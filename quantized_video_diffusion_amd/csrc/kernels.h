@@ -28,6 +28,11 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
 int launch_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                           const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt,
                           int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st);
+// the same attention writing the E4M3 codes of bf16 O under the static scale *out_scale
+int launch_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
+                               const float* k_scale, const uint16_t* vt, int L, int H,
+                               const int32_t* kv_idx, const int32_t* kv_cnt, int kmax, float sm_scale,
+                               const float* out_scale, uint8_t* out_q, hipStream_t st);
 size_t vt_bytes(int L, int H);
 
 }  // namespace qvd

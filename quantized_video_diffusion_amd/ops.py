@@ -129,6 +129,20 @@ def sparse_attn(q8, q_scale, k8, k_scale, v, kv_idx, kv_cnt, sm_scale: float = S
     return (out, part) if want_amax else out
 
 
+def sparse_attn_vt_e4m3(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, out_scale,
+                        sm_scale: float = SM_SCALE):
+    """As sparse_attn_vt, returning the E4M3 codes of bf16 O under the static scale out_scale
+    (a device fp32 [1] tensor) instead of O: uint8 [L][H][128]."""
+    L, H, D = q8.shape
+    _check(vt, torch.float16, "vt")
+    _check(out_scale, torch.float32, "out_scale")
+    out = torch.empty((L, H, D), dtype=torch.uint8, device=q8.device)
+    call("qvd_sparse_attn_vt_e4m3", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt), L, H,
+         _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(out_scale), _ptr(out),
+         _stream())
+    return out
+
+
 def sparse_attn_vt(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, sm_scale: float = SM_SCALE,
                    want_amax: bool = False):
     """As sparse_attn, with V given as fp16 V^T [H][128][ceil(L/128)*128]."""
@@ -154,26 +168,26 @@ def gemm_tiles(M: int, N: int) -> int:
 
 
 def gemm_fp8(a, s_a, w, s_w, bias=None, mode: int = _lib.QVD_EPI_F32, out=None, resid=None,
-             gate=None, amax_partials=None, n_heads: int = 0):
+             gate=None, amax_partials=None, n_heads: int = 0, out_scale=None):
     """E4M3 a [M][K] x E4M3 w [N][K] with the per-tensor scales fused in the epilogue.
 
     mode F32/BF16/GELU: returns the output tensor; RESID_GATE: writes ``out`` (may be ``resid``);
     QKV: returns (q8, k8, v, q_scale, k_scale)."""
     _check(w, torch.uint8, "w")
     return _gemm("qvd_gemm_fp8", a, s_a, w, s_w, w.shape[0], bias, mode, out, resid, gate,
-                 amax_partials, n_heads)
+                 amax_partials, n_heads, out_scale)
 
 
 def gemm_mxfp4(a, s_a, w_packed, e8m0, bias=None, mode: int = _lib.QVD_EPI_F32, out=None,
-               resid=None, gate=None, amax_partials=None, n_heads: int = 0):
+               resid=None, gate=None, amax_partials=None, n_heads: int = 0, out_scale=None):
     """E4M3 a [M][K] (scale s_a) x MXFP4 weights (packed E2M1 [N][K/2] + E8M0 [N][K/32])."""
     _check(w_packed, torch.uint8, "w_packed")
     _check(e8m0, torch.uint8, "e8m0")
     return _gemm("qvd_gemm_mxfp4", a, s_a, w_packed, e8m0, w_packed.shape[0], bias, mode, out, resid,
-                 gate, amax_partials, n_heads)
+                 gate, amax_partials, n_heads, out_scale)
 
 
-def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, n_heads):
+def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, n_heads, out_scale=None):
     M, K = a.shape
     _check(a, torch.uint8, "a")
     e = Epilogue()
@@ -188,6 +202,13 @@ def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, 
         e.out_bf16 = out.data_ptr()
         if amax_partials is not None:
             e.amax_partials = amax_partials.data_ptr()
+        ret = out
+    elif mode == _lib.QVD_EPI_GELU_E4M3:
+        out = torch.empty((M, N), dtype=torch.uint8, device=a.device) if out is None else out
+        _check(out, torch.uint8, "out")
+        _check(out_scale, torch.float32, "out_scale")
+        e.out_e4m3 = out.data_ptr()
+        e.out_scale = out_scale.data_ptr()
         ret = out
     elif mode == _lib.QVD_EPI_RESID_GATE:
         e.out_bf16 = out.data_ptr()

@@ -70,6 +70,52 @@ def test_gemm_gelu_epilogue_and_amax_partials():
     assert float(host(parts).max()) == float(np.abs(bf16_f64(g)).max())
 
 
+@pytest.mark.parametrize("fmt,M,N,K", [("fp8", 333, 1024, 256), ("mxfp4", 391, 768, 512)])
+def test_gemm_gelu_e4m3_epilogue_static_scale(fmt, M, N, K):
+    """GELU -> bf16 -> E4M3 under a static scale, in the epilogue: within the admissible range of the
+    oracle's static quantization of bf16(GELU(y)) (below), mostly equal to it, and bit for bit the
+    standalone static quantizer applied to the same kernel's bf16 GELU output.  Two scales: one that
+    covers the tensor and one that saturates about half of it at 448."""
+    say("gemm gelu e4m3", fmt, M, N, K)
+    a = _codes(M, K, 8)
+    if fmt == "fp8":
+        w = _codes(N, K, 9, "codes_b")
+        sa, sw = np.float32(0.002), np.float32(0.003)
+        y = OG.gemm_fp8(a, sa, w, sw)
+        run = lambda **kw: Q.gemm_fp8(u8_dev(a), f32_dev([sa]), u8_dev(w), f32_dev([sw]), **kw)
+    else:
+        wb = W.normal_bf16((N, K), seed=N + K, scale=0.03)
+        pw, ew = OQ.quant_mxfp4_weight(wb)
+        sa = np.float32(0.05)
+        y = OG.gemm_mxfp4(a, sa, pw, ew)
+        run = lambda **kw: Q.gemm_mxfp4(u8_dev(a), f32_dev([sa]), u8_dev(pw), u8_dev(ew), **kw)
+    g = OG.gelu(y)
+    gb = OC.f64_to_bf16_value(g).astype(np.float32)
+    gbits = run(mode=_lib.QVD_EPI_GELU)
+    for f in (1.25, 0.02):
+        s = np.float32(float(np.abs(gb).max()) / 448.0 * f)
+        want, _ = OQ.quant_fp8_per_tensor(gb, scale_in=s)
+        got = host(run(mode=_lib.QVD_EPI_GELU_E4M3, out_scale=f32_dev([s])))
+        inv = np.float32(1.0) / s
+        # The codes are those of bf16(GELU(y')) for the GPU's fp32 y', which differs from the exact
+        # y by the GEMM's accumulation error.  Bound it by 2.5e-4 RMS(y) (4x inside the 1e-3 RMS GEMM
+        # bar); GELU's slope is below 1.13.  bf16 rounding and the encoder are monotone, so every
+        # admissible code lies between the codes of bf16(g - e) and bf16(g + e).  Most codes are
+        # the oracle's own (at most 1% differ: under a static scale many outputs fall on the fine
+        # small codes, where that error spans a code or more; 0.27% measured at the FP8 shape).
+        e = 2.5e-4 * 1.13 * float(np.sqrt(np.mean(y ** 2)))
+        lo, _ = OQ.quant_fp8_per_tensor(OC.f64_to_bf16_value(g - e).astype(np.float32), scale_in=s)
+        hi, _ = OQ.quant_fp8_per_tensor(OC.f64_to_bf16_value(g + e).astype(np.float32), scale_in=s)
+        vg, vlo, vhi = (OC.e4m3_decode(c.reshape(-1)) for c in (got, lo, hi))
+        out = np.nonzero((vg < vlo) | (vg > vhi))[0]
+        assert out.size == 0, (f"gelu e4m3 {fmt} x{f}: {out.size} codes outside the admissible range, "
+                               f"e.g. {out[:4].tolist()} got {vg[out[:4]].tolist()} range "
+                               f"{vlo[out[:4]].tolist()}..{vhi[out[:4]].tolist()}")
+        assert np.mean(got.reshape(-1) != want.reshape(-1)) <= 1e-2
+        two_pass, _ = Q.quant_fp8_per_tensor(gbits, scale_in=f32_dev([s]))
+        np.testing.assert_array_equal(got, host(two_pass))
+
+
 def _realistic_codes(M, N, K, seed):
     """Activation codes of N(0,1) data and weight codes of Glorot-uniform weights, both through the
     oracle's per-tensor quantizer (so the accumulators have a realistic dynamic range)."""
@@ -218,6 +264,32 @@ def test_sparse_attn_peaked_rows_large_logit_gap():
     want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx, cnt)
     assert np.isfinite(bf16_f64(out)).all()
     assert_bf16_close(host_bits(out), want, 1e-2, "peaked rows")
+
+
+def test_sparse_attn_e4m3_output_static_scale():
+    """The E4M3 entry equals, bit for bit, the standalone static quantizer applied to the bf16
+    entry's output, and its dequantized codes stay within E4M3 rounding (2^-4 relative) plus 1e-2 RMS
+    of the oracle attention; a second, small scale saturates part of the output."""
+    L, H = 1290, 2
+    qb, kb, vb, idx, cnt = _attn_inputs(L, H, 13, True)
+    (q8, qs, k8, ks), (oq, oqs, ok, oks) = _quantize_both(qb, kb, L, H)
+    T = (L + 127) // 128
+    vt = np.zeros((H, 128, T * 128), np.float16)
+    vt[:, :, :L] = OC.bf16_to_f64(vb).transpose(1, 2, 0).astype(np.float16)
+    vt_d = torch.from_numpy(vt).cuda()
+    out = Q.sparse_attn_vt(q8, qs, k8, ks, vt_d, i32_dev(idx), i32_dev(cnt))
+    want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx, cnt)
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    for f in (1.1, 0.1):
+        s = np.float32(float(np.abs(want).max()) / 448.0 * f)
+        got = Q.sparse_attn_vt_e4m3(q8, qs, k8, ks, vt_d, i32_dev(idx), i32_dev(cnt), f32_dev([s]))
+        two_pass, _ = Q.quant_fp8_per_tensor(out, scale_in=f32_dev([s]))
+        np.testing.assert_array_equal(host(got), host(two_pass))
+        deq = OC.e4m3_decode(host(got).reshape(-1)) * float(s)
+        ref = np.clip(want.reshape(-1), -448.0 * float(s), 448.0 * float(s))
+        err = np.abs(deq - ref)
+        assert (err <= 2.0 ** -4 * np.abs(ref) + 1e-2 * rms + 2.0 ** -9 * float(s)).all(), \
+            f"attn e4m3 x{f}: worst {float(err.max()):.3e} (RMS {rms:.3e})"
 
 
 def test_sparse_attn_vt_entry_matches_bf16_entry():
