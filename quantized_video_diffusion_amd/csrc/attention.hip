@@ -126,7 +126,11 @@ QVD_DEV void stage_vt(uint16_t* vbuf, const uint16_t* __restrict__ vt, int Lp, i
         const int blk = 8 * wv + u;
         const int d = blk * 4 + (lane >> 4);
         const int c = (lane & 15) ^ (d & 15);
-        const uint32_t off = ((uint32_t)(h * 128 + d) * (uint32_t)Lp + (uint32_t)(8 * c)) * 2u;
+        uint32_t off = ((uint32_t)(h * 128 + d) * (uint32_t)Lp + (uint32_t)(8 * c)) * 2u;
+        // a 32-bit lane offset from a wave-uniform base: the scalar-base form of the DMA, with no
+        // 64-bit address arithmetic per instruction (the empty asm keeps the compiler from hoisting
+        // 64-bit copies of the offsets out of the tile loop)
+        asm volatile("" : "+v"(off));
         dma16(base + off, vbuf + blk * 512);
     }
 }
@@ -345,7 +349,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     // each LDS read
     __shared__ __attribute__((aligned(16))) AttnSmem sm;
     const int T = (L + 127) >> 7, total = T * H;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = wv >> 2, wg = wv & 3;
     const int fr = lane & 15, fg = lane >> 4;
 
@@ -417,8 +421,11 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     if (g == 1) lds_barrier();                   // group 1: B_-1 (its phase 0 is idle)
     dma_barrier();                                // group 0: B_-1; group 1: B_0
     int passed = 1 + g;                           // barriers passed
+    // j is made wave-uniform so that the K scale comes through the scalar cache (counted by lgkmcnt,
+    // which the phase barrier waits for): as a vector load it would make the VALU phase wait for
+    // vmcnt, i.e. for the V^T DMA just issued.
     if (n > 0) {
-        j = gs.tiles[0];
+        j = __builtin_amdgcn_readfirstlane(gs.tiles[0]);
         ksc = k_scale[h * T + j];
         mfma_qk(0);
         lds_barrier();
@@ -427,7 +434,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
             valu_phase();
             dma_barrier();
             if (t + 1 < n) {
-                j = gs.tiles[t + 1];
+                j = __builtin_amdgcn_readfirstlane(gs.tiles[t + 1]);
                 ksc = k_scale[h * T + j];
             }
             pv_tile(gs.vt, pb, fr, fg, o, lacc);
