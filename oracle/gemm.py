@@ -56,6 +56,20 @@ def gemm_mxfp4(a_codes, s_a, w_packed, w_e8, bias=None) -> np.ndarray:
     return y
 
 
+def gemm_mxfp4_w4a4(a_packed, a_e8, w_packed, w_e8, bias=None) -> np.ndarray:
+    """Both operands MXFP4 (E2M1 elements, an E8M0 scale per 32 consecutive K; the activations
+    quantized per token row exactly as the weights are per output row): y = sum_k dec(a) dec(w) + b,
+    float64 [M][N].  [farwalk] post 6/8 runs the transformer's linear layers in 4 bits on both
+    operands (NVFP4 on Blackwell); OCP MX v1.0 fixes the block format used here instead.  No
+    per-tensor factor: the block scales carry the magnitudes.  Each product is a multiple of
+    2^(e_a + e_w - 256) below 36 * 2^(e_a + e_w - 254), so the float64 sum is exact while the block
+    exponents of a row pair span fewer than about 45 binades, as they do for every input drawn here."""
+    y = dequant_mxfp4(a_packed, a_e8) @ dequant_mxfp4(w_packed, w_e8).T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    return y
+
+
 def gelu(u) -> np.ndarray:
     """Exact (erf) GELU: u * (1 + erf(u / sqrt 2)) / 2 in float64 (scipy's erf as the library
     primitive).  Reading: the workloads name a GELU MLP; the erf form is taken, not tanh."""

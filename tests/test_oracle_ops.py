@@ -115,6 +115,50 @@ def test_mxfp4_weight_quant_and_gemm():
     assert (packed[0, 0] & 0xF) == codes.reshape(6, 96)[0, 0]
 
 
+def _frac_mx(packed, e8):
+    """Exact rationals of MXFP4 data, element by element from the pinned codecs."""
+    codes = Q.unpack_e2m1(packed)
+    vals = C.e2m1_decode(codes)
+    X = C.e8m0_decode(e8)
+    R, K = codes.shape
+    return [[Fraction(float(vals[r, k])) * Fraction(float(X[r, k // 32])) for k in range(K)] for r in range(R)]
+
+
+def test_mxfp4_w4a4_gemm_exact_vs_rational_brute_force():
+    a = W.normal_bf16((3, 96), seed=21, scale=1.0)
+    w = W.normal_bf16((5, 96), seed=22, scale=0.05)
+    ap, ae = Q.quant_mxfp4_weight(a)
+    wp, we = Q.quant_mxfp4_weight(w)
+    y = G.gemm_mxfp4_w4a4(ap, ae, wp, we)
+    A_, W_ = _frac_mx(ap, ae), _frac_mx(wp, we)
+    for m in range(3):
+        for n in range(5):
+            assert Fraction(float(y[m, n])) == sum(A_[m][k] * W_[n][k] for k in range(96))
+    b = np.linspace(-1, 1, 5).astype(np.float32)
+    np.testing.assert_array_equal(G.gemm_mxfp4_w4a4(ap, ae, wp, we, bias=b), y + b.astype(np.float64)[None, :])
+
+
+def test_mxfp4_w4a4_block_alignment_and_scale_linearity():
+    a = W.normal_bf16((4, 128), seed=23, scale=1.0)
+    w = W.normal_bf16((6, 128), seed=24, scale=0.05)
+    ap, ae = Q.quant_mxfp4_weight(a)
+    wp, we = Q.quant_mxfp4_weight(w)
+    y = G.gemm_mxfp4_w4a4(ap, ae, wp, we)
+    # activations with only 32-block 2 nonzero: the product of that block alone
+    only = ap.copy()
+    only[:, :32] = 0
+    only[:, 48:] = 0
+    Wd = G.dequant_mxfp4(wp, we)
+    Ad = G.dequant_mxfp4(ap, ae)
+    np.testing.assert_array_equal(G.gemm_mxfp4_w4a4(only, ae, wp, we), Ad[:, 64:96] @ Wd[:, 64:96].T)
+    # one more E8M0 step on every block of row 1 doubles row 1 exactly and leaves the others
+    ae2 = ae.copy()
+    ae2[1] += 1
+    y2 = G.gemm_mxfp4_w4a4(ap, ae2, wp, we)
+    np.testing.assert_array_equal(y2[1], 2 * y[1])
+    np.testing.assert_array_equal(np.delete(y2, 1, 0), np.delete(y, 1, 0))
+
+
 def test_gelu_vs_math_erf():
     u = np.linspace(-12, 12, 2001)
     ref = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in u])
