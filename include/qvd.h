@@ -226,6 +226,16 @@ int qvd_gemm_fp8(const uint8_t* a, const float* s_a, const uint8_t* w, const flo
 int qvd_gemm_mxfp4(const uint8_t* a, const float* s_a, const uint8_t* w_packed,
                    const uint8_t* e8m0, const float* bias, int32_t M, int32_t N, int32_t K,
                    const qvd_epilogue* epi, void* stream);
+/* Both operands 4-bit (W4A4; the same story's NVFP4 transformer, in OCP MX form): activations
+ * quantized per 32 consecutive K exactly as qvd_quant_mxfp4 quantizes weights, then
+ *   acc[m][n] = sum_k E2M1(a[m][k]) 2^(a_e8m0[m][k/32] - 127) * E2M1(w[n][k]) 2^(w_e8m0[n][k/32] - 127)
+ *   y[m][n]   = acc + bias[n]              (no per-tensor factor; every epilogue mode applies)
+ * a_packed: uint8 [M][K/2], a_e8m0: uint8 [M][K/32]; w_packed, w_e8m0 as in qvd_gemm_mxfp4 (element
+ * 2j in the low nibble of byte j).  Packed operands 16-byte aligned, scale arrays 4-byte aligned.
+ * Accumulation is fp32 in the matrix cores' own order.  Shapes and errors as qvd_gemm_fp8. */
+int qvd_gemm_mxfp4_w4a4(const uint8_t* a_packed, const uint8_t* a_e8m0, const uint8_t* w_packed,
+                        const uint8_t* w_e8m0, const float* bias, int32_t M, int32_t N, int32_t K,
+                        const qvd_epilogue* epi, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * One DiT block forward -- the reading of the block (pre-norm adaLN-Zero DiT block):
@@ -278,7 +288,7 @@ int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* coun
  * bracketed by a pair of HIP events recorded on the launch's own stream.  qvd_timing_report waits
  * for the recorded work, writes {"<kernel key>": {"count": n, "total_ms": t}, ...} (NUL-terminated
  * JSON) into buf and clears the records.  Keys: "sparse_attn", "adaln_modulate", "adaln_project",
- * "quant_fp8", "amax_bf16", "quant_int8_qk", "gemm_<fp8|mxfp4>_<epilogue>_<M>x<N>x<K>".
+ * "quant_fp8", "amax_bf16", "quant_int8_qk", "gemm_<fp8|mxfp4|w4a4>_<epilogue>_<M>x<N>x<K>".
  * Returns QVD_EINVAL if len is too small (the records are then lost), QVD_EHIP on event errors. */
 int qvd_timing_enable(int on);
 int qvd_timing_report(char* buf, size_t len);

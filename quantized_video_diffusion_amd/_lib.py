@@ -68,6 +68,7 @@ SIGNATURES = {
     "qvd_gemm_tiles": (_i64, [_i32, _i32]),
     "qvd_gemm_fp8": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(Epilogue), _p]),
     "qvd_gemm_mxfp4": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(Epilogue), _p]),
+    "qvd_gemm_mxfp4_w4a4": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(Epilogue), _p]),
     "qvd_block_ws_bytes": (_sz, [C.POINTER(BlockParams), _i32]),
     "dit_block_forward": (C.c_int, [C.POINTER(BlockParams), _p, _p, _i32, _p, _p, _i32, _p, _sz, _p]),
     "qvd_quant_mxfp4": (C.c_int, [_p, _i32, _i32, _p, _p, _p]),

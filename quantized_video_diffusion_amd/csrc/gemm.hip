@@ -30,6 +30,7 @@ struct GemmArgs {
     const uint8_t* a;
     const uint8_t* w;
     const uint8_t* e8;
+    const uint8_t* a_e8;     // E8M0 scales of MXFP4 activations (W4A4), else NULL
     const float* s_a;
     const float* s_w;
     const float* bias;
@@ -676,6 +677,157 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
     gemm_epilogue<EPI, Layout32N64, 64, NWAVE8>(g, acc, *g.s_a, m0, n0, wm, wn, red, smem + wv * 16384);
 }
 
+// ================================================================================================
+// MXFP4 activations x MXFP4 weights (W4A4): v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1
+// (cbsz = blgp = 4), each lane supplying the E8M0 scale of its row's 32-element block for both.
+// Measured on gfx950 with one-hot and all-ones operands: lane half h of either E2M1 operand holds
+// k = 32h .. 32h+31 of its row in order, and lane l's scale byte applies to row l%32, block l/32.
+// Tiles, waves, 128-K stages and the branch-free step schedule are those of k_gemm_mx.  Stage
+// (34 KB): A and W rows of 64 bytes (chunk c of row r at c ^ ((r>>2)&3)), then the 4 E8M0 bytes of
+// each A row and of each W row.
+constexpr int W4A4_W_OFF = BM * BKS / 2;
+constexpr int W4A4_AE_OFF = W4A4_W_OFF + BN * BKS / 2;
+constexpr int W4A4_WE_OFF = W4A4_AE_OFF + BM * 4;
+constexpr int STAGE_W4A4 = W4A4_WE_OFF + BN * 4;
+constexpr int SMEM_W4A4 = 2 * STAGE_W4A4 > NWAVE8 * 16384 ? 2 * STAGE_W4A4 : NWAVE8 * 16384;
+
+// DMA instruction u of wave w's share of a stage: 0..1 A row blocks 2w+u, 2..3 W row blocks 2w+u-2
+// (16 rows of 64 bytes each), 4 the E8M0 words of 64 rows: A rows 64w .. (waves 0..3) or W rows
+// 64(w-4) .. (waves 4..7), 4 bytes per lane.
+QVD_DEV void dma_w4a4(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
+                      const uint32_t* w_off, const uint8_t* e_src, uint32_t e_off, uint32_t e_dst, int u) {
+    uint8_t* st = smem + buf * STAGE_W4A4;
+    if (u < 2)
+        __builtin_amdgcn_global_load_lds(g.a + a_off[u] + k0 / 2, (lds_void*)(st + (2 * wv + u) * 1024), 16, 0, 0);
+    else if (u < 4)
+        __builtin_amdgcn_global_load_lds(g.w + w_off[u - 2] + k0 / 2,
+                                         (lds_void*)(st + W4A4_W_OFF + (2 * wv + u - 2) * 1024), 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(e_src + e_off + k0 / 32, (lds_void*)(st + e_dst), 4, 0, 0);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_W4A4 + 4 * NWAVE8];
+    float* red = reinterpret_cast<float*>(smem + SMEM_W4A4);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv & 1, wn = wv >> 1;
+    int tm, tn;
+    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+
+    // DMA sources.  A and W instruction u: lane l lands in row r = (2w+u)*16 + l/4, slot l%4, and
+    // fetches chunk (l%4) ^ ((r>>2)&3) of the row's 64 stage bytes.  E8M0: lane l brings row
+    // 64(w%4) + l of A (w < 4) or W.  Rows past M (N) repeat the last row; their results are never
+    // stored.
+    uint32_t a_off[2], w_off[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r = (2 * wv + u) * 16 + (lane >> 2);
+        const uint32_t c = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+        const int ra = m0 + r < M ? m0 + r : M - 1;
+        const int rw = n0 + r < N ? n0 + r : N - 1;
+        a_off[u] = (uint32_t)ra * (uint32_t)(K / 2) + 16u * c;
+        w_off[u] = (uint32_t)rw * (uint32_t)(K / 2) + 16u * c;
+    }
+    const bool e_of_a = wv < 4;
+    const uint8_t* e_src = e_of_a ? g.a_e8 : g.e8;
+    uint32_t e_off;
+    {
+        const int r = 64 * (wv & 3) + lane;
+        const int lim = e_of_a ? M : N;
+        const int base = e_of_a ? m0 : n0;
+        const int row = base + r < lim ? base + r : lim - 1;
+        e_off = (uint32_t)row * (uint32_t)(K / 32);
+    }
+    const uint32_t e_dst = (uint32_t)((e_of_a ? W4A4_AE_OFF : W4A4_WE_OFF) + 256 * (wv & 3));
+
+    // fragment offsets per K step j: row l%32 of a 32-row block, logical chunk 2j + h (lane half h)
+    const int lr = lane & 31, hl = lane >> 5;
+    const uint32_t sw4 = (uint32_t)((lr >> 2) & 3), r64 = (uint32_t)lr * 64u;
+    const uint32_t fo0 = r64 + 16u * ((uint32_t)hl ^ sw4), fo1 = r64 + 16u * ((2u + hl) ^ sw4);
+    const int a_blk = 4 * wm, w_blk = 2 * wn;
+    const uint32_t* ae_row = reinterpret_cast<const uint32_t*>(smem + W4A4_AE_OFF) + 32 * a_blk + lr;
+    const uint32_t* we_row = reinterpret_cast<const uint32_t*>(smem + W4A4_WE_OFF) + 32 * w_blk + lr;
+
+    Layout32N64::Acc acc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int S = K / BKS;
+#pragma unroll
+    for (int u = 0; u < 5; ++u) dma_w4a4(g, smem, 0, 0, wv, a_off, w_off, e_src, e_off, e_dst, u);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < 5; ++u) dma_w4a4(g, smem, 1, S > 1 ? BKS : 0, wv, a_off, w_off, e_src, e_off, e_dst, u);
+
+    v8i fw[2][2], fa[2][4];
+    uint32_t scw[2], sca[4], scw_n[2], sca_n[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fw[0][i] = frag_e2m1(smem + W4A4_W_OFF, w_blk + i, fo0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = frag_e2m1(smem, a_blk + i, fo0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) scw[i] = we_row[32 * i] >> (8 * hl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sca[i] = ae_row[32 * i] >> (8 * hl);
+
+    // the step schedule of k_gemm_mx: step 0 of a stage uses blocks h (byte h of the shifted words),
+    // step 1 blocks 2 + h (byte 2); the words of stage s+1 are read at the start of step 1 of stage s
+    auto kstep = [&](auto H, auto REFILL, int s) {
+        constexpr int h = decltype(H)::value;
+        constexpr bool refill = decltype(REFILL)::value == 1;
+        if (h == 1) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int nbuf = (h == 0 ? s : s + 1) & 1;
+        const uint8_t* As = smem + nbuf * STAGE_W4A4;
+        const uint8_t* Ws = As + W4A4_W_OFF;
+        const uint32_t fo = h == 0 ? fo1 : fo0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int swv = (int)(h == 0 ? scw[q >> 2] : scw[q >> 2] >> 16);
+            const int sav = (int)(h == 0 ? sca[q & 3] : sca[q & 3] >> 16);
+            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fw[h][q >> 2], fa[h][q & 3], acc[q >> 2][q & 3], 4, 4, 0, swv, 0, sav);
+            if (h == 1 && refill && q < 5)
+                dma_w4a4(g, smem, s & 1, (s + 2) * BKS, wv, a_off, w_off, e_src, e_off, e_dst, q);
+            if (h == 1 && q == 0) {   // raw words: shifting here would wait for the reads in flight
+#pragma unroll
+                for (int i = 0; i < 2; ++i) scw_n[i] = we_row[nbuf * (STAGE_W4A4 / 4) + 32 * i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sca_n[i] = ae_row[nbuf * (STAGE_W4A4 / 4) + 32 * i];
+            }
+            if (q < 2)
+                fw[h ^ 1][q] = frag_e2m1(Ws, w_blk + q, fo);
+            else if (q < 6)
+                fa[h ^ 1][q - 2] = frag_e2m1(As, a_blk + q - 2, fo);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (h == 1) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) scw[i] = scw_n[i] >> (8 * hl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sca[i] = sca_n[i] >> (8 * hl);
+        }
+    };
+    int s = 0;
+    for (; s < S - 2; ++s) {
+        kstep(IC<0>{}, IC<0>{}, s);
+        kstep(IC<1>{}, IC<1>{}, s);
+    }
+    for (; s < S; ++s) {
+        kstep(IC<0>{}, IC<0>{}, s);
+        kstep(IC<1>{}, IC<0>{}, s);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages are free
+    gemm_epilogue<EPI, Layout32N64, 64, NWAVE8>(g, acc, 1.0f, m0, n0, wm, wn, red, smem + wv * 16384);
+}
+
 template <template <int> class KERN>
 static int launch_epi(const GemmArgs& g, hipStream_t st) {
     const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), blk(KERN<QVD_EPI_F32>::threads);
@@ -692,6 +844,7 @@ static int launch_epi(const GemmArgs& g, hipStream_t st) {
 }
 template <int EPI> struct KF8 { static constexpr auto fn = k_gemm_f8<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
 template <int EPI> struct KMX { static constexpr auto fn = k_gemm_mx<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
+template <int EPI> struct KW4A4 { static constexpr auto fn = k_gemm_w4a4<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
 
 int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t* e8, const float* s_w,
                 int w_fmt, const float* bias, int M, int N, int K, const qvd_epilogue& epi,
@@ -701,6 +854,7 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
     g.a = a;
     g.w = (const uint8_t*)w;
     g.e8 = e8;
+    g.a_e8 = nullptr;
     g.s_a = s_a;
     g.s_w = s_w;
     g.bias = bias;
@@ -718,11 +872,36 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
     return w_fmt == QVD_W_MXFP4 ? launch_epi<KMX>(g, st) : launch_epi<KF8>(g, st);
 }
 
+int launch_gemm_w4a4(const uint8_t* a, const uint8_t* a_e8, const uint8_t* w, const uint8_t* w_e8,
+                     const float* bias, int M, int N, int K, const qvd_epilogue& epi, hipStream_t st) {
+    if (M == 0) return QVD_OK;
+    GemmArgs g;
+    g.a = a;
+    g.w = w;
+    g.e8 = w_e8;
+    g.a_e8 = a_e8;
+    g.s_a = nullptr;
+    g.s_w = nullptr;
+    g.bias = bias;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.tiles_m = (M + BM - 1) / BM;
+    g.tiles_n = (N + BN - 1) / BN;
+    g.epi = epi;
+    static const char* epi_name[] = {"f32", "bf16", "resid_gate", "gelu", "qkv", "gelu_e4m3"};
+    char key[96];
+    snprintf(key, sizeof(key), "gemm_w4a4_%s_%dx%dx%d",
+             (epi.mode >= 0 && epi.mode < 6) ? epi_name[epi.mode] : "?", M, N, K);
+    TimingScope ts(key, st);
+    return launch_epi<KW4A4>(g, st);
+}
+
 }  // namespace qvd
 
 using namespace qvd;
 
-static int validate_gemm(const char* fn, const uint8_t* a, const float* s_a, const void* w,
+static int validate_gemm(const char* fn, const uint8_t* a, const void* s_a, const void* w,
                          const float* bias, int32_t M, int32_t N, int32_t K, const qvd_epilogue* epi) {
     QVD_REQUIRE(epi != nullptr, QVD_EINVAL, "%s: epi is NULL", fn);
     QVD_REQUIRE(M >= 0 && N >= 128 && N % 128 == 0 && K >= 128 && K % 128 == 0, QVD_ESHAPE,
@@ -730,9 +909,15 @@ static int validate_gemm(const char* fn, const uint8_t* a, const float* s_a, con
     QVD_REQUIRE(gemm_tiles(M, N) < (1ll << 31), QVD_ESHAPE, "%s: too many tiles", fn);
     QVD_REQUIRE((double)M * K < 4294967296.0 && (double)N * K < 4294967296.0, QVD_ESHAPE,
                 "%s: operands must stay below 4 GiB (M = %d, N = %d, K = %d)", fn, M, N, K);
-    QVD_REQUIRE(s_a != nullptr && w != nullptr, QVD_EINVAL, "%s: s_a or w is NULL", fn);
+    QVD_REQUIRE(w != nullptr, QVD_EINVAL, "%s: w is NULL", fn);
     QVD_REQUIRE(aligned16(w) && (!bias || aligned16(bias)), QVD_EALIGN, "%s: w/bias not 16-byte aligned", fn);
-    if (M > 0) QVD_REQUIRE(a && aligned16(a), QVD_EINVAL, "%s: a is NULL or misaligned", fn);
+    if (M > 0) {
+        QVD_REQUIRE(a && aligned16(a), QVD_EINVAL, "%s: a is NULL or misaligned", fn);
+        QVD_REQUIRE(s_a != nullptr, QVD_EINVAL, "%s: activation scale is NULL", fn);
+    }
+    QVD_REQUIRE(epi->mode >= QVD_EPI_F32 && epi->mode <= QVD_EPI_GELU_E4M3, QVD_EINVAL,
+                "%s: unknown epilogue mode %d", fn, epi->mode);
+    if (M == 0) return QVD_OK;   // nothing is read or written
     switch (epi->mode) {
         case QVD_EPI_F32:
             QVD_REQUIRE(epi->out_f32 && aligned16(epi->out_f32), QVD_EINVAL, "%s: out_f32 NULL/misaligned", fn);
@@ -791,6 +976,18 @@ int qvd_gemm_mxfp4(const uint8_t* a, const float* s_a, const uint8_t* w_packed,
     QVD_DEVICE_OK();
     return launch_gemm(a, s_a, w_packed, e8m0, nullptr, QVD_W_MXFP4, bias, M, N, K, *epi,
                        (hipStream_t)stream);
+}
+
+int qvd_gemm_mxfp4_w4a4(const uint8_t* a_packed, const uint8_t* a_e8m0, const uint8_t* w_packed,
+                        const uint8_t* w_e8m0, const float* bias, int32_t M, int32_t N, int32_t K,
+                        const qvd_epilogue* epi, void* stream) {
+    int s = validate_gemm("qvd_gemm_mxfp4_w4a4", a_packed, a_e8m0, w_packed, bias, M, N, K, epi);
+    if (s) return s;
+    QVD_PTR(w_e8m0);
+    QVD_REQUIRE(((uintptr_t)a_e8m0 & 3u) == 0 && ((uintptr_t)w_e8m0 & 3u) == 0, QVD_EALIGN,
+                "qvd_gemm_mxfp4_w4a4: a_e8m0 and w_e8m0 must be 4-byte aligned");
+    QVD_DEVICE_OK();
+    return launch_gemm_w4a4(a_packed, a_e8m0, w_packed, w_e8m0, bias, M, N, K, *epi, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -187,8 +187,22 @@ def gemm_mxfp4(a, s_a, w_packed, e8m0, bias=None, mode: int = _lib.QVD_EPI_F32, 
                  gate, amax_partials, n_heads, out_scale)
 
 
-def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, n_heads, out_scale=None):
+def gemm_mxfp4_w4a4(a_packed, a_e8m0, w_packed, w_e8m0, bias=None, mode: int = _lib.QVD_EPI_F32,
+                    out=None, resid=None, gate=None, amax_partials=None, n_heads: int = 0,
+                    out_scale=None):
+    """MXFP4 activations (packed E2M1 [M][K/2] + E8M0 [M][K/32], as quant_mxfp4 makes them) x
+    MXFP4 weights (packed E2M1 [N][K/2] + E8M0 [N][K/32]); no per-tensor factor."""
+    for t, name in ((a_e8m0, "a_e8m0"), (w_packed, "w_packed"), (w_e8m0, "w_e8m0")):
+        _check(t, torch.uint8, name)
+    return _gemm("qvd_gemm_mxfp4_w4a4", a_packed, a_e8m0, w_packed, w_e8m0, w_packed.shape[0], bias,
+                 mode, out, resid, gate, amax_partials, n_heads, out_scale, packed_a=True)
+
+
+def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, n_heads, out_scale=None,
+          packed_a=False):
     M, K = a.shape
+    if packed_a:
+        K *= 2
     _check(a, torch.uint8, "a")
     e = Epilogue()
     e.mode = mode

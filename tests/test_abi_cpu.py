@@ -102,6 +102,12 @@ def test_host_validation_errors(lib):
     e.n_heads = 2
     assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 10, 512, 128, C.byref(e), None) == _lib.QVD_ESHAPE
     assert lib.qvd_gemm_tiles(33784, 8064) == 132 * 32
+    e.mode = _lib.QVD_EPI_F32
+    e.out_f32 = 0x10000
+    assert _status(lib, "qvd_gemm_mxfp4_w4a4", fake, fake, fake, fake, None, 10, 128, 96, C.byref(e), None) == _lib.QVD_ESHAPE
+    assert _status(lib, "qvd_gemm_mxfp4_w4a4", fake, None, fake, fake, None, 10, 128, 128, C.byref(e), None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_gemm_mxfp4_w4a4", fake, fake, fake, None, None, 10, 128, 128, C.byref(e), None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_gemm_mxfp4_w4a4", fake, P(0x10002), fake, fake, None, 10, 128, 128, C.byref(e), None) == _lib.QVD_EALIGN
     # block
     p = _lib.BlockParams()
     p.version = 99
