@@ -19,7 +19,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codecs import bf16_to_f64, fp16_to_f64, f64_to_f32, f32_to_f64
-from .quant import quant_fp8_per_tensor
+from .quant import quant_fp8_per_tensor, quant_mxfp4
 
 N_MOD = 6
 
@@ -64,3 +64,9 @@ def layernorm_modulate(x_bits, mod_f32, half: int, eps: float) -> np.ndarray:
 def adaln_modulate(x_bits, mod_f32, half: int, eps: float = 1e-6, act_scale=None):
     """-> (E4M3 codes [L][d], per-tensor scale s)."""
     return quant_fp8_per_tensor(layernorm_modulate(x_bits, mod_f32, half, eps), act_scale)
+
+
+def adaln_modulate_mxfp4(x_bits, mod_f32, half: int, eps: float = 1e-6):
+    """-> (packed E2M1 [L][d/2], E8M0 [L][d/32]): the fp32 modulated LayerNorm output quantized per
+    token row and 32 consecutive channels (MXFP4 activations; no per-tensor scale)."""
+    return quant_mxfp4(layernorm_modulate(x_bits, mod_f32, half, eps))

@@ -72,12 +72,20 @@ def quant_int8_qk(x_bits, L: int, H: int, head_dim: int = 128, tile: int = TILE)
 
 
 def quant_mxfp4_weight(w_bits):
-    """bf16 master weight [N][K] -> (packed E2M1 [N][K/2] uint8, E8M0 scales [N][K/32] uint8).
+    """bf16 master weight [N][K] -> (packed E2M1 [N][K/2] uint8, E8M0 scales [N][K/32] uint8):
+    quant_mxfp4 of the bf16 values."""
+    return quant_mxfp4(bf16_to_f64(w_bits))
 
-    Per row and per 32 consecutive K: X = 2^(floor(log2 amax) - 2), element = E2M1(w / X) (RNE,
+
+def quant_mxfp4(x):
+    """Real values [N][K] (the exact values given: fp32 or float64, not rounded further) ->
+    (packed E2M1 [N][K/2] uint8, E8M0 scales [N][K/32] uint8).
+
+    Per row and per 32 consecutive K: X = 2^(floor(log2 amax) - 2), element = E2M1(x / X) (RNE,
     saturating at 6).  Element 2j sits in the low nibble of byte j, element 2j+1 in the high one.
+    The same rule quantizes activations per token row (W4A4: both GEMM operands MXFP4).
     """
-    w = bf16_to_f64(w_bits)
+    w = np.asarray(x, dtype=np.float64)
     N, K = w.shape
     assert K % 32 == 0
     blocks = w.reshape(N, K // 32, 32)

@@ -115,6 +115,41 @@ def test_mxfp4_weight_quant_and_gemm():
     assert (packed[0, 0] & 0xF) == codes.reshape(6, 96)[0, 0]
 
 
+def test_mxfp4_quantizes_the_given_values_not_their_bf16_rounding():
+    """OCP MX rule on exact inputs: a block with amax 4 has X = 1; values just above the E2M1
+    midpoints 1.25 and 2.5 round up, the midpoints themselves go to the even code (1.0, 2.0); bf16
+    would have rounded the former onto the midpoints.  An amax one fp32 ulp below 4 takes X = 1/2 and
+    saturates to 6 X = 3."""
+    row = np.zeros((2, 32))
+    row[0, :5] = [4.0, 1.25, 1.25 + 2.0 ** -20, 2.5, 2.5 + 2.0 ** -18]
+    below4 = float(np.nextafter(np.float32(4.0), np.float32(0.0)))
+    row[1, :2] = [below4, -1.0]
+    packed, e8 = Q.quant_mxfp4(row)
+    codes = Q.unpack_e2m1(packed)
+    assert list(e8[:, 0]) == [127, 126]
+    assert list(codes[0, :5]) == [6, 2, 3, 4, 5]
+    assert list(codes[1, :2]) == [7, 12]                      # 6 X = 3 (saturated); -1 = -2 X (code 4, sign 8)
+    pb, eb = Q.quant_mxfp4_weight(C.f64_to_bf16(row))
+    assert list(Q.unpack_e2m1(pb)[0, :5]) == [6, 2, 2, 4, 4]
+    assert eb[1, 0] == 127                                    # bf16 rounds 4 - ulp up to 4
+
+
+def test_mxfp4_activation_error_bound():
+    """Each dequantized element is within half an E2M1 step of its value, or saturated at 6 X when
+    |x| / X > 6 (the block maximum can sit anywhere in [4 X, 8 X))."""
+    x = W.bf16_bits_to_f32(W.normal_bf16((64, 256), seed=9, scale=3.0)).astype(np.float64)
+    x *= np.exp2(np.random.default_rng(1).integers(-30, 30, size=(64, 1)))
+    packed, e8 = Q.quant_mxfp4(x)
+    deq = G.dequant_mxfp4(packed, e8)
+    X = np.repeat(C.e8m0_decode(e8), 32, axis=1)
+    r = np.abs(x) / X
+    step = np.where(r < 2, 0.5, np.where(r < 4, 1.0, 2.0))
+    sat = r > 6
+    assert np.all(np.abs(deq - x)[~sat] <= (step * X)[~sat] / 2)
+    np.testing.assert_array_equal(np.abs(deq[sat]), 6 * X[sat])
+    assert np.all(np.sign(deq[deq != 0]) == np.sign(x[deq != 0]))
+
+
 def _frac_mx(packed, e8):
     """Exact rationals of MXFP4 data, element by element from the pinned codecs."""
     codes = Q.unpack_e2m1(packed)
@@ -365,6 +400,37 @@ def test_block_static_scales_and_mxfp4_run():
     d8 = C.bf16_to_f64(out_dyn) - C.bf16_to_f64(x)
     d4 = C.bf16_to_f64(out4) - C.bf16_to_f64(x)
     assert np.sqrt(((d4 - d8) ** 2).mean() / (d8 ** 2).mean()) < 0.3
+
+
+def _w4a4_weights(w, seed):
+    wb = W.block_weights(w, seed)
+    qm = {}
+    for site in B.SITES:
+        qm["w_" + site], qm["e8_" + site] = Q.quant_mxfp4_weight(wb["w_" + site])
+    return qm
+
+
+def test_block_w4a4_zero_gates_is_identity():
+    w, x, _, mod, idx, cnt = _toy_block(gate=0.0)
+    out = B.dit_block(x, mod, _w4a4_weights(w, 0), idx, cnt, w.n_heads, fmt="w4a4")
+    np.testing.assert_array_equal(out, x)
+
+
+def test_block_w4a4_tracks_fp8_block():
+    """Both operands 4-bit: the block's branch (out - x) stays close to the FP8 block's, and the GEMM
+    inputs are the MXFP4 quantization of the modulated LayerNorm outputs, O and GELU."""
+    w, x, qw, mod, idx, cnt = _toy_block(seed=4)
+    out8 = B.dit_block(x, mod, qw, idx, cnt, w.n_heads)
+    out4, it = B.dit_block(x, mod, _w4a4_weights(w, 4), idx, cnt, w.n_heads, fmt="w4a4", keep=True)
+    d8 = C.bf16_to_f64(out8) - C.bf16_to_f64(x)
+    d4 = C.bf16_to_f64(out4) - C.bf16_to_f64(x)
+    rel = np.sqrt(((d4 - d8) ** 2).mean() / (d8 ** 2).mean())
+    assert 0.01 < rel < 0.4, rel
+    y = A.layernorm_modulate(x, mod, 0, 1e-6).astype(np.float64)
+    deq = G.dequant_mxfp4(*it["h1"])
+    assert np.sqrt(((deq - y) ** 2).mean() / (y ** 2).mean()) < 0.15
+    assert it["s1"] is None and it["so"] is None and it["sg"] is None
+    assert it["g8"][0].shape == (w.L, w.mlp // 2) and it["g8"][1].shape == (w.L, w.mlp // 32)
 
 
 # --- calibration ----------------------------------------------------------------------------------
