@@ -122,6 +122,13 @@ size_t qvd_adaln_modulate_ws_bytes(int32_t L, int32_t d);
 int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
                    float eps, const float* act_scale_in, uint8_t* q, float* act_scale_out,
                    void* ws, size_t ws_bytes, void* stream);
+/* The same modulated LayerNorm with MXFP4 output (W4A4 blocks: the 4-bit transformer of the
+ * news.farwalk.ai FastH3 story, post 6/8, in OCP MX form): y as above, then per token row and 32
+ * consecutive channels X = 2^(floor(log2 max|y|) - 2) (all-zero block: X = 1), codes E2M1(y / X),
+ * round to nearest even, saturating at 6.  packed: uint8 [L][d/2] (channel 2j in the low nibble of
+ * byte j); e8m0: uint8 [L][d/32].  One pass; no workspace. */
+int adaln_modulate_mxfp4(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                         float eps, uint8_t* packed, uint8_t* e8m0, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Block-sparse attention with INT8 scores -- "Trim 改变了什么" training bullet (80% sparsity)
@@ -167,6 +174,14 @@ int qvd_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t*
                             const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
                             const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
                             const float* out_scale, uint8_t* out_q, void* stream);
+/* The same attention writing the MXFP4 codes of bf16 O (W4A4 blocks), per (token, head) and 32
+ * consecutive dims exactly as qvd_quant_mxfp4 quantizes the bf16 tensor O viewed as [L][H*128]:
+ * out_packed uint8 [L][H][64] (dim 2j in the low nibble of byte j; 16-byte aligned), out_e8m0
+ * uint8 [L][H][4] (4-byte aligned).  O itself is not written. */
+int qvd_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int8_t* k,
+                             const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                             const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
+                             uint8_t* out_packed, uint8_t* out_e8m0, void* stream);
 
 /* Exact INT32 accumulators Q8[rows of tile i] . K8[rows of tile j]^T of head h, computed by the
  * same INT8 MFMA tile routine the attention kernel uses, into out int32 [128][128]
@@ -194,10 +209,14 @@ enum qvd_epilogue_mode {
                                written transposed and converted to fp16 into v as
                                [H][128][ceil(M/128)*128], columns M.. of the last tile zeroed
                                (the layout qvd_sparse_attn_vt reads)                            */
-    QVD_EPI_GELU_E4M3 = 5   /* out_e4m3[m][n] = E4M3(bf16(GELU(y)) * fp32(1 / *out_scale)): the
+    QVD_EPI_GELU_E4M3 = 5,  /* out_e4m3[m][n] = E4M3(bf16(GELU(y)) * fp32(1 / *out_scale)): the
                                GELU output quantized with a static per-tensor scale exactly as
                                quant_fp8_per_tensor does with scale_in = out_scale, without the
                                bf16 tensor (static scales: the calibrated path)                 */
+    QVD_EPI_GELU_MXFP4 = 6  /* bf16(GELU(y)) quantized to MXFP4 per row and 32 consecutive columns
+                               exactly as qvd_quant_mxfp4 does from the bf16 tensor, without
+                               writing it: out_e2m1 [M][N/2] (column 2j in the low nibble of byte
+                               j), out_e8m0 [M][N/32] (W4A4 blocks: the down-projection's input) */
 };
 typedef struct {
     int32_t mode;               /* qvd_epilogue_mode                                           */
@@ -214,6 +233,8 @@ typedef struct {
     float* k_scale;
     uint8_t* out_e4m3;          /* QVD_EPI_GELU_E4M3: E4M3 codes [M][N]                          */
     const float* out_scale;     /* QVD_EPI_GELU_E4M3: device fp32 static scale s (> 0)           */
+    uint8_t* out_e2m1;          /* QVD_EPI_GELU_MXFP4: packed E2M1 [M][N/2], 16-byte aligned     */
+    uint8_t* out_e8m0;          /* QVD_EPI_GELU_MXFP4: E8M0 [M][N/32]                            */
 } qvd_epilogue;
 int64_t qvd_gemm_tiles(int32_t M, int32_t N);
 int qvd_gemm_fp8(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
@@ -247,8 +268,12 @@ int qvd_gemm_mxfp4_w4a4(const uint8_t* a_packed, const uint8_t* a_e8m0, const ui
  * Weights are [N][K] (K contiguous).  weight_format QVD_W_FP8: E4M3 codes with per-tensor fp32
  * scales s_*.  QVD_W_MXFP4: packed E2M1 (element 2j in the low nibble of byte j) with E8M0
  * scales e8m0_* [N][K/32]; s_* are ignored.  act_scale: NULL (dynamic scales) or fp32 [4] static
- * scales of the QKV, out, up and down GEMM inputs (required for MXFP4).  Biases may be NULL. */
-enum qvd_weight_format { QVD_W_FP8 = 0, QVD_W_MXFP4 = 1 };
+ * scales of the QKV, out, up and down GEMM inputs (required for MXFP4).  QVD_W_MXFP4_A4 (W4A4):
+ * the weights as for QVD_W_MXFP4 and every GEMM input MXFP4 too -- h1 and h2 from
+ * adaln_modulate_mxfp4, O from qvd_sparse_attn_vt_mxfp4, g from the QVD_EPI_GELU_MXFP4 epilogue --
+ * each with a dynamic E8M0 scale per token row and 32 channels; act_scale is ignored.  Biases may
+ * be NULL. */
+enum qvd_weight_format { QVD_W_FP8 = 0, QVD_W_MXFP4 = 1, QVD_W_MXFP4_A4 = 2 };
 typedef struct {
     int32_t version;            /* QVD_ABI_VERSION                                             */
     int32_t d, n_heads, head_dim, mlp, weight_format;
@@ -288,7 +313,7 @@ int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* coun
  * bracketed by a pair of HIP events recorded on the launch's own stream.  qvd_timing_report waits
  * for the recorded work, writes {"<kernel key>": {"count": n, "total_ms": t}, ...} (NUL-terminated
  * JSON) into buf and clears the records.  Keys: "sparse_attn", "adaln_modulate", "adaln_project",
- * "quant_fp8", "amax_bf16", "quant_int8_qk", "gemm_<fp8|mxfp4|w4a4>_<epilogue>_<M>x<N>x<K>".
+ * "adaln_modulate_mxfp4", "quant_fp8", "amax_bf16", "quant_int8_qk", "gemm_<fp8|mxfp4|w4a4>_<epilogue>_<M>x<N>x<K>".
  * Returns QVD_EINVAL if len is too small (the records are then lost), QVD_EHIP on event errors. */
 int qvd_timing_enable(int on);
 int qvd_timing_report(char* buf, size_t len);

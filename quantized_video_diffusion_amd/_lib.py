@@ -14,8 +14,9 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "qvd.h")
 
 QVD_OK, QVD_EINVAL, QVD_ESHAPE, QVD_EALIGN, QVD_EWORKSPACE, QVD_EUNSUPPORTED, QVD_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
-QVD_EPI_F32, QVD_EPI_BF16, QVD_EPI_RESID_GATE, QVD_EPI_GELU, QVD_EPI_QKV, QVD_EPI_GELU_E4M3 = range(6)
-QVD_W_FP8, QVD_W_MXFP4 = 0, 1
+(QVD_EPI_F32, QVD_EPI_BF16, QVD_EPI_RESID_GATE, QVD_EPI_GELU, QVD_EPI_QKV, QVD_EPI_GELU_E4M3,
+ QVD_EPI_GELU_MXFP4) = range(7)
+QVD_W_FP8, QVD_W_MXFP4, QVD_W_MXFP4_A4 = 0, 1, 2
 ABI_VERSION = 1
 
 _p = C.c_void_p
@@ -30,7 +31,7 @@ class Epilogue(C.Structure):
         ("mode", _i32), ("n_heads", _i32),
         ("out_f32", _p), ("out_bf16", _p), ("resid", _p), ("gate", _p), ("amax_partials", _p),
         ("q8", _p), ("k8", _p), ("v", _p), ("q_scale", _p), ("k_scale", _p),
-        ("out_e4m3", _p), ("out_scale", _p),
+        ("out_e4m3", _p), ("out_scale", _p), ("out_e2m1", _p), ("out_e8m0", _p),
     ]
 
 
@@ -58,12 +59,15 @@ SIGNATURES = {
     "qvd_adaln_project_stack": (C.c_int, [_f32, _p, _i32, _p, _p, _i32, _i32, _p, _p]),
     "qvd_adaln_modulate_ws_bytes": (_sz, [_i32, _i32]),
     "adaln_modulate": (C.c_int, [_p, _i32, _i32, _p, _i32, _f32, _p, _p, _p, _p, _sz, _p]),
+    "adaln_modulate_mxfp4": (C.c_int, [_p, _i32, _i32, _p, _i32, _f32, _p, _p, _p]),
     "qvd_sparse_attn_ws_bytes": (_sz, [_i32, _i32]),
     "sparse_attn": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _f32, _p, _p, _p, _sz,
                               _p]),
     "qvd_sparse_attn_vt": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p, _p]),
     "qvd_sparse_attn_vt_e4m3": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p,
                                           _p]),
+    "qvd_sparse_attn_vt_mxfp4": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p,
+                                           _p]),
     "qvd_qk_int32_tile": (C.c_int, [_p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "qvd_gemm_tiles": (_i64, [_i32, _i32]),
     "qvd_gemm_fp8": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(Epilogue), _p]),

@@ -252,6 +252,65 @@ __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x
     }
 }
 
+// MXFP4 activations (no per-tensor scale, so one pass): y = modulate_one, the float64 modulation
+// rounded once to fp32; then per 32 consecutive channels -- the 16 lanes of one row of the wave at
+// one word column j -- the shared exponent and the E2M1 codes.  packed [L][d/2]: lane l writes byte
+// l + 64 j of its row (channels 2(l + 64 j), +1); e8m0 [L][d/32]: the first lane of each 16-lane
+// row writes block 4 j + l/16.
+template <int NW>
+__global__ void __launch_bounds__(256) k_ln_mx(const uint16_t* __restrict__ x, int L, int d,
+                                               const float* __restrict__ mod, int half, float eps,
+                                               uint8_t* __restrict__ packed, uint8_t* __restrict__ e8m0) {
+    __shared__ float4 tab[4096 / 2];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int nw = d >> 7;
+    load_mod_table(tab, mod, half, d, false, 1.0f);
+    Row<NW> R;
+    for (int row = blockIdx.x * 4 + wv; row < L; row += gridDim.x * 4) {
+        const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)row * d);
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            if (j < nw) R.x[j] = __builtin_nontemporal_load(xr + lane + 64 * j);
+        double mu, rstd;
+        row_stats<NW>(R, nw, d, (double)eps, mu, rstd);
+        uint8_t* pr = packed + (int64_t)row * (d / 2);
+        uint8_t* er = e8m0 + (int64_t)row * (d / 32);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if (j < nw) {
+                const float4 c = tab[lane + 64 * j];
+                const float y0 = modulate_one(bf16lo(R.x[j]), mu, rstd, c.x, c.y);
+                const float y1 = modulate_one(bf16hi(R.x[j]), mu, rstd, c.z, c.w);
+                const int k = mx_exponent(max16_nonneg(fmaxf(fabsf(y0), fabsf(y1))));
+                pr[lane + 64 * j] = (uint8_t)e2m1_encode2(y0, y1, k);
+                if ((lane & 15) == 0) er[4 * j + (lane >> 4)] = (uint8_t)(k + 127);
+            }
+        }
+    }
+}
+
+template <int NW>
+static int launch_modulate_mx_nw(const uint16_t* x, int L, int d, const float* mod, int half, float eps,
+                                 uint8_t* packed, uint8_t* e8m0, hipStream_t st) {
+    TimingScope ts("adaln_modulate_mxfp4", st);
+    int g = (L + 3) / 4;
+    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+    hipLaunchKernelGGL(k_ln_mx<NW>, dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, packed, e8m0);
+    return launch_status("adaln_modulate_mxfp4");
+}
+
+int launch_modulate_mx(const uint16_t* x, int L, int d, const float* mod, int half, float eps,
+                       uint8_t* packed, uint8_t* e8m0, hipStream_t st) {
+    if (L == 0) return QVD_OK;
+    switch (d >> 7) {
+        case 2: return launch_modulate_mx_nw<2>(x, L, d, mod, half, eps, packed, e8m0, st);
+        case 21: return launch_modulate_mx_nw<21>(x, L, d, mod, half, eps, packed, e8m0, st);
+        default:
+            if ((d >> 7) <= 8) return launch_modulate_mx_nw<8>(x, L, d, mod, half, eps, packed, e8m0, st);
+            return launch_modulate_mx_nw<32>(x, L, d, mod, half, eps, packed, e8m0, st);
+    }
+}
+
 constexpr int LN_GRID_STATS = 1024;
 
 size_t adaln_ws_bytes(int L, int d) {
@@ -361,6 +420,25 @@ int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, in
     QVD_DEVICE_OK();
     return launch_modulate(x, L, d, mod, half, eps, act_scale_in, q, act_scale_out, ws,
                            (hipStream_t)stream);
+}
+
+int adaln_modulate_mxfp4(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                         float eps, uint8_t* packed, uint8_t* e8m0, void* stream) {
+    QVD_REQUIRE(L >= 0, QVD_ESHAPE, "adaln_modulate_mxfp4: L = %d", L);
+    QVD_REQUIRE(d >= 128 && d % 128 == 0 && d <= 4096, QVD_ESHAPE,
+                "adaln_modulate_mxfp4: d = %d (multiple of 128, at most 4096)", d);
+    QVD_REQUIRE(half == 0 || half == 1, QVD_EINVAL, "adaln_modulate_mxfp4: half = %d (0 or 1)", half);
+    QVD_REQUIRE(eps >= 0.0f, QVD_EINVAL, "adaln_modulate_mxfp4: eps < 0");
+    QVD_PTR(mod);
+    QVD_ALIGN(mod);
+    if (L > 0) {
+        QVD_PTR(x);
+        QVD_PTR(packed);
+        QVD_PTR(e8m0);
+        QVD_ALIGN(x);
+    }
+    QVD_DEVICE_OK();
+    return launch_modulate_mx(x, L, d, mod, half, eps, packed, e8m0, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -337,14 +337,15 @@ QVD_DEV void softmax_tile(const v4i s[2][8], float c, bool ragged, int key0, int
 
 // Output of the attention kernel: bf16 O; bf16 O and the per-(head, tile) max|O|; or the E4M3 codes
 // of bf16 O under a static per-tensor scale, as the standalone static quantizer computes them.
-enum AttnOut { OUT_BF16 = 0, OUT_BF16_AMAX = 1, OUT_E4M3 = 2 };
+enum AttnOut { OUT_BF16 = 0, OUT_BF16_AMAX = 1, OUT_E4M3 = 2, OUT_MXFP4 = 3 };
 
 template <int OUT>
 __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     const int8_t* __restrict__ q, const float* __restrict__ q_scale, const int8_t* __restrict__ k,
     const float* __restrict__ k_scale, const uint16_t* __restrict__ vt, int L, int H,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int kmax, float c_log2,
-    void* __restrict__ out, float* __restrict__ amax_partials, const float* __restrict__ out_scale) {
+    void* __restrict__ out, float* __restrict__ amax_partials, const float* __restrict__ out_scale,
+    uint8_t* __restrict__ out_e8m0) {
     // a single LDS object: with a second __shared__ array the compiler waits for every DMA before
     // each LDS read
     __shared__ __attribute__((aligned(16))) AttnSmem sm;
@@ -444,6 +445,52 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
         }
     }
     for (; passed < P + 1; ++passed) lds_barrier();
+
+    if (OUT == OUT_MXFP4) {
+        // bf16 O, then MXFP4 per (row, head, 32 dims) with the standalone quantizer's arithmetic.  Dims
+        // 32 b .. 32 b + 31 of a row are this lane's column blocks 2b and 2b+1 in each of the row's
+        // four lanes (fg): the block maximum meets across them before any lane stores.
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float lt = lacc[qb][0];
+            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+            const int row = q0 + 16 * qb + fr;
+            u32 w[8][2];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const v4f cc = o[qb][db];
+                w[db][0] = pack_bf16x2(cc[0] * inv, cc[1] * inv);
+                w[db][1] = pack_bf16x2(cc[2] * inv, cc[3] * inv);
+            }
+            int kx[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                float m = 0.0f;
+#pragma unroll
+                for (int db = 2 * b; db < 2 * b + 2; ++db)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        m = fmaxf(m, fmaxf(fabsf(bf16lo(w[db][u])), fabsf(bf16hi(w[db][u]))));
+                kx[b] = mx_exponent(__int_as_float(max_over_lane_groups(__float_as_int(m))));
+            }
+            if (valid && row < L) {
+                const int64_t orow = (int64_t)row * H + h;
+                uint8_t* pr = static_cast<uint8_t*>(out) + orow * 64;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const int k = kx[db >> 1];
+                    const u32 c = e2m1_encode2(bf16lo(w[db][0]), bf16hi(w[db][0]), k) |
+                                  (e2m1_encode2(bf16lo(w[db][1]), bf16hi(w[db][1]), k) << 8);
+                    *reinterpret_cast<uint16_t*>(pr + 8 * db + 2 * fg) = (uint16_t)c;
+                }
+                if (fg == 0)
+                    *reinterpret_cast<u32*>(out_e8m0 + orow * 4) =
+                        (u32)(kx[0] + 127) | ((u32)(kx[1] + 127) << 8) | ((u32)(kx[2] + 127) << 16) |
+                        ((u32)(kx[3] + 127) << 24);
+            }
+        }
+        return;
+    }
 
     float amax = 0.0f;
     const float inv_s = OUT == OUT_E4M3 ? __fdiv_rn(1.0f, *out_scale) : 0.0f;
@@ -546,14 +593,15 @@ namespace {
 template <int OUT>
 int launch_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                 const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt, int kmax,
-                float sm_scale, void* out, float* amax_partials, const float* out_scale, hipStream_t st) {
+                float sm_scale, void* out, float* amax_partials, const float* out_scale, uint8_t* out_e8m0,
+                hipStream_t st) {
     if (L == 0) return QVD_OK;
     const int T = (L + 127) / 128;
     const unsigned pairs = (unsigned)((T * H + 1) / 2);
     const float c = sm_scale * LOG2E;
     TimingScope ts("sparse_attn", st);
     hipLaunchKernelGGL(k_sparse_attn<OUT>, dim3(pairs), dim3(512), 0, st, q, q_scale, k, k_scale, vt, L, H,
-                       kv_idx, kv_cnt, kmax, c, out, amax_partials, out_scale);
+                       kv_idx, kv_cnt, kmax, c, out, amax_partials, out_scale, out_e8m0);
     return launch_status("sparse_attn");
 }
 }  // namespace
@@ -563,9 +611,9 @@ int launch_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k
                           int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st) {
     if (amax_partials)
         return launch_attn<OUT_BF16_AMAX>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
-                                          out, amax_partials, nullptr, st);
+                                          out, amax_partials, nullptr, nullptr, st);
     return launch_attn<OUT_BF16>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out,
-                                 nullptr, nullptr, st);
+                                 nullptr, nullptr, nullptr, st);
 }
 
 int launch_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
@@ -573,7 +621,15 @@ int launch_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8
                                const int32_t* kv_idx, const int32_t* kv_cnt, int kmax, float sm_scale,
                                const float* out_scale, uint8_t* out_q, hipStream_t st) {
     return launch_attn<OUT_E4M3>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out_q,
-                                 nullptr, out_scale, st);
+                                 nullptr, out_scale, nullptr, st);
+}
+
+int launch_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int8_t* k,
+                                const float* k_scale, const uint16_t* vt, int L, int H,
+                                const int32_t* kv_idx, const int32_t* kv_cnt, int kmax, float sm_scale,
+                                uint8_t* out_packed, uint8_t* out_e8m0, hipStream_t st) {
+    return launch_attn<OUT_MXFP4>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+                                  out_packed, nullptr, nullptr, out_e8m0, st);
 }
 
 size_t vt_bytes(int L, int H) { return (size_t)H * 128 * (size_t)((L + 127) / 128) * 128 * 2; }
@@ -656,6 +712,21 @@ int qvd_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t*
     QVD_DEVICE_OK();
     return launch_sparse_attn_vt_e4m3(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
                                       out_scale, out_q, (hipStream_t)stream);
+}
+
+int qvd_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int8_t* k,
+                             const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                             const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
+                             uint8_t* out_packed, uint8_t* out_e8m0, void* stream) {
+    int s = validate_attn("qvd_sparse_attn_vt_mxfp4", q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt,
+                          kmax, sm_scale, reinterpret_cast<uint16_t*>(out_packed));
+    if (s || L == 0) return s;
+    QVD_PTR(out_e8m0);
+    QVD_REQUIRE(((uintptr_t)out_e8m0 & 3u) == 0, QVD_EALIGN,
+                "qvd_sparse_attn_vt_mxfp4: out_e8m0 must be 4-byte aligned");
+    QVD_DEVICE_OK();
+    return launch_sparse_attn_vt_mxfp4(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+                                       out_packed, out_e8m0, (hipStream_t)stream);
 }
 
 int qvd_qk_int32_tile(const int8_t* q, const int8_t* k, int32_t L, int32_t H, int32_t h,

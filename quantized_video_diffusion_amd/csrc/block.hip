@@ -21,6 +21,11 @@
 // are fused into their producers: the attention writes the E4M3 codes of O and the up-projection's
 // epilogue the E4M3 codes of g, with the same arithmetic as the standalone quantizer, so neither
 // bf16 tensor is written or read back.
+// W4A4 (QVD_W_MXFP4_A4; the 4-bit transformer of the news.farwalk.ai FastH3 story, post 6/8, in
+// OCP MX form): every GEMM input is MXFP4 with one E8M0 scale per token row and 32 channels.  The
+// modulate kernel writes h in MXFP4, the attention writes the MXFP4 codes of bf16 O and the
+// up-projection's epilogue those of bf16 GELU; all four GEMMs take both operands in E2M1.  Block
+// scales are dynamic and local, so nothing is reduced across the tensor and no scale is passed.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,7 +42,9 @@ struct BlockWs {
     uint16_t* v;         // fp16 V^T [H][128][T*128]
     uint16_t* o;         // bf16 [L][d] (dynamic scales only)
     uint16_t* g;         // bf16 [L][F] (dynamic scales only)
-    uint8_t* g8;         // E4M3 [L][F]
+    uint8_t* g8;         // E4M3 [L][F] (W4A4: packed E2M1 [L][F/2])
+    uint8_t* h_e8;       // W4A4: E8M0 [L][d/32] of h, then of O
+    uint8_t* g_e8;       // W4A4: E8M0 [L][F/32] of g
     float* qs;           // [H][T]
     float* ks;           // [H][T]
     float* attn_part;    // [H][T]
@@ -62,10 +69,14 @@ BlockWs carve(const qvd_block_params* p, int L, uint8_t* base) {
     w.q8 = (int8_t*)take(Ld);
     w.k8 = (int8_t*)take(Ld);
     w.v = (uint16_t*)take(vt_bytes(L, p->n_heads));
-    const bool stat = p->act_scale != nullptr;   // static scales: O and g exist only as E4M3 codes
+    const bool a4 = p->weight_format == QVD_W_MXFP4_A4;
+    // static scales or W4A4: O and g exist only as codes
+    const bool stat = p->act_scale != nullptr || a4;
     w.o = (uint16_t*)take(stat ? 0 : 2 * Ld);
     w.g = (uint16_t*)take(stat ? 0 : 2 * LF);
     w.g8 = take(LF);
+    w.h_e8 = take(a4 ? Ld / 32 : 0);
+    w.g_e8 = take(a4 ? LF / 32 : 0);
     w.qs = (float*)take(4 * HT);
     w.ks = (float*)take(4 * HT);
     w.attn_part = (float*)take(4 * HT);
@@ -87,8 +98,9 @@ int validate(const qvd_block_params* p, int L) {
     QVD_REQUIRE(p->mlp >= 128 && p->mlp % 256 == 0, QVD_ESHAPE,
                 "block: mlp = %d (positive multiple of 256)", p->mlp);
     QVD_REQUIRE(L >= 0, QVD_ESHAPE, "block: L = %d", L);
-    QVD_REQUIRE(p->weight_format == QVD_W_FP8 || p->weight_format == QVD_W_MXFP4, QVD_EINVAL,
-                "block: weight_format = %d", p->weight_format);
+    QVD_REQUIRE(p->weight_format == QVD_W_FP8 || p->weight_format == QVD_W_MXFP4 ||
+                    p->weight_format == QVD_W_MXFP4_A4,
+                QVD_EINVAL, "block: weight_format = %d", p->weight_format);
     QVD_REQUIRE(p->ln_eps >= 0.0f, QVD_EINVAL, "block: ln_eps < 0");
     QVD_PTR(p->w_qkv);
     QVD_PTR(p->w_o);
@@ -108,8 +120,9 @@ int validate(const qvd_block_params* p, int L) {
         QVD_PTR(p->e8m0_o);
         QVD_PTR(p->e8m0_up);
         QVD_PTR(p->e8m0_down);
-        QVD_REQUIRE(p->act_scale != nullptr, QVD_EINVAL,
-                    "block: MXFP4 weights need static activation scales (act_scale)");
+        if (p->weight_format == QVD_W_MXFP4)
+            QVD_REQUIRE(p->act_scale != nullptr, QVD_EINVAL,
+                        "block: MXFP4 weights need static activation scales (act_scale)");
     }
     const float* b[4] = {p->b_qkv, p->b_o, p->b_up, p->b_down};
     for (int i = 0; i < 4; ++i)
@@ -158,6 +171,46 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     const float* act = p->act_scale;           // NULL: dynamic
     const float* shift_scale_gate = mod;       // [6][d]
     const float sm_scale = 0.08838834764831845f;   // 1/sqrt(128)
+
+    if (fmt == QVD_W_MXFP4_A4) {
+        s = launch_modulate_mx(x, L, d, mod, 0, p->ln_eps, w.h, w.h_e8, st);
+        if (s) return s;
+        qvd_epilogue e{};
+        e.mode = QVD_EPI_QKV;
+        e.n_heads = H;
+        e.q8 = w.q8;
+        e.k8 = w.k8;
+        e.v = w.v;
+        e.q_scale = w.qs;
+        e.k_scale = w.ks;
+        s = launch_gemm_w4a4(w.h, w.h_e8, (const uint8_t*)p->w_qkv, p->e8m0_qkv, p->b_qkv, L, 3 * d, d, e, st);
+        if (s) return s;
+        s = launch_sparse_attn_vt_mxfp4(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.h,
+                                        w.h_e8, st);
+        if (s) return s;
+        e = qvd_epilogue{};
+        e.mode = QVD_EPI_RESID_GATE;
+        e.out_bf16 = x;
+        e.resid = x;
+        e.gate = shift_scale_gate + 2 * d;
+        s = launch_gemm_w4a4(w.h, w.h_e8, (const uint8_t*)p->w_o, p->e8m0_o, p->b_o, L, d, d, e, st);
+        if (s) return s;
+        s = launch_modulate_mx(x, L, d, mod, 1, p->ln_eps, w.h, w.h_e8, st);
+        if (s) return s;
+        e = qvd_epilogue{};
+        e.mode = QVD_EPI_GELU_MXFP4;
+        e.out_e2m1 = w.g8;
+        e.out_e8m0 = w.g_e8;
+        s = launch_gemm_w4a4(w.h, w.h_e8, (const uint8_t*)p->w_up, p->e8m0_up, p->b_up, L, F, d, e, st);
+        if (s) return s;
+        e = qvd_epilogue{};
+        e.mode = QVD_EPI_RESID_GATE;
+        e.out_bf16 = x;
+        e.resid = x;
+        e.gate = shift_scale_gate + 5 * d;
+        return launch_gemm_w4a4(w.g8, w.g_e8, (const uint8_t*)p->w_down, p->e8m0_down, p->b_down, L, d, F, e,
+                                st);
+    }
 
     // attention branch
     s = launch_modulate(x, L, d, mod, 0, p->ln_eps, act ? act + 0 : nullptr, w.h, w.scales + 0, w.ln_ws, st);

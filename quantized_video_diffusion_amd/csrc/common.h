@@ -68,6 +68,42 @@ QVD_DEV int int8_encode(float x, float inv) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// MXFP4 (OCP MX v1.0 elements E2M1 with one E8M0 scale per 32 consecutive values).  The block scale
+// is X = 2^k with k = floor(log2 amax) - 2 (2 is the exponent of E2M1's largest value, 6), clamped to
+// E8M0's [-127, 127]; an all-zero block takes k = 0.  Elements are E2M1(v / X): round to nearest
+// even on the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6, saturating at 6; sign in bit 3.
+
+QVD_DEV int mx_exponent(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int e;
+    frexpf(amax, &e);                      // amax = f 2^e, f in [0.5, 1): floor(log2 amax) = e - 1
+    const int k = e - 3;
+    return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
+QVD_DEV u32 e2m1_encode(float v) {
+    const float a = fabsf(v);
+    u32 c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+          : a <= 2.5f  ? 4u : a < 3.5f  ? 5u : a <= 5.0f  ? 6u : 7u;
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// two elements of one block -> one byte (first element in the low nibble)
+QVD_DEV u32 e2m1_encode2(float a, float b, int k) {
+    return e2m1_encode(ldexpf(a, -k)) | (e2m1_encode(ldexpf(b, -k)) << 4);
+}
+
+// max of non-negative floats over each row of 16 lanes (DPP: swap neighbours, swap pairs, then the
+// half-row and row mirrors)
+QVD_DEV float max16_nonneg(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+// ---------------------------------------------------------------------------------------------
 // wave / block reductions (wave64)
 
 QVD_DEV float wave_max(float v) {

@@ -228,6 +228,54 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
         return;
     }
 
+    if (EPI == QVD_EPI_GELU_MXFP4) {
+        // GELU and bf16 rounding as in the GELU epilogue, the wave's 128 x WN bf16 block staged in LDS
+        // (one round: 128 rows of 2 WN bytes), then each lane quantizes whole 32-column blocks of a
+        // row with the standalone quantizer's arithmetic: 16 code bytes and one scale byte per block.
+        static_assert(BR == 128, "one staging round");
+        if (!wave_live) return;
+        constexpr int QB = WN / 32;                      // 32-column blocks per row
+#pragma unroll
+        for (int cg = 0; cg < LY::NCG; ++cg) {
+            const int nl = LY::ncol(cg, lane);
+            const float4 b = load_bias4(g.bias, nw0 + nl);
+#pragma unroll
+            for (int r = 0; r < LY::MR; ++r) {
+                const int ml = LY::mrow(r, lane);
+                const v4f c = LY::get(acc, cg, r);
+                const u32 p0 = pack_bf16x2(gelu_erf(c[0] * alpha + b.x), gelu_erf(c[1] * alpha + b.y));
+                const u32 p1 = pack_bf16x2(gelu_erf(c[2] * alpha + b.z), gelu_erf(c[3] * alpha + b.w));
+                *reinterpret_cast<u32x2*>(bslot(ml, nl >> 3) + ((nl >> 2) & 1) * 8) = (u32x2){p0, p1};
+            }
+        }
+        lds_wait();
+        const int Nh = N / 2, Nb = N / 32;
+#pragma unroll
+        for (int it = 0; it < 2 * QB; ++it) {
+            const int idx = 64 * it + lane, ml = idx / QB, bk = idx % QB;
+            u32 ws[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(bslot(ml, 4 * bk + q));
+                ws[4 * q] = v.x; ws[4 * q + 1] = v.y; ws[4 * q + 2] = v.z; ws[4 * q + 3] = v.w;
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(ws[j])), fabsf(bf16hi(ws[j]))));
+            const int k = mx_exponent(amax);
+            u32 o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[j >> 2] |= e2m1_encode2(bf16lo(ws[j]), bf16hi(ws[j]), k) << ((j & 3) * 8);
+            const int m = mw0 + ml;
+            if (m < M) {
+                *reinterpret_cast<u32x4*>(ep.out_e2m1 + (int64_t)m * Nh + (nw0 + 32 * bk) / 2) =
+                    (u32x4){o[0], o[1], o[2], o[3]};
+                ep.out_e8m0[(int64_t)m * Nb + nw0 / 32 + bk] = (uint8_t)(k + 127);
+            }
+        }
+        return;
+    }
+
     if (EPI == QVD_EPI_QKV) {
         const int dm = N / 3;
         // The V columns start at 2 dm = 256 H, a tile boundary, so a workgroup's waves are either all
@@ -838,6 +886,7 @@ static int launch_epi(const GemmArgs& g, hipStream_t st) {
         case QVD_EPI_GELU: hipLaunchKernelGGL(KERN<QVD_EPI_GELU>::fn, grid, blk, 0, st, g); break;
         case QVD_EPI_QKV: hipLaunchKernelGGL(KERN<QVD_EPI_QKV>::fn, grid, blk, 0, st, g); break;
         case QVD_EPI_GELU_E4M3: hipLaunchKernelGGL(KERN<QVD_EPI_GELU_E4M3>::fn, grid, blk, 0, st, g); break;
+        case QVD_EPI_GELU_MXFP4: hipLaunchKernelGGL(KERN<QVD_EPI_GELU_MXFP4>::fn, grid, blk, 0, st, g); break;
         default: return fail(QVD_EINVAL, "gemm: epilogue mode %d", g.epi.mode);
     }
     return launch_status("gemm");
@@ -845,6 +894,11 @@ static int launch_epi(const GemmArgs& g, hipStream_t st) {
 template <int EPI> struct KF8 { static constexpr auto fn = k_gemm_f8<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
 template <int EPI> struct KMX { static constexpr auto fn = k_gemm_mx<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
 template <int EPI> struct KW4A4 { static constexpr auto fn = k_gemm_w4a4<EPI>; static constexpr unsigned threads = 64 * NWAVE8; };
+
+static const char* epi_name(int mode) {
+    static const char* names[] = {"f32", "bf16", "resid_gate", "gelu", "qkv", "gelu_e4m3", "gelu_mxfp4"};
+    return (mode >= 0 && mode < 7) ? names[mode] : "?";
+}
 
 int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t* e8, const float* s_w,
                 int w_fmt, const float* bias, int M, int N, int K, const qvd_epilogue& epi,
@@ -864,10 +918,9 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
     g.tiles_m = (M + BM - 1) / BM;
     g.tiles_n = (N + BN - 1) / BN;
     g.epi = epi;
-    static const char* epi_name[] = {"f32", "bf16", "resid_gate", "gelu", "qkv", "gelu_e4m3"};
     char key[96];
     snprintf(key, sizeof(key), "gemm_%s_%s_%dx%dx%d", w_fmt == QVD_W_MXFP4 ? "mxfp4" : "fp8",
-             (epi.mode >= 0 && epi.mode < 6) ? epi_name[epi.mode] : "?", M, N, K);
+             epi_name(epi.mode), M, N, K);
     TimingScope ts(key, st);
     return w_fmt == QVD_W_MXFP4 ? launch_epi<KMX>(g, st) : launch_epi<KF8>(g, st);
 }
@@ -889,10 +942,8 @@ int launch_gemm_w4a4(const uint8_t* a, const uint8_t* a_e8, const uint8_t* w, co
     g.tiles_m = (M + BM - 1) / BM;
     g.tiles_n = (N + BN - 1) / BN;
     g.epi = epi;
-    static const char* epi_name[] = {"f32", "bf16", "resid_gate", "gelu", "qkv", "gelu_e4m3"};
     char key[96];
-    snprintf(key, sizeof(key), "gemm_w4a4_%s_%dx%dx%d",
-             (epi.mode >= 0 && epi.mode < 6) ? epi_name[epi.mode] : "?", M, N, K);
+    snprintf(key, sizeof(key), "gemm_w4a4_%s_%dx%dx%d", epi_name(epi.mode), M, N, K);
     TimingScope ts(key, st);
     return launch_epi<KW4A4>(g, st);
 }
@@ -915,7 +966,7 @@ static int validate_gemm(const char* fn, const uint8_t* a, const void* s_a, cons
         QVD_REQUIRE(a && aligned16(a), QVD_EINVAL, "%s: a is NULL or misaligned", fn);
         QVD_REQUIRE(s_a != nullptr, QVD_EINVAL, "%s: activation scale is NULL", fn);
     }
-    QVD_REQUIRE(epi->mode >= QVD_EPI_F32 && epi->mode <= QVD_EPI_GELU_E4M3, QVD_EINVAL,
+    QVD_REQUIRE(epi->mode >= QVD_EPI_F32 && epi->mode <= QVD_EPI_GELU_MXFP4, QVD_EINVAL,
                 "%s: unknown epilogue mode %d", fn, epi->mode);
     if (M == 0) return QVD_OK;   // nothing is read or written
     switch (epi->mode) {
@@ -934,6 +985,10 @@ static int validate_gemm(const char* fn, const uint8_t* a, const void* s_a, cons
         case QVD_EPI_GELU_E4M3:
             QVD_REQUIRE(epi->out_e4m3 && aligned16(epi->out_e4m3) && epi->out_scale, QVD_EINVAL,
                         "%s: out_e4m3 NULL/misaligned or out_scale NULL", fn);
+            break;
+        case QVD_EPI_GELU_MXFP4:
+            QVD_REQUIRE(epi->out_e2m1 && aligned16(epi->out_e2m1) && epi->out_e8m0, QVD_EINVAL,
+                        "%s: out_e2m1 NULL/misaligned or out_e8m0 NULL", fn);
             break;
         case QVD_EPI_QKV:
             QVD_REQUIRE(epi->n_heads >= 1 && N == 3 * 128 * epi->n_heads, QVD_ESHAPE,

@@ -166,14 +166,7 @@ __global__ void __launch_bounds__(256) k_quant_int8_qk(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------------------------
-// MXFP4 weights: one thread per 32-element block (OCP MX v1.0 shared-exponent rule).
-
-QVD_DEV u32 e2m1_encode(float v) {
-    const float a = fabsf(v);
-    u32 c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-          : a <= 2.5f  ? 4u : a < 3.5f  ? 5u : a <= 5.0f  ? 6u : 7u;
-    return c | ((__float_as_uint(v) >> 28) & 8u);
-}
+// MXFP4 (weights, or activations per token row): one thread per 32-element block.
 
 __global__ void __launch_bounds__(256) k_quant_mxfp4(const uint16_t* __restrict__ w, int N, int K,
                                                      uint8_t* __restrict__ packed,
@@ -191,21 +184,11 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4(const uint16_t* __restrict_
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(ws[j])), fabsf(bf16hi(ws[j]))));
-    int k = 0;
-    if (amax > 0.0f) {
-        int e;
-        frexpf(amax, &e);
-        k = e - 1 - 2;
-        k = k < -127 ? -127 : (k > 127 ? 127 : k);
-    }
+    const int k = mx_exponent(amax);
     e8[b] = (uint8_t)(k + 127);
     u32 o[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const u32 lo = e2m1_encode(ldexpf(bf16lo(ws[j]), -k));
-        const u32 hi = e2m1_encode(ldexpf(bf16hi(ws[j]), -k));
-        o[j >> 2] |= (lo | (hi << 4)) << ((j & 3) * 8);
-    }
+    for (int j = 0; j < 16; ++j) o[j >> 2] |= e2m1_encode2(bf16lo(ws[j]), bf16hi(ws[j]), k) << ((j & 3) * 8);
     *reinterpret_cast<u32x4*>(packed + b * 16) = (u32x4){o[0], o[1], o[2], o[3]};
 }
 

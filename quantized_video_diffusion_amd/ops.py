@@ -111,6 +111,18 @@ def adaln_modulate(x: torch.Tensor, mod: torch.Tensor, half: int, eps: float = 1
     return q, s
 
 
+def adaln_modulate_mxfp4(x: torch.Tensor, mod: torch.Tensor, half: int, eps: float = 1e-6):
+    """bf16 [L][d] -> (packed E2M1 uint8 [L][d/2], E8M0 uint8 [L][d/32])."""
+    _check(x, torch.bfloat16, "x")
+    _check(mod, torch.float32, "mod")
+    L, d = x.shape
+    packed = _empty((L, d // 2), torch.uint8, x)
+    e8 = _empty((L, d // 32), torch.uint8, x)
+    call("adaln_modulate_mxfp4", _ptr(x), L, d, _ptr(mod), half, float(eps), _ptr(packed), _ptr(e8),
+         _stream())
+    return packed, e8
+
+
 def sparse_attn(q8, q_scale, k8, k_scale, v, kv_idx, kv_cnt, sm_scale: float = SM_SCALE,
                 want_amax: bool = False):
     """int8 Q/K [L][H][128], fp32 scales [H][T], bf16 V [L][H][128], int32 masks -> bf16 out."""
@@ -141,6 +153,18 @@ def sparse_attn_vt_e4m3(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, out_scale,
          _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(out_scale), _ptr(out),
          _stream())
     return out
+
+
+def sparse_attn_vt_mxfp4(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, sm_scale: float = SM_SCALE):
+    """As sparse_attn_vt, returning the MXFP4 codes of bf16 O per (token, head, 32 dims) instead of
+    O: (packed E2M1 uint8 [L][H*64], E8M0 uint8 [L][H*4])."""
+    L, H, D = q8.shape
+    _check(vt, torch.float16, "vt")
+    packed = torch.empty((L, H * D // 2), dtype=torch.uint8, device=q8.device)
+    e8 = torch.empty((L, H * D // 32), dtype=torch.uint8, device=q8.device)
+    call("qvd_sparse_attn_vt_mxfp4", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt), L, H,
+         _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(packed), _ptr(e8), _stream())
+    return packed, e8
 
 
 def sparse_attn_vt(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, sm_scale: float = SM_SCALE,
@@ -224,6 +248,12 @@ def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, 
         e.out_e4m3 = out.data_ptr()
         e.out_scale = out_scale.data_ptr()
         ret = out
+    elif mode == _lib.QVD_EPI_GELU_MXFP4:
+        packed = torch.empty((M, N // 2), dtype=torch.uint8, device=a.device)
+        e8 = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
+        e.out_e2m1 = packed.data_ptr()
+        e.out_e8m0 = e8.data_ptr()
+        ret = (packed, e8)
     elif mode == _lib.QVD_EPI_RESID_GATE:
         e.out_bf16 = out.data_ptr()
         e.resid = resid.data_ptr()
@@ -284,7 +314,7 @@ def calibrated_scale(amax: float) -> np.float32:
 @dataclass
 class BlockWeights:
     """Device weights of one block.  FP8: E4M3 codes [N][K] + fp32 scale [1] per site.
-    MXFP4: packed E2M1 [N][K/2] + E8M0 [N][K/32] per site (scales unused)."""
+    MXFP4 and MXFP4_A4 (W4A4): packed E2M1 [N][K/2] + E8M0 [N][K/32] per site (scales unused)."""
     d: int
     n_heads: int
     mlp: int

@@ -73,6 +73,12 @@ def test_host_validation_errors(lib):
                    fake, 1 << 20, None) == _lib.QVD_ESHAPE
     assert _status(lib, "adaln_modulate", fake, 4, 256, fake, 0, C.c_float(1e-6), None, fake, fake,
                    fake, 8, None) == _lib.QVD_EWORKSPACE
+    assert _status(lib, "adaln_modulate_mxfp4", fake, 4, 200, fake, 0, C.c_float(1e-6), fake, fake,
+                   None) == _lib.QVD_ESHAPE
+    assert _status(lib, "adaln_modulate_mxfp4", fake, 4, 256, fake, 2, C.c_float(1e-6), fake, fake,
+                   None) == _lib.QVD_EINVAL
+    assert _status(lib, "adaln_modulate_mxfp4", fake, 4, 256, fake, 0, C.c_float(1e-6), fake, None,
+                   None) == _lib.QVD_EINVAL
     # sparse_attn
     big = 1 << 30
     assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 300, 2, 64, fake, fake, 3,
@@ -88,6 +94,10 @@ def test_host_validation_errors(lib):
     assert lib.qvd_sparse_attn_ws_bytes(300, 2) == 2 * 128 * 384 * 2
     assert _status(lib, "qvd_sparse_attn_vt", fake, fake, fake, fake, mis, 300, 2, fake, fake, 3,
                    C.c_float(0.1), fake, None, None) == _lib.QVD_EALIGN
+    assert _status(lib, "qvd_sparse_attn_vt_mxfp4", fake, fake, fake, fake, fake, 300, 2, fake, fake, 3,
+                   C.c_float(0.1), fake, P(0x10002), None) == _lib.QVD_EALIGN
+    assert _status(lib, "qvd_sparse_attn_vt_mxfp4", fake, fake, fake, fake, fake, 300, 2, fake, fake, 3,
+                   C.c_float(0.1), fake, None, None) == _lib.QVD_EINVAL
     assert _status(lib, "qvd_qk_int32_tile", fake, fake, 300, 2, 2, 0, 0, fake, None) == _lib.QVD_EINVAL
     assert _status(lib, "qvd_qk_int32_tile", fake, fake, 300, 2, 0, 3, 0, fake, None) == _lib.QVD_EINVAL
     # GEMM
@@ -102,6 +112,12 @@ def test_host_validation_errors(lib):
     e.n_heads = 2
     assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 10, 512, 128, C.byref(e), None) == _lib.QVD_ESHAPE
     assert lib.qvd_gemm_tiles(33784, 8064) == 132 * 32
+    e.mode = _lib.QVD_EPI_GELU_MXFP4
+    e.out_e2m1 = 0x10000
+    assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 10, 128, 128, C.byref(e), None) == _lib.QVD_EINVAL
+    e.out_e8m0 = 0x10000
+    e.out_e2m1 = 0x10008
+    assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 10, 128, 128, C.byref(e), None) == _lib.QVD_EINVAL
     e.mode = _lib.QVD_EPI_F32
     e.out_f32 = 0x10000
     assert _status(lib, "qvd_gemm_mxfp4_w4a4", fake, fake, fake, fake, None, 10, 128, 96, C.byref(e), None) == _lib.QVD_ESHAPE
@@ -118,6 +134,10 @@ def test_host_validation_errors(lib):
     assert lib.qvd_block_ws_bytes(C.byref(p), 256) > 0
     assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 256, fake, fake, 2, fake, 16, None) == _lib.QVD_EWORKSPACE
     p.weight_format = _lib.QVD_W_MXFP4
+    assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 256, fake, fake, 2, fake, 1 << 40, None) == _lib.QVD_EINVAL
+    p.weight_format = _lib.QVD_W_MXFP4_A4        # W4A4 needs the E8M0 weight scales, not act_scale
+    assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 256, fake, fake, 2, fake, 1 << 40, None) == _lib.QVD_EINVAL
+    p.weight_format = 3
     assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 256, fake, fake, 2, fake, 1 << 40, None) == _lib.QVD_EINVAL
     p.weight_format = _lib.QVD_W_FP8
     p.d = 300

@@ -8,8 +8,9 @@ import torch
 import workloads as W
 import quantized_video_diffusion_amd as Q
 from quantized_video_diffusion_amd import _lib
-from oracle import quant as OQ, gemm as OG
-from _gpu_util import say, bf16_dev, u8_dev, f32_dev, host, host_bits, assert_close_rms, assert_bf16_close
+from oracle import codecs as OC, quant as OQ, gemm as OG, adaln as OA, attention as OAT
+from _gpu_util import (say, bf16_dev, u8_dev, i32_dev, f32_dev, host, host_bits, assert_close_rms,
+                       assert_bf16_close)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +109,84 @@ def test_w4a4_768p_mlp_up_shape_sampled():
     oap, oae = OQ.quant_mxfp4_weight(xb[rows])
     want = OG.gemm_mxfp4_w4a4(oap, oae, wp, we)
     assert_close_rms(got, want, 1e-3, "w4a4 768p rows")
+
+
+# --- MXFP4 producers of the W4A4 block -------------------------------------------------------------
+
+@pytest.mark.parametrize("d,L,half", [(256, 300, 0), (2688, 133, 1), (1024, 64, 0)])
+def test_adaln_modulate_mxfp4_bit_exact(d, L, half):
+    """Modulated LayerNorm -> MXFP4: the kernel forms y as the float64 modulation rounded once to fp32,
+    as the oracle does, so codes and block scales agree bit for bit."""
+    say("modulate mxfp4", d, L, half)
+    w = W.Workload("m", 60 + d // 128, d=d, n_heads=d // 128, mlp=4 * d, L=L, sparse=False,
+                   outliers=d >= 1000)
+    x = W.activations(w, 3, L=L)
+    mod = W.random_mod(d, seed=4, tag=w.tag)
+    p, e = Q.adaln_modulate_mxfp4(bf16_dev(x), f32_dev(mod), half)
+    op, oe = OA.adaln_modulate_mxfp4(x, mod, half)
+    np.testing.assert_array_equal(host(e), oe)
+    np.testing.assert_array_equal(host(p), op)
+
+
+def _vt_dev(vb, L, H):
+    T = (L + 127) // 128
+    vt = np.zeros((H, 128, T * 128), np.float16)
+    vt[:, :, :L] = OC.bf16_to_f64(vb).transpose(1, 2, 0).astype(np.float16)
+    return torch.from_numpy(vt).cuda()
+
+
+@pytest.mark.parametrize("L,H,sparse", [(1290, 2, True), (391, 3, False)])
+def test_sparse_attn_mxfp4_output(L, H, sparse):
+    """The MXFP4 entry equals, bit for bit, quant_mxfp4 of the bf16 entry's output viewed as
+    [L][H*128]; dequantized, it lies within half an E2M1 step (or the saturation at 6 X) of the
+    oracle attention, up to the attention's own 1e-2 RMS tolerance."""
+    say("attn mxfp4", L, H, sparse)
+    qb, kb, vb = W.qkv_heads(L, H, seed=L)
+    wl = W.Workload("t", 90 + H, d=128 * H, n_heads=H, mlp=512 * H, L=L, sparse=sparse, outliers=False)
+    idx, cnt = W.block_mask(wl, seed=L, L=L)
+    q8, qs = Q.quant_int8_qk(bf16_dev(qb.reshape(L, H * 128)), H)
+    k8, ks = Q.quant_int8_qk(bf16_dev(kb.reshape(L, H * 128)), H)
+    vt = _vt_dev(vb, L, H)
+    out = Q.sparse_attn_vt(q8, qs, k8, ks, vt, i32_dev(idx), i32_dev(cnt))
+    p, e = Q.sparse_attn_vt_mxfp4(q8, qs, k8, ks, vt, i32_dev(idx), i32_dev(cnt))
+    p2, e2 = Q.quant_mxfp4(out.reshape(L, H * 128))
+    np.testing.assert_array_equal(host(e), host(e2))
+    np.testing.assert_array_equal(host(p), host(p2))
+    oq, oqs = OQ.quant_int8_qk(qb, L, H)
+    ok, oks = OQ.quant_int8_qk(kb, L, H)
+    want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx, cnt).reshape(L, H * 128)
+    deq = OG.dequant_mxfp4(host(p), host(e))
+    X = np.repeat(OC.e8m0_decode(host(e)), 32, axis=1)
+    r = np.abs(want) / X
+    half_step = np.where(r < 2, 0.25, np.where(r < 4, 0.5, 1.0)) * X
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    err = np.abs(deq - np.clip(want, -6 * X, 6 * X))
+    assert (err <= half_step + 1e-2 * rms).all(), f"worst {float((err - half_step).max()):.3e}, RMS {rms:.3e}"
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("w4a4", 391, 768, 512), ("w4a4", 256, 256, 2688), ("fp8", 333, 1024, 256)])
+def test_gemm_gelu_mxfp4_epilogue(fmt, M, N, K):
+    """GELU -> bf16 -> MXFP4 in the epilogue equals, bit for bit, the GELU epilogue followed by
+    quant_mxfp4; and the W4A4 chain agrees with the oracle's within half an E2M1 step (1% of the
+    elements may sit one step off where GELU lands within the accumulation error of a midpoint)."""
+    say("gelu mxfp4", fmt, M, N, K)
+    wp, we = _weights(N, K, N + K)
+    bias = np.linspace(-1, 1, N).astype(np.float32)
+    if fmt == "w4a4":
+        ap, ae = OQ.quant_mxfp4_weight(_acts(M, K, 31))
+        args = (u8_dev(ap), u8_dev(ae), u8_dev(wp), u8_dev(we))
+        gm = Q.gemm_mxfp4_w4a4
+        lin = OG.gemm_mxfp4_w4a4(ap, ae, wp, we, bias)
+    else:
+        a, w8 = W.random_e4m3_codes((M, K), seed=6), W.random_e4m3_codes((N, K), seed=7, tensor="codes_b")
+        args = (u8_dev(a), f32_dev([np.float32(0.002)]), u8_dev(w8), f32_dev([np.float32(0.003)]))
+        gm = Q.gemm_fp8
+        lin = OG.gemm_fp8(a, np.float32(0.002), w8, np.float32(0.003), bias)
+    g = gm(*args, bias=f32_dev(bias), mode=_lib.QVD_EPI_GELU)
+    p, e = gm(*args, bias=f32_dev(bias), mode=_lib.QVD_EPI_GELU_MXFP4)
+    p2, e2 = Q.quant_mxfp4(g)
+    np.testing.assert_array_equal(host(e), host(e2))
+    np.testing.assert_array_equal(host(p), host(p2))
+    op, oe = OQ.quant_mxfp4_weight(OC.f64_to_bf16(OG.gelu(lin)))
+    same = (OQ.unpack_e2m1(host(p)) == OQ.unpack_e2m1(op)) & np.repeat(host(e) == oe, 32, axis=1)
+    assert same.mean() >= 0.99, f"{1 - same.mean():.4f} of the codes differ from the oracle's"
