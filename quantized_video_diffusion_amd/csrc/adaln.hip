@@ -261,7 +261,7 @@ template <int NW>
 __global__ void __launch_bounds__(256) k_ln_mx(const uint16_t* __restrict__ x, int L, int d,
                                                const float* __restrict__ mod, int half, float eps,
                                                uint8_t* __restrict__ packed, uint8_t* __restrict__ e8m0) {
-    __shared__ float4 tab[4096 / 2];
+    __shared__ float4 tab[64 * NW];            // sized for the row width: more workgroups per CU
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int nw = d >> 7;
     load_mod_table(tab, mod, half, d, false, 1.0f);

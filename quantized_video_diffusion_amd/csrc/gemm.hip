@@ -263,9 +263,9 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
 #pragma unroll
             for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(ws[j])), fabsf(bf16hi(ws[j]))));
             const int k = mx_exponent(amax);
-            u32 o[4] = {0u, 0u, 0u, 0u};
+            u32 o[4];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[j >> 2] |= e2m1_encode2(bf16lo(ws[j]), bf16hi(ws[j]), k) << ((j & 3) * 8);
+            for (int j = 0; j < 4; ++j) o[j] = e2m1_encode8_bf16(ws + 4 * j, k);
             const int m = mw0 + ml;
             if (m < M) {
                 *reinterpret_cast<u32x4*>(ep.out_e2m1 + (int64_t)m * Nh + (nw0 + 32 * bk) / 2) =

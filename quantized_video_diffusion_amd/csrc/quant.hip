@@ -186,9 +186,9 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4(const uint16_t* __restrict_
     for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(ws[j])), fabsf(bf16hi(ws[j]))));
     const int k = mx_exponent(amax);
     e8[b] = (uint8_t)(k + 127);
-    u32 o[4] = {0, 0, 0, 0};
+    u32 o[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[j >> 2] |= e2m1_encode2(bf16lo(ws[j]), bf16hi(ws[j]), k) << ((j & 3) * 8);
+    for (int j = 0; j < 4; ++j) o[j] = e2m1_encode8_bf16(ws + 4 * j, k);
     *reinterpret_cast<u32x4*>(packed + b * 16) = (u32x4){o[0], o[1], o[2], o[3]};
 }
 
