@@ -183,6 +183,26 @@ int qvd_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int8_t
                              const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
                              uint8_t* out_packed, uint8_t* out_e8m0, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Sparse-tile selector -- "Trim 改变了什么", training bullet (80% attention sparsity; the pages do
+ * not say how the kept tiles are chosen).  The rule: per head h and 128-token query tile i, key
+ * tile j is ranked by the dot product of the mean-pooled, dequantized query and key tiles,
+ *   score(h, i, j) = (sq[h][i] / n_i)(sk[h][j] / n_j) sum_e Qsum[h][i][e] Ksum[h][j][e]
+ * (Qsum, Ksum: sums of the INT8 codes over the tile's n rows that exist); the diagonal is always
+ * kept and the kept - 1 best other tiles join it (equal scores: lower j first).  The rank is taken
+ * on D * w, D the exact integer dot of the code sums and w = double(sk[h][j]) / n_j, each rounded
+ * once in float64, so it is reproducible bit for bit.
+ *   q, k    : int8 [L][H][128] (the INT8 Q/K of quant_int8_qk or the QKV epilogue), 16-byte aligned
+ *   k_scale : fp32 [H][T]
+ *   kv_idx  : int32 [H][T][kept], out: the kept tiles in ascending order, then -1
+ *   kv_cnt  : int32 [H][T], out: min(kept, T)
+ *   ws      : qvd_select_tiles_ws_bytes(L, H) bytes (the code sums and the [H][T][T] scores)
+ * L <= 131,072 (T <= 1024), 1 <= kept <= 1024. */
+size_t qvd_select_tiles_ws_bytes(int32_t L, int32_t H);
+int qvd_select_tiles(const int8_t* q, const int8_t* k, const float* k_scale, int32_t L, int32_t H,
+                     int32_t kept, int32_t* kv_idx, int32_t* kv_cnt, void* ws, size_t ws_bytes,
+                     void* stream);
+
 /* Exact INT32 accumulators Q8[rows of tile i] . K8[rows of tile j]^T of head h, computed by the
  * same INT8 MFMA tile routine the attention kernel uses, into out int32 [128][128]
  * (out[r][c] = query row i*128+r, key row j*128+c; rows/keys >= L are written as 0). */
@@ -289,7 +309,8 @@ typedef struct {
 size_t qvd_block_ws_bytes(const qvd_block_params* p, int32_t L);
 /* x: bf16 [L][d], read and overwritten with the block output.  mod: fp32 [6][d] of this block at
  * this timestep (qvd_adaln_project).  kv_idx/kv_cnt/kmax: the block's sparse mask as in
- * sparse_attn. */
+ * sparse_attn; or kv_idx = kv_cnt = NULL: the block selects min(kmax, T) key tiles per query tile
+ * from its own INT8 Q/K by the qvd_select_tiles rule, in the workspace. */
 int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
                       const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, void* ws,
                       size_t ws_bytes, void* stream);
@@ -313,7 +334,7 @@ int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* coun
  * bracketed by a pair of HIP events recorded on the launch's own stream.  qvd_timing_report waits
  * for the recorded work, writes {"<kernel key>": {"count": n, "total_ms": t}, ...} (NUL-terminated
  * JSON) into buf and clears the records.  Keys: "sparse_attn", "adaln_modulate", "adaln_project",
- * "adaln_modulate_mxfp4", "quant_fp8", "amax_bf16", "quant_int8_qk", "gemm_<fp8|mxfp4|w4a4>_<epilogue>_<M>x<N>x<K>".
+ * "adaln_modulate_mxfp4", "quant_fp8", "amax_bf16", "quant_int8_qk", "select_tiles", "gemm_<fp8|mxfp4|w4a4>_<epilogue>_<M>x<N>x<K>".
  * Returns QVD_EINVAL if len is too small (the records are then lost), QVD_EHIP on event errors. */
 int qvd_timing_enable(int on);
 int qvd_timing_report(char* buf, size_t len);

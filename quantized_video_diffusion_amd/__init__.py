@@ -7,7 +7,7 @@ library; the first call does, and fails loudly if the library has not been built
 from . import _lib  # noqa: F401
 from .ops import (  # noqa: F401
     quant_fp8_per_tensor, quant_int8_qk, adaln_project, adaln_modulate, adaln_modulate_mxfp4, sparse_attn,
-    sparse_attn_vt, sparse_attn_vt_e4m3, sparse_attn_vt_mxfp4, qk_int32_tile,
+    sparse_attn_vt, sparse_attn_vt_e4m3, sparse_attn_vt_mxfp4, qk_int32_tile, select_tiles,
     gemm_fp8, gemm_mxfp4, gemm_mxfp4_w4a4, gemm_tiles, quant_mxfp4, amax_update, clip_count, BlockWeights,
     quantize_block_weights, block_ws_bytes, dit_block_forward, from_bits, to_bits, timing_enable, timing_report,
     calibrated_scale,

@@ -68,6 +68,8 @@ SIGNATURES = {
                                           _p]),
     "qvd_sparse_attn_vt_mxfp4": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p,
                                            _p]),
+    "qvd_select_tiles_ws_bytes": (_sz, [_i32, _i32]),
+    "qvd_select_tiles": (C.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p, _sz, _p]),
     "qvd_qk_int32_tile": (C.c_int, [_p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "qvd_gemm_tiles": (_i64, [_i32, _i32]),
     "qvd_gemm_fp8": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(Epilogue), _p]),

@@ -51,6 +51,9 @@ struct BlockWs {
     float* gelu_part;    // [tiles of the up GEMM]
     float* scales;       // [4]: s_h1, s_o, s_h2, s_g
     void* ln_ws;         // adaln_modulate workspace
+    int32_t* sel_idx;    // selected mask [H][T][min(kmax, T)] (when the caller passes none)
+    int32_t* sel_cnt;    // [H][T]
+    void* sel_ws;        // selector workspace
     size_t total;
 };
 
@@ -83,6 +86,9 @@ BlockWs carve(const qvd_block_params* p, int L, uint8_t* base) {
     w.gelu_part = (float*)take(4 * (size_t)gemm_tiles(L, p->mlp));
     w.scales = (float*)take(4 * 4);
     w.ln_ws = take(adaln_ws_bytes(L, p->d));
+    w.sel_idx = (int32_t*)take(4 * HT * (size_t)T);
+    w.sel_cnt = (int32_t*)take(4 * HT);
+    w.sel_ws = take(select_ws_bytes(L, p->n_heads));
     w.total = off;
     return w;
 }
@@ -151,13 +157,18 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     if (L == 0) return QVD_OK;
     QVD_PTR(mod);
     QVD_PTR(x);
-    QVD_PTR(kv_idx);
-    QVD_PTR(kv_cnt);
+    const bool select = kv_idx == nullptr && kv_cnt == nullptr;   // the block chooses its mask
+    if (!select) {
+        QVD_PTR(kv_idx);
+        QVD_PTR(kv_cnt);
+    }
     QVD_PTR(ws);
     QVD_ALIGN(mod);
     QVD_ALIGN(x);
     QVD_ALIGN(ws);
     QVD_REQUIRE(kmax >= 1 && kmax <= 1024, QVD_ESHAPE, "dit_block_forward: kmax = %d (1 .. 1024)", kmax);
+    QVD_REQUIRE(!select || L <= 131072, QVD_ESHAPE,
+                "dit_block_forward: L = %d; the block selects its mask for L <= 131,072 only", L);
     const size_t need = qvd_block_ws_bytes(p, L);
     QVD_REQUIRE(ws_bytes >= need, QVD_EWORKSPACE, "dit_block_forward: workspace %zu < %zu bytes",
                 ws_bytes, need);
@@ -171,6 +182,15 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     const float* act = p->act_scale;           // NULL: dynamic
     const float* shift_scale_gate = mod;       // [6][d]
     const float sm_scale = 0.08838834764831845f;   // 1/sqrt(128)
+    // with no mask given, the selector picks min(kmax, T) tiles per row from the block's own INT8 Q/K
+    // (after the QKV GEMM) into the workspace; its row length is then the attention's kmax
+    if (select) kmax = kmax < T ? kmax : T;
+    auto select_mask = [&]() -> int {
+        if (!select) return QVD_OK;
+        kv_idx = w.sel_idx;
+        kv_cnt = w.sel_cnt;
+        return launch_select_tiles(w.q8, w.k8, w.ks, L, H, kmax, w.sel_idx, w.sel_cnt, w.sel_ws, st);
+    };
 
     if (fmt == QVD_W_MXFP4_A4) {
         s = launch_modulate_mx(x, L, d, mod, 0, p->ln_eps, w.h, w.h_e8, st);
@@ -184,6 +204,8 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
         e.q_scale = w.qs;
         e.k_scale = w.ks;
         s = launch_gemm_w4a4(w.h, w.h_e8, (const uint8_t*)p->w_qkv, p->e8m0_qkv, p->b_qkv, L, 3 * d, d, e, st);
+        if (s) return s;
+        s = select_mask();
         if (s) return s;
         s = launch_sparse_attn_vt_mxfp4(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.h,
                                         w.h_e8, st);
@@ -224,6 +246,8 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     e.q_scale = w.qs;
     e.k_scale = w.ks;
     s = launch_gemm(w.h, w.scales + 0, p->w_qkv, p->e8m0_qkv, p->s_qkv, fmt, p->b_qkv, L, 3 * d, d, e, st);
+    if (s) return s;
+    s = select_mask();
     if (s) return s;
     if (act) {
         s = launch_sparse_attn_vt_e4m3(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale,

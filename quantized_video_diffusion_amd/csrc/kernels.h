@@ -46,4 +46,9 @@ int launch_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int
                                 uint8_t* out_packed, uint8_t* out_e8m0, hipStream_t st);
 size_t vt_bytes(int L, int H);
 
+// sparse-tile selector: kv_idx [H][T][kept] (-1 past the count), kv_cnt [H][T]
+size_t select_ws_bytes(int L, int H);
+int launch_select_tiles(const int8_t* q8, const int8_t* k8, const float* k_scale, int L, int H, int kept,
+                        int32_t* kv_idx, int32_t* kv_cnt, void* ws, hipStream_t st);
+
 }  // namespace qvd

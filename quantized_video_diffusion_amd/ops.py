@@ -362,21 +362,43 @@ def block_ws_bytes(bw: BlockWeights, L: int) -> int:
     return int(_lib.lib().qvd_block_ws_bytes(C.byref(p), L))
 
 
-def dit_block_forward(bw: BlockWeights, mod: torch.Tensor, x: torch.Tensor, kv_idx: torch.Tensor,
-                      kv_cnt: torch.Tensor, ws: torch.Tensor | None = None) -> torch.Tensor:
-    """x bf16 [L][d] is updated in place with the block output (and returned)."""
+def dit_block_forward(bw: BlockWeights, mod: torch.Tensor, x: torch.Tensor, kv_idx: torch.Tensor | None,
+                      kv_cnt: torch.Tensor | None, ws: torch.Tensor | None = None,
+                      kmax: int | None = None) -> torch.Tensor:
+    """x bf16 [L][d] is updated in place with the block output (and returned).  With kv_idx and kv_cnt
+    None the block selects kmax key tiles per query tile itself (select_tiles' rule)."""
     _check(x, torch.bfloat16, "x")
     _check(mod, torch.float32, "mod")
-    _check(kv_idx, torch.int32, "kv_idx")
-    _check(kv_cnt, torch.int32, "kv_cnt")
+    if kv_idx is None:
+        assert kv_cnt is None and kmax is not None, "pass both masks, or neither and kmax"
+    else:
+        _check(kv_idx, torch.int32, "kv_idx")
+        _check(kv_cnt, torch.int32, "kv_cnt")
+        kmax = kv_idx.shape[-1]
     L = x.shape[0]
     p = bw.params()
     need = int(_lib.lib().qvd_block_ws_bytes(C.byref(p), L))
     if ws is None:
         ws = torch.empty((need,), dtype=torch.uint8, device=x.device)
     call("dit_block_forward", C.byref(p), _ptr(mod), _ptr(x), L, _ptr(kv_idx), _ptr(kv_cnt),
-         kv_idx.shape[-1], _ptr(ws), ws.numel(), _stream())
+         int(kmax), _ptr(ws), ws.numel(), _stream())
     return x
+
+
+def select_tiles(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor, kept: int):
+    """int8 Q/K [L][H][128] and K scales [H][T] -> (kv_idx int32 [H][T][kept], kv_cnt int32 [H][T]):
+    the diagonal and the kept - 1 key tiles of highest mean-pooled score, in tile order."""
+    _check(q8, torch.int8, "q8")
+    _check(k8, torch.int8, "k8")
+    _check(k_scale, torch.float32, "k_scale")
+    L, H, _ = q8.shape
+    T = (L + 127) // 128
+    idx = torch.empty((H, T, kept), dtype=torch.int32, device=q8.device)
+    cnt = torch.empty((H, T), dtype=torch.int32, device=q8.device)
+    ws = torch.empty((int(_lib.lib().qvd_select_tiles_ws_bytes(L, H)),), dtype=torch.uint8, device=q8.device)
+    call("qvd_select_tiles", _ptr(q8), _ptr(k8), _ptr(k_scale), L, H, kept, _ptr(idx), _ptr(cnt), _ptr(ws),
+         ws.numel(), _stream())
+    return idx, cnt
 
 
 # ----------------------------------------------------------------------------------------------

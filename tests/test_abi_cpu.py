@@ -98,6 +98,11 @@ def test_host_validation_errors(lib):
                    C.c_float(0.1), fake, P(0x10002), None) == _lib.QVD_EALIGN
     assert _status(lib, "qvd_sparse_attn_vt_mxfp4", fake, fake, fake, fake, fake, 300, 2, fake, fake, 3,
                    C.c_float(0.1), fake, None, None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_select_tiles", fake, fake, fake, 300, 2, 0, fake, fake, fake, big, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "qvd_select_tiles", fake, fake, fake, 131073, 2, 4, fake, fake, fake, big, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "qvd_select_tiles", fake, fake, fake, 300, 2, 4, fake, None, fake, big, None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_select_tiles", fake, fake, fake, 300, 2, 4, fake, fake, fake, 16, None) == _lib.QVD_EWORKSPACE
+    assert lib.qvd_select_tiles_ws_bytes(300, 2) == 2 * 2 * 3 * 128 * 4 + 2 * 3 * 3 * 8
     assert _status(lib, "qvd_qk_int32_tile", fake, fake, 300, 2, 2, 0, 0, fake, None) == _lib.QVD_EINVAL
     assert _status(lib, "qvd_qk_int32_tile", fake, fake, 300, 2, 0, 3, 0, fake, None) == _lib.QVD_EINVAL
     # GEMM
