@@ -175,6 +175,26 @@ def recorded_traffic(kernel):
     return rec["traffic_bytes_per_launch"]
 
 
+def time_selector(L, H, kept, seed, reps=5):
+    """Mean ms of qvd_select_tiles over all heads at L tokens (INT8 Q/K drawn on the device)."""
+    import torch
+    import quantized_video_diffusion_amd as Q
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    T = (L + 127) // 128
+    q8 = torch.randint(-127, 128, (L, H, 128), dtype=torch.int8, device="cuda", generator=g)
+    k8 = torch.randint(-127, 128, (L, H, 128), dtype=torch.int8, device="cuda", generator=g)
+    ks = torch.rand((H, T), device="cuda", generator=g) * 0.03 + 0.01
+    Q.select_tiles(q8, k8, ks, kept)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        Q.select_tiles(q8, k8, ks, kept)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) / reps, 4)
+
+
 def run_768p(seed, steps=5, warmup=2):
     """The 768p-shaped block (85,696 tokens) with MXFP4 weights and static activation scales
     calibrated on the GPU: 4 activation sites x 64 heavy-tailed batches x 1,024 tokens, the MLP-down
@@ -287,6 +307,7 @@ def run_768p(seed, steps=5, warmup=2):
             "kernels_ms": kern_ms,
             "w4a4": {"activations": "MXFP4 (E2M1 + dynamic E8M0 per token and 32 channels)",
                      "ms_per_block": round(ms4, 4), "TFLOP/s": round(tf4, 1), "kernels_ms": kern4},
+            "selector_ms": time_selector(L, H, w.kmax, seed),
             "calibration": {"batches": nb, "tokens_per_batch": tok, "A0": A0,
                             "outlier_site": sites[out_site][0], "outlier_ratio": 137.0,
                             "uncalibrated_scale": float(s_unc), "sites": calib,
@@ -440,6 +461,9 @@ def main():
         "kernels": breakdown,
         "setup_s": round(setup_s, 1),
     }
+    # the sparse-tile selector at this token count (all heads): what choosing the mask from the block's
+    # own Q/K would add per block; the timed steps above use the seeded masks
+    result["selector_ms_per_block"] = time_selector(L, w.n_heads, w.kmax, args.seed)
     if not args.no_768p:
         print("[bench] 768p MXFP4 block: calibration and timing ...", file=sys.stderr, flush=True)
         del blocks, ws

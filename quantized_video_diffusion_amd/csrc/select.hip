@@ -12,8 +12,8 @@
 //   k_tile_sums   : per (tile, head, Q|K) the int32 sums of the codes over the tile's rows
 //   k_tile_scores : D * w for 64 x 64 blocks of (i, j), exact: 24-bit integer products summed four at
 //                   a time in int32 (|sum| < 2^30), then in float64 (|D| < 2^36, so every sum is exact)
-//   k_select      : per (head, query tile) a bitonic sort of (descending score, tile) in LDS, then the
-//                   first `kept` tiles written in tile order
+//   k_select      : per (head, query tile) a radix select of the kept - 1 best keys (one byte per
+//                   pass), then the kept tiles written in tile order
 #include "common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -128,50 +128,96 @@ QVD_DEV unsigned long long ordered(double x) {
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// One workgroup per (query tile i, head h).  Keys: the diagonal first (0), then descending score
-// (~ordered), then the tile index; N = the next power of two >= T entries, padding last.
-__global__ void __launch_bounds__(256) k_select(const double* __restrict__ scores, int T, int N, int kept,
+// One workgroup per (query tile i, head h); thread tid owns tiles j = tid + 256 m.  Rank key of a tile
+// other than the diagonal: ~ordered(score), so that a smaller key is a better tile.  The need =
+// min(kept, T) - 1 smallest keys are found by a radix select, one byte per pass from the top: each
+// pass histograms the byte of the keys that still match the prefix, and the bin where the count
+// reaches `need` extends the prefix.  The result is the key K of the need-th best tile: every key
+// below K is kept, and of the keys equal to K the ones of lowest tile index until `need` is met.
+__global__ void __launch_bounds__(256) k_select(const double* __restrict__ scores, int T, int kept,
                                                 int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
-    __shared__ unsigned long long key[SEL_MAX_T];
-    __shared__ int tile[SEL_MAX_T];
+    __shared__ int hist[256];
     __shared__ int flag[SEL_MAX_T];
     __shared__ int wcount[4];
+    __shared__ int pick[2];
     const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const double* row = scores + ((int64_t)h * T + i) * T;
-    for (int j = tid; j < N; j += 256) {
-        unsigned long long k = ~0ull;
-        if (j < T) k = j == i ? 0ull : ~ordered(row[j]);
-        key[j] = k;
-        tile[j] = j;
-        flag[j] = 0;
+    constexpr int M = SEL_MAX_T / 256;
+    unsigned long long key[M];
+    bool live[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int j = tid + 256 * m;
+        live[m] = j < T && j != i;
+        key[m] = live[m] ? ~ordered(row[j]) : ~0ull;
     }
+    for (int j = tid; j < SEL_MAX_T; j += 256) flag[j] = 0;
     __syncthreads();
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int s = k >> 1; s > 0; s >>= 1) {
-            for (int a = tid; a < N; a += 256) {
-                const int b = a ^ s;
-                if (b > a) {
-                    const unsigned long long ka = key[a], kb = key[b];
-                    const int ta = tile[a], tb = tile[b];
-                    const bool a_after_b = ka > kb || (ka == kb && ta > tb);
-                    if (((a & k) == 0) == a_after_b) {      // ascending runs where (a & k) == 0
-                        key[a] = kb;
-                        key[b] = ka;
-                        tile[a] = tb;
-                        tile[b] = ta;
+    const int cnt = kept < T ? kept : T;
+    int need = cnt - 1;
+    unsigned long long prefix = 0ull, hmask = 0ull;
+    if (need > 0) {
+        for (int p = 7; p >= 0; --p) {
+            hist[tid] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                if (live[m] && (key[m] & hmask) == prefix) atomicAdd(&hist[(int)((key[m] >> (8 * p)) & 0xFFull)], 1);
+            __syncthreads();
+            if (wv == 0) {
+                // lane l holds bins 4l .. 4l+3: inclusive scan over the wave, then the bin that reaches `need`
+                int c[4], run = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    run += hist[4 * lane + q];
+                    c[q] = run;
+                }
+                int incl = run;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int t = __shfl_up(incl, o, 64);
+                    if (lane >= o) incl += t;
+                }
+                const int before = incl - run;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int lo = before + (q == 0 ? 0 : c[q - 1]), hi = before + c[q];
+                    if (lo < need && need <= hi) {
+                        pick[0] = 4 * lane + q;
+                        pick[1] = lo;
                     }
                 }
             }
             __syncthreads();
+            const int d = pick[0];
+            need -= pick[1];
+            prefix |= (unsigned long long)d << (8 * p);
+            hmask |= 0xFFull << (8 * p);
+        }
+        // keep every key below the threshold; of the keys equal to it, the first `need` in tile order
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            if (live[m] && key[m] < prefix) flag[tid + 256 * m] = 1;
+        int taken = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const bool eq = live[m] && key[m] == prefix;
+            const unsigned long long b = __ballot(eq);
+            __syncthreads();
+            if (lane == 0) wcount[wv] = __popcll(b);
+            __syncthreads();
+            int off = taken;
+            for (int w = 0; w < wv; ++w) off += wcount[w];
+            if (eq && off + __popcll(b & ((1ull << lane) - 1ull)) < need) flag[tid + 256 * m] = 1;
+            taken += wcount[0] + wcount[1] + wcount[2] + wcount[3];
         }
     }
-    const int cnt = kept < T ? kept : T;
-    for (int r = tid; r < cnt; r += 256) flag[tile[r]] = 1;
+    if (tid == 0) flag[i] = 1;
     __syncthreads();
-    // the flagged tiles in tile order (ballot prefix sums; the loop count depends on N only)
+    // the flagged tiles in tile order (ballot prefix sums)
     int32_t* out = kv_idx + ((int64_t)h * T + i) * kept;
     int base = 0;
-    for (int j0 = 0; j0 < N; j0 += 256) {
+    for (int j0 = 0; j0 < T; j0 += 256) {
         const int j = j0 + tid;
         const bool on = j < T && flag[j] != 0;
         const unsigned long long m = __ballot(on);
@@ -198,8 +244,6 @@ int launch_select_tiles(const int8_t* q8, const int8_t* k8, const float* k_scale
                         int32_t* kv_idx, int32_t* kv_cnt, void* ws, hipStream_t st) {
     if (L == 0) return QVD_OK;
     const int T = (L + 127) / 128;
-    int N = 1;
-    while (N < T) N <<= 1;
     int32_t* sums = (int32_t*)ws;
     double* scores = (double*)((char*)ws + ((2 * (size_t)H * T * 128 * 4 + 255) & ~(size_t)255));
     TimingScope ts("select_tiles", st);
@@ -210,7 +254,7 @@ int launch_select_tiles(const int8_t* q8, const int8_t* k8, const float* k_scale
                        H, T, scores);
     s = launch_status("select_tiles (scores)");
     if (s) return s;
-    hipLaunchKernelGGL(k_select, dim3(T, H), dim3(256), 0, st, scores, T, N, kept, kv_idx, kv_cnt);
+    hipLaunchKernelGGL(k_select, dim3(T, H), dim3(256), 0, st, scores, T, kept, kv_idx, kv_cnt);
     return launch_status("select_tiles (select)");
 }
 
