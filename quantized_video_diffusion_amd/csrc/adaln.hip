@@ -118,6 +118,13 @@ QVD_DEV float modulate_one(float x, double mu, double rstd, float scale, float s
     return (float)y;
 }
 
+// x - mu for a bf16 x, in fp32 with mu split into mu_hi = fp32(mu) and mu_lo = fp32(mu - mu_hi): when x is
+// within a factor two of mu_hi, x - mu_hi is exact (Sterbenz) and the one rounding left is that of the
+// subtraction of mu_lo; otherwise |x - mu| is not small next to |mu| and each of the two roundings is
+// within 2^-24 of it.  Within a few fp32 ulps of fp32(x - mu) computed in float64, without a float64
+// instruction per element.
+QVD_DEV float centered(float x, float mu_hi, float mu_lo) { return (x - mu_hi) - mu_lo; }
+
 // LDS table of the modulation: tab[p] = (a(2p), b(2p), a(2p+1), b(2p+1)) with a = scale, b = shift
 // (raw), or, with inv given, a = (1 + scale) inv and b = shift inv
 QVD_DEV void load_mod_table(float4* tab, const float* __restrict__ mod, int half, int d, bool fold, float inv) {
@@ -134,9 +141,9 @@ QVD_DEV void load_mod_table(float4* tab, const float* __restrict__ mod, int half
 
 // pass 1 (dynamic scales): row statistics to ws, per-workgroup max |y| to partials.
 // max |y| is the float64 modulation's, rounded to fp32, exactly: every element is first evaluated in
-// fp32 as fma(fp32(x - mu), fp32(rstd) fp32(1 + scale), shift), which is within 2^-21 (|y| + |shift|)
-// of it; only elements within 2^-19 (max + max|shift|) of the row's fp32 maximum can hold the exact
-// maximum, and those (usually one) are evaluated in float64.
+// fp32 as fma(centered(x), fp32(rstd) fp32(1 + scale), shift), which is within 6 * 2^-24 (|y| + |shift|)
+// < 2^-21 (|y| + |shift|) of it; only elements within 2^-19 (max + max|shift|) of the row's fp32
+// maximum can hold the exact maximum, and those (usually one) are evaluated in float64.
 template <int NW>
 __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x, int L, int d,
                                                   const float* __restrict__ mod, int half, float eps,
@@ -162,14 +169,15 @@ __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x
         row_stats<NW>(R, nw, d, (double)eps, mu, rstd);
         if (lane == 0) stats[row] = make_double2(mu, rstd);
         const float rs = (float)rstd;
+        const float mu_hi = (float)mu, mu_lo = (float)(mu - (double)mu_hi);
         float ay[2 * NW];
         float m32 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             if (j < nw) {
                 const float4 c = tab[lane + 64 * j];
-                ay[2 * j] = fabsf(fmaf((float)((double)bf16lo(R.x[j]) - mu), rs * (1.0f + c.x), c.y));
-                ay[2 * j + 1] = fabsf(fmaf((float)((double)bf16hi(R.x[j]) - mu), rs * (1.0f + c.z), c.w));
+                ay[2 * j] = fabsf(fmaf(centered(bf16lo(R.x[j]), mu_hi, mu_lo), rs * (1.0f + c.x), c.y));
+                ay[2 * j + 1] = fabsf(fmaf(centered(bf16hi(R.x[j]), mu_hi, mu_lo), rs * (1.0f + c.z), c.w));
                 m32 = fmaxf(m32, fmaxf(ay[2 * j], ay[2 * j + 1]));
             }
         }
@@ -191,9 +199,9 @@ __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x
 
 // pass 2: codes.  Dynamic: stats from pass 1 and the amax of the partials; static: stats computed
 // here and the scale read from scale_in.  The codes are E4M3(y * inv) with y * inv formed in fp32 as
-// fma(x - mu, rstd (1 + scale) inv, shift inv): x - mu is taken in float64 and rounded once, so
-// cancellation cannot cost accuracy; the result is within a few fp32 ulps of the float64 modulation,
-// which moves a code only where the value lies that close to a rounding midpoint.
+// fma(centered(x), rstd (1 + scale) inv, shift inv): x - mu keeps its accuracy under cancellation (see
+// centered); the result is within a few fp32 ulps of the float64 modulation, which moves a code only
+// where the value lies that close to a rounding midpoint.
 template <int NW>
 __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x, int L, int d,
                                                   const float* __restrict__ mod, int half, float eps,
@@ -239,13 +247,14 @@ __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x
             rstd = st.y;
         }
         const float rs = (float)rstd;
+        const float mu_hi = (float)mu, mu_lo = (float)(mu - (double)mu_hi);
         uint16_t* qr = reinterpret_cast<uint16_t*>(q + (int64_t)row * d);
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             if (j < nw) {
                 const float4 c = tab[lane + 64 * j];
-                const float v0 = fmaf((float)((double)bf16lo(R.x[j]) - mu), rs * c.x, c.y);
-                const float v1 = fmaf((float)((double)bf16hi(R.x[j]) - mu), rs * c.z, c.w);
+                const float v0 = fmaf(centered(bf16lo(R.x[j]), mu_hi, mu_lo), rs * c.x, c.y);
+                const float v1 = fmaf(centered(bf16hi(R.x[j]), mu_hi, mu_lo), rs * c.z, c.w);
                 qr[lane + 64 * j] = (uint16_t)e4m3_encode2(v0, v1);
             }
         }
