@@ -76,18 +76,25 @@ __global__ void __launch_bounds__(QBLOCK) k_quant_fp8_bf16(const uint16_t* __res
     const int64_t nvec = n >> 3;
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
     u32x2* qv = reinterpret_cast<u32x2*>(q);
-    for (int64_t i = (int64_t)blockIdx.x * QBLOCK + threadIdx.x; i < nvec;
-         i += (int64_t)gridDim.x * QBLOCK) {
-        u32x4 w = __builtin_nontemporal_load(xv + i);
-        u32 ws[4] = {w.x, w.y, w.z, w.w};
-        u32 o[2] = {0, 0};
+    // QU independent 16-byte loads in flight per thread before any is consumed: one per thread left
+    // the HBM pipe half empty
+    constexpr int QU = 4;
+    for (int64_t i0 = (int64_t)blockIdx.x * QBLOCK * QU + threadIdx.x; i0 < nvec;
+         i0 += (int64_t)gridDim.x * QBLOCK * QU) {
+        u32x4 w[QU];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u32 c0 = e4m3_encode(bf16lo(ws[j]) * inv);
-            u32 c1 = e4m3_encode(bf16hi(ws[j]) * inv);
-            o[j >> 1] |= (c0 | (c1 << 8)) << ((j & 1) * 16);
+        for (int u = 0; u < QU; ++u)
+            if (i0 + u * QBLOCK < nvec) w[u] = __builtin_nontemporal_load(xv + i0 + u * QBLOCK);
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+            if (i0 + u * QBLOCK < nvec) {
+                const u32 o0 = e4m3_encode2(bf16lo(w[u].x) * inv, bf16hi(w[u].x) * inv) |
+                               (e4m3_encode2(bf16lo(w[u].y) * inv, bf16hi(w[u].y) * inv) << 16);
+                const u32 o1 = e4m3_encode2(bf16lo(w[u].z) * inv, bf16hi(w[u].z) * inv) |
+                               (e4m3_encode2(bf16lo(w[u].w) * inv, bf16hi(w[u].w) * inv) << 16);
+                qv[i0 + u * QBLOCK] = (u32x2){o0, o1};
+            }
         }
-        qv[i] = (u32x2){o[0], o[1]};
     }
     if (blockIdx.x == 0) {
         for (int64_t i = (nvec << 3) + threadIdx.x; i < n; i += QBLOCK)
