@@ -731,27 +731,49 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
 // Measured on gfx950 with one-hot and all-ones operands: lane half h of either E2M1 operand holds
 // k = 32h .. 32h+31 of its row in order, and lane l's scale byte applies to row l%32, block l/32.
 // Tiles, waves, 128-K stages and the branch-free step schedule are those of k_gemm_mx.  Stage
-// (34 KB): A and W rows of 64 bytes (chunk c of row r at c ^ ((r>>2)&3)), then the 4 E8M0 bytes of
-// each A row and of each W row.
+// (32 KB): A and W rows of 64 bytes (chunk c of row r at c ^ ((r>>2)&3)).
+// E8M0 scales travel in chunks of 8 stages: per operand 256 rows x 32 bytes (the 4 bytes of each of
+// the 8 stages), two chunk buffers per operand.  A row's 32 bytes are contiguous in the [rows][K/32]
+// array, so a DMA of 8 lanes per row covers 8 consecutive rows in a few cache lines; loading each
+// stage's 4 bytes for 64 rows instead touched a line per row and cost 15-25% of the kernel.  Each
+// stage's refill adds one 32-row slice of the chunk after next-but-one stage's: stage s loads slice
+// (s+1) % 8 of chunk (s+1)/8 + 1, so chunk c is complete at stage 8c - 2 and first read (for stage
+// 8c) after the barrier of stage 8c - 1.
 constexpr int W4A4_W_OFF = BM * BKS / 2;
-constexpr int W4A4_AE_OFF = W4A4_W_OFF + BN * BKS / 2;
-constexpr int W4A4_WE_OFF = W4A4_AE_OFF + BM * 4;
-constexpr int STAGE_W4A4 = W4A4_WE_OFF + BN * 4;
-constexpr int SMEM_W4A4 = 2 * STAGE_W4A4 > NWAVE8 * 16384 ? 2 * STAGE_W4A4 : NWAVE8 * 16384;
+constexpr int STAGE_W4A4 = W4A4_W_OFF + BN * BKS / 2;
+constexpr int W4A4_SC_STAGES = 8;                      // stages per scale chunk
+constexpr int W4A4_SC_ROW = 4 * W4A4_SC_STAGES;        // bytes per row per chunk
+constexpr int W4A4_SC_BUF = BM * W4A4_SC_ROW;          // one operand's chunk (BM == BN)
+constexpr int W4A4_SC_OFF = 2 * STAGE_W4A4;
+constexpr int W4A4_MAIN = W4A4_SC_OFF + 4 * W4A4_SC_BUF;
+constexpr int SMEM_W4A4 = W4A4_MAIN > NWAVE8 * 16384 ? W4A4_MAIN : NWAVE8 * 16384;
 
 // DMA instruction u of wave w's share of a stage: 0..1 A row blocks 2w+u, 2..3 W row blocks 2w+u-2
-// (16 rows of 64 bytes each), 4 the E8M0 words of 64 rows: A rows 64w .. (waves 0..3) or W rows
-// 64(w-4) .. (waves 4..7), 4 bytes per lane.
+// (16 rows of 64 bytes each)
 QVD_DEV void dma_w4a4(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
-                      const uint32_t* w_off, const uint8_t* e_src, uint32_t e_off, uint32_t e_dst, int u) {
+                      const uint32_t* w_off, int u) {
     uint8_t* st = smem + buf * STAGE_W4A4;
     if (u < 2)
         __builtin_amdgcn_global_load_lds(g.a + a_off[u] + k0 / 2, (lds_void*)(st + (2 * wv + u) * 1024), 16, 0, 0);
-    else if (u < 4)
+    else
         __builtin_amdgcn_global_load_lds(g.w + w_off[u - 2] + k0 / 2,
                                          (lds_void*)(st + W4A4_W_OFF + (2 * wv + u - 2) * 1024), 16, 0, 0);
-    else
-        __builtin_amdgcn_global_load_lds(e_src + e_off + k0 / 32, (lds_void*)(st + e_dst), 4, 0, 0);
+}
+
+// One wave's part of scale slice sl of chunk ch: operand o (waves 0..3 A, 4..7 W), rows
+// 32 sl + 8 part .. +7 of the tile, 8 lanes per row, 4 bytes each.  Chunks past the last re-read the
+// last one (never used); columns past K/32 read the row's first word; rows past the matrix its last.
+QVD_DEV void dma_w4a4_scales(const uint8_t* src, int base, int lim, int kb, int nch, uint8_t* smem, int ch,
+                             int sl, int part, int o, int lane) {
+    const int chc = ch < nch ? ch : nch - 1;
+    int row = base + 32 * sl + 8 * part + (lane >> 3);
+    row = row < lim ? row : lim - 1;
+    int col = W4A4_SC_ROW * chc + 4 * (lane & 7);
+    col = col < kb ? col : 0;
+    __builtin_amdgcn_global_load_lds(
+        src + (uint32_t)row * (uint32_t)kb + (uint32_t)col,
+        (lds_void*)(smem + W4A4_SC_OFF + ((ch & 1) * 2 + o) * W4A4_SC_BUF + (32 * sl + 8 * part) * W4A4_SC_ROW),
+        4, 0, 0);
 }
 
 template <int EPI>
@@ -767,9 +789,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
     const int M = g.M, N = g.N, K = g.K;
 
     // DMA sources.  A and W instruction u: lane l lands in row r = (2w+u)*16 + l/4, slot l%4, and
-    // fetches chunk (l%4) ^ ((r>>2)&3) of the row's 64 stage bytes.  E8M0: lane l brings row
-    // 64(w%4) + l of A (w < 4) or W.  Rows past M (N) repeat the last row; their results are never
-    // stored.
+    // fetches chunk (l%4) ^ ((r>>2)&3) of the row's 64 stage bytes.  Rows past M (N) repeat the last
+    // row; their results are never stored.
     uint32_t a_off[2], w_off[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -780,25 +801,21 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
         a_off[u] = (uint32_t)ra * (uint32_t)(K / 2) + 16u * c;
         w_off[u] = (uint32_t)rw * (uint32_t)(K / 2) + 16u * c;
     }
-    const bool e_of_a = wv < 4;
-    const uint8_t* e_src = e_of_a ? g.a_e8 : g.e8;
-    uint32_t e_off;
-    {
-        const int r = 64 * (wv & 3) + lane;
-        const int lim = e_of_a ? M : N;
-        const int base = e_of_a ? m0 : n0;
-        const int row = base + r < lim ? base + r : lim - 1;
-        e_off = (uint32_t)row * (uint32_t)(K / 32);
-    }
-    const uint32_t e_dst = (uint32_t)((e_of_a ? W4A4_AE_OFF : W4A4_WE_OFF) + 256 * (wv & 3));
+    const int so = wv >> 2, spart = wv & 3;               // scale DMA: operand and part of this wave
+    const uint8_t* e_src = so == 0 ? g.a_e8 : g.e8;
+    const int e_base = so == 0 ? m0 : n0, e_lim = so == 0 ? M : N;
+    const int S = K / BKS, kb = K / 32, nch = (S + W4A4_SC_STAGES - 1) / W4A4_SC_STAGES;
 
     // fragment offsets per K step j: row l%32 of a 32-row block, logical chunk 2j + h (lane half h)
     const int lr = lane & 31, hl = lane >> 5;
     const uint32_t sw4 = (uint32_t)((lr >> 2) & 3), r64 = (uint32_t)lr * 64u;
     const uint32_t fo0 = r64 + 16u * ((uint32_t)hl ^ sw4), fo1 = r64 + 16u * ((2u + hl) ^ sw4);
     const int a_blk = 4 * wm, w_blk = 2 * wn;
-    const uint32_t* ae_row = reinterpret_cast<const uint32_t*>(smem + W4A4_AE_OFF) + 32 * a_blk + lr;
-    const uint32_t* we_row = reinterpret_cast<const uint32_t*>(smem + W4A4_WE_OFF) + 32 * w_blk + lr;
+    // scale word of stage t for fragment row block b of operand o: chunk buffer (t/8)&1, word t%8
+    auto sc_word = [&](int o, int b, int t) {
+        return *reinterpret_cast<const uint32_t*>(smem + W4A4_SC_OFF + (((t >> 3) & 1) * 2 + o) * W4A4_SC_BUF +
+                                                  (32 * b + lr) * W4A4_SC_ROW + 4 * (t & 7));
+    };
 
     Layout32N64::Acc acc;
 #pragma unroll
@@ -808,12 +825,14 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int S = K / BKS;
 #pragma unroll
-    for (int u = 0; u < 5; ++u) dma_w4a4(g, smem, 0, 0, wv, a_off, w_off, e_src, e_off, e_dst, u);
+    for (int u = 0; u < 4; ++u) dma_w4a4(g, smem, 0, 0, wv, a_off, w_off, u);
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) dma_w4a4_scales(e_src, e_base, e_lim, kb, nch, smem, 0, sl, spart, so, lane);
+    dma_w4a4_scales(e_src, e_base, e_lim, kb, nch, smem, 1, 0, spart, so, lane);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int u = 0; u < 5; ++u) dma_w4a4(g, smem, 1, S > 1 ? BKS : 0, wv, a_off, w_off, e_src, e_off, e_dst, u);
+    for (int u = 0; u < 4; ++u) dma_w4a4(g, smem, 1, S > 1 ? BKS : 0, wv, a_off, w_off, u);
 
     v8i fw[2][2], fa[2][4];
     uint32_t scw[2], sca[4], scw_n[2], sca_n[4];
@@ -822,9 +841,9 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[0][i] = frag_e2m1(smem, a_blk + i, fo0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) scw[i] = we_row[32 * i] >> (8 * hl);
+    for (int i = 0; i < 2; ++i) scw[i] = sc_word(1, w_blk + i, 0) >> (8 * hl);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sca[i] = ae_row[32 * i] >> (8 * hl);
+    for (int i = 0; i < 4; ++i) sca[i] = sc_word(0, a_blk + i, 0) >> (8 * hl);
 
     // the step schedule of k_gemm_mx: step 0 of a stage uses blocks h (byte h of the shifted words),
     // step 1 blocks 2 + h (byte 2); the words of stage s+1 are read at the start of step 1 of stage s
@@ -842,13 +861,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
             const int sav = (int)(h == 0 ? sca[q & 3] : sca[q & 3] >> 16);
             acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 fw[h][q >> 2], fa[h][q & 3], acc[q >> 2][q & 3], 4, 4, 0, swv, 0, sav);
-            if (h == 1 && refill && q < 5)
-                dma_w4a4(g, smem, s & 1, (s + 2) * BKS, wv, a_off, w_off, e_src, e_off, e_dst, q);
+            if (h == 1 && refill && q < 4)
+                dma_w4a4(g, smem, s & 1, (s + 2) * BKS, wv, a_off, w_off, q);
+            if (h == 1 && refill && q == 4)
+                dma_w4a4_scales(e_src, e_base, e_lim, kb, nch, smem, ((s + 1) >> 3) + 1, (s + 1) & 7, spart, so,
+                                lane);
             if (h == 1 && q == 0) {   // raw words: shifting here would wait for the reads in flight
 #pragma unroll
-                for (int i = 0; i < 2; ++i) scw_n[i] = we_row[nbuf * (STAGE_W4A4 / 4) + 32 * i];
+                for (int i = 0; i < 2; ++i) scw_n[i] = sc_word(1, w_blk + i, s + 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sca_n[i] = ae_row[nbuf * (STAGE_W4A4 / 4) + 32 * i];
+                for (int i = 0; i < 4; ++i) sca_n[i] = sc_word(0, a_blk + i, s + 1);
             }
             if (q < 2)
                 fw[h ^ 1][q] = frag_e2m1(Ws, w_blk + q, fo);
