@@ -567,34 +567,62 @@ __global__ void __launch_bounds__(512, 1) k_gemm_f8(GemmArgs g) {
 // of the E2M1 operand holds k = 32h .. 32h+31 of its row in order -- 16 bytes, exactly one 32-element
 // block, whose scale the lane supplies -- and lane half h of the E4M3 operand holds k = 16h .. 16h+15
 // in its first 16 bytes and k = 32+16h .. 32+16h+15 in its last 16.
-// Stage layout (49 KB): A rows of 128 bytes as in the E4M3 kernel; W rows of 64 bytes (128 packed E2M1
+// Stage layout (48 KB): A rows of 128 bytes as in the E4M3 kernel; W rows of 64 bytes (128 packed E2M1
 // values), 16-byte chunk c of row r at c ^ ((r>>2)&3), so rows r .. r+15 at one logical chunk cover
-// 16 distinct bank quads; then the 4 E8M0 bytes of each W row (blocks k0/32 .. k0/32+3).
+// 16 distinct bank quads.  The W scales come in chunks of 8 stages (below).
+// E8M0 scales of the block-scaled kernels travel in chunks of 8 stages: per operand 256 rows x 32
+// bytes (the 4 bytes of each of the 8 stages), two chunk buffers.  A row's 32 bytes are contiguous
+// in the [rows][K/32] array, so a DMA of 8 lanes per row covers 8 consecutive rows in a few cache
+// lines; loading each stage's 4 bytes for 64 rows instead touched a line per row and cost the W4A4
+// kernel 15-25%.  Each stage's refill adds one 32-row slice: stage s loads slice (s+1) % 8 of chunk
+// (s+1)/8 + 1 (the prologue loads chunk 0 and slice 0 of chunk 1), so chunk c is complete at stage
+// 8c - 2 and first read, for stage 8c, after the barrier of stage 8c - 1.
+constexpr int SC_STAGES = 8;                       // stages per scale chunk
+constexpr int SC_ROW = 4 * SC_STAGES;              // bytes per row per chunk
+constexpr int SC_BUF = BN * SC_ROW;                // one operand's chunk (BM == BN)
+
+// One wave's part of scale slice sl of chunk ch: rows 32 sl + 8 part .. +7 of the tile (base ..),
+// 8 lanes per row, 4 bytes each, into the chunk buffer at sc + (ch & 1) * stride.  Chunks past the
+// last re-read the last one (never used); columns past K/32 read the row's first word; rows past the
+// matrix its last row.
+QVD_DEV void dma_scale_slice(const uint8_t* src, int base, int lim, int kb, int nch, uint8_t* sc, int stride,
+                             int ch, int sl, int part, int lane) {
+    const int chc = ch < nch ? ch : nch - 1;
+    int row = base + 32 * sl + 8 * part + (lane >> 3);
+    row = row < lim ? row : lim - 1;
+    int col = SC_ROW * chc + 4 * (lane & 7);
+    col = col < kb ? col : 0;
+    __builtin_amdgcn_global_load_lds(src + (uint32_t)row * (uint32_t)kb + (uint32_t)col,
+                                     (lds_void*)(sc + (ch & 1) * stride + (32 * sl + 8 * part) * SC_ROW), 4, 0, 0);
+}
+
+// the word of stage t of row r from the chunk buffers at sc (stride between the two)
+QVD_DEV uint32_t scale_word(const uint8_t* sc, int stride, int r, int t) {
+    return *reinterpret_cast<const uint32_t*>(sc + ((t >> 3) & 1) * stride + r * SC_ROW + 4 * (t & 7));
+}
+
 constexpr int W4_OFF = BM * BKS;                  // W rows of a stage
-constexpr int E8_OFF = W4_OFF + BN * BKS / 2;     // E8M0 words of a stage
-constexpr int STAGE_MX = E8_OFF + BN * 4;
-constexpr int SMEM_MX = 2 * STAGE_MX > NWAVE8 * 16384 ? 2 * STAGE_MX : NWAVE8 * 16384;
+constexpr int STAGE_MX = W4_OFF + BN * BKS / 2;
+constexpr int MX_SC_OFF = 2 * STAGE_MX;           // W scale chunks
+constexpr int MX_MAIN = MX_SC_OFF + 2 * SC_BUF;
+constexpr int SMEM_MX = MX_MAIN > NWAVE8 * 16384 ? MX_MAIN : NWAVE8 * 16384;
 
 // DMA instruction u of wave w's share of a stage: 0..3 A row blocks 4w+u (8 rows of 128 bytes each),
-// 4..5 W row blocks 2w+u-4 (16 rows of 64 bytes each), 6 the E8M0 words of W rows 64(w%4) .. +63
-// (4 bytes per lane; waves w and w+4 write the same words, which keeps the code free of branches).
+// 4..5 W row blocks 2w+u-4 (16 rows of 64 bytes each)
 QVD_DEV void dma_mx(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
-                    const uint32_t* w_off, uint32_t e_off, int u) {
+                    const uint32_t* w_off, int u) {
     uint8_t* st = smem + buf * STAGE_MX;
     if (u < 4)
         __builtin_amdgcn_global_load_lds(g.a + a_off[u] + k0, (lds_void*)(st + (4 * wv + u) * 1024), 16, 0, 0);
-    else if (u < 6)
+    else
         __builtin_amdgcn_global_load_lds(g.w + w_off[u - 4] + k0 / 2,
                                          (lds_void*)(st + W4_OFF + (2 * wv + u - 4) * 1024), 16, 0, 0);
-    else
-        __builtin_amdgcn_global_load_lds(g.e8 + e_off + k0 / 32, (lds_void*)(st + E8_OFF + 256 * (wv & 3)),
-                                         4, 0, 0);
 }
 
 QVD_DEV void stage_mx(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
-                      const uint32_t* w_off, uint32_t e_off) {
+                      const uint32_t* w_off) {
 #pragma unroll
-    for (int u = 0; u < 7; ++u) dma_mx(g, smem, buf, k0, wv, a_off, w_off, e_off, u);
+    for (int u = 0; u < 6; ++u) dma_mx(g, smem, buf, k0, wv, a_off, w_off, u);
 }
 
 // 16-byte E2M1 operand (32 elements) of rows 32 b .. 32 b + 31 of a 64-byte-row tile; the MFMA reads
@@ -620,9 +648,10 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
     const int M = g.M, N = g.N, K = g.K;
 
     // DMA sources.  A as in k_gemm_f8.  W instruction u: lane l lands in row r = (2w+u)*16 + l/4, slot
-    // l%4, and fetches chunk (l%4) ^ ((r>>2)&3) of the row's 64 stage bytes.  E8M0: lane l brings row
-    // 64(w%4) + l.  Rows past M (N) repeat the last row; their results are never stored.
-    uint32_t a_off[4], w_off[2], e_off;
+    // l%4, and fetches chunk (l%4) ^ ((r>>2)&3) of the row's 64 stage bytes.  Rows past M (N) repeat
+    // the last row; their results are never stored.  Scale slices: waves w and w+4 load the same part
+    // w%4 (the same bytes), which keeps the code free of branches.
+    uint32_t a_off[4], w_off[2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int r = (4 * wv + u) * 8 + (lane >> 3);
@@ -637,11 +666,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
         const int rw = n0 + r < N ? n0 + r : N - 1;
         w_off[u] = (uint32_t)rw * (uint32_t)(K / 2) + 16u * c;
     }
-    {
-        const int r = 64 * (wv & 3) + lane;
-        const int rw = n0 + r < N ? n0 + r : N - 1;
-        e_off = (uint32_t)rw * (uint32_t)(K / 32);
-    }
+    const int kb = K / 32, S = K / BKS, nch = (S + SC_STAGES - 1) / SC_STAGES;
+    uint8_t* const sc = smem + MX_SC_OFF;
     // fragment offsets per K step j of a stage.  A (E4M3): row l%32, logical chunks 4j + h and
     // 4j + 2 + h for lane half h.  W (E2M1): row l%32, logical chunk 2j + h.  Scale word: row l%32.
     const int lr = lane & 31, hl = lane >> 5;
@@ -651,7 +677,6 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
     const uint32_t ws = (uint32_t)((lr >> 2) & 3), rw64 = (uint32_t)lr * 64u;
     const uint32_t wo0 = rw64 + 16u * ((uint32_t)hl ^ ws), wo1 = rw64 + 16u * ((2u + hl) ^ ws);
     const int a_blk = 4 * wm, w_blk = 2 * wn;
-    const uint32_t* e_row = reinterpret_cast<const uint32_t*>(smem + E8_OFF) + 32 * w_blk + lr;
 
     Layout32N64::Acc acc;
 #pragma unroll
@@ -662,25 +687,27 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     // K is a multiple of 128: S stages, 2 S steps
-    const int S = K / BKS;
-    stage_mx(g, smem, 0, 0, wv, a_off, w_off, e_off);
+    stage_mx(g, smem, 0, 0, wv, a_off, w_off);
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) dma_scale_slice(g.e8, n0, N, kb, nch, sc, SC_BUF, 0, sl, wv & 3, lane);
+    dma_scale_slice(g.e8, n0, N, kb, nch, sc, SC_BUF, 1, 0, wv & 3, lane);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    stage_mx(g, smem, 1, S > 1 ? BKS : 0, wv, a_off, w_off, e_off);
+    stage_mx(g, smem, 1, S > 1 ? BKS : 0, wv, a_off, w_off);
 
     v8i fw[2][2], fa[2][4];                      // [set][W blocks] / [set][A blocks]
-    uint32_t sc[2], sc_next[2];                  // E8M0 words of this stage, shifted to the lane half's block
+    uint32_t scw[2], scw_next[2];                // E8M0 words of this stage, shifted to the lane half's block
 #pragma unroll
     for (int i = 0; i < 2; ++i) fw[0][i] = frag_e2m1(smem + W4_OFF, w_blk + i, wo0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[0][i] = frag32(smem, a_blk + i, alo0, ahi0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) sc[i] = e_row[32 * i] >> (8 * hl);
+    for (int i = 0; i < 2; ++i) scw[i] = scale_word(sc, SC_BUF, 32 * (w_blk + i) + lr, 0) >> (8 * hl);
 
     // The step schedule of k_gemm_f8, with step bodies free of branches: with the refill and the E8M0
     // loads of waves 0..3 behind branches, the compiler moved every MFMA of the loop behind the last
     // of them (out of its interleave with the fragment reads) and spilled.  So the main loop always
     // refills, the last two stages never do, step 1 always waits at the barrier (once more than
-    // needed, in the last stage), and all eight waves load E8M0 words.  Step 0 of a stage uses blocks
+    // needed, in the last stage), and all eight waves load scale slices.  Step 0 of a stage uses blocks
     // h of the stage (byte h of the shifted words), step 1 blocks 2 + h (byte 2); the words of stage
     // s+1 are read at the start of step 1 of stage s.
     auto kstep = [&](auto H, auto REFILL, int s) {
@@ -693,13 +720,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
         const uint32_t lo = h == 0 ? alo1 : alo0, hi = h == 0 ? ahi1 : ahi0, wo = h == 0 ? wo1 : wo0;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int sw = (int)(h == 0 ? sc[q >> 2] : sc[q >> 2] >> 16);
+            const int sw = (int)(h == 0 ? scw[q >> 2] : scw[q >> 2] >> 16);
             acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 fw[h][q >> 2], fa[h][q & 3], acc[q >> 2][q & 3], 4, 0, 0, sw, 0, 127);
-            if (h == 1 && refill && q < 7) dma_mx(g, smem, s & 1, (s + 2) * BKS, wv, a_off, w_off, e_off, q);
+            if (h == 1 && refill && q < 6) dma_mx(g, smem, s & 1, (s + 2) * BKS, wv, a_off, w_off, q);
+            if (h == 1 && refill && q == 6)
+                dma_scale_slice(g.e8, n0, N, kb, nch, sc, SC_BUF, ((s + 1) >> 3) + 1, (s + 1) & 7, wv & 3, lane);
             if (h == 1 && q == 0) {             // first, so that LDS (which answers in order) has
 #pragma unroll                                  // them back before the fragments
-                for (int i = 0; i < 2; ++i) sc_next[i] = e_row[nbuf * (STAGE_MX / 4) + 32 * i] >> (8 * hl);
+                for (int i = 0; i < 2; ++i)
+                    scw_next[i] = scale_word(sc, SC_BUF, 32 * (w_blk + i) + lr, s + 1) >> (8 * hl);
             }
             if (q < 2)
                 fw[h ^ 1][q] = frag_e2m1(Ws, w_blk + q, wo);
@@ -708,8 +738,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
         }
         if (h == 1) {
-            sc[0] = sc_next[0];
-            sc[1] = sc_next[1];
+            scw[0] = scw_next[0];
+            scw[1] = scw_next[1];
         }
     };
     int s = 0;
@@ -732,20 +762,12 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
 // k = 32h .. 32h+31 of its row in order, and lane l's scale byte applies to row l%32, block l/32.
 // Tiles, waves, 128-K stages and the branch-free step schedule are those of k_gemm_mx.  Stage
 // (32 KB): A and W rows of 64 bytes (chunk c of row r at c ^ ((r>>2)&3)).
-// E8M0 scales travel in chunks of 8 stages: per operand 256 rows x 32 bytes (the 4 bytes of each of
-// the 8 stages), two chunk buffers per operand.  A row's 32 bytes are contiguous in the [rows][K/32]
-// array, so a DMA of 8 lanes per row covers 8 consecutive rows in a few cache lines; loading each
-// stage's 4 bytes for 64 rows instead touched a line per row and cost 15-25% of the kernel.  Each
-// stage's refill adds one 32-row slice of the chunk after next-but-one stage's: stage s loads slice
-// (s+1) % 8 of chunk (s+1)/8 + 1, so chunk c is complete at stage 8c - 2 and first read (for stage
-// 8c) after the barrier of stage 8c - 1.
+// E8M0 scales of both operands in chunks of 8 stages, as in k_gemm_mx: buffer (ch & 1) of operand o
+// at W4A4_SC_OFF + ((ch & 1) * 2 + o) * SC_BUF.
 constexpr int W4A4_W_OFF = BM * BKS / 2;
 constexpr int STAGE_W4A4 = W4A4_W_OFF + BN * BKS / 2;
-constexpr int W4A4_SC_STAGES = 8;                      // stages per scale chunk
-constexpr int W4A4_SC_ROW = 4 * W4A4_SC_STAGES;        // bytes per row per chunk
-constexpr int W4A4_SC_BUF = BM * W4A4_SC_ROW;          // one operand's chunk (BM == BN)
 constexpr int W4A4_SC_OFF = 2 * STAGE_W4A4;
-constexpr int W4A4_MAIN = W4A4_SC_OFF + 4 * W4A4_SC_BUF;
+constexpr int W4A4_MAIN = W4A4_SC_OFF + 4 * SC_BUF;
 constexpr int SMEM_W4A4 = W4A4_MAIN > NWAVE8 * 16384 ? W4A4_MAIN : NWAVE8 * 16384;
 
 // DMA instruction u of wave w's share of a stage: 0..1 A row blocks 2w+u, 2..3 W row blocks 2w+u-2
@@ -760,20 +782,10 @@ QVD_DEV void dma_w4a4(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv,
                                          (lds_void*)(st + W4A4_W_OFF + (2 * wv + u - 2) * 1024), 16, 0, 0);
 }
 
-// One wave's part of scale slice sl of chunk ch: operand o (waves 0..3 A, 4..7 W), rows
-// 32 sl + 8 part .. +7 of the tile, 8 lanes per row, 4 bytes each.  Chunks past the last re-read the
-// last one (never used); columns past K/32 read the row's first word; rows past the matrix its last.
+// one wave's part of a scale slice: operand o (waves 0..3 A, 4..7 W), part w % 4
 QVD_DEV void dma_w4a4_scales(const uint8_t* src, int base, int lim, int kb, int nch, uint8_t* smem, int ch,
                              int sl, int part, int o, int lane) {
-    const int chc = ch < nch ? ch : nch - 1;
-    int row = base + 32 * sl + 8 * part + (lane >> 3);
-    row = row < lim ? row : lim - 1;
-    int col = W4A4_SC_ROW * chc + 4 * (lane & 7);
-    col = col < kb ? col : 0;
-    __builtin_amdgcn_global_load_lds(
-        src + (uint32_t)row * (uint32_t)kb + (uint32_t)col,
-        (lds_void*)(smem + W4A4_SC_OFF + ((ch & 1) * 2 + o) * W4A4_SC_BUF + (32 * sl + 8 * part) * W4A4_SC_ROW),
-        4, 0, 0);
+    dma_scale_slice(src, base, lim, kb, nch, smem + W4A4_SC_OFF + o * SC_BUF, 2 * SC_BUF, ch, sl, part, lane);
 }
 
 template <int EPI>
@@ -804,7 +816,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
     const int so = wv >> 2, spart = wv & 3;               // scale DMA: operand and part of this wave
     const uint8_t* e_src = so == 0 ? g.a_e8 : g.e8;
     const int e_base = so == 0 ? m0 : n0, e_lim = so == 0 ? M : N;
-    const int S = K / BKS, kb = K / 32, nch = (S + W4A4_SC_STAGES - 1) / W4A4_SC_STAGES;
+    const int S = K / BKS, kb = K / 32, nch = (S + SC_STAGES - 1) / SC_STAGES;
 
     // fragment offsets per K step j: row l%32 of a 32-row block, logical chunk 2j + h (lane half h)
     const int lr = lane & 31, hl = lane >> 5;
@@ -813,8 +825,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
     const int a_blk = 4 * wm, w_blk = 2 * wn;
     // scale word of stage t for fragment row block b of operand o: chunk buffer (t/8)&1, word t%8
     auto sc_word = [&](int o, int b, int t) {
-        return *reinterpret_cast<const uint32_t*>(smem + W4A4_SC_OFF + (((t >> 3) & 1) * 2 + o) * W4A4_SC_BUF +
-                                                  (32 * b + lr) * W4A4_SC_ROW + 4 * (t & 7));
+        return scale_word(smem + W4A4_SC_OFF + o * SC_BUF, 2 * SC_BUF, 32 * b + lr, t);
     };
 
     Layout32N64::Acc acc;
