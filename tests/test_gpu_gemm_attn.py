@@ -161,7 +161,8 @@ def test_gemm_qkv_epilogue(M, H):
         say(f"qkv part {part}: {n} tie flips")
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (391, 384, 256), (300, 2688, 2688)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (391, 384, 256), (300, 2688, 2688), (130, 256, 10752),
+                                   (257, 128, 1152)])
 def test_gemm_mxfp4_f32_and_bf16(M, N, K):
     say("gemm mxfp4", M, N, K)
     a = _codes(M, K, M + 1)

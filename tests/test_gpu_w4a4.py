@@ -33,7 +33,7 @@ def _weights(N, K, seed):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (391, 384, 256), (33, 2688, 2688), (700, 768, 1024),
-                                   (1, 128, 384)])
+                                   (1, 128, 384), (130, 256, 10752), (300, 128, 1152)])
 def test_w4a4_f32_and_bf16_vs_oracle(M, N, K):
     say("w4a4", M, N, K)
     ap, ae = OQ.quant_mxfp4_weight(_acts(M, K, M + K))
