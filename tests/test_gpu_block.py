@@ -62,7 +62,11 @@ def _run_both(w, L, seed=0, mod=None, t=999.0, sparse=None, act_scale=None, fmt=
 # W4A4 moves codes on the same near-midpoint inputs, but one E2M1 step is up to 1/3 of the value
 # (2^-4 for E4M3), so a single moved code of g shifts one output row by a step times a column of
 # W_down.  There the guard reads: at most 0.1% of the outputs beyond 2 ulp + 0.1 RMS(ref), none
-# beyond 2 ulp + 0.5 RMS(ref).
+# beyond 2 ulp + 0.5 RMS(ref).  And the RMS bars are three times the FP8 ones (3e-2 output, 7.5e-2
+# branch): the oracle's own W4A4 block at Trim width moves by 6.4e-3 / 1.4e-2 (output / branch) when
+# its attention output is perturbed by 1e-5 relative, 2.5e-2 / 5.5e-2 at 2e-4, about three times what
+# its FP8 block does under the same perturbations, and the kernel's attention differs from the
+# oracle's at that level (fp16 numerators).
 def _check(x, got, want, name, branch_rel=2.5e-2, a4=False):
     g, o, xi = OC.bf16_to_f64(got), OC.bf16_to_f64(want), OC.bf16_to_f64(x)
     err = np.abs(g - o)
@@ -73,7 +77,9 @@ def _check(x, got, want, name, branch_rel=2.5e-2, a4=False):
     say(f"{name}: out RMS rel err {np.sqrt(np.mean(err ** 2)) / rms:.2e}; max {err.max():.3e} at "
         f"{np.unravel_index(k, g.shape)} (want {o.flat[k]:.4f}, got {g.flat[k]:.4f}, x {xi.flat[k]:.4f}); "
         f"branch RMS rel err {rel:.2e}")
-    assert np.sqrt(np.mean(err ** 2)) <= 1e-2 * rms, f"{name}: block output RMS error"
+    out_rel = 3e-2 if a4 else 1e-2
+    branch_rel = 3 * branch_rel if a4 else branch_rel
+    assert np.sqrt(np.mean(err ** 2)) <= out_rel * rms, f"{name}: block output RMS error"
     if a4:
         ulp2 = 2 * np.abs(o) * 2.0 ** -7
         frac = float(np.mean(err > ulp2 + 0.1 * rms))
@@ -165,6 +171,18 @@ def test_block_trim_width_L4096():
     mod = W.random_mod(w.d, seed=8, tag=w.tag, gate=1.0)
     x, got, want = _run_both(w, w.L, seed=0, mod=mod)
     _check(x, got, want, "trim L=4096 gate=1")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "w4a4"])
+def test_block_trim_width_4bit(fmt):
+    """Full Trim width with 4-bit weights, 1,100 tokens (9 tiles, ragged), 80%-sparse masks: W4A8 with
+    static activation scales, and W4A4 with dynamic MXFP4 activation blocks."""
+    w = W.WORKLOADS["trim_block_L4096"]
+    say("trim block 4-bit", fmt)
+    mod = W.random_mod(w.d, seed=9, tag=w.tag, gate=1.0)
+    act = np.array([0.02, 0.01, 0.02, 0.004], np.float32) if fmt == "mxfp4" else None
+    x, got, want = _run_both(w, 1100, seed=3, mod=mod, act_scale=act, fmt=fmt, sparse=True)
+    _check(x, got, want, f"trim {fmt} L=1100", a4=fmt == "w4a4")
 
 
 def test_block_deterministic():
