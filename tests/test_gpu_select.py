@@ -7,6 +7,7 @@ import torch
 
 import workloads as W
 import quantized_video_diffusion_amd as Q
+from quantized_video_diffusion_amd import _lib
 from oracle import quant as OQ, selector as OS, block as OB, adaln as OA
 from _gpu_util import say, bf16_dev, fp16_dev, i32_dev, f32_dev, host, host_bits
 
@@ -112,3 +113,40 @@ def test_block_selects_its_own_mask():
     want = OB.dit_block(x, mod, qw, oi, oc, w.n_heads)
     from test_gpu_block import _check
     _check(x, got, want, "block with selected mask")
+
+
+def test_w4a4_block_selects_its_own_mask():
+    """W4A4 block with no mask passed: the selector runs on the block's INT8 Q/K between the QKV GEMM
+    and the attention, as in the FP8 block."""
+    w = W.WORKLOADS["toy_d256_L256"]
+    L, kept = 1290, 3
+    x = W.activations(w, 13, L=L)
+    wbits = W.block_weights(w, 13)
+    mod = W.random_mod(w.d, seed=14, tag=w.tag, gate=1.0)
+    bw = Q.quantize_block_weights({k: bf16_dev(v) for k, v in wbits.items()}, w.d, w.n_heads, w.mlp,
+                                  fmt=_lib.QVD_W_MXFP4_A4)
+    xd = bf16_dev(x)
+    Q.dit_block_forward(bw, f32_dev(mod), xd, None, None, kmax=kept)
+    got = host_bits(xd)
+    qm = {}
+    for site in OB.SITES:
+        qm["w_" + site], qm["e8_" + site] = OQ.quant_mxfp4_weight(wbits["w_" + site])
+    T = (L + 127) // 128
+    dummy_idx = np.tile(np.arange(T, dtype=np.int32), (w.n_heads, T, 1))
+    _, it = OB.dit_block(x, mod, qm, dummy_idx, np.full((w.n_heads, T), T, np.int32), w.n_heads,
+                         fmt="w4a4", keep=True)
+    oi, oc = OS.select_tiles(it["q8"], it["k8"], it["sk"], L, w.n_heads, kept)
+    want = OB.dit_block(x, mod, qm, oi, oc, w.n_heads, fmt="w4a4")
+    from test_gpu_block import _check
+    _check(x, got, want, "w4a4 block with selected mask", a4=True)
+
+
+def test_select_kept_at_least_tiles_and_single_tile():
+    """kept >= T keeps every tile in order; L <= 128 (one tile) keeps the diagonal only."""
+    for L, kept in ((700, 9), (100, 3)):
+        qb, kb, _ = W.qkv_heads(L, 2, seed=kept)
+        dev, orc = _both_codes(qb, kb, L, 2)
+        idx, cnt = Q.select_tiles(*dev, kept)
+        oi, oc = OS.select_tiles(*orc, L, 2, kept)
+        np.testing.assert_array_equal(host(idx), oi)
+        np.testing.assert_array_equal(host(cnt), oc)
