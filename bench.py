@@ -164,6 +164,76 @@ def parse_traffic(fetch_dir, write_dir):
     print(json.dumps(out))
 
 
+# Kernels of the 480p block reported by --parse-counters.  The FP8 quantizer also runs when the weights
+# are quantized at set-up; only its last 2 x blocks dispatches (those of the step) are taken.
+COUNTER_KERNELS = [
+    ("k_sparse_attn<1>", "attention (INT8 QK + fp16 PV)", False),
+    ("k_gemm_f8<4>", "QKV GEMM, INT8 Q/K + V^T epilogue", False),
+    ("k_gemm_f8<3>", "up GEMM, GELU epilogue", False),
+    ("k_gemm_f8<2>", "out / down GEMM, gated residual (mean of both)", False),
+    ("k_ln_stats<21>", "modulate pass 1", False),
+    ("k_ln_quant<21>", "modulate pass 2", False),
+    ("k_quant_fp8_bf16", "FP8 quantizer of O and GELU (mean of both)", True),
+]
+N_XCD, N_SIMD = 8, 1024
+
+
+def parse_counters(mfma_dir, fetch_dir, write_dir, trace_dir, blocks=2):
+    """Per-kernel MFMA utilisation, clock and HBM bytes from three rocprofv3 counter runs of the same
+    command, with durations from a kernel-trace run (the counter runs' own timestamps include the
+    collection): GRBM_GUI_ACTIVE (summed over the 8 XCDs) gives the kernel's GPU cycles, so
+    SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) is the fraction of SIMD-cycles with the matrix core
+    busy at the clock the kernel ran at; FETCH_SIZE / WRITE_SIZE are scaled by the copy probe."""
+    import csv
+    import glob
+    trace = []   # (dispatch id, kernel, grid threads, µs)
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            trace.append((int(r["Dispatch_Id"]), r["Kernel_Name"], grid,
+                          (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    # the 480p stack's dispatches: from the first step's AdaLN projection (set-up work, the weights'
+    # quantization, is before it) to the 6 kernels that follow the last INT8-score attention (any 768p
+    # blocks come after)
+    trace.sort()
+    first = min((i for i, k, _, _ in trace if "k_adaln_project" in k), default=0)
+    att = [n for n, (_, k, _, _) in enumerate(trace) if "k_sparse_attn<1>" in k]
+    end = trace[min(att[-1] + 6, len(trace) - 1)][0] if att else 0
+    rows = []
+    for f in glob.glob(os.path.join(mfma_dir, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    disp = {}
+    for r in rows:
+        d = disp.setdefault((r["Kernel_Name"], int(r["Dispatch_Id"])), {"grid": int(r["Grid_Size"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    fe = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    wr = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    f_fetch = COPY_PROBE_BYTES / (max(v for (k, _), v in fe.items() if "copyBuffer" in k) * 1024.0)
+    f_write = COPY_PROBE_BYTES / (max(v for (k, _), v in wr.items() if "copyBuffer" in k) * 1024.0)
+    def last(items, late):
+        items = sorted(items, key=lambda t: int(t[0]))
+        return items[-2 * blocks:] if late else items
+
+    lines = ["| kernel | what | dispatches | GPU cycles | µs | clock GHz | MFMA busy | MFMA busy x clock / 2.4 GHz "
+             "| HBM GB | HBM TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for sym, what, late in COUNTER_KERNELS:
+        ds = [v for _, v in last([(i, v) for (k, i), v in disp.items() if sym in k], late)]
+        grids = {d["grid"] for d in ds}
+        tr = [u for i, k, g, u in trace if sym in k and g in grids and first <= i <= end]
+        if not ds or not tr:
+            continue
+        cyc = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / len(ds) / N_XCD
+        us = sum(tr) / len(tr)
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / len(ds) / (N_SIMD * cyc)
+        fk = [v for _, v in last([(i, v) for (k, i), v in fe.items() if sym in k], late)]
+        wk = [v for _, v in last([(i, v) for (k, i), v in wr.items() if sym in k], late)]
+        gb = (sum(fk) / len(fk) * 1024 * f_fetch + sum(wk) / len(wk) * 1024 * f_write) / 1e9
+        lines.append(f"| `{sym}` | {what} | {len(ds)} | {cyc:,.0f} | {us:,.1f} | {cyc / us / 1e3:.2f} | "
+                     f"{100 * busy:.1f}% | {100 * busy * cyc / us / 1e3 / 2.4:.1f}% | {gb:.3f} | "
+                     f"{gb / us * 1e3:.2f} |")
+    print("\n".join(lines))
+
+
 def recorded_traffic(kernel):
     """HBM bytes per launch from the committed counter summary, if the kernel source is unchanged."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_480p_traffic.json")
@@ -329,9 +399,15 @@ def main():
                     help="also run one 1 GiB device-to-device copy (calibrates the HBM byte counters)")
     ap.add_argument("--parse-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="reduce two rocprofv3 counter runs to profiles/<kernel>_480p_traffic.json")
+    ap.add_argument("--parse-counters", nargs=4, metavar=("MFMA_DIR", "FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
+                    help="print the per-kernel MFMA utilisation / clock / HBM table of three counter runs "
+                         "and a kernel-trace run")
     args = ap.parse_args()
     if args.parse_traffic:
         parse_traffic(*args.parse_traffic)
+        return
+    if args.parse_counters:
+        parse_counters(*args.parse_counters)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
