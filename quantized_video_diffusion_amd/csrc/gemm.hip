@@ -58,15 +58,16 @@ QVD_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
     tn = in / gm;
 }
 
-// GELU(y) = y/2 (1 + erf(y/sqrt 2)) = y/2 erfc(|y|/sqrt 2) for y < 0, y/2 (2 - erfc(y/sqrt 2)) for
-// y >= 0.  erfc from the Chebyshev fit of W. H. Press et al., Numerical Recipes, section 6.2
-// (function erfcc): erfc(z) = t exp(-z^2 - 1.26551223 + t (1.00002368 + ... + 0.17087277 t^8)),
-// t = 1/(1 + z/2), with fractional error below 1.2e-7 for every z >= 0 -- also in the tail, where
-// a form built on 1 - erf would lose the small values that a static E4M3 scale can still resolve.
-// The exponent is evaluated in log2 units (coefficients times log2 e) for exp2.
+// GELU(y) = y Phi(y), with Phi(y) = h for y < 0 and 1 - h for y >= 0, h = erfc(z) / 2, z = |y|/sqrt 2.
+// erfc from the Chebyshev fit of W. H. Press et al., Numerical Recipes, section 6.2 (function erfcc):
+// erfc(z) = t exp(-z^2 - 1.26551223 + t (1.00002368 + ... + 0.17087277 t^8)), t = 1/(1 + z/2), with
+// fractional error below 1.2e-7 for every z >= 0 -- also in the tail, where a form built on 1 - erf
+// would lose the small values that a static E4M3 scale can still resolve.  The exponent is evaluated
+// in log2 units (coefficients times log2 e) for exp2, with the halving folded into its constant term
+// (-1.8257482 - 1), and z enters through |y| (t = 1/(1 + |y|/(2 sqrt 2)), z^2 log2 e = |y|^2 log2(e)/2).
 QVD_DEV float gelu_erf(float y) {
-    const float z = fabsf(y) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+    const float ay = fabsf(y);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.35355339059327373f, ay, 1.0f));
     float p = fmaf(0.2465173f, t, -1.1861149f);
     p = fmaf(p, t, 2.1474745f);
     p = fmaf(p, t, -1.6377531f);
@@ -75,10 +76,19 @@ QVD_DEV float gelu_erf(float y) {
     p = fmaf(p, t, 0.13963005f);
     p = fmaf(p, t, 0.5397006f);
     p = fmaf(p, t, 1.4427292f);
-    p = fmaf(p, t, -1.8257482f);
-    const float arg = fmaf(-(z * 1.4426950408889634f), z, p);
-    const float ec = t * __builtin_amdgcn_exp2f(arg);            // erfc(z)
-    return 0.5f * y * (y < 0.0f ? ec : 2.0f - ec);
+    p = fmaf(p, t, -2.8257482f);
+    const float arg = fmaf(-(ay * 0.72134752044448170f), ay, p);
+    const float h = t * __builtin_amdgcn_exp2f(arg);             // erfc(z) / 2
+    return y * (y < 0.0f ? h : 1.0f - h);
+}
+
+// Running max of |v| over the bf16 halves of packed pairs, kept as two 16-bit magnitudes: for finite
+// bf16 values the order of |v| is the order of (bits & 0x7FFF) as unsigned integers, so one packed
+// 16-bit max per pair does what two extractions and float maxima would.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+QVD_DEV u32 absmax_bf16x2(u32 m, u32 p) {
+    return __builtin_bit_cast(u32, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m),
+                                                             __builtin_bit_cast(u16x2, p & 0x7FFF7FFFu)));
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -128,6 +138,7 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
     auto bf16_rounds = [&](auto mode, float& amax) {
         constexpr int MODE = decltype(mode)::value;      // 0 plain, 1 GELU, 2 x += gate y
         constexpr int RPR = BR / LY::RB;
+        u32 amb = 0u;                                    // MODE 1: packed |bf16| maxima
 #pragma unroll
         for (int rd = 0; rd < 128 / BR; ++rd) {
             if (MODE == 2) {
@@ -166,9 +177,7 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
                         }
                         p0 = pack_bf16x2(y[0], y[1]);
                         p1 = pack_bf16x2(y[2], y[3]);
-                        if (MODE == 1 && mw0 + BR * rd + ml < M)
-                            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(p0)), fabsf(bf16hi(p0))),
-                                                     fmaxf(fabsf(bf16lo(p1)), fabsf(bf16hi(p1)))));
+                        if (MODE == 1 && mw0 + BR * rd + ml < M) amb = absmax_bf16x2(absmax_bf16x2(amb, p0), p1);
                     }
                     *slot = (u32x2){p0, p1};
                 }
@@ -183,6 +192,7 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
             }
             lds_wait();
         }
+        if (MODE == 1) amax = fmaxf(amax, fmaxf(bf16lo(amb), bf16hi(amb)));
     };
 
     if (EPI == QVD_EPI_GELU) {
@@ -259,10 +269,10 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
                 const u32x4 v = *reinterpret_cast<const u32x4*>(bslot(ml, 4 * bk + q));
                 ws[4 * q] = v.x; ws[4 * q + 1] = v.y; ws[4 * q + 2] = v.z; ws[4 * q + 3] = v.w;
             }
-            float amax = 0.0f;
+            u32 amb = 0u;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(ws[j])), fabsf(bf16hi(ws[j]))));
-            const int k = mx_exponent(amax);
+            for (int j = 0; j < 16; ++j) amb = absmax_bf16x2(amb, ws[j]);
+            const int k = mx_exponent(fmaxf(bf16lo(amb), bf16hi(amb)));
             u32 o[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) o[j] = e2m1_encode8_bf16(ws + 4 * j, k);
@@ -336,6 +346,7 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
         // LDS: 128 token rows of WN codes.
         float amax = 0.0f;
         if (wave_live) {
+            u32 amb = 0u;
 #pragma unroll
             for (int cg = 0; cg < LY::NCG; ++cg) {
                 const float4 b = load_bias4(g.bias, nw0 + LY::ncol(cg, lane));
@@ -345,11 +356,10 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
                     const v4f c = LY::get(acc, cg, r);
                     const u32 p0 = pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y);
                     const u32 p1 = pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w);
-                    if (m < M)
-                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(p0)), fabsf(bf16hi(p0))),
-                                                 fmaxf(fabsf(bf16lo(p1)), fabsf(bf16hi(p1)))));
+                    if (m < M) amb = absmax_bf16x2(absmax_bf16x2(amb, p0), p1);
                 }
             }
+            amax = fmaxf(bf16lo(amb), bf16hi(amb));
         }
         amax = wave_max(amax);
         if (WN == 64) {                                // every wave takes part: the barrier is shared
