@@ -197,3 +197,94 @@ def test_block_deterministic():
         Q.dit_block_forward(bw, mod, xd, i32_dev(idx), i32_dev(cnt))
         outs.append(host_bits(xd))
     np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_block_480p_full_size_equals_its_steps():
+    """The 480p block at full size, in the configuration the stack step times (33,784 tokens, Trim
+    width, block 0's weights and 80%-sparse mask, the timestep-999 modulation): dit_block_forward must
+    equal, bit for bit, the same block computed step by step through the separately exported entry
+    points -- modulate, the QKV GEMM, the attention, the per-tensor quantizer, the residual GEMMs --
+    whose outputs the 480p-shape tests compare with the oracle.  (The oracle's whole block at this size
+    would take minutes: the per-tensor scales of O and GELU couple every token.)  Then zero gates leave
+    the values of x unchanged at this size."""
+    w = W.WORKLOADS["trim_stack42_480p"]
+    L, d, H = w.L, w.d, w.n_heads
+    say("480p block vs its steps", L, d, H)
+    x = W.activations(w, 0)
+    bw = _gpu_weights(W.block_weights(w, 0, 0), w)
+    idx, cnt = W.block_mask(w, 0, 0)
+    idx_d, cnt_d = i32_dev(idx), i32_dev(cnt)
+    mod = Q.adaln_project(999.0, fp16_dev(W.adaln_basis(w, 0)), fp16_dev(W.adaln_proj(w, 0, 0)))
+
+    xb = bf16_dev(x)
+    Q.dit_block_forward(bw, mod, xb, idx_d, cnt_d)
+
+    xs = bf16_dev(x)
+    h1, s1 = Q.adaln_modulate(xs, mod, 0)
+    q8, k8, vt, qs, ks = Q.gemm_fp8(h1, s1, bw.w["qkv"], bw.s["qkv"], mode=_lib.QVD_EPI_QKV, n_heads=H)
+    o = Q.sparse_attn_vt(q8, qs, k8, ks, vt, idx_d, cnt_d)
+    o8, so = Q.quant_fp8_per_tensor(o.reshape(L, d))
+    Q.gemm_fp8(o8, so, bw.w["o"], bw.s["o"], mode=_lib.QVD_EPI_RESID_GATE, out=xs, resid=xs, gate=mod[2])
+    h2, s2 = Q.adaln_modulate(xs, mod, 1)
+    g = Q.gemm_fp8(h2, s2, bw.w["up"], bw.s["up"], mode=_lib.QVD_EPI_GELU)
+    g8, sg = Q.quant_fp8_per_tensor(g)
+    Q.gemm_fp8(g8, sg, bw.w["down"], bw.s["down"], mode=_lib.QVD_EPI_RESID_GATE, out=xs, resid=xs,
+               gate=mod[5])
+    got, steps = host_bits(xb), host_bits(xs)
+    say("480p block: differing outputs", int(np.count_nonzero(got != steps)), "of", got.size)
+    np.testing.assert_array_equal(got, steps)
+    assert not np.array_equal(got, x), "the block left x unchanged"
+
+    mod0 = mod.clone()
+    mod0[2].zero_()
+    mod0[5].zero_()
+    xz = bf16_dev(x)
+    Q.dit_block_forward(bw, mod0, xz, idx_d, cnt_d)
+    # x + 0 * y: a negative zero of x plus +0 rounds to +0, so compare values, not bits
+    np.testing.assert_array_equal(OC.bf16_to_f64(host_bits(xz)), OC.bf16_to_f64(x))
+
+
+@pytest.mark.parametrize("fmt", ["w4a8_static", "w4a4"])
+def test_block_768p_4bit_full_size_equals_its_steps(fmt):
+    """The 768p block at full size with MXFP4 weights (85,696 tokens, the last query tile of 64 rows,
+    135 of 670 key tiles kept), as the 768p report times it: W4A8 with static E4M3 activation scales,
+    and W4A4.  dit_block_forward must equal, bit for bit, the block computed through the exported
+    steps, each of which has its own oracle tests."""
+    w = W.WORKLOADS["block_768p_mxfp4"]
+    L, d, H = w.L, w.d, w.n_heads
+    say("768p block vs its steps", fmt, L, d, H)
+    x = W.activations(w, 0)
+    gfmt = _lib.QVD_W_MXFP4 if fmt == "w4a8_static" else _lib.QVD_W_MXFP4_A4
+    act = np.array([1.6, 4.0, 1.4, 600.0], np.float32) if fmt == "w4a8_static" else None
+    bw = _gpu_weights(W.block_weights(w, 0, 0), w, gfmt, act)
+    idx, cnt = W.block_mask(w, 0, 0)
+    idx_d, cnt_d = i32_dev(idx), i32_dev(cnt)
+    mod = Q.adaln_project(999.0, fp16_dev(W.adaln_basis(w, 0)), fp16_dev(W.adaln_proj(w, 0, 0)))
+
+    xb = bf16_dev(x)
+    Q.dit_block_forward(bw, mod, xb, idx_d, cnt_d)
+
+    xs = bf16_dev(x)
+    wq = {s: (bw.w[s], bw.e8[s]) for s in ("qkv", "o", "up", "down")}
+    rg = dict(mode=_lib.QVD_EPI_RESID_GATE, out=xs, resid=xs)
+    if fmt == "w4a4":
+        hp, he = Q.adaln_modulate_mxfp4(xs, mod, 0)
+        q8, k8, vt, qs, ks = Q.gemm_mxfp4_w4a4(hp, he, *wq["qkv"], mode=_lib.QVD_EPI_QKV, n_heads=H)
+        op, oe = Q.sparse_attn_vt_mxfp4(q8, qs, k8, ks, vt, idx_d, cnt_d)
+        Q.gemm_mxfp4_w4a4(op, oe, *wq["o"], gate=mod[2], **rg)
+        hp, he = Q.adaln_modulate_mxfp4(xs, mod, 1)
+        gp, ge = Q.gemm_mxfp4_w4a4(hp, he, *wq["up"], mode=_lib.QVD_EPI_GELU_MXFP4)
+        Q.gemm_mxfp4_w4a4(gp, ge, *wq["down"], gate=mod[5], **rg)
+    else:
+        a = bw.act_scale
+        h, s = Q.adaln_modulate(xs, mod, 0, act_scale=a[0:1])
+        q8, k8, vt, qs, ks = Q.gemm_mxfp4(h, s, *wq["qkv"], mode=_lib.QVD_EPI_QKV, n_heads=H)
+        o8 = Q.sparse_attn_vt_e4m3(q8, qs, k8, ks, vt, idx_d, cnt_d, a[1:2])
+        Q.gemm_mxfp4(o8.reshape(L, d), a[1:2], *wq["o"], gate=mod[2], **rg)
+        h, s = Q.adaln_modulate(xs, mod, 1, act_scale=a[2:3])
+        g8 = Q.gemm_mxfp4(h, s, *wq["up"], mode=_lib.QVD_EPI_GELU_E4M3, out_scale=a[3:4])
+        Q.gemm_mxfp4(g8, a[3:4], *wq["down"], gate=mod[5], **rg)
+    got, steps = host_bits(xb), host_bits(xs)
+    say("768p block: differing outputs", int(np.count_nonzero(got != steps)), "of", got.size)
+    np.testing.assert_array_equal(got, steps)
+    assert not np.array_equal(got, x), "the block left x unchanged"
