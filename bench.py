@@ -76,7 +76,7 @@ def make_stack(w, n_blocks, seed, threads=8):
     return blocks, proj_all, masks, kept, host_block0
 
 
-def cpu_baseline(w, seed, host_block0, sample_tokens=4096):
+def cpu_baseline(w, seed, host_block0, sample_tokens=6144):
     """The oracle (as it stands) on a bounded sample of the workload: one block of the stack on the
     first `sample_tokens` tokens of the 480p input, with the block's weights and an 80%-sparse mask
     drawn for that token count; reported in the metric's unit (algorithmic TFLOP/s)."""
