@@ -39,7 +39,6 @@ QVD_DEV u32 pack_bf16x2(float lo, float hi) {
     r.y = (__bf16)hi;
     return __builtin_bit_cast(u32, r);
 }
-QVD_DEV uint16_t f32_to_bf16(float x) { return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu); }
 
 // ---------------------------------------------------------------------------------------------
 // E4M3 ("FN") encoding, round to nearest even, saturating at 448, NaN -> 0x7F.  Written from the
