@@ -8,17 +8,14 @@ Plain definition, per head h and 128-row query tile i:
   keys(h, i)  = the rows of the kept key tiles kv_idx[h][i][:kv_cnt[h][i]] that exist (< L);
   S[r][c]     = sum_e q[r][h][e] * k[c][h][e]                      (exact integer)
   s[r][c]     = S[r][c] * q_scale[h][i] * k_scale[h][tile(c)] * sm_scale
-  e[r][c]     = fp16(exp(s[r][c] - max_c' s[r][c']))                (softmax numerator, row max
-                                                                       over every kept key)
-  out[r][h][:] = sum_c e[r][c] * fp16(v[c][h][:]) / sum_c e[r][c]
+  out[r][h][:] = sum_c softmax_c(s[r][:]) * v[c][h][:]
+with V taken as the bf16 values it is given in, and everything after the integer scores in float64
+(the row maximum is subtracted before exponentiating; that changes nothing but the range).
 Readings: a key tile not in the list weighs zero (it is skipped, not attended with -inf after the
 fact); key rows >= L do not exist; sm_scale = 1/sqrt(head_dim) with the natural exponential.  The
-pages give no precision for softmax.V; the reading taken is that the softmax numerators, taken
-against the row maximum, are rounded once to fp16 (round to nearest even) and that V enters the
-product as fp16 (bf16 values convert exactly between 2^-14 and 65,504; larger magnitudes saturate
-at 65,504); the products, sums and the normalisation by the sum of the rounded numerators are
-exact (float64).  Without the rounding of the numerators this is the exact softmax attention;
-each rounded weight is within a relative 2^-11 of the exact one.
+pages give no precision for softmax.V, so the oracle fixes none: it is the exact softmax attention
+of the quantized scores, and an implementation's own rounding of the weights or of V is a deviation
+to be bounded, not part of the definition.
 """
 from __future__ import annotations
 
@@ -27,13 +24,6 @@ import numpy as np
 from .codecs import bf16_to_f64
 
 TILE = 128
-F16_MAX = 65504.0
-
-
-def f16_round(x) -> np.ndarray:
-    """float64 -> nearest fp16 value (ties to even, fp16 subnormals kept), as float64.
-    numpy's float64 -> float16 cast rounds once, directly from the float64 value."""
-    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
 def kept_keys(kv_idx, kv_cnt, h: int, i: int, L: int) -> tuple[np.ndarray, np.ndarray]:
@@ -48,17 +38,20 @@ def kept_keys(kv_idx, kv_cnt, h: int, i: int, L: int) -> tuple[np.ndarray, np.nd
 
 def sparse_attn_tile(q, q_scale, k, k_scale, v_bits, kv_idx, kv_cnt, h: int, i: int,
                      sm_scale: float) -> np.ndarray:
-    """Output rows of query tile i of head h, float64 [rows][head_dim]."""
+    """Output rows of query tile i of head h, float64 [rows][head_dim] (zeros for a row with no
+    kept key)."""
     L = q.shape[0]
     rows = np.arange(i * TILE, min(L, (i + 1) * TILE))
     keys, key_tile = kept_keys(kv_idx, kv_cnt, h, i, L)
+    if keys.size == 0:
+        return np.zeros((len(rows), q.shape[2]))
     # exact: |S| <= 128 * 127 * 127 < 2^53, so the float64 library product is the integer sum
     S = q[rows, h, :].astype(np.float64) @ k[keys, h, :].astype(np.float64).T
     fac = (np.float64(q_scale[h, i]) * np.asarray(k_scale[h], dtype=np.float64)[key_tile]
            * sm_scale)
     s = S * fac[None, :]
-    e = f16_round(np.exp(s - s.max(axis=1, keepdims=True)))
-    V = f16_round(np.clip(bf16_to_f64(v_bits[keys, h, :]), -F16_MAX, F16_MAX))
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    V = bf16_to_f64(v_bits[keys, h, :])
     return (e @ V) / e.sum(axis=1, keepdims=True)
 
 
