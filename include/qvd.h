@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define QVD_ABI_VERSION 1
+#define QVD_ABI_VERSION 2
 
 enum qvd_status {
     QVD_OK = 0,
@@ -135,43 +135,59 @@ int adaln_modulate_mxfp4(const uint16_t* x, int32_t L, int32_t d, const float* m
  * and the "运行速度如何" note (INT8 Q/K).  For head h and query tile i (128 rows):
  *   keys   = rows of the key tiles kv_idx[h][i][0 .. kv_cnt[h][i]-1] that exist (< L)
  *   s      = (Q8 K8^T)[exact int32] * q_scale[h][i] * k_scale[h][j] * sm_scale
- *   e      = fp16(exp(s - max over all kept keys of the row))     (softmax numerators)
- *   out    = sum e * fp16(V) / sum e  per query row, written as bf16.
+ *   out    = softmax over the kept keys of s, times V (bf16 values)  per query row, as bf16.
  *   q, k   : int8 [L][H][head_dim];  q_scale, k_scale: fp32 [H][T], T = ceil(L/128).
  *   v      : bf16 [L][H][head_dim];  out: bf16 [L][H][head_dim].
  *   kv_idx : int32 [H][T][kmax], 1 <= kmax <= 1024; kv_cnt: int32 [H][T].  Entries outside [0, T) and counts outside
  *            [0, kmax] are ignored (clamped), so device data can never send the kernel out of
  *            bounds; a row with no kept key outputs zeros.  Tile lists are expected ascending
  *            with the diagonal present; another order changes the result only at the level of
- *            fp16/fp32 rounding.
+ *            bf16/fp32 rounding.
  *   out_amax_partials : NULL, or fp32 [H][T] receiving max|out| of each (h, i) tile (feeds the
  *            dynamic FP8 quantization of the attention output without another pass).
- *   ws     : qvd_sparse_attn_ws_bytes(L, H) bytes: V transposed to fp16 [H][128][T*128].
+ *   ws     : qvd_sparse_attn_ws_bytes(L, H) bytes: V transposed to fp16 with one power-of-two
+ *            scale per head (as the QKV GEMM epilogue and qvd_vt_unify write it), and its exponents.
  * Arithmetic: INT8 MFMA scores (exact int32); one pass over the kept tiles with a reference
  * maximum m per row, moved (and the fp32 sums rescaled) only when a tile's row maximum exceeds it
  * by more than 8 in log2 units: numerators exp2((s - m) log2 e) <= 2^8 rounded to fp16, fp16 MFMA
- * P.V and numerator sums with fp32 accumulation.  Each weight is within one fp16 rounding of the
- * numerator taken against the final maximum.  |V| above 65504 saturates to 65504. */
+ * P.V and numerator sums with fp32 accumulation, normalised by the sum of the rounded numerators.
+ * Each weight is the exact one up to a relative 2^-11 (the numerator's fp16 rounding) and fp32
+ * arithmetic.  V enters at any finite bf16 magnitude: fp16 V 2^-E per head, exact for every
+ * element within 2^28 of the head's max|V|, and the output is multiplied back by 2^E. */
 size_t qvd_sparse_attn_ws_bytes(int32_t L, int32_t H);
 int sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                 const uint16_t* v, int32_t L, int32_t H, int32_t head_dim,
                 const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
                 uint16_t* out, float* out_amax_partials, void* ws, size_t ws_bytes, void* stream);
-/* The same attention with V already transposed to fp16: vt [H][128][T*128] (keys contiguous per
- * (head, dim) row; columns L .. T*128-1 must hold finite values, e.g. zeros).  This is the layout
- * the QKV GEMM epilogue writes. */
+/* bf16 V [L][H][128] -> fp16 V^T [H][128][T*128] (columns L.. zeroed) with one exponent per
+ * (head, 128-token tile) in tile_exp [H][T], by the rule of the QKV epilogue (QVD_EPI_QKV): the
+ * transpose sparse_attn runs on its V, exported for callers that hold V token-major. */
+int qvd_vt_from_bf16(const uint16_t* v, int32_t L, int32_t H, uint16_t* vt, int32_t* tile_exp, void* stream);
+
+/* One V scale per head, in place: vt fp16 [H][128][T*128] holds each (head, 128-token tile) j as
+ * fp16(v 2^-tile_exp[h][j]) (the QKV GEMM epilogue's output).  Writes head_exp[h] = E = the largest
+ * of the head's tile exponents and rescales every tile with a smaller exponent e by 2^(e - E), so the
+ * head holds fp16(v 2^-E) (exact wherever that is an fp16 normal; a value more than 2^28 below the
+ * head's max|v| may round to the fp16 subnormal grid).  Tiles already at E are not touched.
+ * tile_exp: int32 [H][T]; head_exp: int32 [H]. */
+int qvd_vt_unify(uint16_t* vt, int32_t L, int32_t H, const int32_t* tile_exp, int32_t* head_exp,
+                 void* stream);
+
+/* The same attention with V already transposed: vt fp16 [H][128][T*128] holding V 2^-v_exp[h]
+ * (keys contiguous per (head, dim) row; columns L .. T*128-1 must hold finite values, e.g. zeros),
+ * v_exp int32 [H].  This is the layout the QKV GEMM epilogue and qvd_vt_unify write. */
 int qvd_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k,
-                       const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                       const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int32_t L, int32_t H,
                        const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
                        uint16_t* out, float* out_amax_partials, void* stream);
 
-/* The same attention over fp16 V^T writing, instead of bf16 O, the E4M3 codes
+/* The same attention over fp16 V^T (and its head exponents) writing, instead of bf16 O, the E4M3 codes
  *   out_q[l][h][d] = E4M3(bf16(O[l][h][d]) * fp32(1 / *out_scale))
  * that quant_fp8_per_tensor computes from bf16 O with scale_in = out_scale (a static, calibrated
  * per-tensor scale > 0), without writing O: the attention output enters the out-projection GEMM
  * directly.  out_q: uint8 [L][H][128], 16-byte aligned. */
 int qvd_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
-                            const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                            const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int32_t L, int32_t H,
                             const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
                             const float* out_scale, uint8_t* out_q, void* stream);
 /* The same attention writing the MXFP4 codes of bf16 O (W4A4 blocks), per (token, head) and 32
@@ -179,7 +195,7 @@ int qvd_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t*
  * out_packed uint8 [L][H][64] (dim 2j in the low nibble of byte j; 16-byte aligned), out_e8m0
  * uint8 [L][H][4] (4-byte aligned).  O itself is not written. */
 int qvd_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int8_t* k,
-                             const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                             const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int32_t L, int32_t H,
                              const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
                              uint8_t* out_packed, uint8_t* out_e8m0, void* stream);
 
@@ -226,9 +242,13 @@ enum qvd_epilogue_mode {
                                K parts are then quantized per (head, 128-token tile) exactly as
                                quant_int8_qk does, into q8/k8 int8 [M][H][128] with scales
                                q_scale/k_scale [H][ceil(M/128)]; the V part (bf16 values) is
-                               written transposed and converted to fp16 into v as
-                               [H][128][ceil(M/128)*128], columns M.. of the last tile zeroed
-                               (the layout qvd_sparse_attn_vt reads)                            */
+                               written transposed in fp16 into v as [H][128][ceil(M/128)*128],
+                               columns M.. of the last tile zeroed, each (head, 128-token tile)
+                               as fp16(v 2^-e) with its exponent e in v_exp [H][ceil(M/128)]:
+                               e = 0 while the tile's max|v| is in [2^-6, 2^15), else
+                               floor(log2 max|v|) - 14 (exact wherever v 2^-e is an fp16
+                               normal).  qvd_vt_unify then gives the head one exponent, the
+                               layout qvd_sparse_attn_vt reads                                  */
     QVD_EPI_GELU_E4M3 = 5,  /* out_e4m3[m][n] = E4M3(bf16(GELU(y)) * fp32(1 / *out_scale)): the
                                GELU output quantized with a static per-tensor scale exactly as
                                quant_fp8_per_tensor does with scale_in = out_scale, without the
@@ -251,6 +271,7 @@ typedef struct {
     uint16_t* v;                /* QVD_EPI_QKV: fp16 V^T [H][128][ceil(M/128)*128]               */
     float* q_scale;
     float* k_scale;
+    int32_t* v_exp;             /* QVD_EPI_QKV: int32 [H][ceil(M/128)] V tile exponents          */
     uint8_t* out_e4m3;          /* QVD_EPI_GELU_E4M3: E4M3 codes [M][N]                          */
     const float* out_scale;     /* QVD_EPI_GELU_E4M3: device fp32 static scale s (> 0)           */
     uint8_t* out_e2m1;          /* QVD_EPI_GELU_MXFP4: packed E2M1 [M][N/2], 16-byte aligned     */
@@ -314,6 +335,43 @@ size_t qvd_block_ws_bytes(const qvd_block_params* p, int32_t L);
 int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
                       const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* Stage-by-stage inspection of the same block (for parity tests that feed each stage's GPU inputs to
+ * a reference of the next stage).  qvd_block_forward_until runs dit_block_forward's own launches, with
+ * the same arguments, and returns after `stage`; the intermediates are then in the workspace (and x),
+ * at the offsets qvd_block_ws_layout gives.  After:
+ *   QVD_STAGE_MODULATE1 : h = h1 codes (E4M3 [L][d], or packed E2M1 [L][d/2] + h_e8m0 [L][d/32] in
+ *                         W4A4), scales[0] = s1 (dynamic FP8)
+ *   QVD_STAGE_QKV       : q8, k8 [L][H][128], q_scale, k_scale [H][T]; vt fp16 [H][128][T*128] with
+ *                         vt_tile_exp [H][T] (the QVD_EPI_QKV outputs)
+ *   QVD_STAGE_VT        : vt with one exponent per head, vt_head_exp [H] (qvd_vt_unify)
+ *   QVD_STAGE_ATTN      : o bf16 [L][d] (dynamic FP8); with static scales or W4A4 the attention writes
+ *                         the codes of O into h directly, as at QVD_STAGE_OQUANT
+ *   QVD_STAGE_OQUANT    : h = codes of O, scales[1] = s_O (dynamic FP8)
+ *   QVD_STAGE_OPROJ     : x = x1
+ *   QVD_STAGE_MODULATE2 : h = h2 codes (+ h_e8m0), scales[2] = s2
+ *   QVD_STAGE_UP        : g bf16 [L][F] (dynamic FP8); static scales or W4A4: the codes of g, as at
+ *                         QVD_STAGE_GQUANT
+ *   QVD_STAGE_GQUANT    : g8 = codes of g (E4M3 [L][F], or packed E2M1 [L][F/2] + g_e8m0 [L][F/32]),
+ *                         scales[3] = s_g (dynamic FP8)
+ *   QVD_STAGE_ALL       : x = x2 (the whole block, as dit_block_forward)
+ * Later stages overwrite h and x.  Errors as dit_block_forward; QVD_EINVAL for an unknown stage. */
+enum qvd_block_stage {
+    QVD_STAGE_MODULATE1 = 1, QVD_STAGE_QKV = 2, QVD_STAGE_VT = 3, QVD_STAGE_ATTN = 4, QVD_STAGE_OQUANT = 5,
+    QVD_STAGE_OPROJ = 6, QVD_STAGE_MODULATE2 = 7, QVD_STAGE_UP = 8, QVD_STAGE_GQUANT = 9, QVD_STAGE_ALL = 10
+};
+int qvd_block_forward_until(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
+                            const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, int32_t stage,
+                            void* ws, size_t ws_bytes, void* stream);
+/* Byte offsets, in dit_block_forward's workspace for L tokens, of its intermediates: offsets[i] for
+ * i in qvd_block_ws_slot.  Slots the configuration does not use (o and g with static scales or W4A4,
+ * the E8M0 arrays outside W4A4) have zero-length regions.  scales: fp32 [4] (s1, s_O, s2, s_g). */
+enum qvd_block_ws_slot {
+    QVD_WS_H = 0, QVD_WS_Q8, QVD_WS_K8, QVD_WS_VT, QVD_WS_VT_TILE_EXP, QVD_WS_VT_HEAD_EXP, QVD_WS_O, QVD_WS_G,
+    QVD_WS_G8, QVD_WS_H_E8M0, QVD_WS_G_E8M0, QVD_WS_Q_SCALE, QVD_WS_K_SCALE, QVD_WS_SCALES, QVD_WS_SEL_IDX,
+    QVD_WS_SEL_CNT, QVD_WS_SLOT_COUNT
+};
+int qvd_block_ws_layout(const qvd_block_params* p, int32_t L, int64_t* offsets);
 
 /* ------------------------------------------------------------------------------------------
  * MXFP4 weights and static-scale calibration -- farwalk post 6/8 (calibrated 4-bit layers).

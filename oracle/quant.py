@@ -45,6 +45,15 @@ def quant_fp8_per_tensor(x_f32, scale_in=None):
     return e4m3_encode(x * inv), s
 
 
+def quant_fp8_with_amax(x_f32, amax_f32):
+    """The dynamic per-tensor rule applied to part of a tensor whose amax (over the whole tensor) is
+    given: codes E4M3(x * fp32(448/amax)), s = fp32(amax/448).  Lets rows of a large tensor be
+    checked one by one once its amax is known."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    s, inv = fp8_scale_dynamic(amax_f32)
+    return e4m3_encode(x * inv), s
+
+
 def quant_fp8_bf16(x_bits, scale_in=None):
     """Per-tensor FP8 of a bf16 tensor (given as bit patterns)."""
     return quant_fp8_per_tensor(bf16_to_f64(x_bits).astype(np.float32), scale_in)

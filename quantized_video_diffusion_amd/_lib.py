@@ -17,7 +17,11 @@ QVD_OK, QVD_EINVAL, QVD_ESHAPE, QVD_EALIGN, QVD_EWORKSPACE, QVD_EUNSUPPORTED, QV
 (QVD_EPI_F32, QVD_EPI_BF16, QVD_EPI_RESID_GATE, QVD_EPI_GELU, QVD_EPI_QKV, QVD_EPI_GELU_E4M3,
  QVD_EPI_GELU_MXFP4) = range(7)
 QVD_W_FP8, QVD_W_MXFP4, QVD_W_MXFP4_A4 = 0, 1, 2
-ABI_VERSION = 1
+(QVD_STAGE_MODULATE1, QVD_STAGE_QKV, QVD_STAGE_VT, QVD_STAGE_ATTN, QVD_STAGE_OQUANT, QVD_STAGE_OPROJ,
+ QVD_STAGE_MODULATE2, QVD_STAGE_UP, QVD_STAGE_GQUANT, QVD_STAGE_ALL) = range(1, 11)
+WS_SLOTS = ("h", "q8", "k8", "vt", "vt_tile_exp", "vt_head_exp", "o", "g", "g8", "h_e8m0", "g_e8m0",
+            "q_scale", "k_scale", "scales", "sel_idx", "sel_cnt")
+ABI_VERSION = 2
 
 _p = C.c_void_p
 _i32 = C.c_int32
@@ -30,7 +34,7 @@ class Epilogue(C.Structure):
     _fields_ = [
         ("mode", _i32), ("n_heads", _i32),
         ("out_f32", _p), ("out_bf16", _p), ("resid", _p), ("gate", _p), ("amax_partials", _p),
-        ("q8", _p), ("k8", _p), ("v", _p), ("q_scale", _p), ("k_scale", _p),
+        ("q8", _p), ("k8", _p), ("v", _p), ("q_scale", _p), ("k_scale", _p), ("v_exp", _p),
         ("out_e4m3", _p), ("out_scale", _p), ("out_e2m1", _p), ("out_e8m0", _p),
     ]
 
@@ -63,11 +67,14 @@ SIGNATURES = {
     "qvd_sparse_attn_ws_bytes": (_sz, [_i32, _i32]),
     "sparse_attn": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _f32, _p, _p, _p, _sz,
                               _p]),
-    "qvd_sparse_attn_vt": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p, _p]),
-    "qvd_sparse_attn_vt_e4m3": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p,
-                                          _p]),
-    "qvd_sparse_attn_vt_mxfp4": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p,
-                                           _p]),
+    "qvd_vt_from_bf16": (C.c_int, [_p, _i32, _i32, _p, _p, _p]),
+    "qvd_vt_unify": (C.c_int, [_p, _i32, _i32, _p, _p, _p]),
+    "qvd_sparse_attn_vt": (C.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p, _p,
+                                     _p]),
+    "qvd_sparse_attn_vt_e4m3": (C.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32, _p,
+                                          _p, _p]),
+    "qvd_sparse_attn_vt_mxfp4": (C.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _f32,
+                                           _p, _p, _p]),
     "qvd_select_tiles_ws_bytes": (_sz, [_i32, _i32]),
     "qvd_select_tiles": (C.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p, _sz, _p]),
     "qvd_qk_int32_tile": (C.c_int, [_p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]),
@@ -77,6 +84,9 @@ SIGNATURES = {
     "qvd_gemm_mxfp4_w4a4": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, C.POINTER(Epilogue), _p]),
     "qvd_block_ws_bytes": (_sz, [C.POINTER(BlockParams), _i32]),
     "dit_block_forward": (C.c_int, [C.POINTER(BlockParams), _p, _p, _i32, _p, _p, _i32, _p, _sz, _p]),
+    "qvd_block_forward_until": (C.c_int, [C.POINTER(BlockParams), _p, _p, _i32, _p, _p, _i32, _i32, _p,
+                                          _sz, _p]),
+    "qvd_block_ws_layout": (C.c_int, [C.POINTER(BlockParams), _i32, C.POINTER(_i64)]),
     "qvd_quant_mxfp4": (C.c_int, [_p, _i32, _i32, _p, _p, _p]),
     "qvd_amax_update": (C.c_int, [_p, _i64, _p, _p]),
     "qvd_clip_count": (C.c_int, [_p, _i64, _p, _p, _p]),

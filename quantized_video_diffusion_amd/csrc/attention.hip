@@ -18,17 +18,19 @@
 //                  see SCORE_BIAS).
 // The reference m moves only when a tile's row maximum exceeds it by more than 8 (log2 units), and
 // then the fp32 sums so far are multiplied by exp2(m_old - m_new); otherwise the numerators stay
-// below 2^8.  A numerator rounded against such a reference and rescaled differs from the one rounded
-// against the final maximum by at most one fp16 rounding (relative 2^-11), and the output is
-// normalised by the sum of the numerators actually used.
+// below 2^8.  Each weight is the exact softmax weight up to one fp16 rounding of its numerator
+// (relative 2^-11) and fp32 arithmetic; the output is normalised by the sum of the numerators
+// actually used.  V arrives in fp16 scaled by one power of two 2^-E[h] per head (vt_tile_exponent,
+// k_vt_unify), exact for every element within 2^28 of the head's max|V|, whatever its magnitude;
+// the output stage multiplies by 2^E[h].
 //
 // Staging: tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no register round trip).  The K
 // tile's rows are permuted (key_of_row) so that each lane's 8 numerators of a 32-key block are 8
 // consecutive keys, read from V^T in one 16-byte access.  Each lane picks the global 16-byte chunk
 // that belongs at its LDS slot, which applies an XOR swizzle:
 // K rows (128 B) swizzle chunks by row & 7, V^T rows (256 B, fp16, keys contiguous) by row & 15,
-// so the 16-row MFMA fragment reads hit distinct banks.  V arrives transposed and in fp16 from the
-// QKV GEMM epilogue (or from a conversion pass for bf16 callers).  Computing the transposed products
+// so the 16-row MFMA fragment reads hit distinct banks.  V arrives transposed from the QKV GEMM
+// epilogue (or from a transpose pass for callers holding V token-major).  Computing the transposed products
 // makes each lane own one query row in both MFMA outputs.
 #include "common.h"
 #include "kernels.h"
@@ -50,6 +52,7 @@ struct GroupSmem {
 struct AttnSmem {
     GroupSmem grp[2];
     int wcount[2][4];
+    float wkmax[2][4];              // per-wave maxima of the kept tiles' K scales
     int n[2];                       // kept tiles per group
     float red[8];                   // per-group reductions of max|O|
 };
@@ -57,6 +60,10 @@ struct AttnSmem {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+
+// a 32-bit word as two fp16 values, taken by value (a bit_cast applied to a vector element lvalue
+// reads element 0)
+QVD_DEV v2h as_v2h(u32 w) { return __builtin_bit_cast(v2h, w); }
 
 QVD_DEV u32 pack_f16x2(float lo, float hi) {
     v2h r;
@@ -172,11 +179,39 @@ QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v
 // the int32 result is the bit pattern of the float SCORE_BIAS + s, exactly (|s| <= 128^3 = 2^21 <
 // 2^22 keeps it in the binade of SCORE_BIAS, where the float spacing is 1).  The row maximum is then
 // an integer maximum of the patterns (positive floats order as their patterns), and the numerator
-// argument s c - m is a single fma, fma(SCORE_BIAS + s, c, -(m + SCORE_BIAS c)), with no int -> float
-// conversion; the folded constant is rounded once, an absolute error of at most
-// 2^-24 (SCORE_BIAS c + |m|) in log2 units, far below the fp16 rounding of the numerator.
+// argument s c - m is a single fma, fma(SCORE_BIAS + s, c, -(SCORE_BIAS c + m)), with no int -> float
+// conversion.
+//
+// That fma is exact before its one rounding only if the folded constant SCORE_BIAS c + m is itself
+// an fp32 number.  The kernel makes it one (ScoreGrid): per work item, G = 2^(ceil(log2 cmax) + 1)
+// for the largest factor cmax = |sQ| max|sK| sm_scale log2(e) over its kept tiles; each tile's factor
+// c is rounded to a multiple of u = G 2^-22 (so SCORE_BIAS c = 3 (c/u) G is a multiple of G), and the
+// reference maxima m are kept on multiples of G.  Then |SCORE_BIAS c + m| <= (3 2^21 + 2^20 + 2) G
+// < 2^23 G: an exact multiple of G with fewer than 24 significant bits, which fma(SCORE_BIAS, c, m)
+// forms with no rounding.  The tiles' references therefore agree exactly, and the argument's only
+// errors are its final fp32 rounding and the rounding of c, |s| u / 2 <= |s c| 2^-23 G / c (a few
+// fp32 ulps of the argument when the kept tiles' K scales are alike).
 constexpr int SCORE_BIAS_BITS = 0x4B400000;
 constexpr float SCORE_BIAS = 12582912.0f;
+
+struct ScoreGrid {
+    float g, inv_g;      // G and 1/G
+    float u, inv_u;      // u = G 2^-22 and its inverse
+
+    QVD_DEV explicit ScoreGrid(float cmax) {
+        int e = 0;
+        if (cmax > 0.0f && cmax < 3.0e38f) frexpf(cmax, &e);   // cmax = f 2^e, f in [0.5, 1)
+        e = e < -98 ? -98 : (e > 100 ? 100 : e);            // keeps G, u and their inverses normal
+        g = ldexpf(1.0f, e + 1);
+        inv_g = ldexpf(1.0f, -(e + 1));
+        u = ldexpf(1.0f, e + 1 - 22);
+        inv_u = ldexpf(1.0f, 22 - (e + 1));
+    }
+    // the tile's factor on the grid of u (both products are exact power-of-two scalings)
+    QVD_DEV float factor(float c) const { return __builtin_rintf(c * inv_u) * u; }
+    // the smallest multiple of G at or above x
+    QVD_DEV float ceil_g(float x) const { return __builtin_ceilf(x * inv_g) * g; }
+};
 
 // Vector elements reach a bit_cast through this by-value helper: a bit_cast applied to a vector
 // element lvalue reads element 0.
@@ -212,7 +247,8 @@ QVD_DEV void tile_max(const v4i s[2][8], float c, int key0, int L, int fg, float
     }
 }
 
-// fp16 numerators of this tile against the reference maxima, as the B operand of the P.V MFMA
+// fp16 numerators of this tile against the reference maxima, as the B operand of the P.V MFMA.
+// c is on the grid of u and m on the grid of G (ScoreGrid), so mb below is exact.
 template <bool RAGGED>
 QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int key0, int L, int fg,
                              v8h pb[2][4]) {
@@ -241,16 +277,20 @@ QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int k
 }
 
 // The valid entries (0 <= j < T) of the first `cnt` list elements, in list order, into tiles; their
-// number into *n_out.  Run by both groups of the workgroup at once (gtid: thread index in the group,
-// wg: wave in the group): the iteration count depends on kmax only, so every wave meets the same
-// barriers.  Ballot-based prefix sums keep the order deterministic.
-QVD_DEV void compact_tiles(int* tiles, int* wcount, int* n_out, const int32_t* __restrict__ list, int cnt,
-                           int kmax, int T, int gtid, int lane, int wg) {
+// number into *n_out.  Returns the largest |K scale| of those tiles (ks_row: the head's K scales).
+// Run by both groups of the workgroup at once (gtid: thread index in the group, wg: wave in the
+// group): the iteration count depends on kmax only, so every wave meets the same barriers.
+// Ballot-based prefix sums keep the order deterministic.
+QVD_DEV float compact_tiles(int* tiles, int* wcount, float* wkmax, int* n_out,
+                            const int32_t* __restrict__ list, int cnt, int kmax, int T,
+                            const float* __restrict__ ks_row, int gtid, int lane, int wg) {
     int total = 0;
+    float km = 0.0f;
     for (int base = 0; base < kmax; base += 256) {
         const int t = base + gtid;
         const int j = t < cnt ? list[t] : -1;
         const bool ok = j >= 0 && j < T;
+        if (ok) km = fmaxf(km, fabsf(ks_row[j]));
         const unsigned long long mask = __ballot(ok);
         const int pos = __popcll(mask & ((1ull << lane) - 1ull));
         __syncthreads();
@@ -261,8 +301,11 @@ QVD_DEV void compact_tiles(int* tiles, int* wcount, int* n_out, const int32_t* _
         if (ok) tiles[off + pos] = j;
         total += wcount[0] + wcount[1] + wcount[2] + wcount[3];
     }
+    km = wave_max(km);
+    if (lane == 0) wkmax[wg] = km;
     if (gtid == 0) *n_out = total;
     __syncthreads();
+    return fmaxf(fmaxf(wkmax[0], wkmax[1]), fmaxf(wkmax[2], wkmax[3]));
 }
 
 // O^T += V^T . P^T and the numerator sums, this wave's share, from the V^T tile in LDS.  Lane group
@@ -307,9 +350,10 @@ constexpr float RESCALE_SLACK = 8.0f;   // log2 units a tile maximum may exceed 
 
 // Numerators of one tile against the reference maxima m (moved, and the sums rescaled, when a row's
 // tile maximum exceeds its reference by more than RESCALE_SLACK; the wave takes or skips the rescale
-// as a whole).
-QVD_DEV void softmax_tile(const v4i s[2][8], float c, bool ragged, int key0, int L, int fg, float m[2],
-                          v4f o[2][8], v4f lacc[2], v8h pb[2][4]) {
+// as a whole).  c is the tile's factor on the grid of u; a moved reference is the tile maximum
+// raised to the next multiple of G, so the numerators stay at most 2^8.
+QVD_DEV void softmax_tile(const v4i s[2][8], float c, const ScoreGrid& grid, bool ragged, int key0, int L,
+                          int fg, float m[2], v4f o[2][8], v4f lacc[2], v8h pb[2][4]) {
     float tmax[2];
     if (ragged) tile_max<true>(s, c, key0, L, fg, tmax);
     else tile_max<false>(s, c, key0, L, fg, tmax);
@@ -318,7 +362,7 @@ QVD_DEV void softmax_tile(const v4i s[2][8], float c, bool ragged, int key0, int
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const bool u = tmax[qb] > m[qb] + RESCALE_SLACK;
-        const float mnew = u ? tmax[qb] : m[qb];
+        const float mnew = u ? grid.ceil_g(tmax[qb]) : m[qb];
         alpha[qb] = m[qb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[qb] - mnew);
         m[qb] = mnew;
         up = up || u;
@@ -342,8 +386,8 @@ enum AttnOut { OUT_BF16 = 0, OUT_BF16_AMAX = 1, OUT_E4M3 = 2, OUT_MXFP4 = 3 };
 template <int OUT>
 __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     const int8_t* __restrict__ q, const float* __restrict__ q_scale, const int8_t* __restrict__ k,
-    const float* __restrict__ k_scale, const uint16_t* __restrict__ vt, int L, int H,
-    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int kmax, float c_log2,
+    const float* __restrict__ k_scale, const uint16_t* __restrict__ vt, const int32_t* __restrict__ v_exp,
+    int L, int H, const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int kmax, float c_log2,
     void* __restrict__ out, float* __restrict__ amax_partials, const float* __restrict__ out_scale,
     uint8_t* __restrict__ out_e8m0) {
     // a single LDS object: with a second __shared__ array the compiler waits for every DMA before
@@ -379,7 +423,9 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     int cnt = valid ? kv_cnt[h * T + i] : 0;
     cnt = cnt < 0 ? 0 : (cnt > kmax ? kmax : cnt);
     const int32_t* list = kv_idx + ((int64_t)h * T + i) * kmax;
-    compact_tiles(gs.tiles, sm.wcount[g], &sm.n[g], list, cnt, kmax, T, tid & 255, lane, wg);
+    const float ks_max = compact_tiles(gs.tiles, sm.wcount[g], sm.wkmax[g], &sm.n[g], list, cnt, kmax, T,
+                                       k_scale + (int64_t)h * T, tid & 255, lane, wg);
+    const ScoreGrid grid(fabsf(qsc) * ks_max);
     const int n = sm.n[g];
     const int n_other = sm.n[g ^ 1];
 
@@ -415,7 +461,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     int j = 0;                                    // tile of the next VALU phase (read in the MFMA phase)
     auto valu_phase = [&]() {
         stage_vt(gs.vt, vt, Lp, h, j, wg, lane);
-        softmax_tile(s, qsc * ksc, ragged_L && j == T - 1, j * 128, L, fg, m, o, lacc, pb);
+        softmax_tile(s, grid.factor(qsc * ksc), grid, ragged_L && j == T - 1, j * 128, L, fg, m, o, lacc, pb);
     };
 
     if (n > 0) stage_k(gs.k[0], k, L, H, h, gs.tiles[0], wg, lane);
@@ -445,6 +491,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
         }
     }
     for (; passed < P + 1; ++passed) lds_barrier();
+    const int ve = valid ? v_exp[h] : 0;          // the head's V scale: O = (P.V') 2^ve / sum P
 
     if (OUT == OUT_MXFP4) {
         // bf16 O, then MXFP4 per (row, head, 32 dims) with the standalone quantizer's arithmetic.  Dims
@@ -453,7 +500,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const float lt = lacc[qb][0];
-            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+            const float inv = lt > 0.0f ? ldexpf(1.0f / lt, ve) : 0.0f;
             const int row = q0 + 16 * qb + fr;
             u32 w[8][2];
 #pragma unroll
@@ -497,7 +544,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const float lt = lacc[qb][0];
-        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        const float inv = lt > 0.0f ? ldexpf(1.0f / lt, ve) : 0.0f;
         const int row = q0 + 16 * qb + fr;
         if (valid && row < L) {
             const int64_t orow = ((int64_t)row * H + h) * 128;
@@ -530,26 +577,40 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     }
 }
 
-// bf16 V [L][H][128] -> fp16 V^T [H][128][T*128] (zeros past L).  One workgroup per (token tile,
-// head): the tile goes through LDS so both the reads and the writes are 16-byte coalesced.
+// bf16 V [L][H][128] -> fp16 V^T [H][128][T*128] (zeros past L), each (tile, head) scaled by
+// 2^-e with e = vt_tile_exponent of its max|V|, written to tile_exp[h][j].  One workgroup per (token
+// tile, head): the tile goes through registers and LDS so both the reads and the writes are 16-byte
+// coalesced.
 __global__ void __launch_bounds__(256) k_vt_from_bf16(const uint16_t* __restrict__ v, int L, int H,
-                                                      uint16_t* __restrict__ vt) {
+                                                      uint16_t* __restrict__ vt, int32_t* __restrict__ tile_exp) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[128][136];   // [dim][token], fp16
+    __shared__ float red[4];
     const int j = blockIdx.x, h = blockIdx.y, T = gridDim.x;
     const int tid = threadIdx.x;
+    u32x4 w[8];
+    u32 amb = 0u;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int c = tid + 256 * u;               // 2048 chunks of 8 dims
         const int tok = c >> 4, d0 = (c & 15) * 8;
         const int row = j * 128 + tok;
-        u32x4 w = {0, 0, 0, 0};
-        if (row < L) w = *reinterpret_cast<const u32x4*>(v + ((int64_t)row * H + h) * 128 + d0);
+        w[u] = (u32x4){0, 0, 0, 0};
+        if (row < L) w[u] = *reinterpret_cast<const u32x4*>(v + ((int64_t)row * H + h) * 128 + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amb = max(amb, max(w[u][e] & 0x7FFFu, (w[u][e] >> 16) & 0x7FFFu));
+    }
+    // the largest |v| as a bf16 magnitude pattern (finite magnitudes order as their patterns)
+    const float amax = block_max_nonneg<4>(bf16_to_f32((uint16_t)amb), red);
+    const int ve = vt_tile_exponent(amax);
+    if (tid == 0) tile_exp[h * T + j] = ve;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int c = tid + 256 * u;
+        const int tok = c >> 4, d0 = (c & 15) * 8;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float a = fminf(fmaxf(bf16lo(w[e]), -65504.0f), 65504.0f);
-            const float b = fminf(fmaxf(bf16hi(w[e]), -65504.0f), 65504.0f);
-            tile[d0 + 2 * e][tok] = __builtin_bit_cast(uint16_t, (_Float16)a);
-            tile[d0 + 2 * e + 1][tok] = __builtin_bit_cast(uint16_t, (_Float16)b);
+            tile[d0 + 2 * e][tok] = f16_scaled(bf16lo(w[u][e]), ve);
+            tile[d0 + 2 * e + 1][tok] = f16_scaled(bf16hi(w[u][e]), ve);
         }
     }
     __syncthreads();
@@ -560,6 +621,42 @@ __global__ void __launch_bounds__(256) k_vt_from_bf16(const uint16_t* __restrict
         const int d = c >> 4, t0 = (c & 15) * 8;
         *reinterpret_cast<u32x4*>(vt + ((int64_t)h * 128 + d) * Lp + j * 128 + t0) =
             *reinterpret_cast<const u32x4*>(&tile[d][t0]);
+    }
+}
+
+// One V scale per head: head_exp[h] = E = the largest of the head's tile exponents, and every tile
+// stored with a smaller exponent e is rescaled in place by 2^(e - E) (exact wherever the result is an
+// fp16 normal; a value more than 2^28 below the head's max|V| may round to the fp16 subnormal grid).
+// One workgroup per (token tile, head); a tile already at E is not touched, so with V in the usual
+// range (every exponent 0) the pass reads only the exponents.
+__global__ void __launch_bounds__(256) k_vt_unify(uint16_t* __restrict__ vt, int T,
+                                                  const int32_t* __restrict__ tile_exp,
+                                                  int32_t* __restrict__ head_exp) {
+    __shared__ int red[4];
+    const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    int e = INT_MIN;
+    for (int t = tid; t < T; t += 256) e = max(e, tile_exp[h * T + t]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = e;
+    __syncthreads();
+    const int E = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (j == 0 && tid == 0) head_exp[h] = E;
+    const int sh = tile_exp[h * T + j] - E;
+    if (sh == 0) return;
+    const int64_t Lp = (int64_t)T * 128;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int c = tid + 256 * u;               // 2048 chunks of 8 keys: rows (h, d), d < 128
+        const int d = c >> 4, t0 = (c & 15) * 8;
+        u32x4* p = reinterpret_cast<u32x4*>(vt + ((int64_t)h * 128 + d) * Lp + j * 128 + t0);
+        u32x4 w = *p;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const v2h x = as_v2h(w[k]);
+            w[k] = pack_f16x2(ldexpf((float)x.x, sh), ldexpf((float)x.y, sh));
+        }
+        *p = w;
     }
 }
 
@@ -592,43 +689,52 @@ __global__ void __launch_bounds__(256) k_qk_tile(const int8_t* __restrict__ q, c
 namespace {
 template <int OUT>
 int launch_attn(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
-                const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt, int kmax,
-                float sm_scale, void* out, float* amax_partials, const float* out_scale, uint8_t* out_e8m0,
-                hipStream_t st) {
+                const uint16_t* vt, const int32_t* v_exp, int L, int H, const int32_t* kv_idx,
+                const int32_t* kv_cnt, int kmax, float sm_scale, void* out, float* amax_partials,
+                const float* out_scale, uint8_t* out_e8m0, hipStream_t st) {
     if (L == 0) return QVD_OK;
     const int T = (L + 127) / 128;
     const unsigned pairs = (unsigned)((T * H + 1) / 2);
     const float c = sm_scale * LOG2E;
     TimingScope ts("sparse_attn", st);
-    hipLaunchKernelGGL(k_sparse_attn<OUT>, dim3(pairs), dim3(512), 0, st, q, q_scale, k, k_scale, vt, L, H,
-                       kv_idx, kv_cnt, kmax, c, out, amax_partials, out_scale, out_e8m0);
+    hipLaunchKernelGGL(k_sparse_attn<OUT>, dim3(pairs), dim3(512), 0, st, q, q_scale, k, k_scale, vt, v_exp,
+                       L, H, kv_idx, kv_cnt, kmax, c, out, amax_partials, out_scale, out_e8m0);
     return launch_status("sparse_attn");
 }
 }  // namespace
 
+int launch_vt_unify(uint16_t* vt, int L, int H, const int32_t* tile_exp, int32_t* head_exp, hipStream_t st) {
+    if (L == 0) return QVD_OK;
+    const int T = (L + 127) / 128;
+    TimingScope ts("vt_unify", st);
+    hipLaunchKernelGGL(k_vt_unify, dim3(T, H), dim3(256), 0, st, vt, T, tile_exp, head_exp);
+    return launch_status("vt_unify");
+}
+
 int launch_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
-                          const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt,
-                          int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st) {
+                          const uint16_t* vt, const int32_t* v_exp, int L, int H, const int32_t* kv_idx,
+                          const int32_t* kv_cnt, int kmax, float sm_scale, uint16_t* out,
+                          float* amax_partials, hipStream_t st) {
     if (amax_partials)
-        return launch_attn<OUT_BF16_AMAX>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
-                                          out, amax_partials, nullptr, nullptr, st);
-    return launch_attn<OUT_BF16>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out,
+        return launch_attn<OUT_BF16_AMAX>(q, q_scale, k, k_scale, vt, v_exp, L, H, kv_idx, kv_cnt, kmax,
+                                          sm_scale, out, amax_partials, nullptr, nullptr, st);
+    return launch_attn<OUT_BF16>(q, q_scale, k, k_scale, vt, v_exp, L, H, kv_idx, kv_cnt, kmax, sm_scale, out,
                                  nullptr, nullptr, nullptr, st);
 }
 
 int launch_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
-                               const float* k_scale, const uint16_t* vt, int L, int H,
+                               const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int L, int H,
                                const int32_t* kv_idx, const int32_t* kv_cnt, int kmax, float sm_scale,
                                const float* out_scale, uint8_t* out_q, hipStream_t st) {
-    return launch_attn<OUT_E4M3>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out_q,
-                                 nullptr, out_scale, nullptr, st);
+    return launch_attn<OUT_E4M3>(q, q_scale, k, k_scale, vt, v_exp, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+                                 out_q, nullptr, out_scale, nullptr, st);
 }
 
 int launch_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int8_t* k,
-                                const float* k_scale, const uint16_t* vt, int L, int H,
+                                const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int L, int H,
                                 const int32_t* kv_idx, const int32_t* kv_cnt, int kmax, float sm_scale,
                                 uint8_t* out_packed, uint8_t* out_e8m0, hipStream_t st) {
-    return launch_attn<OUT_MXFP4>(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+    return launch_attn<OUT_MXFP4>(q, q_scale, k, k_scale, vt, v_exp, L, H, kv_idx, kv_cnt, kmax, sm_scale,
                                   out_packed, nullptr, nullptr, out_e8m0, st);
 }
 
@@ -656,23 +762,59 @@ int validate_attn(const char* fn, const int8_t* q, const float* q_scale, const i
     return QVD_OK;
 }
 
+// sparse_attn's workspace: fp16 V^T, then the tile exponents [H][T] and the head exponents [H]
+size_t attn_ws_tile_exp_off(int L, int H) { return (vt_bytes(L, H) + 255) & ~(size_t)255; }
+size_t attn_ws_head_exp_off(int L, int H) {
+    const size_t T = (size_t)(L + 127) / 128;
+    return (attn_ws_tile_exp_off(L, H) + 4 * (size_t)H * T + 255) & ~(size_t)255;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t qvd_sparse_attn_ws_bytes(int32_t L, int32_t H) {
-    return (L < 0 || H < 1) ? 0 : vt_bytes(L, H);
+    return (L < 0 || H < 1) ? 0 : attn_ws_head_exp_off(L, H) + 4 * (size_t)H;
+}
+
+int qvd_vt_from_bf16(const uint16_t* v, int32_t L, int32_t H, uint16_t* vt, int32_t* tile_exp, void* stream) {
+    QVD_REQUIRE(L >= 0 && H >= 1 && H <= 65535, QVD_ESHAPE, "qvd_vt_from_bf16: L = %d, H = %d", L, H);
+    QVD_REQUIRE((double)vt_bytes(L, H) < 4294967296.0, QVD_ESHAPE, "qvd_vt_from_bf16: V^T must stay below 4 GiB");
+    if (L == 0) return QVD_OK;
+    QVD_PTR(v);
+    QVD_PTR(vt);
+    QVD_PTR(tile_exp);
+    QVD_ALIGN(v);
+    QVD_ALIGN(vt);
+    QVD_DEVICE_OK();
+    hipStream_t st = (hipStream_t)stream;
+    TimingScope ts("vt_from_bf16", st);
+    hipLaunchKernelGGL(k_vt_from_bf16, dim3((L + 127) / 128, H), dim3(256), 0, st, v, L, H, vt, tile_exp);
+    return launch_status("qvd_vt_from_bf16");
+}
+
+int qvd_vt_unify(uint16_t* vt, int32_t L, int32_t H, const int32_t* tile_exp, int32_t* head_exp,
+                 void* stream) {
+    QVD_REQUIRE(L >= 0 && H >= 1 && H <= 65535, QVD_ESHAPE, "qvd_vt_unify: L = %d, H = %d", L, H);
+    if (L == 0) return QVD_OK;
+    QVD_PTR(vt);
+    QVD_PTR(tile_exp);
+    QVD_PTR(head_exp);
+    QVD_ALIGN(vt);
+    QVD_DEVICE_OK();
+    return launch_vt_unify(vt, L, H, tile_exp, head_exp, (hipStream_t)stream);
 }
 
 int qvd_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k,
-                       const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
+                       const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int32_t L, int32_t H,
                        const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
                        uint16_t* out, float* out_amax_partials, void* stream) {
     int s = validate_attn("qvd_sparse_attn_vt", q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax,
                           sm_scale, out);
     if (s || L == 0) return s;
+    QVD_PTR(v_exp);
     QVD_DEVICE_OK();
-    return launch_sparse_attn_vt(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out,
+    return launch_sparse_attn_vt(q, q_scale, k, k_scale, vt, v_exp, L, H, kv_idx, kv_cnt, kmax, sm_scale, out,
                                  out_amax_partials, (hipStream_t)stream);
 }
 
@@ -686,47 +828,53 @@ int sparse_attn(const int8_t* q, const float* q_scale, const int8_t* k, const fl
     if (s || L == 0) return s;
     QVD_PTR(ws);
     QVD_ALIGN(ws);
-    QVD_REQUIRE(ws_bytes >= vt_bytes(L, H), QVD_EWORKSPACE, "sparse_attn: workspace %zu < %zu bytes",
-                ws_bytes, vt_bytes(L, H));
+    const size_t need = qvd_sparse_attn_ws_bytes(L, H);
+    QVD_REQUIRE(ws_bytes >= need, QVD_EWORKSPACE, "sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
     QVD_DEVICE_OK();
     hipStream_t st = (hipStream_t)stream;
     uint16_t* vt = (uint16_t*)ws;
+    int32_t* tile_exp = (int32_t*)((char*)ws + attn_ws_tile_exp_off(L, H));
+    int32_t* head_exp = (int32_t*)((char*)ws + attn_ws_head_exp_off(L, H));
     {
         TimingScope ts("vt_from_bf16", st);
-        hipLaunchKernelGGL(k_vt_from_bf16, dim3((L + 127) / 128, H), dim3(256), 0, st, v, L, H, vt);
-        s = launch_status("sparse_attn (V conversion)");
+        hipLaunchKernelGGL(k_vt_from_bf16, dim3((L + 127) / 128, H), dim3(256), 0, st, v, L, H, vt, tile_exp);
+        s = launch_status("sparse_attn (V transpose)");
         if (s) return s;
     }
-    return launch_sparse_attn_vt(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale, out,
-                                 out_amax_partials, st);
+    s = launch_vt_unify(vt, L, H, tile_exp, head_exp, st);
+    if (s) return s;
+    return launch_sparse_attn_vt(q, q_scale, k, k_scale, vt, head_exp, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+                                 out, out_amax_partials, st);
 }
 
 int qvd_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
-                            const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
-                            const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
-                            const float* out_scale, uint8_t* out_q, void* stream) {
+                            const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int32_t L,
+                            int32_t H, const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax,
+                            float sm_scale, const float* out_scale, uint8_t* out_q, void* stream) {
     int s = validate_attn("qvd_sparse_attn_vt_e4m3", q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt,
                           kmax, sm_scale, reinterpret_cast<uint16_t*>(out_q));
     if (s || L == 0) return s;
+    QVD_PTR(v_exp);
     QVD_PTR(out_scale);
     QVD_DEVICE_OK();
-    return launch_sparse_attn_vt_e4m3(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+    return launch_sparse_attn_vt_e4m3(q, q_scale, k, k_scale, vt, v_exp, L, H, kv_idx, kv_cnt, kmax, sm_scale,
                                       out_scale, out_q, (hipStream_t)stream);
 }
 
 int qvd_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int8_t* k,
-                             const float* k_scale, const uint16_t* vt, int32_t L, int32_t H,
-                             const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, float sm_scale,
-                             uint8_t* out_packed, uint8_t* out_e8m0, void* stream) {
+                             const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int32_t L,
+                             int32_t H, const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax,
+                             float sm_scale, uint8_t* out_packed, uint8_t* out_e8m0, void* stream) {
     int s = validate_attn("qvd_sparse_attn_vt_mxfp4", q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt,
                           kmax, sm_scale, reinterpret_cast<uint16_t*>(out_packed));
     if (s || L == 0) return s;
+    QVD_PTR(v_exp);
     QVD_PTR(out_e8m0);
     QVD_REQUIRE(((uintptr_t)out_e8m0 & 3u) == 0, QVD_EALIGN,
                 "qvd_sparse_attn_vt_mxfp4: out_e8m0 must be 4-byte aligned");
     QVD_DEVICE_OK();
-    return launch_sparse_attn_vt_mxfp4(q, q_scale, k, k_scale, vt, L, H, kv_idx, kv_cnt, kmax, sm_scale,
-                                       out_packed, out_e8m0, (hipStream_t)stream);
+    return launch_sparse_attn_vt_mxfp4(q, q_scale, k, k_scale, vt, v_exp, L, H, kv_idx, kv_cnt, kmax,
+                                       sm_scale, out_packed, out_e8m0, (hipStream_t)stream);
 }
 
 int qvd_qk_int32_tile(const int8_t* q, const int8_t* k, int32_t L, int32_t H, int32_t h,

@@ -8,7 +8,9 @@
 //   (per-tensor FP8 linear layers with the scales applied to the output; INT8 query/key).
 //
 //   adaln_modulate(x, shift1, scale1)             -> h (E4M3) + s_h
-//   GEMM h . W_qkv^T, epilogue: bf16 Q|K|V, INT8 Q/K per (head, 128-token tile), V^T in fp16
+//   GEMM h . W_qkv^T, epilogue: bf16 Q|K|V, INT8 Q/K per (head, 128-token tile), V^T in fp16 with
+//                                                    one power-of-two scale per (head, tile)
+//   vt_unify                                      -> one V scale per head
 //   sparse_attn                                   -> O (bf16) + per-tile max|O|
 //   per-tensor FP8 of O (amax from those partials) -> O8
 //   GEMM O8 . W_o^T, epilogue: x += gate1 * y      (in place)
@@ -40,6 +42,8 @@ struct BlockWs {
     int8_t* q8;          // [L][d]
     int8_t* k8;          // [L][d]
     uint16_t* v;         // fp16 V^T [H][128][T*128]
+    int32_t* v_texp;     // [H][T] V tile exponents (QKV epilogue)
+    int32_t* v_hexp;     // [H] V head exponents (vt_unify)
     uint16_t* o;         // bf16 [L][d] (dynamic scales only)
     uint16_t* g;         // bf16 [L][F] (dynamic scales only)
     uint8_t* g8;         // E4M3 [L][F] (W4A4: packed E2M1 [L][F/2])
@@ -72,6 +76,8 @@ BlockWs carve(const qvd_block_params* p, int L, uint8_t* base) {
     w.q8 = (int8_t*)take(Ld);
     w.k8 = (int8_t*)take(Ld);
     w.v = (uint16_t*)take(vt_bytes(L, p->n_heads));
+    w.v_texp = (int32_t*)take(4 * HT);
+    w.v_hexp = (int32_t*)take(4 * (size_t)p->n_heads);
     const bool a4 = p->weight_format == QVD_W_MXFP4_A4;
     // static scales or W4A4: O and g exist only as codes
     const bool stat = p->act_scale != nullptr || a4;
@@ -149,9 +155,15 @@ size_t qvd_block_ws_bytes(const qvd_block_params* p, int32_t L) {
     return carve(p, L, nullptr).total;
 }
 
-int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
-                      const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, void* ws,
-                      size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The block, ending after stage `stop` (QVD_STAGE_*; QVD_STAGE_ALL runs it whole).  Every partial run
+// executes exactly the kernels and arguments of the whole block up to that stage.
+int block_forward(const char* fn, const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
+                  const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, void* ws, size_t ws_bytes,
+                  int stop, hipStream_t st) {
     int s = validate(p, L);
     if (s) return s;
     if (L == 0) return QVD_OK;
@@ -166,15 +178,13 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     QVD_ALIGN(mod);
     QVD_ALIGN(x);
     QVD_ALIGN(ws);
-    QVD_REQUIRE(kmax >= 1 && kmax <= 1024, QVD_ESHAPE, "dit_block_forward: kmax = %d (1 .. 1024)", kmax);
+    QVD_REQUIRE(kmax >= 1 && kmax <= 1024, QVD_ESHAPE, "%s: kmax = %d (1 .. 1024)", fn, kmax);
     QVD_REQUIRE(!select || L <= 131072, QVD_ESHAPE,
-                "dit_block_forward: L = %d; the block selects its mask for L <= 131,072 only", L);
-    const size_t need = qvd_block_ws_bytes(p, L);
-    QVD_REQUIRE(ws_bytes >= need, QVD_EWORKSPACE, "dit_block_forward: workspace %zu < %zu bytes",
-                ws_bytes, need);
+                "%s: L = %d; the block selects its mask for L <= 131,072 only", fn, L);
+    const size_t need = carve(p, L, nullptr).total;
+    QVD_REQUIRE(ws_bytes >= need, QVD_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
     QVD_DEVICE_OK();
 
-    hipStream_t st = (hipStream_t)stream;
     const BlockWs w = carve(p, L, (uint8_t*)ws);
     const int d = p->d, F = p->mlp, H = p->n_heads;
     const int T = (L + 127) / 128;
@@ -191,10 +201,9 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
         kv_cnt = w.sel_cnt;
         return launch_select_tiles(w.q8, w.k8, w.ks, L, H, kmax, w.sel_idx, w.sel_cnt, w.sel_ws, st);
     };
-
     if (fmt == QVD_W_MXFP4_A4) {
         s = launch_modulate_mx(x, L, d, mod, 0, p->ln_eps, w.h, w.h_e8, st);
-        if (s) return s;
+        if (s || stop <= QVD_STAGE_MODULATE1) return s;
         qvd_epilogue e{};
         e.mode = QVD_EPI_QKV;
         e.n_heads = H;
@@ -203,28 +212,31 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
         e.v = w.v;
         e.q_scale = w.qs;
         e.k_scale = w.ks;
+        e.v_exp = w.v_texp;
         s = launch_gemm_w4a4(w.h, w.h_e8, (const uint8_t*)p->w_qkv, p->e8m0_qkv, p->b_qkv, L, 3 * d, d, e, st);
-        if (s) return s;
+        if (s || stop <= QVD_STAGE_QKV) return s;
+        s = launch_vt_unify(w.v, L, H, w.v_texp, w.v_hexp, st);
+        if (s || stop <= QVD_STAGE_VT) return s;
         s = select_mask();
         if (s) return s;
-        s = launch_sparse_attn_vt_mxfp4(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.h,
-                                        w.h_e8, st);
-        if (s) return s;
+        s = launch_sparse_attn_vt_mxfp4(w.q8, w.qs, w.k8, w.ks, w.v, w.v_hexp, L, H, kv_idx, kv_cnt, kmax,
+                                        sm_scale, w.h, w.h_e8, st);
+        if (s || stop <= QVD_STAGE_OQUANT) return s;
         e = qvd_epilogue{};
         e.mode = QVD_EPI_RESID_GATE;
         e.out_bf16 = x;
         e.resid = x;
         e.gate = shift_scale_gate + 2 * d;
         s = launch_gemm_w4a4(w.h, w.h_e8, (const uint8_t*)p->w_o, p->e8m0_o, p->b_o, L, d, d, e, st);
-        if (s) return s;
+        if (s || stop <= QVD_STAGE_OPROJ) return s;
         s = launch_modulate_mx(x, L, d, mod, 1, p->ln_eps, w.h, w.h_e8, st);
-        if (s) return s;
+        if (s || stop <= QVD_STAGE_MODULATE2) return s;
         e = qvd_epilogue{};
         e.mode = QVD_EPI_GELU_MXFP4;
         e.out_e2m1 = w.g8;
         e.out_e8m0 = w.g_e8;
         s = launch_gemm_w4a4(w.h, w.h_e8, (const uint8_t*)p->w_up, p->e8m0_up, p->b_up, L, F, d, e, st);
-        if (s) return s;
+        if (s || stop <= QVD_STAGE_GQUANT) return s;
         e = qvd_epilogue{};
         e.mode = QVD_EPI_RESID_GATE;
         e.out_bf16 = x;
@@ -236,7 +248,7 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
 
     // attention branch
     s = launch_modulate(x, L, d, mod, 0, p->ln_eps, act ? act + 0 : nullptr, w.h, w.scales + 0, w.ln_ws, st);
-    if (s) return s;
+    if (s || stop <= QVD_STAGE_MODULATE1) return s;
     qvd_epilogue e{};
     e.mode = QVD_EPI_QKV;
     e.n_heads = H;
@@ -245,20 +257,23 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     e.v = w.v;
     e.q_scale = w.qs;
     e.k_scale = w.ks;
+    e.v_exp = w.v_texp;
     s = launch_gemm(w.h, w.scales + 0, p->w_qkv, p->e8m0_qkv, p->s_qkv, fmt, p->b_qkv, L, 3 * d, d, e, st);
-    if (s) return s;
+    if (s || stop <= QVD_STAGE_QKV) return s;
+    s = launch_vt_unify(w.v, L, H, w.v_texp, w.v_hexp, st);
+    if (s || stop <= QVD_STAGE_VT) return s;
     s = select_mask();
     if (s) return s;
     if (act) {
-        s = launch_sparse_attn_vt_e4m3(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale,
-                                       act + 1, w.h, st);
+        s = launch_sparse_attn_vt_e4m3(w.q8, w.qs, w.k8, w.ks, w.v, w.v_hexp, L, H, kv_idx, kv_cnt, kmax,
+                                       sm_scale, act + 1, w.h, st);
     } else {
-        s = launch_sparse_attn_vt(w.q8, w.qs, w.k8, w.ks, w.v, L, H, kv_idx, kv_cnt, kmax, sm_scale, w.o,
-                                  w.attn_part, st);
-        if (s) return s;
+        s = launch_sparse_attn_vt(w.q8, w.qs, w.k8, w.ks, w.v, w.v_hexp, L, H, kv_idx, kv_cnt, kmax, sm_scale,
+                                  w.o, w.attn_part, st);
+        if (s || stop <= QVD_STAGE_ATTN) return s;
         s = launch_quant_fp8(w.o, (int64_t)L * d, nullptr, w.attn_part, H * T, w.h, w.scales + 1, st);
     }
-    if (s) return s;
+    if (s || stop <= QVD_STAGE_OQUANT) return s;
     e = qvd_epilogue{};
     e.mode = QVD_EPI_RESID_GATE;
     e.out_bf16 = x;
@@ -266,11 +281,11 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     e.gate = shift_scale_gate + 2 * d;
     s = launch_gemm(w.h, act ? act + 1 : w.scales + 1, p->w_o, p->e8m0_o, p->s_o, fmt, p->b_o, L, d, d, e,
                     st);
-    if (s) return s;
+    if (s || stop <= QVD_STAGE_OPROJ) return s;
 
     // MLP branch
     s = launch_modulate(x, L, d, mod, 1, p->ln_eps, act ? act + 2 : nullptr, w.h, w.scales + 2, w.ln_ws, st);
-    if (s) return s;
+    if (s || stop <= QVD_STAGE_MODULATE2) return s;
     e = qvd_epilogue{};
     if (act) {
         e.mode = QVD_EPI_GELU_E4M3;
@@ -282,12 +297,13 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
         e.amax_partials = w.gelu_part;
     }
     s = launch_gemm(w.h, w.scales + 2, p->w_up, p->e8m0_up, p->s_up, fmt, p->b_up, L, F, d, e, st);
-    if (s) return s;
+    if (s || stop <= QVD_STAGE_UP) return s;
     if (!act) {
         s = launch_quant_fp8(w.g, (int64_t)L * F, nullptr, w.gelu_part, (int)gemm_tiles(L, F), w.g8,
                              w.scales + 3, st);
         if (s) return s;
     }
+    if (stop <= QVD_STAGE_GQUANT) return QVD_OK;
     e = qvd_epilogue{};
     e.mode = QVD_EPI_RESID_GATE;
     e.out_bf16 = x;
@@ -295,6 +311,53 @@ int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, 
     e.gate = shift_scale_gate + 5 * d;
     return launch_gemm(w.g8, act ? act + 3 : w.scales + 3, p->w_down, p->e8m0_down, p->s_down, fmt,
                        p->b_down, L, d, F, e, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
+                      const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, void* ws,
+                      size_t ws_bytes, void* stream) {
+    return block_forward("dit_block_forward", p, mod, x, L, kv_idx, kv_cnt, kmax, ws, ws_bytes,
+                         QVD_STAGE_ALL, (hipStream_t)stream);
+}
+
+int qvd_block_forward_until(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
+                            const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, int32_t stage,
+                            void* ws, size_t ws_bytes, void* stream) {
+    QVD_REQUIRE(stage >= QVD_STAGE_MODULATE1 && stage <= QVD_STAGE_ALL, QVD_EINVAL,
+                "qvd_block_forward_until: stage = %d", stage);
+    return block_forward("qvd_block_forward_until", p, mod, x, L, kv_idx, kv_cnt, kmax, ws, ws_bytes, stage,
+                         (hipStream_t)stream);
+}
+
+int qvd_block_ws_layout(const qvd_block_params* p, int32_t L, int64_t* offsets) {
+    QVD_PTR(p);
+    QVD_PTR(offsets);
+    QVD_REQUIRE(L >= 0 && p->d > 0 && p->mlp > 0 && p->n_heads > 0, QVD_ESHAPE, "qvd_block_ws_layout: shape");
+    // offsets from a carve at a stand-in base address (carve gives NULL pointers for a NULL base)
+    uint8_t* base = reinterpret_cast<uint8_t*>(static_cast<uintptr_t>(0x100));
+    const BlockWs b = carve(p, L, base);
+    auto off = [&](const void* ptr) { return (int64_t)(static_cast<const uint8_t*>(ptr) - base); };
+    offsets[QVD_WS_H] = off(b.h);
+    offsets[QVD_WS_Q8] = off(b.q8);
+    offsets[QVD_WS_K8] = off(b.k8);
+    offsets[QVD_WS_VT] = off(b.v);
+    offsets[QVD_WS_VT_TILE_EXP] = off(b.v_texp);
+    offsets[QVD_WS_VT_HEAD_EXP] = off(b.v_hexp);
+    offsets[QVD_WS_O] = off(b.o);
+    offsets[QVD_WS_G] = off(b.g);
+    offsets[QVD_WS_G8] = off(b.g8);
+    offsets[QVD_WS_H_E8M0] = off(b.h_e8);
+    offsets[QVD_WS_G_E8M0] = off(b.g_e8);
+    offsets[QVD_WS_Q_SCALE] = off(b.qs);
+    offsets[QVD_WS_K_SCALE] = off(b.ks);
+    offsets[QVD_WS_SCALES] = off(b.scales);
+    offsets[QVD_WS_SEL_IDX] = off(b.sel_idx);
+    offsets[QVD_WS_SEL_CNT] = off(b.sel_cnt);
+    return QVD_OK;
 }
 
 }  // extern "C"

@@ -41,10 +41,26 @@ QVD_DEV u32 pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// E4M3 ("FN") encoding, round to nearest even, saturating at 448, NaN -> 0x7F.  Written from the
-// format definition: a normal value keeps 3 fraction bits of the fp32 significand (rounding added
-// at bit 19 with the tie going to the even result), exponent rebased from 127 to 7; below 2^-6
-// the code is the count of 2^-9 quanta.
+// V in fp16 for the attention's P.V product.  One (head, 128-token tile) of V is stored as fp16 of
+// v 2^-e, with e = 0 while the tile's max|v| lies in [2^-6, 2^15) (fp16's normal range then holds
+// everything down to 2^-20 of the maximum), else e = floor(log2 max|v|) - 14, which brings the
+// maximum into [2^14, 2^15), below fp16's largest value 65,504.  An all-zero or non-finite maximum
+// takes e = 0.  A bf16 value scaled by a power of two converts to fp16 exactly while it stays an fp16
+// normal (bf16 has 8 significant bits, fp16 11).
+
+QVD_DEV int vt_tile_exponent(float amax) {
+    if (!(amax > 0.0f) || !(amax < 3.0e38f) || (amax >= 0x1p-6f && amax < 32768.0f)) return 0;
+    int k;
+    frexpf(amax, &k);                      // amax = f 2^k, f in [0.5, 1): floor(log2 amax) = k - 1
+    return k - 15;
+}
+
+QVD_DEV uint16_t f16_scaled(float v, int e) {
+    return __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v, -e));
+}
+
+// ---------------------------------------------------------------------------------------------
+// E4M3 ("FN") encoding.
 // fp32 -> E4M3 (OCP "FN"): round to nearest even, finite values beyond 448 saturate to +-448, NaN -> 0x7F.
 // The gfx950 converter rounds to nearest even; clamping to +-448 first makes it saturate (the pair
 // agrees with a direct implementation of the rule on all 2^32 fp32 inputs, checked on the device).

@@ -296,10 +296,37 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
         const int head = hc >> 7;
         const int Tm = (M + 127) >> 7;
         if (v_tile) {
+            // V: rounded to bf16, then stored in fp16, transposed as V^T[head][dim][token] with tokens
+            // M .. Lp-1 zeroed, scaled by 2^-e with one exponent e per (head, 128-token tile):
+            // vt_tile_exponent of the tile's max|V| (0 for the usual range, else the power of two that
+            // brings the maximum into [2^14, 2^15)).  The fp16 value is the bf16 value times 2^-e
+            // exactly wherever it is an fp16 normal.  The two waves of a head meet in LDS (every wave
+            // of the workgroup is a V wave, so all take the barrier).  LDS: WN dimension rows of TR
+            // tokens per round.
+            float amax = 0.0f;
+            if (wave_live) {
+                u32 amb = 0u;
+#pragma unroll
+                for (int cg = 0; cg < LY::NCG; ++cg) {
+                    const float4 b = load_bias4(g.bias, nw0 + LY::ncol(cg, lane));
+#pragma unroll
+                    for (int r = 0; r < LY::MR; ++r) {
+                        const int m = mw0 + LY::mrow(r, lane);
+                        const v4f c = LY::get(acc, cg, r);
+                        const u32 p0 = pack_bf16x2(c[0] * alpha + b.x, c[1] * alpha + b.y);
+                        const u32 p1 = pack_bf16x2(c[2] * alpha + b.z, c[3] * alpha + b.w);
+                        if (m < M) amb = absmax_bf16x2(absmax_bf16x2(amb, p0), p1);
+                    }
+                }
+                amax = fmaxf(bf16lo(amb), bf16hi(amb));
+            }
+            amax = wave_max(amax);
+            if (lane == 0) red[wv] = amax;
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            amax = fmaxf(amax, red[wv ^ 2]);
             if (!wave_live) return;
-            // V: bf16 rounding, then fp16 (exact for 2^-14 <= |v| <= 65504; larger saturate), stored
-            // transposed as V^T[head][dim][token] with tokens M .. Lp-1 zeroed.  LDS: WN dimension rows
-            // of TR tokens per round.
+            const int ve = vt_tile_exponent(amax);
+            if (lane == 0 && (hc & 127) == 0) ep.v_exp[head * Tm + (mw0 >> 7)] = ve;
             constexpr int TR = 16384 / (2 * WN);
             constexpr int CT = TR / 8;
             constexpr int RPR = TR / LY::RB;
@@ -321,9 +348,7 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
                                             c[3] * alpha + b.w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float vb = bf16lo(pack_bf16x2(y[i], 0.0f));
-                            const float vc = fminf(fmaxf(vb, -65504.0f), 65504.0f);
-                            const uint16_t h16 = ok ? __builtin_bit_cast(uint16_t, (_Float16)vc) : (uint16_t)0;
+                            const uint16_t h16 = ok ? f16_scaled(bf16lo(pack_bf16x2(y[i], 0.0f)), ve) : (uint16_t)0;
                             const int row = dd + i;
                             *reinterpret_cast<uint16_t*>(stage + row * (2 * TR) + (((ml >> 3) ^ (row & (CT - 1))) << 4) +
                                                          (ml & 7) * 2) = h16;
@@ -1037,7 +1062,7 @@ static int validate_gemm(const char* fn, const uint8_t* a, const void* s_a, cons
             QVD_REQUIRE(epi->n_heads >= 1 && N == 3 * 128 * epi->n_heads, QVD_ESHAPE,
                         "%s: QKV epilogue needs N = 3*128*n_heads (N = %d, n_heads = %d)", fn, N,
                         epi->n_heads);
-            QVD_REQUIRE(epi->q8 && epi->k8 && epi->v && epi->q_scale && epi->k_scale, QVD_EINVAL,
+            QVD_REQUIRE(epi->q8 && epi->k8 && epi->v && epi->q_scale && epi->k_scale && epi->v_exp, QVD_EINVAL,
                         "%s: QKV outputs NULL", fn);
             QVD_REQUIRE(aligned16(epi->q8) && aligned16(epi->k8) && aligned16(epi->v), QVD_EALIGN,
                         "%s: QKV outputs not 16-byte aligned", fn);

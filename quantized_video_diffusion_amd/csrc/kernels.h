@@ -30,20 +30,23 @@ int launch_gemm(const uint8_t* a, const float* s_a, const void* w, const uint8_t
 int launch_gemm_w4a4(const uint8_t* a, const uint8_t* a_e8, const uint8_t* w, const uint8_t* w_e8,
                      const float* bias, int M, int N, int K, const qvd_epilogue& epi, hipStream_t st);
 
-// attention over fp16 V^T [H][128][ceil(L/128)*128]
+// attention over fp16 V^T [H][128][ceil(L/128)*128] holding V 2^-v_exp[h] (one exponent per head)
 int launch_sparse_attn_vt(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
-                          const uint16_t* vt, int L, int H, const int32_t* kv_idx, const int32_t* kv_cnt,
-                          int kmax, float sm_scale, uint16_t* out, float* amax_partials, hipStream_t st);
+                          const uint16_t* vt, const int32_t* v_exp, int L, int H, const int32_t* kv_idx,
+                          const int32_t* kv_cnt, int kmax, float sm_scale, uint16_t* out,
+                          float* amax_partials, hipStream_t st);
 // the same attention writing the E4M3 codes of bf16 O under the static scale *out_scale
 int launch_sparse_attn_vt_e4m3(const int8_t* q, const float* q_scale, const int8_t* k,
-                               const float* k_scale, const uint16_t* vt, int L, int H,
+                               const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int L, int H,
                                const int32_t* kv_idx, const int32_t* kv_cnt, int kmax, float sm_scale,
                                const float* out_scale, uint8_t* out_q, hipStream_t st);
 // ... and the MXFP4 codes of bf16 O: packed E2M1 [L][H][64] + E8M0 [L][H][4]
 int launch_sparse_attn_vt_mxfp4(const int8_t* q, const float* q_scale, const int8_t* k,
-                                const float* k_scale, const uint16_t* vt, int L, int H,
+                                const float* k_scale, const uint16_t* vt, const int32_t* v_exp, int L, int H,
                                 const int32_t* kv_idx, const int32_t* kv_cnt, int kmax, float sm_scale,
                                 uint8_t* out_packed, uint8_t* out_e8m0, hipStream_t st);
+// V^T tiles stored with per-(head, tile) exponents tile_exp [H][T] -> one exponent per head head_exp [H]
+int launch_vt_unify(uint16_t* vt, int L, int H, const int32_t* tile_exp, int32_t* head_exp, hipStream_t st);
 size_t vt_bytes(int L, int H);
 
 // sparse-tile selector: kv_idx [H][T][kept] (-1 past the count), kv_cnt [H][T]

@@ -36,8 +36,21 @@ def _check(t, dtype, name, device=None):
         raise ValueError(f"{name}: must be contiguous")
 
 
+# When set (the GPU tests set it), every output and workspace this module allocates is first filled
+# with 0xFF bytes -- NaN for bf16/fp32, -1 for int8/int32, 255 for codes -- so an element a kernel
+# fails to write shows up in the comparison instead of passing on stale zeros.
+POISON = False
+
+
+def _out(shape, dtype, device):
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if POISON and t.numel():
+        t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
 def _empty(shape, dtype, like):
-    return torch.empty(shape, dtype=dtype, device=like.device)
+    return _out(shape, dtype, like.device)
 
 
 def from_bits(bits, dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
@@ -76,8 +89,8 @@ def quant_int8_qk(x: torch.Tensor, n_heads: int, row_stride: int | None = None):
         raise ValueError("x: must be contiguous (or pass row_stride for a strided row view)")
     L = x.shape[0]
     rs = n_heads * 128 if row_stride is None else row_stride
-    q = torch.empty((L, n_heads, 128), dtype=torch.int8, device=x.device)
-    s = torch.empty((n_heads, (L + 127) // 128), dtype=torch.float32, device=x.device)
+    q = _out((L, n_heads, 128), torch.int8, x.device)
+    s = _out((n_heads, (L + 127) // 128), torch.float32, x.device)
     call("quant_int8_qk", _ptr(x), L, n_heads, 128, 128, rs, _ptr(q), _ptr(s), _stream())
     return q, s
 
@@ -91,7 +104,7 @@ def adaln_project(t: float, basis: torch.Tensor, proj: torch.Tensor, bias=None) 
     nb = proj.shape[0] if stacked else 1
     six_d = proj.shape[-2]
     d = six_d // 6
-    mod = torch.empty((nb, 6, d) if stacked else (6, d), dtype=torch.float32, device=basis.device)
+    mod = _out((nb, 6, d) if stacked else (6, d), torch.float32, basis.device)
     call("qvd_adaln_project_stack", float(t), _ptr(basis), dt, _ptr(proj), _ptr(bias), d, nb,
          _ptr(mod), _stream())
     return mod
@@ -132,49 +145,87 @@ def sparse_attn(q8, q_scale, k8, k_scale, v, kv_idx, kv_cnt, sm_scale: float = S
     _check(v, torch.bfloat16, "v")
     _check(kv_idx, torch.int32, "kv_idx")
     _check(kv_cnt, torch.int32, "kv_cnt")
-    out = torch.empty((L, H, D), dtype=torch.bfloat16, device=q8.device)
-    part = torch.empty(q_scale.shape, dtype=torch.float32, device=q8.device) if want_amax else None
-    ws = torch.empty((_lib.lib().qvd_sparse_attn_ws_bytes(L, H),), dtype=torch.uint8, device=q8.device)
+    out = _out((L, H, D), torch.bfloat16, q8.device)
+    part = _out(q_scale.shape, torch.float32, q8.device) if want_amax else None
+    ws = _out((_lib.lib().qvd_sparse_attn_ws_bytes(L, H),), torch.uint8, q8.device)
     call("sparse_attn", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), L, H, D,
          _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(out), _ptr(part),
          _ptr(ws), ws.numel(), _stream())
     return (out, part) if want_amax else out
 
 
-def sparse_attn_vt_e4m3(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, out_scale,
+@dataclass
+class VTiles:
+    """V^T as the QKV GEMM epilogue writes it: fp16 [H][128][T*128] with one power-of-two exponent
+    per (head, 128-token tile), int32 [H][T]."""
+    t: torch.Tensor
+    tile_exp: torch.Tensor
+
+
+@dataclass
+class VT:
+    """V^T as the attention reads it: fp16 [H][128][T*128] holding V 2^-exp[h], int32 exp [H]."""
+    t: torch.Tensor
+    exp: torch.Tensor
+
+
+def vt_from_bf16(v: torch.Tensor) -> VTiles:
+    """bf16 V [L][H][128] -> VTiles (the transpose sparse_attn applies to its V)."""
+    _check(v, torch.bfloat16, "v")
+    L, H, D = v.shape
+    T = (L + 127) // 128
+    vt = _out((H, 128, T * 128), torch.float16, v.device)
+    te = _out((H, T), torch.int32, v.device)
+    call("qvd_vt_from_bf16", _ptr(v), L, H, _ptr(vt), _ptr(te), _stream())
+    return VTiles(vt, te)
+
+
+def vt_unify(vt: VTiles) -> VT:
+    """One exponent per head (qvd_vt_unify, in place on vt.t)."""
+    H, _, Lp = vt.t.shape
+    he = _out((H,), torch.int32, vt.t.device)
+    call("qvd_vt_unify", _ptr(vt.t), Lp, H, _ptr(vt.tile_exp), _ptr(he), _stream())
+    return VT(vt.t, he)
+
+
+def _vt_args(vt: VT):
+    _check(vt.t, torch.float16, "vt")
+    _check(vt.exp, torch.int32, "vt.exp")
+    return _ptr(vt.t), _ptr(vt.exp)
+
+
+def sparse_attn_vt_e4m3(q8, q_scale, k8, k_scale, vt: VT, kv_idx, kv_cnt, out_scale,
                         sm_scale: float = SM_SCALE):
     """As sparse_attn_vt, returning the E4M3 codes of bf16 O under the static scale out_scale
     (a device fp32 [1] tensor) instead of O: uint8 [L][H][128]."""
     L, H, D = q8.shape
-    _check(vt, torch.float16, "vt")
     _check(out_scale, torch.float32, "out_scale")
-    out = torch.empty((L, H, D), dtype=torch.uint8, device=q8.device)
-    call("qvd_sparse_attn_vt_e4m3", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt), L, H,
+    out = _out((L, H, D), torch.uint8, q8.device)
+    call("qvd_sparse_attn_vt_e4m3", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), *_vt_args(vt), L, H,
          _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(out_scale), _ptr(out),
          _stream())
     return out
 
 
-def sparse_attn_vt_mxfp4(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, sm_scale: float = SM_SCALE):
+def sparse_attn_vt_mxfp4(q8, q_scale, k8, k_scale, vt: VT, kv_idx, kv_cnt, sm_scale: float = SM_SCALE):
     """As sparse_attn_vt, returning the MXFP4 codes of bf16 O per (token, head, 32 dims) instead of
     O: (packed E2M1 uint8 [L][H*64], E8M0 uint8 [L][H*4])."""
     L, H, D = q8.shape
-    _check(vt, torch.float16, "vt")
-    packed = torch.empty((L, H * D // 2), dtype=torch.uint8, device=q8.device)
-    e8 = torch.empty((L, H * D // 32), dtype=torch.uint8, device=q8.device)
-    call("qvd_sparse_attn_vt_mxfp4", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt), L, H,
+    packed = _out((L, H * D // 2), torch.uint8, q8.device)
+    e8 = _out((L, H * D // 32), torch.uint8, q8.device)
+    call("qvd_sparse_attn_vt_mxfp4", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), *_vt_args(vt), L, H,
          _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(packed), _ptr(e8), _stream())
     return packed, e8
 
 
-def sparse_attn_vt(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, sm_scale: float = SM_SCALE,
+def sparse_attn_vt(q8, q_scale, k8, k_scale, vt: VT, kv_idx, kv_cnt, sm_scale: float = SM_SCALE,
                    want_amax: bool = False):
-    """As sparse_attn, with V given as fp16 V^T [H][128][ceil(L/128)*128]."""
+    """As sparse_attn, with V given transposed (VT: fp16 V^T [H][128][ceil(L/128)*128] and the head
+    exponents)."""
     L, H, D = q8.shape
-    _check(vt, torch.float16, "vt")
-    out = torch.empty((L, H, D), dtype=torch.bfloat16, device=q8.device)
-    part = torch.empty(q_scale.shape, dtype=torch.float32, device=q8.device) if want_amax else None
-    call("qvd_sparse_attn_vt", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt), L, H,
+    out = _out((L, H, D), torch.bfloat16, q8.device)
+    part = _out(q_scale.shape, torch.float32, q8.device) if want_amax else None
+    call("qvd_sparse_attn_vt", _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), *_vt_args(vt), L, H,
          _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], float(sm_scale), _ptr(out), _ptr(part),
          _stream())
     return (out, part) if want_amax else out
@@ -182,7 +233,7 @@ def sparse_attn_vt(q8, q_scale, k8, k_scale, vt, kv_idx, kv_cnt, sm_scale: float
 
 def qk_int32_tile(q8, k8, h: int, i: int, j: int) -> torch.Tensor:
     L, H, _ = q8.shape
-    out = torch.empty((128, 128), dtype=torch.int32, device=q8.device)
+    out = _out((128, 128), torch.int32, q8.device)
     call("qvd_qk_int32_tile", _ptr(q8), _ptr(k8), L, H, h, i, j, _ptr(out), _stream())
     return out
 
@@ -232,25 +283,25 @@ def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, 
     e.mode = mode
     ret = None
     if mode == _lib.QVD_EPI_F32:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.device) if out is None else out
+        out = _out((M, N), torch.float32, a.device) if out is None else out
         e.out_f32 = out.data_ptr()
         ret = out
     elif mode in (_lib.QVD_EPI_BF16, _lib.QVD_EPI_GELU):
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if out is None else out
+        out = _out((M, N), torch.bfloat16, a.device) if out is None else out
         e.out_bf16 = out.data_ptr()
         if amax_partials is not None:
             e.amax_partials = amax_partials.data_ptr()
         ret = out
     elif mode == _lib.QVD_EPI_GELU_E4M3:
-        out = torch.empty((M, N), dtype=torch.uint8, device=a.device) if out is None else out
+        out = _out((M, N), torch.uint8, a.device) if out is None else out
         _check(out, torch.uint8, "out")
         _check(out_scale, torch.float32, "out_scale")
         e.out_e4m3 = out.data_ptr()
         e.out_scale = out_scale.data_ptr()
         ret = out
     elif mode == _lib.QVD_EPI_GELU_MXFP4:
-        packed = torch.empty((M, N // 2), dtype=torch.uint8, device=a.device)
-        e8 = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
+        packed = _out((M, N // 2), torch.uint8, a.device)
+        e8 = _out((M, N // 32), torch.uint8, a.device)
         e.out_e2m1 = packed.data_ptr()
         e.out_e8m0 = e8.data_ptr()
         ret = (packed, e8)
@@ -262,14 +313,15 @@ def _gemm(fn, a, s_a, w, extra, N, bias, mode, out, resid, gate, amax_partials, 
     elif mode == _lib.QVD_EPI_QKV:
         H = n_heads
         T = (M + 127) // 128
-        q8 = torch.empty((M, H, 128), dtype=torch.int8, device=a.device)
-        k8 = torch.empty_like(q8)
-        v = torch.empty((H, 128, T * 128), dtype=torch.float16, device=a.device)   # V^T, fp16
-        qs = torch.empty((H, T), dtype=torch.float32, device=a.device)
-        ks = torch.empty_like(qs)
+        q8 = _out((M, H, 128), torch.int8, a.device)
+        k8 = _out(q8.shape, q8.dtype, q8.device)
+        v = VTiles(_out((H, 128, T * 128), torch.float16, a.device), _out((H, T), torch.int32, a.device))
+        qs = _out((H, T), torch.float32, a.device)
+        ks = _out(qs.shape, qs.dtype, qs.device)
         e.n_heads = H
-        e.q8, e.k8, e.v, e.q_scale, e.k_scale = (q8.data_ptr(), k8.data_ptr(), v.data_ptr(),
-                                                 qs.data_ptr(), ks.data_ptr())
+        e.q8, e.k8, e.v, e.q_scale, e.k_scale, e.v_exp = (q8.data_ptr(), k8.data_ptr(), v.t.data_ptr(),
+                                                          qs.data_ptr(), ks.data_ptr(),
+                                                          v.tile_exp.data_ptr())
         ret = (q8, k8, v, qs, ks)
     call(fn, _ptr(a), _ptr(s_a), _ptr(w), _ptr(extra), _ptr(bias), M, N, K, C.byref(e), _stream())
     return ret
@@ -279,8 +331,8 @@ def quant_mxfp4(w: torch.Tensor):
     """bf16 [N][K] -> (packed E2M1 uint8 [N][K/2], E8M0 uint8 [N][K/32])."""
     _check(w, torch.bfloat16, "w")
     N, K = w.shape
-    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
-    e8 = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    packed = _out((N, K // 2), torch.uint8, w.device)
+    e8 = _out((N, K // 32), torch.uint8, w.device)
     call("qvd_quant_mxfp4", _ptr(w), N, K, _ptr(packed), _ptr(e8), _stream())
     return packed, e8
 
@@ -379,10 +431,63 @@ def dit_block_forward(bw: BlockWeights, mod: torch.Tensor, x: torch.Tensor, kv_i
     p = bw.params()
     need = int(_lib.lib().qvd_block_ws_bytes(C.byref(p), L))
     if ws is None:
-        ws = torch.empty((need,), dtype=torch.uint8, device=x.device)
+        ws = _out((need,), torch.uint8, x.device)
     call("dit_block_forward", C.byref(p), _ptr(mod), _ptr(x), L, _ptr(kv_idx), _ptr(kv_cnt),
          int(kmax), _ptr(ws), ws.numel(), _stream())
     return x
+
+
+def block_forward_until(bw: BlockWeights, mod, x, kv_idx, kv_cnt, stage: int, ws=None,
+                        kmax: int | None = None) -> torch.Tensor:
+    """dit_block_forward stopped after ``stage`` (_lib.QVD_STAGE_*); returns the workspace, whose
+    intermediates block_intermediates() exposes.  x is updated as far as the stage goes."""
+    _check(x, torch.bfloat16, "x")
+    _check(mod, torch.float32, "mod")
+    if kv_idx is not None:
+        kmax = kv_idx.shape[-1]
+    L = x.shape[0]
+    p = bw.params()
+    need = int(_lib.lib().qvd_block_ws_bytes(C.byref(p), L))
+    if ws is None:
+        ws = _out((need,), torch.uint8, x.device)
+    call("qvd_block_forward_until", C.byref(p), _ptr(mod), _ptr(x), L, _ptr(kv_idx), _ptr(kv_cnt),
+         int(kmax), int(stage), _ptr(ws), ws.numel(), _stream())
+    return ws
+
+
+def block_intermediates(bw: BlockWeights, ws: torch.Tensor, L: int) -> dict:
+    """Views (no copies) of the block's intermediates in its workspace, by qvd_block_ws_layout."""
+    p = bw.params()
+    offs = (C.c_int64 * len(_lib.WS_SLOTS))()
+    call("qvd_block_ws_layout", C.byref(p), L, offs)
+    d, H, F = bw.d, bw.n_heads, bw.mlp
+    T = (L + 127) // 128
+    a4 = bw.fmt == _lib.QVD_W_MXFP4_A4
+    shapes = {
+        "h": ((L, d // 2) if a4 else (L, d), torch.uint8), "q8": ((L, H, 128), torch.int8),
+        "k8": ((L, H, 128), torch.int8), "vt": ((H, 128, T * 128), torch.float16),
+        "vt_tile_exp": ((H, T), torch.int32), "vt_head_exp": ((H,), torch.int32),
+        "o": ((L, d), torch.bfloat16), "g": ((L, F), torch.bfloat16),
+        "g8": ((L, F // 2) if a4 else (L, F), torch.uint8), "h_e8m0": ((L, d // 32), torch.uint8),
+        "g_e8m0": ((L, F // 32), torch.uint8), "q_scale": ((H, T), torch.float32),
+        "k_scale": ((H, T), torch.float32), "scales": ((4,), torch.float32),
+    }
+    unused = set()
+    if a4 or bw.act_scale is not None:
+        unused |= {"o", "g"}                       # O and g exist only as codes
+    if not a4:
+        unused |= {"h_e8m0", "g_e8m0"}
+    out = {}
+    for i, name in enumerate(_lib.WS_SLOTS):
+        if name not in shapes or name in unused:
+            continue
+        shape, dt = shapes[name]
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dt).element_size()
+        o = int(offs[i])
+        if o + n > ws.numel():
+            continue
+        out[name] = ws[o:o + n].view(dt).view(shape)
+    return out
 
 
 def select_tiles(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor, kept: int):
@@ -393,9 +498,9 @@ def select_tiles(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor, kept
     _check(k_scale, torch.float32, "k_scale")
     L, H, _ = q8.shape
     T = (L + 127) // 128
-    idx = torch.empty((H, T, kept), dtype=torch.int32, device=q8.device)
-    cnt = torch.empty((H, T), dtype=torch.int32, device=q8.device)
-    ws = torch.empty((int(_lib.lib().qvd_select_tiles_ws_bytes(L, H)),), dtype=torch.uint8, device=q8.device)
+    idx = _out((H, T, kept), torch.int32, q8.device)
+    cnt = _out((H, T), torch.int32, q8.device)
+    ws = _out((int(_lib.lib().qvd_select_tiles_ws_bytes(L, H)),), torch.uint8, q8.device)
     call("qvd_select_tiles", _ptr(q8), _ptr(k8), _ptr(k_scale), L, H, kept, _ptr(idx), _ptr(cnt), _ptr(ws),
          ws.numel(), _stream())
     return idx, cnt

@@ -1,0 +1,223 @@
+"""Teacher-forced, stage-by-stage parity of dit_block_forward against the oracle (FP8 block, dynamic
+per-tensor scales).
+
+The block chains four per-tensor requantizations, so a comparison of its output alone mixes each
+stage's own error with codes moved upstream.  Here every stage is checked on its own: the GPU block is
+stopped after each stage (qvd_block_forward_until runs the block's own launches), its intermediates
+are read from the workspace, and the oracle computes the next stage from the GPU's own inputs and
+scales.  With the scales forced, every stage is row-local (modulate, the GEMMs, the quantizers with
+the tensor's amax given) or tile-local (INT8 Q/K, attention), so large blocks are checked on sampled
+token tiles; the per-tensor amax values are taken over the whole tensors.
+
+Bars (stated per stage below):
+  codes of the fused modulate quantizer (h1, h2): equal, except within 2^-12 of a rounding midpoint of
+      the oracle's pre-rounding value (counted; the near-tie rule);
+  the QKV and down-projection GEMMs: their fp32 accumulator output (the same GEMM run with the fp32
+      epilogue) within 1e-3 RMS of the oracle's exact one; the QKV epilogue from those fp32 values --
+      bf16 V, INT8 Q/K codes and scales -- bit-exact;
+  standalone quantizers (O and g) and the per-tensor scales s1, s_O, s2, s_g: bit-exact;
+  bf16 GEMM outputs x1 and GELU(g): one bf16 ulp + 1e-3 RMS;
+  attention output: one bf16 ulp + 1e-2 RMS;
+  block output x2: max |err| <= 1e-2 RMS(x2); beyond it only a one-ulp rounding flip of an element whose
+      oracle value lies within |gate2 (y_gpu - y)| (+ two fp32 roundings) of a bf16 midpoint (counted,
+      at most 1e-3 of the elements).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import quantized_video_diffusion_amd as Q
+from quantized_video_diffusion_amd import _lib
+from oracle import codecs as OC, quant as OQ, adaln as OA, gemm as OG, attention as OAT
+from _gpu_util import (say, bf16_dev, host, host_bits, assert_codes_equal_except_ties, assert_bf16_close,
+                       assert_close_rms)
+
+SM_SCALE = 1.0 / math.sqrt(128.0)
+
+
+def _ln_amax(x_bits, mod, half, eps, chunk=4096):
+    """max |LN(x)(1 + scale) + shift| over the whole tensor (the oracle's fp32 values), by row chunks."""
+    a = np.float32(0.0)
+    for r in range(0, x_bits.shape[0], chunk):
+        y = OA.layernorm_modulate(x_bits[r:r + chunk], mod, half, eps)
+        a = max(a, np.float32(np.abs(y).max()))
+    return np.float32(a)
+
+
+def _bf16_amax(bits) -> np.float32:
+    """max |v| of a bf16 tensor from its bit patterns (finite magnitudes order as their patterns)."""
+    m = int((np.asarray(bits).reshape(-1) & 0x7FFF).max())
+    return np.float32(OC.bf16_to_f64(np.array([m], np.uint16))[0])
+
+
+def _near_bf16_mid(v, win):
+    """|v - nearest bf16 rounding midpoint| <= win, elementwise (v float64, win >= 0)."""
+    a = np.abs(v)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    q = np.ldexp(1.0, e - 1 - 7)                      # bf16 spacing in a's binade
+    t = a / q
+    return np.abs(t - (np.floor(t) + 0.5)) * q <= win
+
+
+def run_stages(bw, mod_d, x_bits, idx_d, cnt_d, rows=None):
+    """Run the GPU block whole and stopped after the stages whose outputs later stages overwrite;
+    return host copies of every intermediate.  Also the GPU's own fp32 accumulator outputs of the QKV
+    and down-projection GEMMs on `rows` (the same GEMM run with the fp32-output epilogue: the main
+    loop and its accumulation order are the same, only the epilogue differs), which the fused
+    epilogues then round (y_qkv, y_down)."""
+    L = x_bits.shape[0]
+    rows_d = None if rows is None else torch.from_numpy(np.asarray(rows)).cuda()
+    pick = (lambda t: host(t)) if rows is None else (lambda t: host(t[rows_d]))
+    xd = bf16_dev(x_bits)
+    ws = Q.block_forward_until(bw, mod_d, xd, idx_d, cnt_d, _lib.QVD_STAGE_ALL)
+    it = Q.block_intermediates(bw, ws, L)
+    g = {"x2": host_bits(xd), "q8": host(it["q8"]), "k8": host(it["k8"]), "qs": host(it["q_scale"]),
+         "ks": host(it["k_scale"]), "vt": host(it["vt"]), "v_exp": host(it["vt_head_exp"]),
+         "o": host_bits(it["o"]), "h2": host(it["h"]), "g": host_bits(it["g"]), "g8": host(it["g8"]),
+         "scales": host(it["scales"])}
+    y = Q.gemm_fp8(it["g8"], it["scales"][3:4].clone(), bw.w["down"], bw.s["down"], bias=bw.b.get("down"))
+    g["y_down"] = pick(y)
+    del it, ws, y
+    for stage, keys in ((_lib.QVD_STAGE_MODULATE1, ("h1",)), (_lib.QVD_STAGE_OQUANT, ("o8",)),
+                        (_lib.QVD_STAGE_OPROJ, ("x1",))):
+        xd = bf16_dev(x_bits)
+        ws = Q.block_forward_until(bw, mod_d, xd, idx_d, cnt_d, stage)
+        it = Q.block_intermediates(bw, ws, L)
+        if stage == _lib.QVD_STAGE_OPROJ:
+            g["x1"] = host_bits(xd)
+        else:
+            g[keys[0]] = host(it["h"])
+            g["scales_" + keys[0]] = host(it["scales"])
+        if stage == _lib.QVD_STAGE_MODULATE1:
+            y = Q.gemm_fp8(it["h"], it["scales"][0:1].clone(), bw.w["qkv"], bw.s["qkv"], bias=bw.b.get("qkv"))
+            g["y_qkv"] = pick(y)
+            del y
+        del it, ws
+    torch.cuda.synchronize()
+    return g
+
+
+def v_bits_from_vt(vt, v_exp, L):
+    """The bf16 V the attention consumed: fp16 V^T [H][128][Lp] times 2^E[h], as bf16 bit patterns
+    [L][H][128] (exact: each value is a bf16 value scaled by a power of two)."""
+    v = vt[:, :, :L].astype(np.float32) * np.ldexp(np.float32(1.0), v_exp.astype(np.int32))[:, None, None]
+    return OC.f64_to_bf16(v.transpose(2, 0, 1).astype(np.float64))
+
+
+def check_block_stages(name, qw, mod, x_bits, idx, cnt, g, n_heads, rows=None, eps=1e-6):
+    """Every stage of the FP8 block against the oracle, fed the GPU's own inputs.  qw: the oracle's
+    quantized weights (codes and scales, as the GPU block holds them); mod: fp32 [6][d] (the GPU's);
+    rows: the token rows checked (whole 128-row tiles, or None for all).  Returns per-stage stats."""
+    L, d = x_bits.shape
+    H = n_heads
+    T = (L + 127) // 128
+    if rows is None:
+        rows = np.arange(L)
+    tiles = np.unique(rows // 128)
+    assert np.array_equal(np.concatenate([np.arange(i * 128, min(L, (i + 1) * 128)) for i in tiles]),
+                          rows), "rows must be whole tiles"
+    mod64 = mod.astype(np.float64)
+    st = {}
+
+    # S1: modulate (attention branch) -> E4M3 with the dynamic scale s1
+    a1 = _ln_amax(x_bits, mod, 0, eps)
+    s1 = g["scales_h1"][0]
+    assert s1 == OQ.fp8_scale_dynamic(a1)[0], f"{name}: s1 {s1} != oracle {OQ.fp8_scale_dynamic(a1)[0]}"
+    y = OA.layernorm_modulate(x_bits[rows], mod, 0, eps)
+    want, _ = OQ.quant_fp8_with_amax(y, a1)
+    inv = OQ.fp8_scale_dynamic(a1)[1]
+    st["h1_flips"] = assert_codes_equal_except_ties(g["h1"][rows], want, y * inv, "e4m3", name=name + " h1")
+
+    # S2: QKV GEMM from the GPU's h1 and s1 (fp32 accumulator output within 1e-3 RMS of the oracle's
+    # exact one); its epilogue from the GPU's own fp32 values: bf16 V, and INT8 Q/K per (head, tile)
+    # with their scales, bit for bit as the oracle's quantizer gives them from bf16(y_gpu)
+    yq = OG.gemm_fp8(g["h1"][rows], s1, qw["w_qkv"], qw["s_qkv"], qw.get("b_qkv"))
+    yg = g["y_qkv"].astype(np.float64)
+    st["qkv_gemm_err_rel"] = assert_close_rms(yg, yq, 1e-3, name + " QKV GEMM (fp32)")
+    yb = OC.f64_to_bf16(yg)                          # fp32 -> bf16 in one rounding, as the epilogue
+    for part, (c8, sc) in enumerate(((g["q8"], g["qs"]), (g["k8"], g["ks"]))):
+        blk = np.ascontiguousarray(yb[:, part * d:(part + 1) * d]).reshape(len(rows), H, 128)
+        for k, i in enumerate(tiles):
+            r = slice(k * 128, k * 128 + min(128, L - i * 128))
+            cw, sw = OQ.quant_int8_qk(blk[r], r.stop - r.start, H)
+            np.testing.assert_array_equal(sc[:, i], sw[:, 0], err_msg=f"{name} part {part} tile {i} scales")
+            np.testing.assert_array_equal(c8[rows[r]], cw, err_msg=f"{name} part {part} tile {i} codes")
+    v_bits = v_bits_from_vt(g["vt"], g["v_exp"], L)
+    vr = v_bits[rows].reshape(len(rows), d)
+    vn = np.abs(OC.bf16_to_f64(vr)) >= 2.0 ** -14 * np.ldexp(1.0, np.repeat(g["v_exp"], 128))[None, :]
+    np.testing.assert_array_equal(vr[vn], yb[:, 2 * d:][vn], err_msg=name + " V = bf16 of the GEMM output")
+
+    # S3: attention from the GPU's Q8, K8, scales and V
+    o_gpu = g["o"].reshape(L, H, 128)
+    for h in range(H):
+        for i in tiles:
+            r = slice(i * 128, min(L, (i + 1) * 128))
+            want = OAT.sparse_attn_tile(g["q8"], g["qs"], g["k8"], g["ks"], v_bits, idx, cnt, h, i, SM_SCALE)
+            assert_bf16_close(np.ascontiguousarray(o_gpu[r, h]), want, 1e-2, f"{name} attention ({h}, {i})")
+
+    # S4: per-tensor FP8 of O (standalone quantizer: bit-exact), amax over the whole O
+    ao = _bf16_amax(g["o"])
+    so = g["scales_o8"][1]
+    assert so == OQ.fp8_scale_dynamic(ao)[0], f"{name}: s_O"
+    want, _ = OQ.quant_fp8_with_amax(OC.bf16_to_f64(g["o"][rows]).astype(np.float32), ao)
+    np.testing.assert_array_equal(g["o8"][rows], want)
+
+    # S5: out-projection + gated residual from the GPU's O8 and s_O
+    y1 = OG.gemm_fp8(g["o8"][rows], so, qw["w_o"], qw["s_o"], qw.get("b_o"))
+    x1_want = OC.bf16_to_f64(x_bits[rows]) + mod64[2][None, :] * y1
+    assert_bf16_close(g["x1"][rows], x1_want, 1e-3, name + " x1")
+
+    # S6: modulate (MLP branch) of the GPU's x1
+    a2 = _ln_amax(g["x1"], mod, 1, eps)
+    s2 = g["scales"][2]
+    assert s2 == OQ.fp8_scale_dynamic(a2)[0], f"{name}: s2"
+    y = OA.layernorm_modulate(g["x1"][rows], mod, 1, eps)
+    want, _ = OQ.quant_fp8_with_amax(y, a2)
+    st["h2_flips"] = assert_codes_equal_except_ties(g["h2"][rows], want, y * OQ.fp8_scale_dynamic(a2)[1],
+                                                    "e4m3", name=name + " h2")
+
+    # S7: up-projection + GELU from the GPU's h2 and s2
+    gw = OG.gelu(OG.gemm_fp8(g["h2"][rows], s2, qw["w_up"], qw["s_up"], qw.get("b_up")))
+    assert_bf16_close(g["g"][rows], gw, 1e-3, name + " GELU")
+
+    # S8: per-tensor FP8 of g (standalone: bit-exact), amax over the whole g
+    ag = _bf16_amax(g["g"])
+    sg = g["scales"][3]
+    assert sg == OQ.fp8_scale_dynamic(ag)[0], f"{name}: s_g"
+    want, _ = OQ.quant_fp8_with_amax(OC.bf16_to_f64(g["g"][rows]).astype(np.float32), ag)
+    np.testing.assert_array_equal(g["g8"][rows], want)
+
+    # S9: down-projection + gated residual from the GPU's g8, s_g and x1: the block output.  The GEMM's
+    # fp32 output is within 1e-3 RMS of the exact one; the block output is then compared with the
+    # oracle's, x2 = bf16(x1 + gate2 y) from the exact y.  Where the two differ, the oracle's value must
+    # lie within |gate2 (y_gpu - y)| + two fp32 roundings of a bf16 midpoint (a rounding flip).
+    y2 = OG.gemm_fp8(g["g8"][rows], sg, qw["w_down"], qw["s_down"], qw.get("b_down"))
+    y2g = g["y_down"].astype(np.float64)
+    st["down_gemm_err_rel"] = assert_close_rms(y2g, y2, 1e-3, name + " down GEMM (fp32)")
+    gy = mod64[5][None, :] * y2
+    x2_f64 = OC.bf16_to_f64(g["x1"][rows]) + gy
+    x2_want = OC.bf16_to_f64(OC.f64_to_bf16(x2_f64))
+    got = OC.bf16_to_f64(g["x2"][rows])
+    err = np.abs(got - x2_want)
+    rms = float(np.sqrt(np.mean(x2_want ** 2)))
+    win = np.abs(mod64[5][None, :] * (y2g - y2)) + 2.0 ** -23 * np.abs(x2_f64)
+    tie = _near_bf16_mid(x2_f64, win)
+    ulp = np.abs(x2_want) * 2.0 ** -7
+    far = ~tie
+    st["x2_max_err_rel"] = float(err.max() / rms)
+    st["x2_max_err_rel_off_ties"] = float(err[far].max() / rms) if far.any() else 0.0
+    big = err > 1e-2 * rms
+    st["x2_tie_flips"] = int(np.count_nonzero(big))
+    say(f"{name}: stages ok; h1 {st['h1_flips']} / h2 {st['h2_flips']} near-tie code flips; GEMM fp32 max|err| "
+        f"QKV {st['qkv_gemm_err_rel']:.1e} / down {st['down_gemm_err_rel']:.1e} RMS; "
+        f"block output max|err| {st['x2_max_err_rel']:.2e} RMS "
+        f"({st['x2_max_err_rel_off_ties']:.2e} away from bf16 near-ties; {st['x2_tie_flips']} one-ulp flips of "
+        f"large outputs at near-ties)")
+    # every output within 1e-2 RMS; beyond it only a one-ulp rounding flip of a large output whose
+    # oracle value sits within the GEMM's accumulation error of a bf16 midpoint
+    assert (~big | (tie & (err <= ulp))).all(), f"{name}: block output beyond 1e-2 RMS away from a near-tie"
+    assert st["x2_tie_flips"] <= max(8, 1e-3 * err.size), f"{name}: {st['x2_tie_flips']} near-tie flips"
+    return st

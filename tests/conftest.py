@@ -11,3 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+@pytest.fixture(autouse=True)
+def _poison_gpu_outputs(request):
+    """GPU tests run with every output and workspace the binding allocates pre-filled with 0xFF
+    bytes (NaN / -1 / 255), so an element a kernel leaves unwritten cannot pass as a stale zero."""
+    if request.node.get_closest_marker("gpu") is not None:
+        from quantized_video_diffusion_amd import ops
+        ops.POISON = True
+    yield

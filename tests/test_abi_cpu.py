@@ -91,13 +91,22 @@ def test_host_validation_errors(lib):
                    C.c_float(0.1), fake, None, fake, 16, None) == _lib.QVD_EWORKSPACE
     assert _status(lib, "sparse_attn", fake, fake, fake, fake, fake, 0, 2, 128, None, None, 3,
                    C.c_float(0.1), None, None, None, 0, None) == _lib.QVD_OK
-    assert lib.qvd_sparse_attn_ws_bytes(300, 2) == 2 * 128 * 384 * 2
-    assert _status(lib, "qvd_sparse_attn_vt", fake, fake, fake, fake, mis, 300, 2, fake, fake, 3,
+    # fp16 V^T (2 x 128 x 384 x 2 bytes), then tile exponents [2][3] and head exponents [2], each
+    # region 256-byte aligned
+    assert lib.qvd_sparse_attn_ws_bytes(300, 2) == 2 * 128 * 384 * 2 + 256 + 8
+    assert _status(lib, "qvd_sparse_attn_vt", fake, fake, fake, fake, mis, fake, 300, 2, fake, fake, 3,
                    C.c_float(0.1), fake, None, None) == _lib.QVD_EALIGN
-    assert _status(lib, "qvd_sparse_attn_vt_mxfp4", fake, fake, fake, fake, fake, 300, 2, fake, fake, 3,
-                   C.c_float(0.1), fake, P(0x10002), None) == _lib.QVD_EALIGN
-    assert _status(lib, "qvd_sparse_attn_vt_mxfp4", fake, fake, fake, fake, fake, 300, 2, fake, fake, 3,
+    assert _status(lib, "qvd_sparse_attn_vt", fake, fake, fake, fake, fake, None, 300, 2, fake, fake, 3,
                    C.c_float(0.1), fake, None, None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_sparse_attn_vt_mxfp4", fake, fake, fake, fake, fake, fake, 300, 2, fake, fake,
+                   3, C.c_float(0.1), fake, P(0x10002), None) == _lib.QVD_EALIGN
+    assert _status(lib, "qvd_sparse_attn_vt_mxfp4", fake, fake, fake, fake, fake, fake, 300, 2, fake, fake,
+                   3, C.c_float(0.1), fake, None, None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_vt_unify", fake, 300, 0, fake, fake, None) == _lib.QVD_ESHAPE
+    assert _status(lib, "qvd_vt_unify", fake, 300, 2, None, fake, None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_vt_unify", mis, 300, 2, fake, fake, None) == _lib.QVD_EALIGN
+    assert _status(lib, "qvd_vt_from_bf16", fake, 300, 2, fake, None, None) == _lib.QVD_EINVAL
+    assert _status(lib, "qvd_vt_from_bf16", fake, 0, 2, None, None, None) == _lib.QVD_OK
     assert _status(lib, "qvd_select_tiles", fake, fake, fake, 300, 2, 0, fake, fake, fake, big, None) == _lib.QVD_ESHAPE
     assert _status(lib, "qvd_select_tiles", fake, fake, fake, 131073, 2, 4, fake, fake, fake, big, None) == _lib.QVD_ESHAPE
     assert _status(lib, "qvd_select_tiles", fake, fake, fake, 300, 2, 4, fake, None, fake, big, None) == _lib.QVD_EINVAL
@@ -133,7 +142,7 @@ def test_host_validation_errors(lib):
     p = _lib.BlockParams()
     p.version = 99
     assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 10, fake, fake, 1, fake, 1, None) == _lib.QVD_EINVAL
-    p.version, p.d, p.n_heads, p.head_dim, p.mlp = 1, 256, 2, 128, 1024
+    p.version, p.d, p.n_heads, p.head_dim, p.mlp = _lib.ABI_VERSION, 256, 2, 128, 1024
     for f in ("w_qkv", "w_o", "w_up", "w_down", "s_qkv", "s_o", "s_up", "s_down"):
         setattr(p, f, 0x10000)
     assert lib.qvd_block_ws_bytes(C.byref(p), 256) > 0
@@ -155,7 +164,7 @@ def test_host_validation_errors(lib):
 
 def test_workspace_sizes_scale_with_tokens(lib):
     p = _lib.BlockParams()
-    p.version, p.d, p.n_heads, p.head_dim, p.mlp = 1, 2688, 21, 128, 10752
+    p.version, p.d, p.n_heads, p.head_dim, p.mlp = _lib.ABI_VERSION, 2688, 21, 128, 10752
     a = lib.qvd_block_ws_bytes(C.byref(p), 4096)
     b = lib.qvd_block_ws_bytes(C.byref(p), 33784)
     assert b > 8 * a * 0.95

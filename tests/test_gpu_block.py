@@ -222,7 +222,7 @@ def test_block_480p_full_size_equals_its_steps():
     xs = bf16_dev(x)
     h1, s1 = Q.adaln_modulate(xs, mod, 0)
     q8, k8, vt, qs, ks = Q.gemm_fp8(h1, s1, bw.w["qkv"], bw.s["qkv"], mode=_lib.QVD_EPI_QKV, n_heads=H)
-    o = Q.sparse_attn_vt(q8, qs, k8, ks, vt, idx_d, cnt_d)
+    o = Q.sparse_attn_vt(q8, qs, k8, ks, Q.vt_unify(vt), idx_d, cnt_d)
     o8, so = Q.quant_fp8_per_tensor(o.reshape(L, d))
     Q.gemm_fp8(o8, so, bw.w["o"], bw.s["o"], mode=_lib.QVD_EPI_RESID_GATE, out=xs, resid=xs, gate=mod[2])
     h2, s2 = Q.adaln_modulate(xs, mod, 1)
@@ -270,7 +270,7 @@ def test_block_768p_4bit_full_size_equals_its_steps(fmt):
     if fmt == "w4a4":
         hp, he = Q.adaln_modulate_mxfp4(xs, mod, 0)
         q8, k8, vt, qs, ks = Q.gemm_mxfp4_w4a4(hp, he, *wq["qkv"], mode=_lib.QVD_EPI_QKV, n_heads=H)
-        op, oe = Q.sparse_attn_vt_mxfp4(q8, qs, k8, ks, vt, idx_d, cnt_d)
+        op, oe = Q.sparse_attn_vt_mxfp4(q8, qs, k8, ks, Q.vt_unify(vt), idx_d, cnt_d)
         Q.gemm_mxfp4_w4a4(op, oe, *wq["o"], gate=mod[2], **rg)
         hp, he = Q.adaln_modulate_mxfp4(xs, mod, 1)
         gp, ge = Q.gemm_mxfp4_w4a4(hp, he, *wq["up"], mode=_lib.QVD_EPI_GELU_MXFP4)
@@ -279,7 +279,7 @@ def test_block_768p_4bit_full_size_equals_its_steps(fmt):
         a = bw.act_scale
         h, s = Q.adaln_modulate(xs, mod, 0, act_scale=a[0:1])
         q8, k8, vt, qs, ks = Q.gemm_mxfp4(h, s, *wq["qkv"], mode=_lib.QVD_EPI_QKV, n_heads=H)
-        o8 = Q.sparse_attn_vt_e4m3(q8, qs, k8, ks, vt, idx_d, cnt_d, a[1:2])
+        o8 = Q.sparse_attn_vt_e4m3(q8, qs, k8, ks, Q.vt_unify(vt), idx_d, cnt_d, a[1:2])
         Q.gemm_mxfp4(o8.reshape(L, d), a[1:2], *wq["o"], gate=mod[2], **rg)
         h, s = Q.adaln_modulate(xs, mod, 1, act_scale=a[2:3])
         g8 = Q.gemm_mxfp4(h, s, *wq["up"], mode=_lib.QVD_EPI_GELU_E4M3, out_scale=a[3:4])

@@ -42,6 +42,35 @@ def test_gemm_fp8_480p_qkv_shape_sampled():
     assert_close_rms(got, want, 1e-3, "gemm 480p rows")
 
 
+def test_gemm_fp8_480p_down_shape_sampled():
+    """The 480p down-projection shape: M = 33,784 (ragged last tile), N = 2,688 (10.5 tiles wide),
+    K = 10,752; realistic codes (per-tensor quantized N(0,1) activations and Glorot weights); 64
+    sampled rows in fp32 at 1e-3 RMS, and the gated-residual epilogue the block uses at that shape on
+    the same rows at 1 bf16 ulp + 1e-3 RMS."""
+    M, N, K = W.TOKENS_480P, 2688, 10752
+    say("gemm 480p down", M, N, K)
+    # 2,048 distinct activation rows, quantized by the oracle, repeated down the 33,784 rows (the
+    # oracle quantizer would take about a minute over the whole tensor)
+    a0, sa = OQ.quant_fp8_bf16(W.normal_bf16((2048, K), seed=41))
+    a = np.ascontiguousarray(np.resize(a0, (M, K)))
+    wt, sw = OQ.quant_fp8_bf16(W.f32_to_bf16_bits(W.glorot_uniform(N, K, W.rng_for(41, 81, 0, "w_down"))))
+    rows = np.r_[np.random.default_rng(2).choice(M, 60, replace=False), [0, M - 1, M - 120, M - 248]]
+    rows_d = torch.from_numpy(rows).cuda()
+    ad, wd = u8_dev(a), u8_dev(wt)
+    y = Q.gemm_fp8(ad, f32_dev([sa]), wd, f32_dev([sw]))
+    got = host(y[rows_d])
+    del y
+    want = OG.gemm_fp8(a[rows], sa, wt, sw)
+    assert_close_rms(got, want, 1e-3, "gemm 480p down rows")
+    x = W.normal_bf16((M, N), seed=42)
+    gate = np.linspace(-0.2, 0.2, N).astype(np.float32)
+    xd = bf16_dev(x)
+    Q.gemm_fp8(ad, f32_dev([sa]), wd, f32_dev([sw]), mode=_lib.QVD_EPI_RESID_GATE, out=xd, resid=xd,
+               gate=f32_dev(gate))
+    want_r = OC.bf16_to_f64(x[rows]) + gate[None, :].astype(np.float64) * want
+    assert_bf16_close(host_bits(xd[rows_d]), want_r, 1e-3, "gemm 480p down resid-gate rows")
+
+
 def test_gemm_bf16_and_resid_gate_epilogues():
     M, N, K = 300, 512, 384
     a, w = _codes(M, K, 3), _codes(N, K, 4, "codes_b")
@@ -116,6 +145,14 @@ def test_gemm_gelu_e4m3_epilogue_static_scale(fmt, M, N, K):
         np.testing.assert_array_equal(got, host(two_pass))
 
 
+def _vt_tile_exponent(amax: float) -> int:
+    """The V^T tile exponent rule as the header states it: 0 while max|v| is in [2^-6, 2^15) (or the
+    tile is zero), else floor(log2 max|v|) - 14."""
+    if amax == 0 or 2.0 ** -6 <= amax < 2.0 ** 15:
+        return 0
+    return int(np.floor(np.log2(amax))) - 14
+
+
 def _realistic_codes(M, N, K, seed):
     """Activation codes of N(0,1) data and weight codes of Glorot-uniform weights, both through the
     oracle's per-tensor quantizer (so the accumulators have a realistic dynamic range)."""
@@ -134,15 +171,23 @@ def test_gemm_qkv_epilogue(M, H):
                                    mode=_lib.QVD_EPI_QKV, n_heads=H)
     y = OG.gemm_fp8(a, sa, w, sw)
     ybits = OC.f64_to_bf16(y)
-    # V part: V^T [H][128][Lp] in fp16 holding the bf16-rounded values, zeros past M
+    # V part: fp16 V^T [H][128][Lp] holding the bf16-rounded values times 2^-e per (head, tile),
+    # zeros past M; the exponents follow the tile rule, and fp16 * 2^e is a bf16 value exactly
     T = (M + 127) // 128
-    vt = host(v.view(torch.float16)).astype(np.float64)
-    assert vt.shape == (H, 128, T * 128)
+    vt = host(v.t).astype(np.float64)
+    te = host(v.tile_exp)
+    assert vt.shape == (H, 128, T * 128) and te.shape == (H, T)
     assert not vt[:, :, M:].any()
-    v_got = vt[:, :, :M].transpose(2, 0, 1).reshape(M, d)
-    v_bits = OC.f64_to_bf16(v_got)           # fp16 holding a bf16 value converts back exactly
-    np.testing.assert_array_equal(OC.bf16_to_f64(v_bits), v_got)
+    vv = vt[:, :, :M] * np.ldexp(1.0, np.repeat(te, 128, axis=1)[:, None, :M])
+    v_got = vv.transpose(2, 0, 1).reshape(M, d)
+    v_bits = OC.f64_to_bf16(v_got)
+    normal = np.abs(vt[:, :, :M].transpose(2, 0, 1).reshape(M, d)) >= 2.0 ** -14
+    np.testing.assert_array_equal(OC.bf16_to_f64(v_bits)[normal], v_got[normal])
     assert_bf16_close(v_bits, y[:, 2 * d:], 1e-3, "V part")
+    for h in range(H):
+        for i in range(T):
+            a_ = np.abs(v_got[i * 128: min(M, (i + 1) * 128), h * 128: (h + 1) * 128]).max()
+            assert te[h, i] == _vt_tile_exponent(a_), (h, i, a_, te[h, i])
     for part, (g8, gs) in enumerate(((q8, qs), (k8, ks))):
         cw, sw_ = OQ.quant_int8_qk(np.ascontiguousarray(ybits[:, part * d:(part + 1) * d]), M, H)
         # scales: bf16 rounding of the fp32 accumulators can differ at near-ties only
@@ -274,10 +319,7 @@ def test_sparse_attn_e4m3_output_static_scale():
     L, H = 1290, 2
     qb, kb, vb, idx, cnt = _attn_inputs(L, H, 13, True)
     (q8, qs, k8, ks), (oq, oqs, ok, oks) = _quantize_both(qb, kb, L, H)
-    T = (L + 127) // 128
-    vt = np.zeros((H, 128, T * 128), np.float16)
-    vt[:, :, :L] = OC.bf16_to_f64(vb).transpose(1, 2, 0).astype(np.float16)
-    vt_d = torch.from_numpy(vt).cuda()
+    vt_d = Q.vt_unify(Q.vt_from_bf16(bf16_dev(vb)))
     out = Q.sparse_attn_vt(q8, qs, k8, ks, vt_d, i32_dev(idx), i32_dev(cnt))
     want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx, cnt)
     rms = float(np.sqrt(np.mean(want ** 2)))
@@ -294,16 +336,124 @@ def test_sparse_attn_e4m3_output_static_scale():
 
 
 def test_sparse_attn_vt_entry_matches_bf16_entry():
-    """The fp16 V^T entry point on a host-transposed V gives the same bits as the bf16 entry."""
+    """The V^T entry point, on V transposed by qvd_vt_from_bf16 and unified per head, gives the same
+    bits as the bf16 entry."""
     L, H = 1290, 2
     qb, kb, vb, idx, cnt = _attn_inputs(L, H, 12, True)
     (q8, qs, k8, ks), _ = _quantize_both(qb, kb, L, H)
-    T = (L + 127) // 128
-    vt = np.zeros((H, 128, T * 128), np.float16)
-    vt[:, :, :L] = OC.bf16_to_f64(vb).transpose(1, 2, 0).astype(np.float16)
     a = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt))
-    b = Q.sparse_attn_vt(q8, qs, k8, ks, torch.from_numpy(vt).cuda(), i32_dev(idx), i32_dev(cnt))
+    b = Q.sparse_attn_vt(q8, qs, k8, ks, Q.vt_unify(Q.vt_from_bf16(bf16_dev(vb))), i32_dev(idx),
+                         i32_dev(cnt))
     np.testing.assert_array_equal(host_bits(a), host_bits(b))
+
+
+def test_vt_transpose_and_unify():
+    """qvd_vt_from_bf16 then qvd_vt_unify on a V whose tiles need different exponents: one tile of
+    head 0 is scaled up to 1e6 (exponent 5), one of head 1 down to 1e-4 (exponent -28), the rest are
+    in the usual range (exponent 0).  Every tile's exponent follows the rule; each head then holds
+    fp16(v 2^-E) with E the head's largest exponent, equal to the bf16 value times 2^-E wherever that
+    is an fp16 normal, and within the fp16 subnormal spacing (2^-25) below it."""
+    L, H = 700, 2
+    _, _, vb = W.qkv_heads(L, H, seed=17)
+    v = OC.bf16_to_f64(vb)
+    v[256:384, 0, :] *= 1e6 / np.abs(v[256:384, 0, :]).max()
+    v[128:256, 1, :] *= 1e-4 / np.abs(v[128:256, 1, :]).max()
+    vb2 = OC.f64_to_bf16(v)
+    v = OC.bf16_to_f64(vb2)
+    T = (L + 127) // 128
+    tiles = Q.vt_from_bf16(bf16_dev(vb2))
+    te = host(tiles.tile_exp)
+    for h in range(H):
+        for j in range(T):
+            assert te[h, j] == _vt_tile_exponent(np.abs(v[j * 128: (j + 1) * 128, h]).max()), (h, j)
+    assert te[0, 2] == 5 and te[1, 1] == -28 and te[0, 0] == 0
+    vt = Q.vt_unify(tiles)
+    he = host(vt.exp)
+    np.testing.assert_array_equal(he, te.max(axis=1))
+    got = host(vt.t).astype(np.float64)
+    assert not got[:, :, L:].any()
+    want = np.ldexp(v.transpose(1, 2, 0), -he[:, None, None])
+    err = np.abs(got[:, :, :L] - want)
+    normal = np.abs(want) >= 2.0 ** -14
+    assert not err[normal].any()
+    assert (err[~normal] <= 2.0 ** -25).all()
+
+
+def test_sparse_attn_v_outside_fp16_range():
+    """V as bf16 at magnitudes fp16 cannot hold: head 0 has every third key row scaled by 1e6 in
+    dims 0..31 (above 65,504; those outputs are dominated by them), head 1 is scaled by 1e-9
+    throughout (below fp16's smallest normal, 2^-14).  Each head must match the oracle within one
+    bf16 ulp + 1e-2 of its own output RMS."""
+    L, H = 1290, 2
+    qb, kb, vb, idx, cnt = _attn_inputs(L, H, 21, True)
+    v = OC.bf16_to_f64(vb)
+    v[::3, 0, :32] *= 1e6
+    v[:, 1, :] *= 1e-9
+    vb2 = OC.f64_to_bf16(v)
+    (q8, qs, k8, ks), (oq, oqs, ok, oks) = _quantize_both(qb, kb, L, H)
+    out = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb2), i32_dev(idx), i32_dev(cnt))
+    want = OAT.sparse_attn(oq, oqs, ok, oks, vb2, idx, cnt)
+    ob = host_bits(out)
+    assert np.abs(want[:, 0, :32]).max() > 65504 * 4
+    for h in range(H):
+        assert_bf16_close(np.ascontiguousarray(ob[:, h]), want[:, h], 1e-2, f"V outside fp16, head {h}")
+    # the same through the V^T entry (the layout the QKV epilogue writes)
+    out_t = Q.sparse_attn_vt(q8, qs, k8, ks, Q.vt_unify(Q.vt_from_bf16(bf16_dev(vb2))), i32_dev(idx),
+                             i32_dev(cnt))
+    np.testing.assert_array_equal(host_bits(out_t), ob)
+
+
+def test_sparse_attn_large_qk_scales_tile_varying_k():
+    """Q and K scaled so that tile maxima reach about 100, and each key tile's K rows further scaled by
+    its own factor in [1/4, 4]: the per-tile score factors sQ sK / sqrt(128) log2(e) then differ by up
+    to 16x within one row and reach ~0.5 log2 units per integer score step.  The numerator arguments
+    must stay exact up to fp32 rounding across tiles (a constant rounded per tile would skew the
+    tiles' relative weights by up to ~0.4 log2 units here)."""
+    L, H = 1290, 2
+    qb, kb, vb, idx, cnt = _attn_inputs(L, H, 23, True)
+    T = (L + 127) // 128
+    f = np.exp(np.random.default_rng(5).uniform(np.log(0.25), np.log(4.0), size=(H, T)))
+    qv = OC.bf16_to_f64(qb) * 25.0
+    kv = OC.bf16_to_f64(kb) * 25.0
+    for h in range(H):
+        kv[:, h, :] *= f[h][np.arange(L) // 128][:, None]
+    qb2, kb2 = OC.f64_to_bf16(qv), OC.f64_to_bf16(kv)
+    (q8, qs, k8, ks), (oq, oqs, ok, oks) = _quantize_both(qb2, kb2, L, H)
+    say("large scales: max q scale", float(host(qs).max()), "k scale range",
+        float(host(ks).min()), float(host(ks).max()))
+    out = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt))
+    want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx, cnt)
+    assert_bf16_close(host_bits(out), want, 1e-2, "large Q/K scales")
+
+
+def test_sparse_attn_row_varying_kept_counts():
+    """Each (head, query tile) keeps its own number of tiles, 0 .. kmax, drawn so that the two work
+    items of one workgroup (neighbouring query tiles of a head) mostly differ; the lists are random
+    ascending tile sets with or without the diagonal.  Rows with no kept tile give zeros."""
+    L, H = 2000, 3
+    T = (L + 127) // 128
+    kmax = 12
+    rng = np.random.default_rng(31)
+    qb, kb, vb = W.qkv_heads(L, H, seed=31)
+    idx = np.full((H, T, kmax), -1, np.int32)
+    cnt = np.zeros((H, T), np.int32)
+    for h in range(H):
+        for i in range(T):
+            c = int(rng.integers(0, kmax + 1)) if (h * T + i) % 5 else 0
+            tiles = np.sort(rng.choice(T, size=c, replace=False)).astype(np.int32)
+            idx[h, i, :c] = tiles
+            cnt[h, i] = c
+    pairs = cnt.reshape(-1)[: (H * T) // 2 * 2].reshape(-1, 2)
+    assert (pairs[:, 0] != pairs[:, 1]).mean() > 0.5
+    (q8, qs, k8, ks), (oq, oqs, ok, oks) = _quantize_both(qb, kb, L, H)
+    out, part = Q.sparse_attn(q8, qs, k8, ks, bf16_dev(vb), i32_dev(idx), i32_dev(cnt), want_amax=True)
+    want = OAT.sparse_attn(oq, oqs, ok, oks, vb, idx, cnt)
+    got = bf16_f64(out)
+    assert_bf16_close(host_bits(out), want, 1e-2, "row-varying counts")
+    for h in range(H):
+        for i in range(T):
+            if cnt[h, i] == 0:
+                assert not got[i * 128: min(L, (i + 1) * 128), h].any()
 
 
 def test_sparse_attn_diag_only_and_out_of_range_entries():

@@ -28,6 +28,20 @@ def test_fp8_dynamic_scale_hits_448_and_bounds_error():
     assert rel.max() <= 2 ** -4 * (1 + 1e-6)
 
 
+def test_fp8_with_given_amax_matches_whole_tensor_rule():
+    """Row by row with the whole tensor's amax gives the whole-tensor dynamic codes and scale; a
+    different amax gives different codes."""
+    x = W.bf16_bits_to_f32(W.normal_bf16((200, 64), seed=4, scale=2.0))
+    codes, s = Q.quant_fp8_per_tensor(x)
+    amax = np.float32(np.abs(x).max())
+    for r in (slice(0, 1), slice(50, 120), slice(199, 200)):
+        c, s2 = Q.quant_fp8_with_amax(x[r], amax)
+        np.testing.assert_array_equal(c, codes[r])
+        assert s2 == s
+    c, _ = Q.quant_fp8_with_amax(x, amax * np.float32(2))
+    assert (c != codes).any()
+
+
 def test_fp8_zero_tensor_and_static_scale():
     codes, s = Q.quant_fp8_per_tensor(np.zeros(10, np.float32))
     assert s == 1.0 and not codes.any()
