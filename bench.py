@@ -305,7 +305,7 @@ def run_768p(seed, steps=5, warmup=2):
         for b in range(nb):
             Q.amax_update(batch(site, din, b), amax)
         a = float(amax.item())
-        s_cal = Q.calibrated_scale(a)
+        s_cal = np.float32(Q.calibrated_scale(amax).item())
         counts = {}
         for tag, sc in (("cal", s_cal), ("uncal", s_unc)):
             st = torch.tensor([sc], dtype=torch.float32, device="cuda")

@@ -381,11 +381,16 @@ int qvd_block_ws_layout(const qvd_block_params* p, int32_t L, int64_t* offsets);
  * qvd_amax_update: *amax = max(*amax, max|x|) over n fp32 values (running calibration amax; the
  *   caller zeroes *amax once before the first batch).
  * qvd_clip_count: *count += #{ |x| > s*448 } (exact comparison in float64) over n fp32 values,
- *   s = *scale; *count is a device uint64 the caller zeroes. */
+ *   s = *scale; *count is a device uint64 the caller zeroes.
+ * qvd_calibrated_scale: the static per-tensor scale of each of n calibration maxima (the farwalk
+ *   post's calibrated 4-bit layers; the rule is this library's reading): scale[i] = fp32(amax[i]/448),
+ *   raised by one fp32 ulp when 448 scale[i] (exact) would fall below amax[i], so that no value of
+ *   the calibration set clips; amax[i] = 0 gives 1.  amax, scale: device fp32 [n]. */
 int qvd_quant_mxfp4(const uint16_t* w, int32_t N, int32_t K, uint8_t* packed, uint8_t* e8m0,
                     void* stream);
 int qvd_amax_update(const float* x, int64_t n, float* amax, void* stream);
 int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* count, void* stream);
+int qvd_calibrated_scale(const float* amax, float* scale, int32_t n, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Per-kernel timing (off by default).  While enabled, each kernel launch the library makes is

@@ -90,6 +90,7 @@ SIGNATURES = {
     "qvd_quant_mxfp4": (C.c_int, [_p, _i32, _i32, _p, _p, _p]),
     "qvd_amax_update": (C.c_int, [_p, _i64, _p, _p]),
     "qvd_clip_count": (C.c_int, [_p, _i64, _p, _p, _p]),
+    "qvd_calibrated_scale": (C.c_int, [_p, _p, _i32, _p]),
     "qvd_timing_enable": (C.c_int, [C.c_int]),
     "qvd_timing_report": (C.c_int, [C.c_char_p, _sz]),
 }

@@ -213,6 +213,22 @@ __global__ void __launch_bounds__(QBLOCK) k_amax_update(const float* __restrict_
     if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
 }
 
+// Static scale from a calibration amax: s = fp32(amax / 448) (correctly rounded), raised to the next
+// fp32 value when 448 s (exact in float64) falls below amax, so that no calibration value clips;
+// amax = 0 gives 1.
+__global__ void __launch_bounds__(256) k_calibrated_scale(const float* __restrict__ amax,
+                                                          float* __restrict__ scale, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float a = amax[i];
+    float s = 1.0f;
+    if (a != 0.0f) {
+        s = __fdiv_rn(a, 448.0f);
+        if ((double)s * 448.0 < (double)a) s = nextafterf(s, INFINITY);
+    }
+    scale[i] = s;
+}
+
 __global__ void __launch_bounds__(QBLOCK) k_clip_count(const float* __restrict__ x, int64_t n,
                                                        const float* __restrict__ scale,
                                                        unsigned long long* __restrict__ count) {
@@ -308,6 +324,17 @@ int qvd_quant_mxfp4(const uint16_t* w, int32_t N, int32_t K, uint8_t* packed, ui
     hipLaunchKernelGGL(k_quant_mxfp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, w, N, K, packed, e8m0);
     return launch_status("qvd_quant_mxfp4");
+}
+
+int qvd_calibrated_scale(const float* amax, float* scale, int32_t n, void* stream) {
+    QVD_REQUIRE(n >= 0, QVD_ESHAPE, "qvd_calibrated_scale: n < 0");
+    if (n == 0) return QVD_OK;
+    QVD_PTR(amax);
+    QVD_PTR(scale);
+    QVD_DEVICE_OK();
+    hipLaunchKernelGGL(k_calibrated_scale, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, amax,
+                       scale, n);
+    return launch_status("qvd_calibrated_scale");
 }
 
 int qvd_amax_update(const float* x, int64_t n, float* amax, void* stream) {

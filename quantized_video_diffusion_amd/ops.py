@@ -350,16 +350,11 @@ def clip_count(x: torch.Tensor, scale: torch.Tensor, count: torch.Tensor):
 # ----------------------------------------------------------------------------------------------
 # block
 
-def calibrated_scale(amax: float) -> np.float32:
-    """Static per-tensor FP8 scale from a calibration amax: fp32(amax / 448), moved up by one fp32 ulp
-    when 448 s (exact) would fall below amax, so that no calibration value exceeds the E4M3 range.
-    amax = 0 gives 1."""
-    a = np.float32(amax)
-    if a == 0:
-        return np.float32(1.0)
-    s = np.float32(a / np.float32(448.0))
-    while float(s) * 448.0 < float(a):
-        s = np.nextafter(s, np.float32(np.inf))
+def calibrated_scale(amax: torch.Tensor) -> torch.Tensor:
+    """Device fp32 calibration maxima [n] -> their static per-tensor scales [n] (qvd_calibrated_scale)."""
+    _check(amax, torch.float32, "amax")
+    s = _out(amax.shape, torch.float32, amax.device)
+    call("qvd_calibrated_scale", _ptr(amax), _ptr(s), amax.numel(), _stream())
     return s
 
 

@@ -171,16 +171,3 @@ def test_workspace_sizes_scale_with_tokens(lib):
     # h, q8, k8 (1 B), v, o (2 B) per L*d; g (2 B) + g8 (1 B) per L*F -> at least 7 L d + 3 L F
     assert b >= 7 * 33784 * 2688 + 3 * 33784 * 10752
     assert lib.qvd_quant_ws_bytes(10) >= 4 * 1024
-
-
-def test_calibrated_scale_host_rule_matches_oracle():
-    """The package's host-side calibration rule against the oracle's, on random and edge amax values."""
-    import numpy as np
-    import quantized_video_diffusion_amd as Q
-    from oracle import quant as OQ
-    rng = np.random.default_rng(3)
-    vals = list(np.exp(rng.uniform(-30, 30, 2000)).astype(np.float32)) + [0.0, 448.0, 1.0, 3e-38, 1e38]
-    for a in vals:
-        got, want = Q.calibrated_scale(a), OQ.calibrated_scale(a)
-        assert got == want and got.dtype == np.float32, (a, got, want)
-        assert float(got) * 448.0 >= float(np.float32(a))

@@ -182,3 +182,17 @@ def test_calibration_amax_and_clip_counts():
         want_cnt = sum(OQ.clip_count(b, s_val) for b in batches)
         assert int(host(cnt)[0]) == want_cnt
         assert (want_cnt == 0) == expect_zero
+
+
+def test_calibrated_scale_vs_oracle():
+    """qvd_calibrated_scale equals the oracle's rule bit for bit: values whose fp32(a/448) needs the
+    one-ulp raise (448 s < a) and values that do not, powers of two, 0, the extremes of fp32."""
+    rng = np.random.default_rng(7)
+    a = np.concatenate([rng.uniform(0, 1000, 3000), np.exp(rng.uniform(-80, 80, 3000)),
+                        2.0 ** np.arange(-120, 120, 7), [0.0, 448.0, 1.0, 3.4e38, 1.2e-38]]).astype(np.float32)
+    got = host(Q.calibrated_scale(f32_dev(a)))
+    want = np.array([OQ.calibrated_scale(v) for v in a], np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    raised = np.array([float(np.float32(v / np.float32(448.0))) * 448.0 < float(v) for v in a])
+    assert raised.sum() > 100 and (~raised).sum() > 100
+    assert ((got.astype(np.float64) * 448.0) >= a.astype(np.float64)).all()
