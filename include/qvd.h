@@ -122,6 +122,19 @@ size_t qvd_adaln_modulate_ws_bytes(int32_t L, int32_t d);
 int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
                    float eps, const float* act_scale_in, uint8_t* q, float* act_scale_out,
                    void* ws, size_t ws_bytes, void* stream);
+/* adaln_modulate for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same computation and results, with no ws argument.
+ * The dynamic scale's workspace (row statistics and partial maxima) is a 4 MiB array inside the
+ * library, one per GPU, held until the process ends; its device address is looked up once per
+ * device on the first call there.  Dynamic scales (act_scale_in == NULL) therefore accept
+ * L <= 261,872 tokens (QVD_EWORKSPACE beyond, with nothing launched); a static scale needs no
+ * workspace and takes any L.  The call allocates nothing (no hipMalloc/hipFree, no timer events:
+ * the library's opt-in per-kernel timer skips it).  Every call on one GPU uses that GPU's single
+ * array: calls that overlap on one GPU (concurrent streams or threads) race and must be serialized
+ * by the caller.  Nothing in the array needs clearing between calls. */
+int adaln_modulate_noalloc(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                           float eps, const float* act_scale_in, uint8_t* q, float* act_scale_out,
+                           void* stream);
 /* The same modulated LayerNorm with MXFP4 output (W4A4 blocks: the 4-bit transformer of the
  * news.farwalk.ai FastH3 story, post 6/8, in OCP MX form): y as above, then per token row and 32
  * consecutive channels X = 2^(floor(log2 max|y|) - 2) (all-zero block: X = 1), codes E2M1(y / X),

@@ -64,6 +64,7 @@ SIGNATURES = {
     "qvd_adaln_modulate_ws_bytes": (_sz, [_i32, _i32]),
     "adaln_modulate": (C.c_int, [_p, _i32, _i32, _p, _i32, _f32, _p, _p, _p, _p, _sz, _p]),
     "adaln_modulate_mxfp4": (C.c_int, [_p, _i32, _i32, _p, _i32, _f32, _p, _p, _p]),
+    "adaln_modulate_noalloc": (C.c_int, [_p, _i32, _i32, _p, _i32, _f32, _p, _p, _p, _p]),
     "qvd_sparse_attn_ws_bytes": (_sz, [_i32, _i32]),
     "sparse_attn": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _f32, _p, _p, _p, _sz,
                               _p]),

@@ -10,6 +10,8 @@
 // codes do not depend on the summation order of the row statistics (the fp64 sum of bf16 values is
 // exact at these widths).  The kernel is bound by HBM traffic: one wave owns a row, keeps it in
 // registers, and stores its codes as 16-bit pairs.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -432,6 +434,72 @@ int adaln_modulate(const uint16_t* x, int32_t L, int32_t d, const float* mod, in
     QVD_DEVICE_OK();
     return launch_modulate(x, L, d, mod, half, eps, act_scale_in, q, act_scale_out, ws,
                            (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Allocation-free modulate: the dynamic scale's row statistics and partial maxima (the workspace of
+// adaln_modulate) live in this file-scope device array, one copy per GPU for the life of the
+// process.  In host code `scratch` names a host-side stand-in, never its device memory: the device
+// address comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t MODULATE_SCRATCH_BYTES = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[MODULATE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_ptr_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QVD_EHIP, "adaln_modulate_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    QVD_REQUIRE(dev >= 0 && dev < MAX_DEVICES, QVD_EUNSUPPORTED, "adaln_modulate_noalloc: device %d", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(QVD_EHIP, "adaln_modulate_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QVD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int adaln_modulate_noalloc(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                           float eps, const float* act_scale_in, uint8_t* q, float* act_scale_out,
+                           void* stream) {
+    QVD_REQUIRE(L >= 0, QVD_ESHAPE, "adaln_modulate_noalloc: L = %d", L);
+    QVD_REQUIRE(d >= 128 && d % 128 == 0 && d <= 4096, QVD_ESHAPE,
+                "adaln_modulate_noalloc: d = %d (multiple of 128, at most 4096)", d);
+    QVD_REQUIRE(half == 0 || half == 1, QVD_EINVAL, "adaln_modulate_noalloc: half = %d (0 or 1)", half);
+    QVD_REQUIRE(eps >= 0.0f, QVD_EINVAL, "adaln_modulate_noalloc: eps < 0");
+    QVD_PTR(mod);
+    QVD_PTR(act_scale_out);
+    QVD_ALIGN(mod);
+    if (L > 0) {
+        QVD_PTR(x);
+        QVD_PTR(q);
+        QVD_ALIGN(x);
+        QVD_ALIGN(q);
+    }
+    QVD_REQUIRE(act_scale_in != nullptr || adaln_ws_bytes(L, d) <= MODULATE_SCRATCH_BYTES, QVD_EWORKSPACE,
+                "adaln_modulate_noalloc: L = %d needs %zu bytes of scratch; the library holds %zu per device "
+                "(dynamic scales up to L = %d)", L, adaln_ws_bytes(L, d), MODULATE_SCRATCH_BYTES,
+                (int)((MODULATE_SCRATCH_BYTES - adaln_ws_bytes(0, d)) / sizeof(double2)));
+    QVD_DEVICE_OK();
+    void* ws = nullptr;
+    int s = scratch_ptr_current_device(&ws);
+    if (s) return s;
+    TimingOff no_events;
+    return launch_modulate(x, L, d, mod, half, eps, act_scale_in, q, act_scale_out, ws, (hipStream_t)stream);
 }
 
 int adaln_modulate_mxfp4(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,

@@ -9,6 +9,16 @@ namespace qvd {
 
 bool timing_enabled();
 
+// While one of these lives on a thread, that thread's launches record no events (the timer creates
+// events on demand, which an allocation-free entry point must not do).
+class TimingOff {
+public:
+    TimingOff();
+    ~TimingOff();
+    TimingOff(const TimingOff&) = delete;
+    TimingOff& operator=(const TimingOff&) = delete;
+};
+
 // Records an event pair around the launches made during its lifetime, when timing is enabled.
 class TimingScope {
 public:

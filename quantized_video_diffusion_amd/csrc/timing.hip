@@ -38,8 +38,15 @@ hipEvent_t take_event() {
 
 bool timing_enabled() { return g_on; }
 
+namespace {
+thread_local int t_off = 0;
+}
+
+TimingOff::TimingOff() { ++t_off; }
+TimingOff::~TimingOff() { --t_off; }
+
 TimingScope::TimingScope(const char* key, hipStream_t st) : st_(st) {
-    if (!g_on) return;
+    if (!g_on || t_off > 0) return;
     std::lock_guard<std::mutex> lk(g_mu);
     start_ = take_event();
     stop_ = take_event();

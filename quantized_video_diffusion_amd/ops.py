@@ -124,6 +124,21 @@ def adaln_modulate(x: torch.Tensor, mod: torch.Tensor, half: int, eps: float = 1
     return q, s
 
 
+def adaln_modulate_noalloc(x: torch.Tensor, mod: torch.Tensor, half: int, q: torch.Tensor,
+                           scale_out: torch.Tensor, eps: float = 1e-6,
+                           act_scale: torch.Tensor | None = None):
+    """adaln_modulate into caller-owned q (uint8 [L][d]) and scale_out (fp32 [1]); the library
+    allocates nothing (its per-GPU scratch holds the workspace)."""
+    _check(x, torch.bfloat16, "x")
+    _check(mod, torch.float32, "mod")
+    _check(q, torch.uint8, "q")
+    _check(scale_out, torch.float32, "scale_out")
+    L, d = x.shape
+    call("adaln_modulate_noalloc", _ptr(x), L, d, _ptr(mod), half, float(eps), _ptr(act_scale), _ptr(q),
+         _ptr(scale_out), _stream())
+    return q, scale_out
+
+
 def adaln_modulate_mxfp4(x: torch.Tensor, mod: torch.Tensor, half: int, eps: float = 1e-6):
     """bf16 [L][d] -> (packed E2M1 uint8 [L][d/2], E8M0 uint8 [L][d/32])."""
     _check(x, torch.bfloat16, "x")
