@@ -27,4 +27,4 @@ that takes it. Every function here is pinned by a CPU test under tests/ against 
 brute force, a special case or an invariant.
 """
 
-from . import codecs, quant, adaln, gemm, attention, block  # noqa: F401
+from . import codecs, quant, adaln, gemm, attention, block, sampler  # noqa: F401
