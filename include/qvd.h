@@ -406,11 +406,50 @@ int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* coun
 int qvd_calibrated_scale(const float* amax, float* scale, int32_t n, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * The sampler around the stack -- comfyui-wiki page, "Trim 改变了什么" training bullet (eight steps
+ * at t = 999, 874, 749, 624, 500, 375, 250, 125) and "在 ComfyUI 中运行" (8 steps of res_multistep,
+ * simple schedule, sigma shift 10 on video and 3 on audio).  Readings this library takes:
+ *   sigma = t / 1000, rectified flow x_sigma = (1 - sigma) x0 + sigma eps; per modality the time
+ *   shift sigma' = s sigma / (1 + (s - 1) sigma) (s = shift_video for rows < L_video, shift_audio for
+ *   the rest) and a final sigma' = 0;
+ *   the stack's output is the velocity v, so x0_hat = x - sigma' v (the latent head is the identity:
+ *   the latent is the token sequence itself);
+ *   res_multistep: the two-step exponential Adams-Bashforth step of the refined exponential solver in
+ *   lambda = log((1 - sigma) / sigma), h = lambda_next - lambda:
+ *     x_next = (sigma_next / sigma) x + alpha_next [(1 - e^-h) x0_hat + (h - 1 + e^-h) / h_prev
+ *              (x0_hat - x0_hat_prev)]
+ *   (first order at step 0; the last step, to sigma' = 0, returns x0_hat).
+ * Coefficients are computed in double precision on the host; the state is fp32.
+ * timesteps: NULL for the pages' eight (n_steps = 8: rint(999 - 999 i / n_steps)), or a host array
+ * of n_steps values, strictly decreasing, in (0, 1000). */
+#define QVD_SAMPLER_MAX_STEPS 64
+typedef struct {
+    int32_t n_steps;
+    const float* timesteps;
+    float shift_video, shift_audio;
+    int32_t L_video;
+} qvd_sampler_config;
+/* The n_steps + 1 noise levels of modality 0 (video) or 1 (audio) into host doubles. */
+int qvd_sampler_sigmas(const qvd_sampler_config* c, int32_t modality, double* sigmas);
+/* Start from noise: eps bf16 [L][d] -> x_state fp32 [L][d] = sigma'_0 eps (per modality), and
+ * x_in bf16 [L][d] = bf16(x_state), the first step's stack input.  d a multiple of 8; 16-byte aligned. */
+int qvd_sampler_start(const qvd_sampler_config* c, const uint16_t* eps, int32_t L, int32_t d, float* x_state,
+                      uint16_t* x_in, void* stream);
+/* Step `step` (0 .. n_steps-1) after the stack has run at its timestep: v bf16 [L][d] is the stack's
+ * output for the input bf16(x_state).  Updates x_state (fp32) to the next state; x0_hat (fp32 [L][d])
+ * holds the previous step's estimate on entry (unused at step 0) and this step's on return; writes
+ * x_in = bf16(new state), the next step's stack input.  x_in may be the same buffer as v (the stack
+ * works in place).  After the last step x_state holds the final latent. */
+int qvd_sampler_step(const qvd_sampler_config* c, int32_t step, const uint16_t* v, float* x_state, float* x0_hat,
+                     uint16_t* x_in, int32_t L, int32_t d, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Per-kernel timing (off by default).  While enabled, each kernel launch the library makes is
  * bracketed by a pair of HIP events recorded on the launch's own stream.  qvd_timing_report waits
  * for the recorded work, writes {"<kernel key>": {"count": n, "total_ms": t}, ...} (NUL-terminated
  * JSON) into buf and clears the records.  Keys: "sparse_attn", "adaln_modulate", "adaln_project",
- * "adaln_modulate_mxfp4", "quant_fp8", "amax_bf16", "quant_int8_qk", "select_tiles", "gemm_<fp8|mxfp4|w4a4>_<epilogue>_<M>x<N>x<K>".
+ * "adaln_modulate_mxfp4", "quant_fp8", "amax_bf16", "quant_int8_qk", "select_tiles", "vt_unify", "vt_from_bf16",
+ * "sampler", "gemm_<fp8|mxfp4|w4a4>_<epilogue>_<M>x<N>x<K>".
  * Returns QVD_EINVAL if len is too small (the records are then lost), QVD_EHIP on event errors. */
 int qvd_timing_enable(int on);
 int qvd_timing_report(char* buf, size_t len);

@@ -39,6 +39,11 @@ class Epilogue(C.Structure):
     ]
 
 
+class SamplerConfig(C.Structure):
+    _fields_ = [("n_steps", _i32), ("timesteps", _p), ("shift_video", _f32), ("shift_audio", _f32),
+                ("L_video", _i32)]
+
+
 class BlockParams(C.Structure):
     _fields_ = [
         ("version", _i32), ("d", _i32), ("n_heads", _i32), ("head_dim", _i32), ("mlp", _i32),
@@ -92,6 +97,9 @@ SIGNATURES = {
     "qvd_amax_update": (C.c_int, [_p, _i64, _p, _p]),
     "qvd_clip_count": (C.c_int, [_p, _i64, _p, _p, _p]),
     "qvd_calibrated_scale": (C.c_int, [_p, _p, _i32, _p]),
+    "qvd_sampler_sigmas": (C.c_int, [C.POINTER(SamplerConfig), _i32, C.POINTER(C.c_double)]),
+    "qvd_sampler_start": (C.c_int, [C.POINTER(SamplerConfig), _p, _i32, _i32, _p, _p, _p]),
+    "qvd_sampler_step": (C.c_int, [C.POINTER(SamplerConfig), _i32, _p, _p, _p, _p, _i32, _i32, _p]),
     "qvd_timing_enable": (C.c_int, [C.c_int]),
     "qvd_timing_report": (C.c_int, [C.c_char_p, _sz]),
 }

@@ -529,3 +529,55 @@ def timing_report() -> dict:
     buf = C.create_string_buffer(1 << 20)
     call("qvd_timing_report", buf, len(buf))
     return json.loads(buf.value.decode())
+
+
+# ----------------------------------------------------------------------------------------------
+# sampler
+
+@dataclass
+class Sampler:
+    """The eight-step sampler's configuration (qvd_sampler_config) and its device state."""
+    L_video: int
+    shift_video: float = 10.0
+    shift_audio: float = 3.0
+    timesteps: tuple | None = None            # None: the eight of the pages
+    x_state: torch.Tensor | None = None       # fp32 [L][d]
+    x0_hat: torch.Tensor | None = None        # fp32 [L][d]
+
+    def config(self):
+        c = _lib.SamplerConfig()
+        n = 8 if self.timesteps is None else len(self.timesteps)
+        c.n_steps, c.shift_video, c.shift_audio, c.L_video = n, self.shift_video, self.shift_audio, self.L_video
+        if self.timesteps is not None:
+            self._ts = (C.c_float * n)(*self.timesteps)
+            c.timesteps = C.cast(self._ts, C.c_void_p)
+        return c
+
+    def sigmas(self, modality: int) -> np.ndarray:
+        c = self.config()
+        out = (C.c_double * (c.n_steps + 1))()
+        call("qvd_sampler_sigmas", C.byref(c), modality, out)
+        return np.array(out[:])
+
+    def start(self, eps: torch.Tensor, x_in: torch.Tensor | None = None) -> torch.Tensor:
+        """eps bf16 [L][d] -> the first stack input (bf16); allocates the fp32 state."""
+        _check(eps, torch.bfloat16, "eps")
+        L, d = eps.shape
+        self.x_state = _out((L, d), torch.float32, eps.device)
+        self.x0_hat = _out((L, d), torch.float32, eps.device)
+        x_in = _out((L, d), torch.bfloat16, eps.device) if x_in is None else x_in
+        c = self.config()
+        call("qvd_sampler_start", C.byref(c), _ptr(eps), L, d, _ptr(self.x_state), _ptr(x_in), _stream())
+        return x_in
+
+    def step(self, i: int, v: torch.Tensor, x_in: torch.Tensor | None = None) -> torch.Tensor:
+        """After the stack ran at step i with output v (bf16 [L][d]): advance the state; returns the
+        next stack input (written into x_in, which may be v)."""
+        _check(v, torch.bfloat16, "v")
+        L, d = v.shape
+        x_in = v if x_in is None else x_in
+        c = self.config()
+        call("qvd_sampler_step", C.byref(c), int(i), _ptr(v), _ptr(self.x_state), _ptr(self.x0_hat), _ptr(x_in),
+             L, d, _stream())
+        return x_in
+

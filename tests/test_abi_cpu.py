@@ -171,3 +171,29 @@ def test_workspace_sizes_scale_with_tokens(lib):
     # h, q8, k8 (1 B), v, o (2 B) per L*d; g (2 B) + g8 (1 B) per L*F -> at least 7 L d + 3 L F
     assert b >= 7 * 33784 * 2688 + 3 * 33784 * 10752
     assert lib.qvd_quant_ws_bytes(10) >= 4 * 1024
+
+
+def test_sampler_schedule_matches_oracle(lib):
+    """qvd_sampler_sigmas (host code, no GPU) against the oracle's schedule: the pages' eight steps with
+    both shifts, and a caller-given set of timesteps."""
+    import numpy as np
+    from oracle import sampler as OS
+    for ts, sv, sa in ((None, 10.0, 3.0), ((900.0, 600.0, 300.0, 50.0), 4.0, 1.0)):
+        c = _lib.SamplerConfig()
+        n = 8 if ts is None else len(ts)
+        c.n_steps, c.shift_video, c.shift_audio, c.L_video = n, sv, sa, 100
+        if ts is not None:
+            arr = (C.c_float * n)(*ts)
+            c.timesteps = C.cast(arr, C.c_void_p)
+        for mod, s in ((0, sv), (1, sa)):
+            out = (C.c_double * (n + 1))()
+            assert lib.qvd_sampler_sigmas(C.byref(c), mod, out) == _lib.QVD_OK
+            want = OS.sigmas(s, None if ts is None else np.array(ts, np.float32).astype(np.float64))
+            np.testing.assert_allclose(np.array(out[:]), want, rtol=1e-15, atol=0)
+    c = _lib.SamplerConfig()
+    c.n_steps, c.shift_video, c.shift_audio = 0, 10.0, 3.0
+    out = (C.c_double * 2)()
+    assert lib.qvd_sampler_sigmas(C.byref(c), 0, out) == _lib.QVD_EINVAL
+    bad = (C.c_float * 2)(500.0, 600.0)
+    c.n_steps, c.timesteps = 2, C.cast(bad, C.c_void_p)
+    assert lib.qvd_sampler_sigmas(C.byref(c), 0, out) == _lib.QVD_EINVAL   # not decreasing
