@@ -265,12 +265,25 @@ def time_selector(L, H, kept, seed, reps=5):
     return round(e0.elapsed_time(e1) / reps, 4)
 
 
+def _code_fractions(codes):
+    """Fractions of E4M3 codes that are zero and that are subnormal (exponent field 0, non-zero)."""
+    import numpy as np
+    c = np.asarray(codes).reshape(-1) & 0x7F
+    zero = float(np.count_nonzero(c == 0)) / c.size
+    sub = float(np.count_nonzero((c != 0) & (c < 0x08))) / c.size
+    return {"zero": round(zero, 5), "subnormal": round(sub, 5)}
+
+
 def run_768p(seed, steps=5, warmup=2):
-    """The 768p-shaped block (85,696 tokens) with MXFP4 weights and static activation scales
-    calibrated on the GPU: 4 activation sites x 64 heavy-tailed batches x 1,024 tokens, the MLP-down
-    input carrying outlier channels at 137x the typical amax A0.  Reports the block's throughput, the
-    clips under the calibrated scales (64 calibration batches and a held-out 65th) and under the
-    uncalibrated scale A0/448."""
+    """The 768p-shaped block (85,696 tokens) with MXFP4 weights, its static E4M3 activation scales
+    calibrated on the block's own GEMM inputs: 64 seeded heavy-tailed (Student-t, nu = 3) input batches
+    of 1,024 tokens run through the same block with dynamic scales, and each of the four GEMM inputs
+    (h1, O, h2, g) contributes its amax (qvd_amax_update).  One layer carries outliers: 0.1% of the
+    up-projection's output channels are scaled so that the down-projection input g reaches 137x the
+    amax it has without them (A0).  Reports the clips under the calibrated scales (64 batches and a
+    held-out 65th) and under uncalibrated ones (each site's outlier-free amax / 448), each site's
+    zero and subnormal E4M3 code fractions in the full-size block under the calibrated scales beside
+    the dynamic-scale block's, and the block's timing as W4A8 (calibrated) and W4A4 (same weights)."""
     import numpy as np
     import torch
     import workloads as W
@@ -279,67 +292,109 @@ def run_768p(seed, steps=5, warmup=2):
 
     w = W.WORKLOADS["block_768p_mxfp4"]
     L, d, F, H = w.L, w.d, w.mlp, w.n_heads
-    nb, tok, out_site = 64, 1024, 3
-    sites = [("qkv_in", d), ("o_in", d), ("up_in", d), ("down_in", F)]
+    nb, tok = 64, 1024
     t0 = time.perf_counter()
-    ch = W.outlier_channels_device(F, seed, w.tag, out_site)
-    a0 = torch.zeros(1, dtype=torch.float32, device="cuda")
-    chmax = torch.zeros((), dtype=torch.float32, device="cuda")
-    for b in range(nb):
-        xb = W.calibration_batch_device(F, b, seed, w.tag, out_site, tok)
-        Q.amax_update(xb, a0)
-        chmax = torch.maximum(chmax, xb[:, ch].abs().max())
-    A0 = float(a0.item())
-    factor = np.float32(137.0 * A0 / float(chmax.item()))
-
-    def batch(site, din, b):
-        xb = W.calibration_batch_device(din, b, seed, w.tag, site, tok)
-        if site == out_site:
-            xb[:, ch] *= float(factor)
-        return xb
-
-    s_unc = np.float32(A0 / np.float32(448.0))
-    calib, scales = [], []
-    for site, (name, din) in enumerate(sites):
-        amax = torch.zeros(1, dtype=torch.float32, device="cuda")
-        for b in range(nb):
-            Q.amax_update(batch(site, din, b), amax)
-        a = float(amax.item())
-        s_cal = np.float32(Q.calibrated_scale(amax).item())
-        counts = {}
-        for tag, sc in (("cal", s_cal), ("uncal", s_unc)):
-            st = torch.tensor([sc], dtype=torch.float32, device="cuda")
-            c64 = torch.zeros(1, dtype=torch.int64, device="cuda")
-            cho = torch.zeros(1, dtype=torch.int64, device="cuda")
-            for b in range(nb):
-                Q.clip_count(batch(site, din, b), st, c64)
-            Q.clip_count(batch(site, din, nb), st, cho)
-            counts[tag] = (int(c64.item()), int(cho.item()))
-        n64 = nb * tok * din
-        calib.append({"site": name, "d_in": din, "amax": a, "amax_over_A0": round(a / A0, 3),
-                      "scale_calibrated": float(s_cal),
-                      "clips_calibrated_64_batches": counts["cal"][0],
-                      "clips_calibrated_held_out": counts["cal"][1],
-                      "clips_uncalibrated_64_batches": counts["uncal"][0],
-                      "clip_rate_uncalibrated": counts["uncal"][0] / n64})
-        scales.append(s_cal)
-    calib_s = time.perf_counter() - t0
-
-    x0 = Q.from_bits(W.activations(w, seed))
-    wb = {k: Q.from_bits(v) for k, v in W.block_weights(w, seed, 0).items()}
-    bw = Q.quantize_block_weights(wb, d, H, F, fmt=_lib.QVD_W_MXFP4)
-    del wb
-    bw.act_scale = torch.tensor(scales, dtype=torch.float32, device="cuda")
+    wbits = W.block_weights(w, seed, 0)
+    ch = W.outlier_channels_device(F, seed, w.tag, 3).cpu().numpy()
     basis = Q.from_bits(W.adaln_basis(w, seed), torch.float16)
     proj = Q.from_bits(W.adaln_proj(w, seed, 0), torch.float16)
     mod = Q.adaln_project(999.0, basis, proj)
+    idx_c, cnt_c = W.block_mask(w, seed, 0, L=tok)
+    idx_cd, cnt_cd = torch.from_numpy(idx_c).cuda(), torch.from_numpy(cnt_c).cuda()
+    ch_d = torch.from_numpy(ch).cuda()
+    sites = ("qkv_in", "o_in", "up_in", "down_in")
+
+    def make_weights(factor, fmt):
+        wb = dict(wbits)
+        if factor != 1.0:
+            up = W.bf16_bits_to_f32(wb["w_up"]).copy()
+            up[ch] *= np.float32(factor)
+            wb["w_up"] = W.f32_to_bf16_bits(up)
+        return Q.quantize_block_weights({k: Q.from_bits(v) for k, v in wb.items()}, d, H, F, fmt=fmt)
+
+    def batch(b):
+        return W.calibration_batch_device(d, b, seed, w.tag, 0, tok).to(torch.bfloat16).contiguous()
+
+    def site_values(bw, xb):
+        """The block's four GEMM inputs on one batch (dynamic scales): h1, h2 fp32; O, g bf16."""
+        h1 = Q.layernorm_modulate_f32(xb, mod, 0)
+        x = xb.clone()
+        ws = Q.block_forward_until(bw, mod, x, idx_cd, cnt_cd, _lib.QVD_STAGE_OPROJ)
+        o = Q.block_intermediates(bw, ws, tok)["o"].clone()
+        h2 = Q.layernorm_modulate_f32(x, mod, 1)
+        x = xb.clone()
+        ws = Q.block_forward_until(bw, mod, x, idx_cd, cnt_cd, _lib.QVD_STAGE_UP)
+        g = Q.block_intermediates(bw, ws, tok)["g"].clone()
+        return [h1, o, h2, g]
+
+    def amax_pass(bw):
+        amax = torch.zeros(4, dtype=torch.float32, device="cuda")
+        chmax = torch.zeros(1, dtype=torch.float32, device="cuda")
+        for b in range(nb):
+            vals = site_values(bw, batch(b))
+            for k, v in enumerate(vals):
+                Q.amax_update(v, amax[k:k + 1])
+            Q.amax_update(vals[3][:, ch_d].contiguous(), chmax)
+        return amax, chmax
+
+    # pass 1: the block without outliers -> each site's outlier-free amax A0 and the outlier channels' amax
+    bw1 = make_weights(1.0, _lib.QVD_W_MXFP4)
+    a0, ch0 = amax_pass(bw1)
+    a0_h = a0.cpu().numpy()
+    factor = float(137.0 * a0_h[3] / float(ch0.item()))
+    del bw1
+    # pass 2: with the up-projection's outlier channels scaled -> the calibration amax of every site
+    bw_dyn = make_weights(factor, _lib.QVD_W_MXFP4)
+    amax, _ = amax_pass(bw_dyn)
+    s_cal = Q.calibrated_scale(amax)
+    s_unc = Q.calibrated_scale(a0)
+    # clip counts under both scales: the 64 calibration batches and a held-out 65th
+    counts = {k: torch.zeros(4, dtype=torch.int64, device="cuda") for k in ("cal", "cal_ho", "unc", "unc_ho")}
+    for b in range(nb + 1):
+        vals = site_values(bw_dyn, batch(b))
+        for k, v in enumerate(vals):
+            Q.clip_count(v, s_cal[k:k + 1], counts["cal" if b < nb else "cal_ho"][k:k + 1])
+            Q.clip_count(v, s_unc[k:k + 1], counts["unc" if b < nb else "unc_ho"][k:k + 1])
+    amax_h, s_cal_h, s_unc_h = amax.cpu().numpy(), s_cal.cpu().numpy(), s_unc.cpu().numpy()
+    cnt_h = {k: v.cpu().numpy() for k, v in counts.items()}
+    calib_s = time.perf_counter() - t0
+
+    # the full-size block: static (calibrated) and dynamic scales, codes at each GEMM input
+    x0 = Q.from_bits(W.activations(w, seed))
     idx, cnt = W.block_mask(w, seed, 0)
     kept = kept_scores(idx, cnt, L)
     kv_idx, kv_cnt = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
-    # the same MXFP4 weights with MXFP4 activations (W4A4: dynamic E8M0 scales, no act_scale)
+    bw = Q.BlockWeights(d=d, n_heads=H, mlp=F, fmt=_lib.QVD_W_MXFP4, w=bw_dyn.w, e8=bw_dyn.e8,
+                        act_scale=s_cal.clone())
+
+    def code_fractions(weights):
+        out = []
+        x = torch.empty_like(x0)
+        for stage, key in ((_lib.QVD_STAGE_MODULATE1, "h"), (_lib.QVD_STAGE_OQUANT, "h"),
+                           (_lib.QVD_STAGE_MODULATE2, "h"), (_lib.QVD_STAGE_GQUANT, "g8")):
+            x.copy_(x0)
+            ws = Q.block_forward_until(weights, mod, x, kv_idx, kv_cnt, stage)
+            out.append(_code_fractions(Q.block_intermediates(weights, ws, L)[key].cpu().numpy()))
+            del ws
+        torch.cuda.empty_cache()
+        return out
+
+    frac_static = code_fractions(bw)
+    frac_dynamic = code_fractions(bw_dyn)
+    calib = []
+    for k, name in enumerate(sites):
+        n64 = nb * tok * (F if k == 3 else d)
+        calib.append({"site": name, "amax_without_outliers": float(a0_h[k]), "amax": float(amax_h[k]),
+                      "amax_over_A0": round(float(amax_h[k] / a0_h[k]), 3),
+                      "scale_calibrated": float(s_cal_h[k]), "scale_uncalibrated": float(s_unc_h[k]),
+                      "clips_calibrated_64_batches": int(cnt_h["cal"][k]),
+                      "clips_calibrated_held_out": int(cnt_h["cal_ho"][k]),
+                      "clips_uncalibrated_64_batches": int(cnt_h["unc"][k]),
+                      "clip_rate_uncalibrated": int(cnt_h["unc"][k]) / n64,
+                      "codes_calibrated_block": frac_static[k], "codes_dynamic_block": frac_dynamic[k]})
+
     bw4 = Q.BlockWeights(d=d, n_heads=H, mlp=F, fmt=_lib.QVD_W_MXFP4_A4, w=bw.w, e8=bw.e8)
-    ws = torch.empty(max(Q.block_ws_bytes(bw, L), Q.block_ws_bytes(bw4, L)), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(max(Q.block_ws_bytes(bw, L), Q.block_ws_bytes(bw4, L)), dtype=torch.uint8, device="cuda")
     x = torch.empty_like(x0)
     gemm = 2.0 * L * (3 * d * d + d * d + d * F + F * d)
     attn = 2.0 * 2.0 * 128 * kept
@@ -369,7 +424,7 @@ def run_768p(seed, steps=5, warmup=2):
     ms_block, tf, kern_ms = time_block(bw)
     ms4, tf4, kern4 = time_block(bw4)
     return {"workload": "block_768p_mxfp4", "tokens": L, "weights": "MXFP4 (E2M1 + E8M0 per 32)",
-            "activations": "E4M3, static calibrated scales",
+            "activations": "E4M3, static scales calibrated on the block's own GEMM inputs",
             "kept_key_tiles_per_row": w.kmax, "key_tiles": w.n_tiles,
             "ms_per_block": round(ms_block, 4), "TFLOP/s": round(tf, 1),
             "pct_of_fp8_int8_peak": round(100 * tf / PEAK_TFLOPS["fp8"], 2),
@@ -378,10 +433,117 @@ def run_768p(seed, steps=5, warmup=2):
             "w4a4": {"activations": "MXFP4 (E2M1 + dynamic E8M0 per token and 32 channels)",
                      "ms_per_block": round(ms4, 4), "TFLOP/s": round(tf4, 1), "kernels_ms": kern4},
             "selector_ms": time_selector(L, H, w.kmax, seed),
-            "calibration": {"batches": nb, "tokens_per_batch": tok, "A0": A0,
-                            "outlier_site": sites[out_site][0], "outlier_ratio": 137.0,
-                            "uncalibrated_scale": float(s_unc), "sites": calib,
-                            "seconds": round(calib_s, 1)}}
+            "calibration": {"batches": nb, "tokens_per_batch": tok,
+                            "input": "Student-t (nu = 3) token batches through the block, dynamic scales",
+                            "outlier": {"site": "down_in", "channels": int(len(ch)),
+                                        "up_rows_scaled_by": round(factor, 3),
+                                        "amax_over_A0": round(float(amax_h[3] / a0_h[3]), 3)},
+                            "sites": calib, "seconds": round(calib_s, 1)}}
+
+
+def system_info():
+    """Device, software versions, and the clocks rocm-smi reports right now."""
+    import subprocess
+    import torch
+    info = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(r.stdout).values()))
+        info["rocm_smi_clocks_idle"] = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception as e:                      # noqa: BLE001 - informational only
+        info["rocm_smi_clocks_idle"] = f"unavailable ({type(e).__name__})"
+    return info
+
+
+def measured_peaks():
+    """Register-only MFMA rates of the instruction kinds the kernels use, and the shader clock the
+    FP8 loop ran at (from the shader-clock / wall-clock counter ratio)."""
+    import quantized_video_diffusion_amd as Q
+    from quantized_video_diffusion_amd import _lib
+    out = {}
+    for name, kind in (("fp8_32x32x64", _lib.QVD_PROBE_FP8), ("fp4_32x32x64", _lib.QVD_PROBE_FP4),
+                       ("int8_16x16x64", _lib.QVD_PROBE_INT8), ("f16_16x16x32", _lib.QVD_PROBE_F16),
+                       ("int8_32x32x32", _lib.QVD_PROBE_INT8_32), ("f16_32x32x16", _lib.QVD_PROBE_F16_32),
+                       ("fp8_16x16x128", _lib.QVD_PROBE_FP8_16)):
+        r = Q.mfma_probe(kind)
+        out[name] = {"TFLOP/s": round(r["tflops"], 1),
+                     "clock_MHz": None if r["clock_mhz"] is None else round(r["clock_mhz"], 1)}
+    return out
+
+
+def attention_only_480p(seed, reps=10):
+    """The attention-only 480p workload: 21 heads, 33,784 tokens, 53 of 264 key tiles per row; Q, K
+    quantized to INT8 on the GPU, V^T prepared, then sparse_attn timed alone (median of reps)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import quantized_video_diffusion_amd as Q
+    w = W.WORKLOADS["attn_480p"]
+    L, H = w.L, w.n_heads
+    qb, kb, vb = W.qkv_heads(L, H, seed=seed, tag=w.tag)
+    idx, cnt = W.block_mask(w, seed=seed)
+    q8, qs = Q.quant_int8_qk(Q.from_bits(qb.reshape(L, -1)), H)
+    k8, ks = Q.quant_int8_qk(Q.from_bits(kb.reshape(L, -1)), H)
+    vt = Q.vt_unify(Q.vt_from_bf16(Q.from_bits(vb)))
+    kv_idx, kv_cnt = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    del qb, kb, vb
+    for _ in range(2):
+        Q.sparse_attn_vt(q8, qs, k8, ks, vt, kv_idx, kv_cnt)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        Q.sparse_attn_vt(q8, qs, k8, ks, vt, kv_idx, kv_cnt)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    t = sorted(ms)[len(ms) // 2]
+    pairs = kept_scores(idx, cnt, L)
+    ops = 4.0 * 128 * pairs
+    peak = 2.0 / (1.0 / PEAK_TFLOPS["int8"] + 1.0 / PEAK_TFLOPS["fp16"])
+    tf = ops / (t * 1e-3) / 1e12
+    return {"workload": "attn_480p", "tokens": L, "heads": H, "kept_key_tiles_per_row": w.kmax,
+            "key_tiles": w.n_tiles, "ms": round(t, 4), "TFLOP/s": round(tf, 1),
+            "frac_of_int8_fp16_peak": round(tf / peak, 4), "pct_of_5PF": round(100 * tf / PEAK_TFLOPS["fp8"], 2)}
+
+
+def block_trim_L4096(seed, reps=10):
+    """One block at Trim width with 4,096 tokens and dense attention (all 32 key tiles), dynamic FP8
+    scales, timed alone (median of reps, the input restored before each)."""
+    import torch
+    import workloads as W
+    import quantized_video_diffusion_amd as Q
+    w = W.WORKLOADS["trim_block_L4096"]
+    L, d, F = w.L, w.d, w.mlp
+    x0 = Q.from_bits(W.activations(w, seed))
+    wb = {k: Q.from_bits(v) for k, v in W.block_weights(w, seed).items()}
+    bw = Q.quantize_block_weights(wb, d, w.n_heads, F)
+    mod = Q.adaln_project(999.0, Q.from_bits(W.adaln_basis(w, seed), torch.float16),
+                          Q.from_bits(W.adaln_proj(w, seed), torch.float16))
+    idx, cnt = W.block_mask(w, seed)
+    kv_idx, kv_cnt = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    ws = torch.empty(Q.block_ws_bytes(bw, L), dtype=torch.uint8, device="cuda")
+    x = torch.empty_like(x0)
+    ms = []
+    for r in range(reps + 2):
+        x.copy_(x0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        Q.dit_block_forward(bw, mod, x, kv_idx, kv_cnt, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ms.append(e0.elapsed_time(e1))
+    t = sorted(ms)[len(ms) // 2]
+    ops = 2.0 * L * (3 * d * d + d * d + d * F + F * d) + 4.0 * 128 * kept_scores(idx, cnt, L)
+    tf = ops / (t * 1e-3) / 1e12
+    return {"workload": "trim_block_L4096", "tokens": L, "attention": "dense", "ms": round(t, 4),
+            "TFLOP/s": round(tf, 1), "pct_of_5PF": round(100 * tf / PEAK_TFLOPS["fp8"], 2)}
 
 
 def main():
@@ -393,8 +555,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-768p", action="store_true", help="skip the 768p MXFP4 block report")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the sampler loop, the MFMA probes and the attention-only / L=4096 block records")
     ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="time the steps without the per-kernel HIP events")
+                    help="skip the instrumented pass (per-kernel HIP events, breakdown and roofline)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device-to-device copy (calibrates the HBM byte counters)")
     ap.add_argument("--parse-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -419,6 +583,9 @@ def main():
     import workloads as W
     import quantized_video_diffusion_amd as Q
 
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     torch.cuda.set_device(0)
     w = W.WORKLOADS["trim_stack42_480p"]
     L, d = w.L, w.d
@@ -430,11 +597,9 @@ def main():
     ws = torch.empty(Q.block_ws_bytes(blocks[0], L), dtype=torch.uint8, device="cuda")
     x = torch.empty_like(x0)
     setup_s = time.perf_counter() - t_setup
-    print(f"[bench] setup {setup_s:.1f} s: {nb} blocks, L={L}, ws {ws.numel() / 2**30:.2f} GiB",
-          file=sys.stderr, flush=True)
+    log(f"setup {setup_s:.1f} s: {nb} blocks, L={L}, ws {ws.numel() / 2**30:.2f} GiB")
 
     ts = W.SAMPLER_TIMESTEPS
-    step_ms = []
     if args.copy_probe:
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -442,30 +607,38 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def step(k):
-        x.copy_(x0)                                   # the same input enters every step
+    def stack(k):
         mods = Q.adaln_project(float(ts[k % len(ts)]), basis, proj_all)
         for b in range(nb):
             Q.dit_block_forward(blocks[b], mods[b], x, masks[b][0], masks[b][1], ws)
 
+    def step(k):
+        x.copy_(x0)                                   # the same input enters every step
+        stack(k)
+
+    def timed_steps():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record()
+        for k in range(args.steps):
+            step(k)
+            ev[k + 1].record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+
+    # ---- the headline: warm-up, then the timed steps with no per-kernel instrumentation -------------
     for k in range(args.warmup):
         step(k)
-    torch.cuda.synchronize()
+    elapsed, step_ms = timed_steps()
+    log(f"timed {args.steps} steps: {elapsed * 1e3 / args.steps:.2f} ms/step")
+
+    # ---- the same steps again with the library's per-kernel HIP events (breakdown, roofline) --------
+    kernels, elapsed_inst = {}, None
     if not args.no_kernel_timing:
         Q.timing_enable(True)
-        Q.timing_report()                             # drop the warm-up records
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record()
-    for k in range(args.steps):
-        step(k)
-        ev[k + 1].record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
-    kernels = {}
-    if not args.no_kernel_timing:
+        Q.timing_report()                             # drop earlier records
+        elapsed_inst, _ = timed_steps()
         kernels = Q.timing_report()
         Q.timing_enable(False)
 
@@ -487,7 +660,6 @@ def main():
     breakdown = {}
     if kernels:
         steps = args.steps
-        shapes = gemm_shapes(w, L)
         work = {}
         for key, v in kernels.items():
             avg_ms = v["total_ms"] / v["count"]
@@ -533,6 +705,7 @@ def main():
         "pct_of_fp8_int8_peak": round(100 * tflops / PEAK_TFLOPS["fp8"], 2),
         "pct_of_block_roofline": round(100 * t_bound_ms / ms_per_block, 2),
         "step_ms_by_timestep": per_ts,
+        "ms_per_step_with_kernel_events": None if elapsed_inst is None else round(elapsed_inst * 1e3 / args.steps, 3),
         "roofline": roofline,
         "kernels": breakdown,
         "setup_s": round(setup_s, 1),
@@ -540,13 +713,52 @@ def main():
     # the sparse-tile selector at this token count (all heads): what choosing the mask from the block's
     # own Q/K would add per block; the timed steps above use the seeded masks
     result["selector_ms_per_block"] = time_selector(L, w.n_heads, w.kmax, args.seed)
-    if not args.no_768p:
-        print("[bench] 768p MXFP4 block: calibration and timing ...", file=sys.stderr, flush=True)
+
+    if not args.no_extras:
+        # ---- the eight-step sampler loop, the state carried from step to step ------------------------
+        smp = Q.Sampler(L_video=w.L_video)
+
+        def sampler_loop():
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(ts) + 1)]
+            smp.start(x0, x_in=x)                     # x0 stands for the initial noise
+            ev[0].record()
+            for i in range(len(ts)):
+                stack(i)
+                smp.step(i, x)
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            return [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ts))]
+
+        sampler_loop()                                # warm
+        loop_ms = sampler_loop()
+        fin = smp.x_state
+        result["sampler_loop"] = {
+            "steps": len(ts), "timesteps": list(ts), "shift_video": smp.shift_video, "shift_audio": smp.shift_audio,
+            "video_tokens": w.L_video, "ms_total": round(sum(loop_ms), 2),
+            "ms_per_step": [round(m, 3) for m in loop_ms],
+            "final_latent_rms": float(torch.sqrt(torch.mean(fin.double() ** 2)).item()),
+            "note": "8 steps of the 42-block stack with the sampler update between them (state carried); "
+                    "the headline steps above re-feed the same input each step"}
+        log(f"sampler loop: {sum(loop_ms):.1f} ms for {len(ts)} steps")
+        del smp, fin
+        result["system"] = system_info()
+        result["mfma_measured_peak"] = measured_peaks()
+        result["mfma_nominal_peak"] = {"fp8": PEAK_TFLOPS["fp8"], "int8": PEAK_TFLOPS["int8"],
+                                       "fp16": PEAK_TFLOPS["fp16"], "fp4": 10100.0}
         del blocks, ws
         torch.cuda.empty_cache()
+        log("attention only (480p) and the L=4096 block ...")
+        result["records"] = {"attention_only_480p": attention_only_480p(args.seed),
+                             "block_trim_L4096": block_trim_L4096(args.seed)}
+        torch.cuda.empty_cache()
+    if not args.no_768p:
+        log("768p MXFP4 block: calibration and timing ...")
+        if args.no_extras:
+            del blocks, ws
+            torch.cuda.empty_cache()
         result["block_768p_mxfp4"] = run_768p(args.seed)
     if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on a bounded sample ...", file=sys.stderr, flush=True)
+        log("timing the oracle on a bounded sample (median of 3) ...")
         result["cpu_baseline"] = cpu_baseline(w, args.seed, host_block0)
     else:
         result["cpu_baseline"] = None

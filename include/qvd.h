@@ -140,6 +140,11 @@ int adaln_modulate_noalloc(const uint16_t* x, int32_t L, int32_t d, const float*
  * consecutive channels X = 2^(floor(log2 max|y|) - 2) (all-zero block: X = 1), codes E2M1(y / X),
  * round to nearest even, saturating at 6.  packed: uint8 [L][d/2] (channel 2j in the low nibble of
  * byte j); e8m0: uint8 [L][d/32].  One pass; no workspace. */
+/* The values the modulate quantizers encode, for calibration: y fp32 [L][d] =
+ * fp32(LN(x)(1 + scale) + shift) with the statistics and the affine map in float64, rounded once
+ * (the same y as adaln_modulate).  No workspace. */
+int adaln_layernorm_modulate_f32(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                                 float eps, float* y, void* stream);
 int adaln_modulate_mxfp4(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
                          float eps, uint8_t* packed, uint8_t* e8m0, void* stream);
 
@@ -322,7 +327,8 @@ int qvd_gemm_mxfp4_w4a4(const uint8_t* a_packed, const uint8_t* a_e8m0, const ui
  * Weights are [N][K] (K contiguous).  weight_format QVD_W_FP8: E4M3 codes with per-tensor fp32
  * scales s_*.  QVD_W_MXFP4: packed E2M1 (element 2j in the low nibble of byte j) with E8M0
  * scales e8m0_* [N][K/32]; s_* are ignored.  act_scale: NULL (dynamic scales) or fp32 [4] static
- * scales of the QKV, out, up and down GEMM inputs (required for MXFP4).  QVD_W_MXFP4_A4 (W4A4):
+ * scales of the QKV, out, up and down GEMM inputs (with MXFP4 weights too; NULL there gives dynamic
+ * per-tensor E4M3 activations, the calibration configuration).  QVD_W_MXFP4_A4 (W4A4):
  * the weights as for QVD_W_MXFP4 and every GEMM input MXFP4 too -- h1 and h2 from
  * adaln_modulate_mxfp4, O from qvd_sparse_attn_vt_mxfp4, g from the QVD_EPI_GELU_MXFP4 epilogue --
  * each with a dynamic E8M0 scale per token row and 32 channels; act_scale is ignored.  Biases may
@@ -403,6 +409,9 @@ int qvd_quant_mxfp4(const uint16_t* w, int32_t N, int32_t K, uint8_t* packed, ui
                     void* stream);
 int qvd_amax_update(const float* x, int64_t n, float* amax, void* stream);
 int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* count, void* stream);
+/* The same two reductions over n bf16 values (activations the block holds in bf16: O and GELU(g)). */
+int qvd_amax_update_bf16(const uint16_t* x, int64_t n, float* amax, void* stream);
+int qvd_clip_count_bf16(const uint16_t* x, int64_t n, const float* scale, uint64_t* count, void* stream);
 int qvd_calibrated_scale(const float* amax, float* scale, int32_t n, void* stream);
 
 /* ------------------------------------------------------------------------------------------
@@ -442,6 +451,26 @@ int qvd_sampler_start(const qvd_sampler_config* c, const uint16_t* eps, int32_t 
  * works in place).  After the last step x_state holds the final latent. */
 int qvd_sampler_step(const qvd_sampler_config* c, int32_t step, const uint16_t* v, float* x_state, float* x0_hat,
                      uint16_t* x_in, int32_t L, int32_t d, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Matrix-core rate probe (measurement support, not part of the method): `workgroups` workgroups of
+ * four waves each run `iters` iterations of four independent MFMAs of one kind, alternating two sets
+ * of random operands, entirely in registers; out (device fp32 [workgroups * 256]) receives one sum per
+ * thread, and clocks (NULL, or device uint64 [2 * workgroups]) each workgroup's elapsed shader-clock
+ * count and constant-rate ("wall") count over its loop, whose ratio times the wall-clock rate
+ * (hipDeviceAttributeWallClockRate) is the clock the loop ran at.  The caller times the launch;
+ * qvd_mfma_probe_flops gives its flop count (ops for INT8).
+ * Kinds: the FP8 GEMMs' 32x32x64 E4M3, the W4A4 GEMMs' 32x32x64 E2M1, INT8 16x16x64, fp16 16x16x32,
+ * INT8 32x32x32, fp16 32x32x16 and E4M3 16x16x128. */
+enum qvd_probe_kind {
+    QVD_PROBE_FP8 = 0, QVD_PROBE_FP4 = 1, QVD_PROBE_INT8 = 2, QVD_PROBE_F16 = 3,
+    QVD_PROBE_INT8_32 = 4, QVD_PROBE_F16_32 = 5, QVD_PROBE_FP8_16 = 6
+};
+int qvd_mfma_probe(int32_t kind, int32_t iters, int32_t workgroups, float* out, uint64_t* clocks,
+                   void* stream);
+double qvd_mfma_probe_flops(int32_t kind, int32_t iters, int32_t workgroups);
+/* The current device's constant wall-clock rate in kHz (QVD_EHIP on a runtime error). */
+int32_t qvd_wall_clock_khz(void);
 
 /* ------------------------------------------------------------------------------------------
  * Per-kernel timing (off by default).  While enabled, each kernel launch the library makes is

@@ -17,6 +17,8 @@ QVD_OK, QVD_EINVAL, QVD_ESHAPE, QVD_EALIGN, QVD_EWORKSPACE, QVD_EUNSUPPORTED, QV
 (QVD_EPI_F32, QVD_EPI_BF16, QVD_EPI_RESID_GATE, QVD_EPI_GELU, QVD_EPI_QKV, QVD_EPI_GELU_E4M3,
  QVD_EPI_GELU_MXFP4) = range(7)
 QVD_W_FP8, QVD_W_MXFP4, QVD_W_MXFP4_A4 = 0, 1, 2
+QVD_PROBE_FP8, QVD_PROBE_FP4, QVD_PROBE_INT8, QVD_PROBE_F16 = 0, 1, 2, 3
+QVD_PROBE_INT8_32, QVD_PROBE_F16_32, QVD_PROBE_FP8_16 = 4, 5, 6
 (QVD_STAGE_MODULATE1, QVD_STAGE_QKV, QVD_STAGE_VT, QVD_STAGE_ATTN, QVD_STAGE_OQUANT, QVD_STAGE_OPROJ,
  QVD_STAGE_MODULATE2, QVD_STAGE_UP, QVD_STAGE_GQUANT, QVD_STAGE_ALL) = range(1, 11)
 WS_SLOTS = ("h", "q8", "k8", "vt", "vt_tile_exp", "vt_head_exp", "o", "g", "g8", "h_e8m0", "g_e8m0",
@@ -96,8 +98,14 @@ SIGNATURES = {
     "qvd_quant_mxfp4": (C.c_int, [_p, _i32, _i32, _p, _p, _p]),
     "qvd_amax_update": (C.c_int, [_p, _i64, _p, _p]),
     "qvd_clip_count": (C.c_int, [_p, _i64, _p, _p, _p]),
+    "qvd_amax_update_bf16": (C.c_int, [_p, _i64, _p, _p]),
+    "qvd_clip_count_bf16": (C.c_int, [_p, _i64, _p, _p, _p]),
+    "adaln_layernorm_modulate_f32": (C.c_int, [_p, _i32, _i32, _p, _i32, _f32, _p, _p]),
     "qvd_calibrated_scale": (C.c_int, [_p, _p, _i32, _p]),
     "qvd_sampler_sigmas": (C.c_int, [C.POINTER(SamplerConfig), _i32, C.POINTER(C.c_double)]),
+    "qvd_mfma_probe": (C.c_int, [_i32, _i32, _i32, _p, _p, _p]),
+    "qvd_mfma_probe_flops": (C.c_double, [_i32, _i32, _i32]),
+    "qvd_wall_clock_khz": (_i32, []),
     "qvd_sampler_start": (C.c_int, [C.POINTER(SamplerConfig), _p, _i32, _i32, _p, _p, _p]),
     "qvd_sampler_step": (C.c_int, [C.POINTER(SamplerConfig), _i32, _p, _p, _p, _p, _i32, _i32, _p]),
     "qvd_timing_enable": (C.c_int, [C.c_int]),

@@ -300,6 +300,57 @@ __global__ void __launch_bounds__(256) k_ln_mx(const uint16_t* __restrict__ x, i
     }
 }
 
+// The modulated LayerNorm values themselves, y = modulate_one (the float64 modulation rounded once to
+// fp32, the values every quantizer of this file encodes), for calibration: y fp32 [L][d].
+template <int NW>
+__global__ void __launch_bounds__(256) k_ln_f32(const uint16_t* __restrict__ x, int L, int d,
+                                                const float* __restrict__ mod, int half, float eps,
+                                                float* __restrict__ y) {
+    __shared__ float4 tab[64 * NW];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int nw = d >> 7;
+    load_mod_table(tab, mod, half, d, false, 1.0f);
+    Row<NW> R;
+    for (int row = blockIdx.x * 4 + wv; row < L; row += gridDim.x * 4) {
+        const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)row * d);
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            if (j < nw) R.x[j] = __builtin_nontemporal_load(xr + lane + 64 * j);
+        double mu, rstd;
+        row_stats<NW>(R, nw, d, (double)eps, mu, rstd);
+        float2* yr = reinterpret_cast<float2*>(y + (int64_t)row * d);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if (j < nw) {
+                const float4 c = tab[lane + 64 * j];
+                yr[lane + 64 * j] = make_float2(modulate_one(bf16lo(R.x[j]), mu, rstd, c.x, c.y),
+                                                modulate_one(bf16hi(R.x[j]), mu, rstd, c.z, c.w));
+            }
+        }
+    }
+}
+
+template <int NW>
+static int launch_ln_f32_nw(const uint16_t* x, int L, int d, const float* mod, int half, float eps, float* y,
+                            hipStream_t st) {
+    int g = (L + 3) / 4;
+    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+    hipLaunchKernelGGL(k_ln_f32<NW>, dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, y);
+    return launch_status("adaln_layernorm_modulate_f32");
+}
+
+int launch_ln_f32(const uint16_t* x, int L, int d, const float* mod, int half, float eps, float* y,
+                  hipStream_t st) {
+    if (L == 0) return QVD_OK;
+    switch (d >> 7) {
+        case 2: return launch_ln_f32_nw<2>(x, L, d, mod, half, eps, y, st);
+        case 21: return launch_ln_f32_nw<21>(x, L, d, mod, half, eps, y, st);
+        default:
+            if ((d >> 7) <= 8) return launch_ln_f32_nw<8>(x, L, d, mod, half, eps, y, st);
+            return launch_ln_f32_nw<32>(x, L, d, mod, half, eps, y, st);
+    }
+}
+
 template <int NW>
 static int launch_modulate_mx_nw(const uint16_t* x, int L, int d, const float* mod, int half, float eps,
                                  uint8_t* packed, uint8_t* e8m0, hipStream_t st) {
@@ -500,6 +551,24 @@ int adaln_modulate_noalloc(const uint16_t* x, int32_t L, int32_t d, const float*
     if (s) return s;
     TimingOff no_events;
     return launch_modulate(x, L, d, mod, half, eps, act_scale_in, q, act_scale_out, ws, (hipStream_t)stream);
+}
+
+int adaln_layernorm_modulate_f32(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                                 float eps, float* y, void* stream) {
+    QVD_REQUIRE(L >= 0, QVD_ESHAPE, "adaln_layernorm_modulate_f32: L = %d", L);
+    QVD_REQUIRE(d >= 128 && d % 128 == 0 && d <= 4096, QVD_ESHAPE,
+                "adaln_layernorm_modulate_f32: d = %d (multiple of 128, at most 4096)", d);
+    QVD_REQUIRE(half == 0 || half == 1, QVD_EINVAL, "adaln_layernorm_modulate_f32: half = %d (0 or 1)", half);
+    QVD_REQUIRE(eps >= 0.0f, QVD_EINVAL, "adaln_layernorm_modulate_f32: eps < 0");
+    QVD_PTR(mod);
+    QVD_ALIGN(mod);
+    if (L == 0) return QVD_OK;
+    QVD_PTR(x);
+    QVD_PTR(y);
+    QVD_ALIGN(x);
+    QVD_ALIGN(y);
+    QVD_DEVICE_OK();
+    return launch_ln_f32(x, L, d, mod, half, eps, y, (hipStream_t)stream);
 }
 
 int adaln_modulate_mxfp4(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,

@@ -132,9 +132,6 @@ int validate(const qvd_block_params* p, int L) {
         QVD_PTR(p->e8m0_o);
         QVD_PTR(p->e8m0_up);
         QVD_PTR(p->e8m0_down);
-        if (p->weight_format == QVD_W_MXFP4)
-            QVD_REQUIRE(p->act_scale != nullptr, QVD_EINVAL,
-                        "block: MXFP4 weights need static activation scales (act_scale)");
     }
     const float* b[4] = {p->b_qkv, p->b_o, p->b_up, p->b_down};
     for (int i = 0; i < 4; ++i)

@@ -202,13 +202,17 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------------------------
 // calibration reductions
 
-__global__ void __launch_bounds__(QBLOCK) k_amax_update(const float* __restrict__ x, int64_t n,
+QVD_DEV float load_f32(const float* x, int64_t i) { return x[i]; }
+QVD_DEV float load_f32(const uint16_t* x, int64_t i) { return bf16_to_f32(x[i]); }
+
+template <class T>
+__global__ void __launch_bounds__(QBLOCK) k_amax_update(const T* __restrict__ x, int64_t n,
                                                         float* __restrict__ amax) {
     __shared__ float red[QBLOCK / 64];
     float m = 0.0f;
     for (int64_t i = (int64_t)blockIdx.x * QBLOCK + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * QBLOCK)
-        m = fmaxf(m, fabsf(x[i]));
+        m = fmaxf(m, fabsf(load_f32(x, i)));
     m = block_max_nonneg<QBLOCK / 64>(m, red);
     if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
 }
@@ -229,7 +233,8 @@ __global__ void __launch_bounds__(256) k_calibrated_scale(const float* __restric
     scale[i] = s;
 }
 
-__global__ void __launch_bounds__(QBLOCK) k_clip_count(const float* __restrict__ x, int64_t n,
+template <class T>
+__global__ void __launch_bounds__(QBLOCK) k_clip_count(const T* __restrict__ x, int64_t n,
                                                        const float* __restrict__ scale,
                                                        unsigned long long* __restrict__ count) {
     __shared__ unsigned long long red[QBLOCK / 64];
@@ -237,7 +242,7 @@ __global__ void __launch_bounds__(QBLOCK) k_clip_count(const float* __restrict__
     unsigned long long c = 0;
     for (int64_t i = (int64_t)blockIdx.x * QBLOCK + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * QBLOCK)
-        c += ((double)fabsf(x[i]) > thr) ? 1ull : 0ull;
+        c += ((double)fabsf(load_f32(x, i)) > thr) ? 1ull : 0ull;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
@@ -337,27 +342,53 @@ int qvd_calibrated_scale(const float* amax, float* scale, int32_t n, void* strea
     return launch_status("qvd_calibrated_scale");
 }
 
-int qvd_amax_update(const float* x, int64_t n, float* amax, void* stream) {
-    QVD_REQUIRE(n >= 0, QVD_ESHAPE, "qvd_amax_update: n < 0");
+}  // extern "C"
+
+namespace {
+
+template <class T>
+int amax_update(const char* fn, const T* x, int64_t n, float* amax, void* stream) {
+    QVD_REQUIRE(n >= 0, QVD_ESHAPE, "%s: n < 0", fn);
     if (n == 0) return QVD_OK;
     QVD_PTR(x);
     QVD_PTR(amax);
     QVD_DEVICE_OK();
-    hipLaunchKernelGGL(k_amax_update, dim3(grid_for(n / 8, 2048)), dim3(QBLOCK), 0,
+    hipLaunchKernelGGL(k_amax_update<T>, dim3(grid_for(n / 8, 2048)), dim3(QBLOCK), 0,
                        (hipStream_t)stream, x, n, amax);
-    return launch_status("qvd_amax_update");
+    return launch_status(fn);
 }
 
-int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* count, void* stream) {
-    QVD_REQUIRE(n >= 0, QVD_ESHAPE, "qvd_clip_count: n < 0");
+template <class T>
+int clip_count(const char* fn, const T* x, int64_t n, const float* scale, uint64_t* count, void* stream) {
+    QVD_REQUIRE(n >= 0, QVD_ESHAPE, "%s: n < 0", fn);
     if (n == 0) return QVD_OK;
     QVD_PTR(x);
     QVD_PTR(scale);
     QVD_PTR(count);
     QVD_DEVICE_OK();
-    hipLaunchKernelGGL(k_clip_count, dim3(grid_for(n / 8, 2048)), dim3(QBLOCK), 0,
+    hipLaunchKernelGGL(k_clip_count<T>, dim3(grid_for(n / 8, 2048)), dim3(QBLOCK), 0,
                        (hipStream_t)stream, x, n, scale, (unsigned long long*)count);
-    return launch_status("qvd_clip_count");
+    return launch_status(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qvd_amax_update(const float* x, int64_t n, float* amax, void* stream) {
+    return amax_update("qvd_amax_update", x, n, amax, stream);
+}
+
+int qvd_amax_update_bf16(const uint16_t* x, int64_t n, float* amax, void* stream) {
+    return amax_update("qvd_amax_update_bf16", x, n, amax, stream);
+}
+
+int qvd_clip_count(const float* x, int64_t n, const float* scale, uint64_t* count, void* stream) {
+    return clip_count("qvd_clip_count", x, n, scale, count, stream);
+}
+
+int qvd_clip_count_bf16(const uint16_t* x, int64_t n, const float* scale, uint64_t* count, void* stream) {
+    return clip_count("qvd_clip_count_bf16", x, n, scale, count, stream);
 }
 
 }  // extern "C"

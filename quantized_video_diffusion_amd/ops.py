@@ -353,13 +353,33 @@ def quant_mxfp4(w: torch.Tensor):
 
 
 def amax_update(x: torch.Tensor, amax: torch.Tensor):
+    """amax (device fp32 [1]) <- max(amax, max|x|) for fp32 or bf16 x."""
+    if x.dtype == torch.bfloat16:
+        _check(x, torch.bfloat16, "x")
+        call("qvd_amax_update_bf16", _ptr(x), x.numel(), _ptr(amax), _stream())
+        return
     _check(x, torch.float32, "x")
     call("qvd_amax_update", _ptr(x), x.numel(), _ptr(amax), _stream())
 
 
 def clip_count(x: torch.Tensor, scale: torch.Tensor, count: torch.Tensor):
+    """count (device int64 [1]) += #{|x| > 448 scale} for fp32 or bf16 x."""
+    if x.dtype == torch.bfloat16:
+        _check(x, torch.bfloat16, "x")
+        call("qvd_clip_count_bf16", _ptr(x), x.numel(), _ptr(scale), _ptr(count), _stream())
+        return
     _check(x, torch.float32, "x")
     call("qvd_clip_count", _ptr(x), x.numel(), _ptr(scale), _ptr(count), _stream())
+
+
+def layernorm_modulate_f32(x: torch.Tensor, mod: torch.Tensor, half: int, eps: float = 1e-6) -> torch.Tensor:
+    """bf16 [L][d] -> fp32 [L][d]: the modulated LayerNorm values the modulate quantizers encode."""
+    _check(x, torch.bfloat16, "x")
+    _check(mod, torch.float32, "mod")
+    L, d = x.shape
+    y = _out((L, d), torch.float32, x.device)
+    call("adaln_layernorm_modulate_f32", _ptr(x), L, d, _ptr(mod), half, float(eps), _ptr(y), _stream())
+    return y
 
 
 # ----------------------------------------------------------------------------------------------
@@ -581,3 +601,26 @@ class Sampler:
              L, d, _stream())
         return x_in
 
+
+def mfma_probe(kind: int, iters: int = 4000, workgroups: int = 1024, reps: int = 3) -> dict:
+    """Measured matrix-core rate of one MFMA kind (_lib.QVD_PROBE_*): TFLOP/s (TOP/s for INT8), the
+    median over `reps` timed launches of qvd_mfma_probe after one warm-up, and the shader clock the
+    loop ran at (MHz, median over workgroups of the last launch)."""
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * workgroups, dtype=torch.int64, device="cuda")
+    flops = _lib.lib().qvd_mfma_probe_flops(kind, iters, workgroups)
+    call("qvd_mfma_probe", kind, iters, workgroups, _ptr(out), None, _stream())
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call("qvd_mfma_probe", kind, iters, workgroups, _ptr(out), _ptr(clocks), _stream())
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ck = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+    wall_khz = int(_lib.lib().qvd_wall_clock_khz())
+    mhz = None
+    if wall_khz > 0:
+        mhz = float(np.median(ck[:, 0] / np.maximum(ck[:, 1], 1.0)) * wall_khz / 1e3)
+    return {"tflops": flops / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e12, "clock_mhz": mhz}

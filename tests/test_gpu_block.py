@@ -127,6 +127,15 @@ def test_block_mxfp4_weights_static_scales():
     _check(x, got, want, "toy mxfp4")
 
 
+def test_block_mxfp4_weights_dynamic_scales():
+    """MXFP4 weights with dynamic per-tensor E4M3 activations (act_scale NULL: the configuration the
+    static scales are calibrated from)."""
+    w = W.WORKLOADS["toy_d256_L256"]
+    mod = W.random_mod(w.d, seed=16, tag=w.tag, gate=1.0)
+    x, got, want = _run_both(w, 391, seed=14, mod=mod, fmt="mxfp4", sparse=True)
+    _check(x, got, want, "toy mxfp4 dynamic")
+
+
 def test_block_w4a4_dynamic_block_scales():
     """W4A4: every GEMM input MXFP4 (h1, O, h2, g), MXFP4 weights, no per-tensor activation scale."""
     w = W.WORKLOADS["toy_d256_L256"]

@@ -196,3 +196,28 @@ def test_calibrated_scale_vs_oracle():
     raised = np.array([float(np.float32(v / np.float32(448.0))) * 448.0 < float(v) for v in a])
     assert raised.sum() > 100 and (~raised).sum() > 100
     assert ((got.astype(np.float64) * 448.0) >= a.astype(np.float64)).all()
+
+
+@pytest.mark.parametrize("wname,L,half", [("toy_d256_L256", 300, 0), ("trim_block_L4096", 257, 1)])
+def test_layernorm_modulate_f32_bit_exact(wname, L, half):
+    """The fp32 modulated LayerNorm values equal the oracle's (float64 statistics and affine map,
+    rounded once) bit for bit."""
+    w = W.WORKLOADS[wname]
+    x = W.activations(w, 5, L=L)
+    mod = W.random_mod(w.d, seed=6, tag=w.tag)
+    got = host(Q.layernorm_modulate_f32(bf16_dev(x), f32_dev(mod), half))
+    want = OA.layernorm_modulate(x, mod, half, 1e-6)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_bf16_amax_and_clip_counts():
+    """qvd_amax_update_bf16 / qvd_clip_count_bf16 against the same reductions on the host."""
+    x = W.normal_bf16((1237, 96), seed=8, scale=3.0)
+    xv = OC.bf16_to_f64(x)
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    Q.amax_update(bf16_dev(x), amax)
+    assert float(host(amax)[0]) == float(np.abs(xv).max())
+    for s in (np.float32(0.01), np.float32(0.02), np.float32(1.0)):
+        cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        Q.clip_count(bf16_dev(x), f32_dev([s]), cnt)
+        assert int(host(cnt)[0]) == int(np.count_nonzero(np.abs(xv) > float(s) * 448.0))

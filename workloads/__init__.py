@@ -31,8 +31,9 @@ SAMPLER_TIMESTEPS = (999, 874, 749, 624, 500, 375, 250, 125)
 N_BLOCKS_TRIM = 42
 
 # token counts: video latent frames x rows x cols, then the audio tokens
-TOKENS_480P = 21 * 30 * 52 + 1024      # 33,784
-TOKENS_768P = 21 * 48 * 84 + 1024      # 85,696
+AUDIO_TOKENS = 1024
+TOKENS_480P = 21 * 30 * 52 + AUDIO_TOKENS      # 33,784
+TOKENS_768P = 21 * 48 * 84 + AUDIO_TOKENS      # 85,696
 
 
 @dataclass(frozen=True)
@@ -55,6 +56,12 @@ class Workload:
     @property
     def n_tiles(self) -> int:
         return (self.L + TILE - 1) // TILE
+
+    @property
+    def L_video(self) -> int:
+        """Video tokens (they come first); the last AUDIO_TOKENS are audio at the 480p and 768p
+        token counts, and every token is video in the other workloads."""
+        return self.L - AUDIO_TOKENS if self.L in (TOKENS_480P, TOKENS_768P) else self.L
 
     @property
     def kmax(self) -> int:
