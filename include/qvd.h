@@ -65,6 +65,13 @@ const char* qvd_last_error(void);
  * Returns QVD_OK, QVD_EUNSUPPORTED or QVD_EHIP. */
 int qvd_init(void);
 
+/* Failure injection for the error paths of callers (testing support, not part of the method): the
+ * launch `after` launches from now (0: the next one) on the calling thread reports QVD_EHIP, as when
+ * the runtime rejects a launch -- the kernel itself still runs -- and the entry point that made it
+ * returns QVD_EHIP with "injected failure" in qvd_last_error().  after = -1 cancels a pending
+ * injection; below -1 is QVD_EINVAL.  Only the calling thread's launches count. */
+int qvd_inject_launch_failure(int32_t after);
+
 /* ------------------------------------------------------------------------------------------
  * Per-tensor FP8 (E4M3) quantization -- "运行速度如何" note: one scale per tensor.
  *   x         : n bf16 values (any shape, contiguous).

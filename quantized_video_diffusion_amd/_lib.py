@@ -63,6 +63,7 @@ SIGNATURES = {
     "qvd_abi_version": (C.c_int, []),
     "qvd_last_error": (C.c_char_p, []),
     "qvd_init": (C.c_int, []),
+    "qvd_inject_launch_failure": (C.c_int, [C.c_int32]),
     "qvd_quant_ws_bytes": (_sz, [_i64]),
     "quant_fp8_per_tensor": (C.c_int, [_p, _i64, _p, _p, _p, _p, _sz, _p]),
     "quant_int8_qk": (C.c_int, [_p, _i32, _i32, _i32, _i32, _i64, _p, _p, _p]),

@@ -48,9 +48,14 @@ int check_device() {
     return QVD_OK;
 }
 
+// Launches left before an injected failure on this thread (-1: none pending).
+static thread_local int64_t t_fail_after = -1;
+
 int launch_status(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QVD_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    if (t_fail_after >= 0 && t_fail_after-- == 0)
+        return fail(QVD_EHIP, "%s: launch failed: injected failure", what);
     return QVD_OK;
 }
 
@@ -63,5 +68,11 @@ int qvd_abi_version(void) { return QVD_ABI_VERSION; }
 const char* qvd_last_error(void) { return qvd::g_err; }
 
 int qvd_init(void) { return qvd::check_device(); }
+
+int qvd_inject_launch_failure(int32_t after) {
+    if (after < -1) return qvd::fail(QVD_EINVAL, "qvd_inject_launch_failure: after = %d (-1 or more)", after);
+    qvd::t_fail_after = after;
+    return QVD_OK;
+}
 
 }  // extern "C"

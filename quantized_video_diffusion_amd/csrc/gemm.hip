@@ -7,15 +7,16 @@
 // per-channel FP8 scaling.  The 4-bit weights stand in for the pages' NVFP4 layers (news.farwalk.ai
 // FastH3 story, post 6/8) in the OCP MX form gfx950 executes natively.
 //
-// Design (gfx950): C^T tiles are computed as W . A^T with v_mfma_f32_16x16x128_f8f6f4, so each lane
-// ends up holding four consecutive output columns of one token row -- the shape every epilogue
+// Design (gfx950): C^T tiles are computed as W . A^T with v_mfma_scale_f32_32x32x64_f8f6f4, so each
+// lane ends up holding four consecutive output columns of one token row -- the shape every epilogue
 // wants (8-byte bf16 stores, per-column bias/gate vectors, per-head INT8 quantization).
-//   workgroup tile 256 (tokens) x 256 (outputs) x 128 (K), four waves of 128 x 128;
-//   both operands K-contiguous, moved HBM/L2 -> LDS by global_load_lds_dwordx4 into a double buffer
-//   (the next K-step lands while this one is multiplied), 16-byte chunks XOR-swizzled by row so the
-//   16-row MFMA fragment reads are bank-conflict free;
+//   workgroup tile 256 (tokens) x 256 (outputs), eight waves (two per SIMD) of 128 x 64 outputs;
+//   K in stages of 128: both operands K-contiguous, moved HBM/L2 -> LDS by global_load_lds_dwordx4
+//   into two 64 KB stage buffers (stage s+2 lands while stage s is multiplied), 16-byte chunks
+//   XOR-swizzled by row so the 32-row MFMA fragment reads are bank-conflict free;
 //   tile order: contiguous tile ranges per XCD (workgroup b runs on XCD b % 8) and groups of 8 token
 //   tiles sweeping the output tiles, so an XCD's L2 holds the operands its tiles share.
+// The E4M3 x MXFP4 and MXFP4 x MXFP4 kernels further down keep the same tiles and schedule.
 #include <type_traits>
 
 #include "common.h"

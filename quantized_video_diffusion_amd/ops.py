@@ -624,3 +624,9 @@ def mfma_probe(kind: int, iters: int = 4000, workgroups: int = 1024, reps: int =
     if wall_khz > 0:
         mhz = float(np.median(ck[:, 0] / np.maximum(ck[:, 1], 1.0)) * wall_khz / 1e3)
     return {"tflops": flops / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e12, "clock_mhz": mhz}
+
+
+def inject_launch_failure(after: int):
+    """The launch `after` launches from now on this thread reports QVD_EHIP (qvd_inject_launch_failure);
+    -1 cancels.  For tests of error handling."""
+    call("qvd_inject_launch_failure", int(after))
