@@ -219,8 +219,10 @@ def parse_counters(mfma_dir, fetch_dir, write_dir, trace_dir, blocks=2):
         items = sorted(items, key=lambda t: int(t[0]))
         return items[-2 * blocks:] if late else items
 
+    has_insts = any("SQ_INSTS_VALU" in d for d in disp.values())
     lines = ["| kernel | what | dispatches | GPU cycles | µs | clock GHz | MFMA busy | MFMA busy x clock / 2.4 GHz "
-             "| HBM GB | HBM TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+             "| HBM GB | HBM TB/s |" + (" VALU instr / wave | MFMA instr / wave |" if has_insts else ""),
+             "|---|---|---|---|---|---|---|---|---|---|" + ("---|---|" if has_insts else "")]
     for sym, what, late in COUNTER_KERNELS:
         ds = [v for _, v in last([(i, v) for (k, i), v in disp.items() if sym in k], late)]
         grids = {d["grid"] for d in ds}
@@ -233,9 +235,15 @@ def parse_counters(mfma_dir, fetch_dir, write_dir, trace_dir, blocks=2):
         fk = [v for _, v in last([(i, v) for (k, i), v in fe.items() if sym in k], late)]
         wk = [v for _, v in last([(i, v) for (k, i), v in wr.items() if sym in k], late)]
         gb = (sum(fk) / len(fk) * 1024 * f_fetch + sum(wk) / len(wk) * 1024 * f_write) / 1e9
-        lines.append(f"| `{sym}` | {what} | {len(ds)} | {cyc:,.0f} | {us:,.1f} | {cyc / us / 1e3:.2f} | "
-                     f"{100 * busy:.1f}% | {100 * busy * cyc / us / 1e3 / 2.4:.1f}% | {gb:.3f} | "
-                     f"{gb / us * 1e3:.2f} |")
+        row = (f"| `{sym}` | {what} | {len(ds)} | {cyc:,.0f} | {us:,.1f} | {cyc / us / 1e3:.2f} | "
+               f"{100 * busy:.1f}% | {100 * busy * cyc / us / 1e3 / 2.4:.1f}% | {gb:.3f} | "
+               f"{gb / us * 1e3:.2f} |")
+        if has_insts:
+            waves = sum(d["grid"] for d in ds) / 64.0          # Grid_Size counts threads
+            valu = sum(d.get("SQ_INSTS_VALU", 0.0) for d in ds) / waves
+            mfma = sum(d.get("SQ_INSTS_MFMA", 0.0) for d in ds) / waves
+            row += f" {valu:,.0f} | {mfma:,.0f} |"
+        lines.append(row)
     print("\n".join(lines))
 
 

@@ -13,16 +13,17 @@
 //   MFMA phase t:  O^T += V^T(t-1) . P^T(t-1) with v_mfma_f32_32x32x16_f16, fp32 accumulation;
 //                  then S^T = K(t) . Q^T with v_mfma_i32_32x32x32_i8 (exact int32, Q fragments in
 //                  registers);
-//   VALU phase t:  row maxima of S * sQ*sK*sm_scale*log2(e); numerators P = exp2(s - m) rounded to
-//                  fp16 against a reference maximum m per row (scores biased into float patterns,
-//                  see SCORE_BIAS), and their fp32 sums (v_dot2_f32_f16 against ones).
+//   VALU phase t:  numerators P = exp2(s - m) of S * sQ*sK*sm_scale*log2(e), rounded to fp16
+//                  against a reference maximum m per row (scores biased into float patterns, see
+//                  SCORE_BIAS), and their fp32 sums (v_dot2_f32_f16 against ones); the row maxima
+//                  only when a numerator overflows fp16 (the lazy reference below).
 // The 32 x 32 instruction shapes: on gfx950 the 16 x 16 INT8 and fp16 shapes reach only about 60% of
 // the matrix cores' rate under load, the 32 x 32 ones nearly all of it.
-// The reference m moves only when a tile's row maximum exceeds it by more than 8 (log2 units), and
-// then the fp32 sums so far are multiplied by exp2(m_old - m_new); otherwise the numerators stay
-// below 2^8.  Each weight is the exact softmax weight up to one fp16 rounding of its numerator
-// (relative 2^-11) and fp32 arithmetic; the output is normalised by the sum of the numerators
-// actually used.  V arrives in fp16 scaled by one power of two 2^-E[h] per head (vt_tile_exponent,
+// The reference m moves only when a numerator formed against it would leave fp16's finite range (the
+// row maxima are computed only then), and then the fp32 sums so far are multiplied by
+// exp2(m_old - m_new); every numerator used is a finite fp16 value.  Each weight is the exact softmax
+// weight up to one fp16 rounding of its numerator (relative 2^-11) and fp32 arithmetic; the output is
+// normalised by the sum of the numerators actually used.  V arrives in fp16 scaled by one power of two 2^-E[h] per head (vt_tile_exponent,
 // k_vt_unify), exact for every element within 2^28 of the head's max|V|, whatever its magnitude;
 // the output stage multiplies by 2^E[h].
 //
@@ -337,27 +338,37 @@ QVD_DEV void pv_tile(const uint16_t* vbuf, const v8h pb[8], int lane, v16f o[4])
     }
 }
 
-constexpr float RESCALE_SLACK = 8.0f;   // log2 units a tile maximum may exceed the reference by
+constexpr float RESCALE_SLACK = 8.0f;   // log2 units a moved reference may sit below a tile maximum
 
-
-// Numerators of one tile against the reference maximum m (moved, and the sums rescaled, when the
-// row's tile maximum exceeds its reference by more than RESCALE_SLACK; the wave takes or skips the
-// rescale as a whole).  c is the tile's factor on the grid of u; a moved reference is the tile
-// maximum raised to the next multiple of G, so the numerators stay at most 2^8.
+// Numerators of one tile against the reference maximum m, as fp16, and their sum added to lsum.
+// The row maxima are not computed on the common path: the numerators are formed against the current
+// reference, and only when one of them leaves fp16's finite range (a tile maximum at least ~16 above
+// the reference -- the row's first tile always, its reference starting at -inf) does the wave compute
+// the tile's row maxima, move the references of the rows whose maximum exceeds theirs by more than
+// RESCALE_SLACK to that maximum raised to the next multiple of G (c is on the grid of u, so the
+// folded constant stays exact), rescale those rows' sums, and form the tile's numerators again.
+// Every numerator used is therefore a finite fp16 value, at most 65,504 (relative precision 2^-11
+// over fp16's normal range).
 QVD_DEV void softmax_tile(const v16i_ s[4], float c, const ScoreGrid& grid, bool ragged, int key0, int L,
                           int hl, float& m, v16f o[4], float& lsum, v8h pb[8]) {
-    const float tmax = ragged ? tile_max<true>(s, c, key0, L, hl) : tile_max<false>(s, c, key0, L, hl);
-    const bool up = tmax > m + RESCALE_SLACK;
-    const float mnew = up ? grid.ceil_g(tmax) : m;
-    const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
-    if (__ballot(up) != 0ull) {
+    float tsum = 0.0f;
+    if (ragged) tile_numerators<true>(s, c, m, key0, L, hl, pb, &tsum);
+    else tile_numerators<false>(s, c, m, key0, L, hl, pb, &tsum);
+    // an fp16 infinity among the numerators makes the (fp32) sum infinite
+    if (__ballot(!(tsum <= 3.0e38f)) != 0ull) {
+        const float tmax = ragged ? tile_max<true>(s, c, key0, L, hl) : tile_max<false>(s, c, key0, L, hl);
+        const bool up = tmax > m + RESCALE_SLACK;
+        const float mnew = up ? grid.ceil_g(tmax) : m;
+        const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
         lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        tsum = 0.0f;
+        if (ragged) tile_numerators<true>(s, c, m, key0, L, hl, pb, &tsum);
+        else tile_numerators<false>(s, c, m, key0, L, hl, pb, &tsum);
     }
-    if (ragged) tile_numerators<true>(s, c, m, key0, L, hl, pb, &lsum);
-    else tile_numerators<false>(s, c, m, key0, L, hl, pb, &lsum);
+    lsum += tsum;
 }
 
 // Output of the attention kernel: bf16 O; bf16 O and the per-(head, tile) max|O|; or the E4M3 codes
