@@ -10,31 +10,28 @@
 // other computes its softmax numerators (VALU), so the matrix cores and the vector ALUs of each SIMD
 // work at the same time.  Per item, over the kept key tiles t (masked tiles are never loaded or
 // multiplied):
-//   MFMA phase t:  O^T += V^T(t-1) . P^T(t-1) with v_mfma_f32_32x32x16_f16, fp32 accumulation;
-//                  then S^T = K(t) . Q^T with v_mfma_i32_32x32x32_i8 (exact int32, Q fragments in
-//                  registers);
-//   VALU phase t:  numerators P = exp2(s - m) of S * sQ*sK*sm_scale*log2(e), rounded to fp16
-//                  against a reference maximum m per row (scores biased into float patterns, see
-//                  SCORE_BIAS), and their fp32 sums (v_dot2_f32_f16 against ones); the row maxima
-//                  only when a numerator overflows fp16 (the lazy reference below).
-// The 32 x 32 instruction shapes: on gfx950 the 16 x 16 INT8 and fp16 shapes reach only about 60% of
-// the matrix cores' rate under load, the 32 x 32 ones nearly all of it.
-// The reference m moves only when a numerator formed against it would leave fp16's finite range (the
-// row maxima are computed only then), and then the fp32 sums so far are multiplied by
-// exp2(m_old - m_new); every numerator used is a finite fp16 value.  Each weight is the exact softmax
-// weight up to one fp16 rounding of its numerator (relative 2^-11) and fp32 arithmetic; the output is
-// normalised by the sum of the numerators actually used.  V arrives in fp16 scaled by one power of two 2^-E[h] per head (vt_tile_exponent,
+//   MFMA phase t:  O^T += V^T(t-1) . P^T(t-1) and the numerator sums (ones . P^T) with
+//                  v_mfma_f32_16x16x32_f16, fp32 accumulation; then S^T = K(t) . Q^T with
+//                  v_mfma_i32_16x16x64_i8 (exact int32, Q fragments in registers);
+//   VALU phase t:  row maxima of S * sQ*sK*sm_scale*log2(e); numerators P = exp2(s - m) rounded to
+//                  fp16 against a reference maximum m per row (scores biased into float patterns,
+//                  see SCORE_BIAS).
+// The reference m moves only when a tile's row maximum exceeds it by more than 8 (log2 units), and
+// then the fp32 sums so far are multiplied by exp2(m_old - m_new); otherwise the numerators stay
+// below 2^8.  Each weight is the exact softmax weight up to one fp16 rounding of its numerator
+// (relative 2^-11) and fp32 arithmetic; the output is normalised by the sum of the numerators
+// actually used.  V arrives in fp16 scaled by one power of two 2^-E[h] per head (vt_tile_exponent,
 // k_vt_unify), exact for every element within 2^28 of the head's max|V|, whatever its magnitude;
 // the output stage multiplies by 2^E[h].
 //
 // Staging: tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no register round trip).  The K
-// tile's rows are permuted (key_of_row) so that each group of 8 numerators a lane holds is 8
+// tile's rows are permuted (key_of_row) so that each lane's 8 numerators of a 32-key block are 8
 // consecutive keys, read from V^T in one 16-byte access.  Each lane picks the global 16-byte chunk
 // that belongs at its LDS slot, which applies an XOR swizzle:
 // K rows (128 B) swizzle chunks by row & 7, V^T rows (256 B, fp16, keys contiguous) by row & 15,
-// so each 8-lane group of an MFMA fragment read hits distinct banks.  V arrives transposed from the QKV GEMM
+// so the 16-row MFMA fragment reads hit distinct banks.  V arrives transposed from the QKV GEMM
 // epilogue (or from a transpose pass for callers holding V token-major).  Computing the transposed products
-// makes each lane own one query row in both MFMA outputs (lanes l and l + 32 share it).
+// makes each lane own one query row in both MFMA outputs.
 #include "common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -61,7 +58,6 @@ struct AttnSmem {
 };
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef int v16i_ __attribute__((ext_vector_type(16)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -86,26 +82,26 @@ QVD_DEV void dma16(const void* g, void* lds_slot_base) {
 QVD_DEV void dma_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 QVD_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// The 32 x 32 MFMA output: element r of lane l is row 8 (r/4) + 4 (l/32) + r%4, column l%32.
-//
-// Key (0..127 within its tile) held by row rho of the LDS K tile.  Row rho = 32 kb + 8 a + 4 hl + b
-// is the score-block row that lane half hl (l/32) receives as element r = 4 a + b of block kb; the
-// map gives it key 32 kb + 16 (r/8) + 8 hl + r%8 (key_of_elem), so elements 8 c .. 8 c + 7 are the 8
-// consecutive keys 32 kb + 16 c + 8 hl .. + 7: the lane's share of one 16-key P.V operand chunk,
-// which one 16-byte read of a V^T row then matches.
+// Key (0..127 within its tile) held by row rho of the LDS K tile.  Row rho = 16 kb + 4 g + r is the
+// score-block row that lane group g receives as element r of block kb; the map gives lane group g the
+// keys 32 (kb/2) + 8 g + 4 (kb%2) + r, i.e. 8 consecutive keys across blocks 2 kp and 2 kp + 1, which
+// one 16-byte read of a V^T row then matches.
 QVD_DEV int key_of_row(int rho) {
-    const int kb = rho >> 5, a = (rho >> 3) & 3, hl = (rho >> 2) & 1, b = rho & 3;
-    return 32 * kb + 16 * (a >> 1) + 8 * hl + 4 * (a & 1) + b;
+    const int kb = rho >> 4, g = (rho >> 2) & 3, r = rho & 3;
+    return 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
 }
-QVD_DEV int key_of_elem(int kb, int r, int hl) { return 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7); }
 
-// Q fragments of this wave (B operand): qf[ks] = Q[q0 + l%32][h][32 ks + 16 (l/32) .. +15]
-QVD_DEV void load_q_frags(const int8_t* __restrict__ q, int L, int H, int h, int q0, int lane, v4i qf[4]) {
-    int row = q0 + (lane & 31);
-    row = row < L ? row : L - 1;
-    const int8_t* p = q + ((int64_t)row * H + h) * 128 + 16 * (lane >> 5);
+// Q fragments of this wave (B operand): qf[qb][ks] = Q[q0 + 16 qb + fr][h][64 ks + 16 fg .. +15]
+QVD_DEV void load_q_frags(const int8_t* __restrict__ q, int L, int H, int h, int q0, int fr, int fg,
+                          v4i qf[2][2]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const v4i*>(p + 32 * ks);
+    for (int qb = 0; qb < 2; ++qb) {
+        int row = q0 + 16 * qb + fr;
+        row = row < L ? row : L - 1;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            qf[qb][ks] = *reinterpret_cast<const v4i*>(q + ((int64_t)row * H + h) * 128 + 64 * ks + 16 * fg);
+    }
 }
 
 // K tile j -> LDS.  Wave w, instruction u fills LDS rows (4w + u)*8 .. +7; lane l lands in row
@@ -146,31 +142,33 @@ QVD_DEV void stage_vt(uint16_t* vbuf, const uint16_t* __restrict__ vt, int Lp, i
     }
 }
 
-// S^T = K . Q^T for this wave: s[kb][r] = s0 + score(query q0 + l%32, key key_of_elem(kb, r, l/32))
-// (exact int32 sums)
-QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[4], int lane, v16i_ s[4], int s0) {
-    // steps ks: the 4 key blocks, so an accumulator's next MFMA comes 4 later; the next step's K
-    // fragments are read while this step multiplies
+// S^T = K . Q^T for this wave: s[qb][kb][r] = s0 + score(query q0 + 16 qb + fr,
+// key key_of_row(16 kb + 4 fg + r)) (exact int32 sums)
+QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v4i s[2][8], int s0) {
+    // steps (ks, half): 4 key blocks x 2 query blocks; an accumulator's next MFMA comes 16 later, and
+    // the next step's K fragments are read while this step multiplies
     auto kfrag = [&](int kb, int ks) {
-        const int row = 32 * kb + (lane & 31);
-        const int c = 2 * ks + (lane >> 5);
-        return *reinterpret_cast<const v4i*>(kbuf + row * 128 + ((c ^ (row & 7)) << 4));
+        const int row = 16 * kb + fr;
+        return *reinterpret_cast<const v4i*>(kbuf + row * 128 + (((4 * ks + fg) ^ (row & 7)) << 4));
     };
-    v16i_ bias;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) bias[r] = s0;
     v4i kcur[4], knext[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) kcur[b] = kfrag(b, 0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        if (ks + 1 < 4) {
+    for (int st = 0; st < 4; ++st) {
+        const int ks = st >> 1, hf = st & 1;
+        if (st + 1 < 4) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) knext[b] = kfrag(b, ks + 1);
+            for (int b = 0; b < 4; ++b) knext[b] = kfrag(4 * ((st + 1) & 1) + b, (st + 1) >> 1);
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-            s[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kcur[b], qf[ks], ks == 0 ? bias : s[b], 0, 0, 0);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int kb = 4 * hf + b;
+                const v4i c = ks == 0 ? (v4i){s0, s0, s0, s0} : s[qb][kb];
+                s[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kcur[b], qf[qb][ks], c, 0, 0, 0);
+            }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < 4; ++b) kcur[b] = knext[b];
@@ -221,62 +219,61 @@ QVD_DEV float as_float(u32 x) { return __builtin_bit_cast(float, x); }
 
 QVD_DEV float unbias(int bits) { return as_float((u32)bits) - SCORE_BIAS; }
 
-// max over lanes l and l^32 with the gfx950 lane swap (pure VALU), so the softmax phase issues no
-// LDS instruction
-QVD_DEV int max_over_halves(int x) {
-    const auto a = __builtin_amdgcn_permlane32_swap((u32)x, (u32)x, false, false);
-    return max((int)a[0], (int)a[1]);
-}
-QVD_DEV float sum_over_halves(float x) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+// max over lanes l, l^16, l^32, l^48 with the gfx950 lane swaps (pure VALU: v_permlane16_swap pairs
+// lane l with l^16, v_permlane32_swap with l^32), so the softmax phase issues no LDS instruction
+QVD_DEV int max_over_lane_groups(int x) {
+    const auto a = __builtin_amdgcn_permlane16_swap((u32)x, (u32)x, false, false);
+    const int y = max((int)a[0], (int)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((u32)y, (u32)y, false, false);
+    return max((int)b[0], (int)b[1]);
 }
 
-// row maximum (log2 units) of this tile's scores: integer maximum of the biased patterns over this
-// lane's keys, then over the row's two lanes
+// row maxima (log2 units) of this tile's scores: integer maxima of the biased patterns over this
+// lane's keys, then over the row's four lane groups
 template <bool RAGGED>
-QVD_DEV float tile_max(const v16i_ s[4], float c, int key0, int L, int hl) {
-    int mx = INT_MIN;
+QVD_DEV void tile_max(const v4i s[2][8], float c, int key0, int L, int fg, float tmax[2]) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int qb = 0; qb < 2; ++qb) {
+        int mx = INT_MIN;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            if (RAGGED && key0 + key_of_elem(kb, r, hl) >= L) continue;
-            mx = max(mx, s[kb][r]);
-        }
-    mx = max_over_halves(mx);                  // every row keeps at least one key of a ragged tile
-    return unbias(mx) * c;
-}
-
-// fp16 numerators of this tile against the reference maximum, as the B operand of the P.V MFMA
-// (pb[kc]: keys 16 kc + 8 hl .. + 7), and their sum added to *lsum.  c is on the grid of u and m on
-// the grid of G (ScoreGrid), so mb below is exact.
-template <bool RAGGED>
-QVD_DEV void tile_numerators(const v16i_ s[4], float c, float m, int key0, int L, int hl, v8h pb[8],
-                             float* lsum) {
-    const float mb = fmaf(SCORE_BIAS, c, m);
-    const v2h ones = {1, 1};
-    float acc = *lsum;
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-        const int kb = kc >> 1;
-        u32 w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            float p[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int r = 8 * (kc & 1) + 2 * e2 + u;
-                p[u] = __builtin_amdgcn_exp2f(fmaf(as_float((u32)s[kb][r]), c, -mb));
-                if (RAGGED && key0 + key_of_elem(kb, r, hl) >= L) p[u] = 0.0f;
+            for (int r = 0; r < 4; ++r) {
+                if (RAGGED && key0 + key_of_row(16 * kb + 4 * fg + r) >= L) continue;
+                mx = max(mx, s[qb][kb][r]);
             }
-            w[e2] = pack_f16x2(p[0], p[1]);
-            acc = __builtin_amdgcn_fdot2(as_v2h(w[e2]), ones, acc, false);
-        }
-        const v4i pw = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-        pb[kc] = __builtin_bit_cast(v8h, pw);
+        mx = max_over_lane_groups(mx);         // every row keeps at least one key of a ragged tile
+        tmax[qb] = unbias(mx) * c;
     }
-    *lsum = acc;
+}
+
+// fp16 numerators of this tile against the reference maxima, as the B operand of the P.V MFMA.
+// c is on the grid of u and m on the grid of G (ScoreGrid), so mb below is exact.
+template <bool RAGGED>
+QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int key0, int L, int fg,
+                             v8h pb[2][4]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const float mb = fmaf(SCORE_BIAS, c, m[qb]);
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp) {
+            u32 w[4];
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+                const int kb = 2 * kp + hlf;
+                float p[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    p[r] = __builtin_amdgcn_exp2f(fmaf(as_float((u32)s[qb][kb][r]), c, -mb));
+                    if (RAGGED && key0 + key_of_row(16 * kb + 4 * fg + r) >= L) p[r] = 0.0f;
+                }
+                w[2 * hlf] = pack_f16x2(p[0], p[1]);
+                w[2 * hlf + 1] = pack_f16x2(p[2], p[3]);
+            }
+            const v4i pw = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+            pb[qb][kp] = __builtin_bit_cast(v8h, pw);
+        }
+    }
 }
 
 // The valid entries (0 <= j < T) of the first `cnt` list elements, in list order, into tiles; their
@@ -311,64 +308,75 @@ QVD_DEV float compact_tiles(int* tiles, int* wcount, float* wkmax, int* n_out,
     return fmaxf(fmaxf(wkmax[0], wkmax[1]), fmaxf(wkmax[2], wkmax[3]));
 }
 
-// O^T += V^T . P^T, this wave's share, from the V^T tile in LDS: o[db][r] is dim
-// 32 db + 8 (r/4) + 4 (l/32) + r%4 of query q0 + l%32.  Lane half hl's 8 numerators of chunk kc meet
-// keys 16 kc + 8 hl .. +7 of V^T row d, one 16-byte read.  Steps kc: the 4 dim blocks, so an
-// accumulator's next MFMA comes 4 later; the next step's fragments are read while this step multiplies.
-QVD_DEV void pv_tile(const uint16_t* vbuf, const v8h pb[8], int lane, v16f o[4]) {
-    auto vfrag = [&](int db, int kc) {
-        const int d = 32 * db + (lane & 31);
-        const int c = 2 * kc + (lane >> 5);
-        return *reinterpret_cast<const v8h*>(vbuf + d * 128 + 8 * (c ^ (d & 15)));
+// O^T += V^T . P^T and the numerator sums, this wave's share, from the V^T tile in LDS.  Lane group
+// g's 8 numerators meet keys 32 kp + 8 g .. +7 of V^T row d, one 16-byte chunk.  Steps (kp, half of
+// the 16-dim blocks): an accumulator's next MFMA comes 16 later, and the next step's fragments are
+// read while this step multiplies.
+QVD_DEV void pv_tile(const uint16_t* vbuf, const v8h pb[2][4], int fr, int fg, v4f o[2][8], v4f lacc[2]) {
+    const v8h ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    auto vfrag = [&](int db, int kp) {
+        const int d = 16 * db + fr;
+        return *reinterpret_cast<const v8h*>(vbuf + d * 128 + 8 * ((4 * kp + fg) ^ (d & 15)));
     };
     v8h vcur[4], vnext[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) vcur[b] = vfrag(b, 0);
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-        if (kc + 1 < 8) {
+    for (int st = 0; st < 8; ++st) {
+        const int kp = st >> 1, hf = st & 1;
+        if (st + 1 < 8) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) vnext[b] = vfrag(b, kc + 1);
+            for (int b = 0; b < 4; ++b) vnext[b] = vfrag(4 * ((st + 1) & 1) + b, (st + 1) >> 1);
+        }
+        if (hf == 0) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[qb][kp], lacc[qb], 0, 0, 0);
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vcur[b], pb[kc], o[b], 0, 0, 0);
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                o[qb][4 * hf + b] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(vcur[b], pb[qb][kp], o[qb][4 * hf + b], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < 4; ++b) vcur[b] = vnext[b];
     }
 }
 
-constexpr float RESCALE_SLACK = 8.0f;   // log2 units a moved reference may sit below a tile maximum
+constexpr float RESCALE_SLACK = 8.0f;   // log2 units a tile maximum may exceed the reference by
 
-// Numerators of one tile against the reference maximum m, as fp16, and their sum added to lsum.
-// The row maxima are not computed on the common path: the numerators are formed against the current
-// reference, and only when one of them leaves fp16's finite range (a tile maximum at least ~16 above
-// the reference -- the row's first tile always, its reference starting at -inf) does the wave compute
-// the tile's row maxima, move the references of the rows whose maximum exceeds theirs by more than
-// RESCALE_SLACK to that maximum raised to the next multiple of G (c is on the grid of u, so the
-// folded constant stays exact), rescale those rows' sums, and form the tile's numerators again.
-// Every numerator used is therefore a finite fp16 value, at most 65,504 (relative precision 2^-11
-// over fp16's normal range).
-QVD_DEV void softmax_tile(const v16i_ s[4], float c, const ScoreGrid& grid, bool ragged, int key0, int L,
-                          int hl, float& m, v16f o[4], float& lsum, v8h pb[8]) {
-    float tsum = 0.0f;
-    if (ragged) tile_numerators<true>(s, c, m, key0, L, hl, pb, &tsum);
-    else tile_numerators<false>(s, c, m, key0, L, hl, pb, &tsum);
-    // an fp16 infinity among the numerators makes the (fp32) sum infinite
-    if (__ballot(!(tsum <= 3.0e38f)) != 0ull) {
-        const float tmax = ragged ? tile_max<true>(s, c, key0, L, hl) : tile_max<false>(s, c, key0, L, hl);
-        const bool up = tmax > m + RESCALE_SLACK;
-        const float mnew = up ? grid.ceil_g(tmax) : m;
-        const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        lsum *= alpha;
+
+// Numerators of one tile against the reference maxima m (moved, and the sums rescaled, when a row's
+// tile maximum exceeds its reference by more than RESCALE_SLACK; the wave takes or skips the rescale
+// as a whole).  c is the tile's factor on the grid of u; a moved reference is the tile maximum
+// raised to the next multiple of G, so the numerators stay at most 2^8.
+QVD_DEV void softmax_tile(const v4i s[2][8], float c, const ScoreGrid& grid, bool ragged, int key0, int L,
+                          int fg, float m[2], v4f o[2][8], v4f lacc[2], v8h pb[2][4]) {
+    float tmax[2];
+    if (ragged) tile_max<true>(s, c, key0, L, fg, tmax);
+    else tile_max<false>(s, c, key0, L, fg, tmax);
+    float alpha[2];
+    bool up = false;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-        tsum = 0.0f;
-        if (ragged) tile_numerators<true>(s, c, m, key0, L, hl, pb, &tsum);
-        else tile_numerators<false>(s, c, m, key0, L, hl, pb, &tsum);
+    for (int qb = 0; qb < 2; ++qb) {
+        const bool u = tmax[qb] > m[qb] + RESCALE_SLACK;
+        const float mnew = u ? grid.ceil_g(tmax[qb]) : m[qb];
+        alpha[qb] = m[qb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[qb] - mnew);
+        m[qb] = mnew;
+        up = up || u;
     }
-    lsum += tsum;
+    if (__ballot(up) != 0ull) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            lacc[qb] *= alpha[qb];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[qb][db] *= alpha[qb];
+        }
+    }
+    if (ragged) tile_numerators<true>(s, c, m, key0, L, fg, pb);
+    else tile_numerators<false>(s, c, m, key0, L, fg, pb);
 }
 
 // Output of the attention kernel: bf16 O; bf16 O and the per-(head, tile) max|O|; or the E4M3 codes
@@ -388,7 +396,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     const int T = (L + 127) >> 7, total = T * H;
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = wv >> 2, wg = wv & 3;
-    const int hl = lane >> 5;
+    const int fr = lane & 15, fg = lane >> 4;
 
     // Workgroup b -> pair index -> work items 2 pair + g, head-major (h = id / T, i = id % T).
     // Workgroups are handed to the 8 XCDs round-robin (b % 8), so each XCD is given one contiguous
@@ -409,8 +417,8 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     const bool ragged_L = (L & 127) != 0;
     GroupSmem& gs = sm.grp[g];
 
-    v4i qf[4];
-    load_q_frags(q, L, H, h, q0, lane, qf);
+    v4i qf[2][2];
+    load_q_frags(q, L, H, h, q0, fr, fg, qf);
     const float qsc = q_scale[h * T + i] * c_log2;
     int cnt = valid ? kv_cnt[h * T + i] : 0;
     cnt = cnt < 0 ? 0 : (cnt > kmax ? kmax : cnt);
@@ -421,15 +429,16 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     const int n = sm.n[g];
     const int n_other = sm.n[g ^ 1];
 
-    float m = -INFINITY;                          // reference row maximum (log2 units)
-    float lsum = 0.0f;                            // this lane's share of the row's numerator sum
-    v16f o[4];
+    float m[2] = {-INFINITY, -INFINITY};         // reference row maxima (log2 units)
+    v4f o[2][8], lacc[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int a = 0; a < 2; ++a) {
+        lacc[a] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[b][r] = 0.0f;
-    v16i_ s[4];                                   // scores of tile t: MFMA phase t -> VALU phase t
-    v8h pb[8];                                    // numerators of tile t: VALU phase t -> MFMA phase t+1
+        for (int b = 0; b < 8; ++b) o[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+    }
+    v4i s[2][8];                                  // scores of tile t: MFMA phase t -> VALU phase t
+    v8h pb[2][4];                                 // numerators of tile t: VALU phase t -> MFMA phase t+1
     float ksc = 0.0f;                             // K scale of the tile the next VALU phase takes
 
     // Phases p = 0, 1, ... end at workgroup barriers B_p (B_-1 before phase 0).  Group 0 runs MFMA
@@ -447,12 +456,12 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     const int P = 2 * n0 + 1 > 2 * n1 + 2 ? 2 * n0 + 1 : 2 * n1 + 2;
     auto mfma_qk = [&](int t) {                   // the QK part of MFMA phase t and its DMA
         if (t + 1 < n) stage_k(gs.k[(t + 1) & 1], k, L, H, h, gs.tiles[t + 1], wg, lane);
-        qk_scores(gs.k[t & 1], qf, lane, s, SCORE_BIAS_BITS);
+        qk_scores(gs.k[t & 1], qf, fr, fg, s, SCORE_BIAS_BITS);
     };
     int j = 0;                                    // tile of the next VALU phase (read in the MFMA phase)
     auto valu_phase = [&]() {
         stage_vt(gs.vt, vt, Lp, h, j, wg, lane);
-        softmax_tile(s, grid.factor(qsc * ksc), grid, ragged_L && j == T - 1, j * 128, L, hl, m, o, lsum, pb);
+        softmax_tile(s, grid.factor(qsc * ksc), grid, ragged_L && j == T - 1, j * 128, L, fg, m, o, lacc, pb);
     };
 
     if (n > 0) stage_k(gs.k[0], k, L, H, h, gs.tiles[0], wg, lane);
@@ -475,7 +484,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
                 j = __builtin_amdgcn_readfirstlane(gs.tiles[t + 1]);
                 ksc = k_scale[h * T + j];
             }
-            pv_tile(gs.vt, pb, lane, o);
+            pv_tile(gs.vt, pb, fr, fg, o, lacc);
             mfma_qk(t + 1);
             lds_barrier();
             passed += 2;
@@ -483,68 +492,79 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     }
     for (; passed < P + 1; ++passed) lds_barrier();
     const int ve = valid ? v_exp[h] : 0;          // the head's V scale: O = (P.V') 2^ve / sum P
-    const float lt = sum_over_halves(lsum);
-    const float inv = lt > 0.0f ? ldexpf(1.0f / lt, ve) : 0.0f;
-    const int row = q0 + (lane & 31);
 
     if (OUT == OUT_MXFP4) {
         // bf16 O, then MXFP4 per (row, head, 32 dims) with the standalone quantizer's arithmetic.  Dims
-        // 32 db .. 32 db + 31 of the row are block db of this lane and of lane l^32: the block maximum
-        // meets across the two before any lane stores.
-        u32 w[4][8];
-        int kx[4];
+        // 32 b .. 32 b + 31 of a row are this lane's column blocks 2b and 2b+1 in each of the row's
+        // four lanes (fg): the block maximum meets across them before any lane stores.
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            float mx = 0.0f;
+        for (int qb = 0; qb < 2; ++qb) {
+            const float lt = lacc[qb][0];
+            const float inv = lt > 0.0f ? ldexpf(1.0f / lt, ve) : 0.0f;
+            const int row = q0 + 16 * qb + fr;
+            u32 w[8][2];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                w[db][u] = pack_bf16x2(o[db][2 * u] * inv, o[db][2 * u + 1] * inv);
-                mx = fmaxf(mx, fmaxf(fabsf(bf16lo(w[db][u])), fabsf(bf16hi(w[db][u]))));
+            for (int db = 0; db < 8; ++db) {
+                const v4f cc = o[qb][db];
+                w[db][0] = pack_bf16x2(cc[0] * inv, cc[1] * inv);
+                w[db][1] = pack_bf16x2(cc[2] * inv, cc[3] * inv);
             }
-            kx[db] = mx_exponent(__int_as_float(max_over_halves(__float_as_int(mx))));
-        }
-        if (valid && row < L) {
-            const int64_t orow = (int64_t)row * H + h;
-            uint8_t* pr = static_cast<uint8_t*>(out) + orow * 64;
+            int kx[4];
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int b = 0; b < 4; ++b) {
+                float m = 0.0f;
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    // dims 32 db + 8 a + 4 hl .. +3: bytes 16 db + 4 a + 2 hl, +1
-                    const u32 c = e2m1_encode2(bf16lo(w[db][2 * a]), bf16hi(w[db][2 * a]), kx[db]) |
-                                  (e2m1_encode2(bf16lo(w[db][2 * a + 1]), bf16hi(w[db][2 * a + 1]), kx[db]) << 8);
-                    *reinterpret_cast<uint16_t*>(pr + 16 * db + 4 * a + 2 * hl) = (uint16_t)c;
+                for (int db = 2 * b; db < 2 * b + 2; ++db)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        m = fmaxf(m, fmaxf(fabsf(bf16lo(w[db][u])), fabsf(bf16hi(w[db][u]))));
+                kx[b] = mx_exponent(__int_as_float(max_over_lane_groups(__float_as_int(m))));
+            }
+            if (valid && row < L) {
+                const int64_t orow = (int64_t)row * H + h;
+                uint8_t* pr = static_cast<uint8_t*>(out) + orow * 64;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const int k = kx[db >> 1];
+                    const u32 c = e2m1_encode2(bf16lo(w[db][0]), bf16hi(w[db][0]), k) |
+                                  (e2m1_encode2(bf16lo(w[db][1]), bf16hi(w[db][1]), k) << 8);
+                    *reinterpret_cast<uint16_t*>(pr + 8 * db + 2 * fg) = (uint16_t)c;
                 }
-            if (hl == 0)
-                *reinterpret_cast<u32*>(out_e8m0 + orow * 4) =
-                    (u32)(kx[0] + 127) | ((u32)(kx[1] + 127) << 8) | ((u32)(kx[2] + 127) << 16) |
-                    ((u32)(kx[3] + 127) << 24);
+                if (fg == 0)
+                    *reinterpret_cast<u32*>(out_e8m0 + orow * 4) =
+                        (u32)(kx[0] + 127) | ((u32)(kx[1] + 127) << 8) | ((u32)(kx[2] + 127) << 16) |
+                        ((u32)(kx[3] + 127) << 24);
+            }
         }
         return;
     }
 
     float amax = 0.0f;
     const float inv_s = OUT == OUT_E4M3 ? __fdiv_rn(1.0f, *out_scale) : 0.0f;
-    if (valid && row < L) {
-        const int64_t orow = ((int64_t)row * H + h) * 128;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+    for (int qb = 0; qb < 2; ++qb) {
+        const float lt = lacc[qb][0];
+        const float inv = lt > 0.0f ? ldexpf(1.0f / lt, ve) : 0.0f;
+        const int row = q0 + 16 * qb + fr;
+        if (valid && row < L) {
+            const int64_t orow = ((int64_t)row * H + h) * 128;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                // dims 32 db + 8 a + 4 hl .. +3
-                const int d0 = 32 * db + 8 * a + 4 * hl;
-                const u32 w0 = pack_bf16x2(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
-                const u32 w1 = pack_bf16x2(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+            for (int db = 0; db < 8; ++db) {
+                const v4f cc = o[qb][db];
+                const u32 w0 = pack_bf16x2(cc[0] * inv, cc[1] * inv);
+                const u32 w1 = pack_bf16x2(cc[2] * inv, cc[3] * inv);
                 if (OUT == OUT_E4M3) {
                     const u32 c4 = e4m3_encode2(bf16lo(w0) * inv_s, bf16hi(w0) * inv_s) |
                                    (e4m3_encode2(bf16lo(w1) * inv_s, bf16hi(w1) * inv_s) << 16);
-                    *reinterpret_cast<u32*>(static_cast<uint8_t*>(out) + orow + d0) = c4;
+                    *reinterpret_cast<u32*>(static_cast<uint8_t*>(out) + orow + 16 * db + 4 * fg) = c4;
                 } else {
                     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16lo(w0)), fabsf(bf16hi(w0))),
                                              fmaxf(fabsf(bf16lo(w1)), fabsf(bf16hi(w1)))));
-                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + d0) = (u32x2){w0, w1};
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + 16 * db + 4 * fg) =
+                        (u32x2){w0, w1};
                 }
             }
+        }
     }
     if (OUT == OUT_BF16_AMAX) {
         // max over the group's four waves (both groups reduce at once)
@@ -646,22 +666,24 @@ __global__ void __launch_bounds__(256) k_qk_tile(const int8_t* __restrict__ q, c
                                                  int32_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) int8_t ktile[128 * 128];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int hl = lane >> 5;
+    const int fr = lane & 15, fg = lane >> 4;
     const int q0 = i * 128 + 32 * wv;
-    v4i qf[4];
-    load_q_frags(q, L, H, h, q0, lane, qf);
+    v4i qf[2][2];
+    load_q_frags(q, L, H, h, q0, fr, fg, qf);
     stage_k(ktile, k, L, H, h, j, wv, lane);
     dma_barrier();
-    v16i_ s[4];
-    qk_scores(ktile, qf, lane, s, SCORE_BIAS_BITS);      // as the attention kernel, bias removed below
+    v4i s[2][8];
+    qk_scores(ktile, qf, fr, fg, s, SCORE_BIAS_BITS);      // as the attention kernel, bias removed below
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rr = 32 * wv + (lane & 31), cc = key_of_elem(kb, r, hl);
-            const bool ok = (i * 128 + rr) < L && (j * 128 + cc) < L;
-            out[rr * 128 + cc] = ok ? s[kb][r] - SCORE_BIAS_BITS : 0;
-        }
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rr = 32 * wv + 16 * qb + fr, cc = key_of_row(16 * kb + 4 * fg + r);
+                const bool ok = (i * 128 + rr) < L && (j * 128 + cc) < L;
+                out[rr * 128 + cc] = ok ? s[qb][kb][r] - SCORE_BIAS_BITS : 0;
+            }
 }
 
 namespace {
