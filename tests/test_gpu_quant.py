@@ -221,3 +221,16 @@ def test_bf16_amax_and_clip_counts():
         cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
         Q.clip_count(bf16_dev(x), f32_dev([s]), cnt)
         assert int(host(cnt)[0]) == int(np.count_nonzero(np.abs(xv) > float(s) * 448.0))
+
+
+def test_mfma_probe_rates_are_sane():
+    """The register-only MFMA probe (measurement support): every kind runs, reports a positive rate
+    below its nominal peak at 2.4 GHz, and a shader clock between 0.5 and 2.6 GHz."""
+    from quantized_video_diffusion_amd import _lib
+    nominal = {_lib.QVD_PROBE_FP8: 5000.0, _lib.QVD_PROBE_FP4: 10100.0, _lib.QVD_PROBE_INT8: 5000.0,
+               _lib.QVD_PROBE_F16: 2500.0, _lib.QVD_PROBE_INT8_32: 5000.0, _lib.QVD_PROBE_F16_32: 2500.0,
+               _lib.QVD_PROBE_FP8_16: 5000.0}
+    for kind, peak in nominal.items():
+        r = Q.mfma_probe(kind, iters=200, workgroups=512, reps=1)
+        assert 0.0 < r["tflops"] < 1.02 * peak, (kind, r)
+        assert r["clock_mhz"] is None or 500.0 < r["clock_mhz"] < 2600.0, (kind, r)
