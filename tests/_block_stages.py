@@ -223,49 +223,62 @@ def check_block_stages(name, qw, mod, x_bits, idx, cnt, g, n_heads, rows=None, e
     return st
 
 
-# ---- the MXFP4-weight block with static E4M3 activation scales (W4A8) --------------------------------
-# Stages of dit_block_forward with QVD_W_MXFP4 and act_scale = (s1, s_O, s2, s_g): modulate -> E4M3
-# with s1; QKV GEMM (E4M3 x MXFP4) and its INT8 Q/K / V^T epilogue; the attention writing E4M3(bf16(O))
-# under s_O (no bf16 O); out-projection + gated residual; modulate -> E4M3 with s2; up-projection with
-# the GELU -> E4M3 epilogue under s_g (no bf16 g); down-projection + gated residual.
+# ---- the MXFP4-weight blocks: static E4M3 activations (W4A8) or MXFP4 activations (W4A4) --------------
+# Stages of dit_block_forward with MXFP4 weights.  W4A8 (QVD_W_MXFP4 with act_scale = (s1, s_O, s2, s_g)):
+# modulate -> E4M3 under s1; QKV GEMM (E4M3 x MXFP4) and its INT8 Q/K / V^T epilogue; the attention
+# writing E4M3(bf16(O)) under s_O (no bf16 O); out-projection + gated residual; modulate -> E4M3 under
+# s2; up-projection with the GELU -> E4M3 epilogue under s_g (no bf16 g); down-projection + gated
+# residual.  W4A4 (QVD_W_MXFP4_A4): the same chain with every GEMM input in MXFP4 per token row and 32
+# channels (E2M1 codes + an E8M0 scale per block) and no per-tensor scale.
 # Bars as for the FP8 block.  The two fused producers are checked in two parts: the bf16 tensor they
 # encode (the attention's bf16 output from the same inputs, the GELU epilogue's bf16 output from the same
-# accumulators) against the oracle at the bf16 bar, and their codes against the standalone static
-# quantizer applied to that bf16 tensor, bit for bit.
+# accumulators) against the oracle at the bf16 bar, and their codes against the oracle's quantizer
+# applied to that bf16 tensor, bit for bit.  The MXFP4 modulate codes are bit-exact (the kernel rounds
+# the float64 modulation once to fp32, as the oracle does); the E4M3 ones follow the near-tie rule.
 
-def run_stages_w4a8(bw, mod_d, x_bits, idx_d, cnt_d, rows):
-    """GPU side of the W4A8 stage check: the block whole and stopped after the stages later ones
+def run_stages_4bit(bw, mod_d, x_bits, idx_d, cnt_d, rows):
+    """GPU side of the 4-bit stage check: the block whole and stopped after the stages later ones
     overwrite, plus, on `rows`, the fp32 accumulator outputs of the QKV, up and down GEMMs and the
     bf16 GELU of the up-projection's accumulators; the bf16 attention output from the block's own
     Q8/K8/V^T.  Host copies."""
     L = x_bits.shape[0]
+    a4 = bw.fmt == _lib.QVD_W_MXFP4_A4
     rows_d = torch.from_numpy(np.asarray(rows)).cuda()
     a = bw.act_scale
     wq = {s: (bw.w[s], bw.e8[s]) for s in ("qkv", "o", "up", "down")}
+
+    def gemm(it, codes, e8_slot, k, site, mode=_lib.QVD_EPI_F32):
+        c = it[codes][rows_d].contiguous()
+        if a4:
+            return Q.gemm_mxfp4_w4a4(c, it[e8_slot][rows_d].contiguous(), *wq[site], mode=mode)
+        return Q.gemm_mxfp4(c, a[k:k + 1], *wq[site], mode=mode)
+
+    def acts(it, codes, e8_slot):
+        return (host(it[codes]), host(it[e8_slot])) if a4 else (host(it[codes]), None)
+
     xd = bf16_dev(x_bits)
     ws = Q.block_forward_until(bw, mod_d, xd, idx_d, cnt_d, _lib.QVD_STAGE_ALL)
     it = Q.block_intermediates(bw, ws, L)
     g = {"x2": host_bits(xd), "q8": host(it["q8"]), "k8": host(it["k8"]), "qs": host(it["q_scale"]),
          "ks": host(it["k_scale"]), "vt": host(it["vt"]), "v_exp": host(it["vt_head_exp"]),
-         "h2": host(it["h"]), "g8": host(it["g8"])}
+         "h2": acts(it, "h", "h_e8m0"), "g8": acts(it, "g8", "g_e8m0")}
     o = Q.sparse_attn_vt(it["q8"], it["q_scale"], it["k8"], it["k_scale"],
                          Q.VT(it["vt"], it["vt_head_exp"]), idx_d, cnt_d)
     g["o_bf16"] = host_bits(o)
     del o
-    h2 = it["h"][rows_d].contiguous()
-    g["y_up"] = host(Q.gemm_mxfp4(h2, a[2:3], *wq["up"]))
-    g["g_bf16"] = host_bits(Q.gemm_mxfp4(h2, a[2:3], *wq["up"], mode=_lib.QVD_EPI_GELU))
-    g["y_down"] = host(Q.gemm_mxfp4(it["g8"][rows_d].contiguous(), a[3:4], *wq["down"]))
-    del it, ws, h2
+    g["y_up"] = host(gemm(it, "h", "h_e8m0", 2, "up"))
+    g["g_bf16"] = host_bits(gemm(it, "h", "h_e8m0", 2, "up", mode=_lib.QVD_EPI_GELU))
+    g["y_down"] = host(gemm(it, "g8", "g_e8m0", 3, "down"))
+    del it, ws
     for stage in (_lib.QVD_STAGE_MODULATE1, _lib.QVD_STAGE_OQUANT, _lib.QVD_STAGE_OPROJ):
         xd = bf16_dev(x_bits)
         ws = Q.block_forward_until(bw, mod_d, xd, idx_d, cnt_d, stage)
         it = Q.block_intermediates(bw, ws, L)
         if stage == _lib.QVD_STAGE_MODULATE1:
-            g["h1"] = host(it["h"])
-            g["y_qkv"] = host(Q.gemm_mxfp4(it["h"][rows_d].contiguous(), a[0:1], *wq["qkv"]))
+            g["h1"] = acts(it, "h", "h_e8m0")
+            g["y_qkv"] = host(gemm(it, "h", "h_e8m0", 0, "qkv"))
         elif stage == _lib.QVD_STAGE_OQUANT:
-            g["o8"] = host(it["h"])
+            g["o8"] = acts(it, "h", "h_e8m0")
         else:
             g["x1"] = host_bits(xd)
         del it, ws
@@ -273,31 +286,58 @@ def run_stages_w4a8(bw, mod_d, x_bits, idx_d, cnt_d, rows):
     return g
 
 
-def check_block_stages_w4a8(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, rows, eps=1e-6):
-    """Every stage of the W4A8 block against the oracle, fed the GPU's own inputs.  wm: the GPU's MXFP4
-    weights on the host ('w_<site>' packed E2M1, 'e8_<site>' E8M0); act: the four static scales."""
+def check_block_stages_4bit(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, rows, eps=1e-6):
+    """Every stage of a 4-bit block against the oracle, fed the GPU's own inputs.  wm: the GPU's MXFP4
+    weights on the host ('w_<site>' packed E2M1, 'e8_<site>' E8M0); act: the four static E4M3 scales
+    (W4A8), or None for MXFP4 activations (W4A4)."""
     L, d = x_bits.shape
     H = n_heads
+    a4 = act is None
     tiles = np.unique(rows // 128)
     assert np.array_equal(np.concatenate([np.arange(i * 128, min(L, (i + 1) * 128)) for i in tiles]),
                           rows), "rows must be whole tiles"
     mod64 = mod.astype(np.float64)
-    s1, so, s2, sg = (np.float32(v) for v in act)
+    s1, so, s2, sg = (None,) * 4 if a4 else (np.float32(v) for v in act)
     st = {}
     w = {s: (wm["w_" + s], wm["e8_" + s]) for s in ("qkv", "o", "up", "down")}
 
-    def static_codes(y, s):
-        """E4M3 codes of fp32 values under the static scale s (the static rule: y * fp32(1/s))."""
-        codes, _ = OQ.quant_fp8_per_tensor(np.asarray(y, np.float32), scale_in=s)
-        return codes, np.asarray(y, np.float32) * (np.float32(1.0) / np.float32(s))
+    def sub(c):
+        """The checked rows of a GPU activation (codes, E8M0 or None)."""
+        return (c[0][rows], None if c[1] is None else c[1][rows])
 
-    # S1: modulate (attention branch) -> E4M3 under s1
-    y = OA.layernorm_modulate(x_bits[rows], mod, 0, eps)
-    want, pre = static_codes(y, s1)
-    st["h1_flips"] = assert_codes_equal_except_ties(g["h1"][rows], want, pre, "e4m3", name=name + " h1")
+    def gemm(c, s, site):
+        """The oracle's GEMM of the GPU's activation codes (rows already taken) with the site's weights."""
+        if a4:
+            return OG.gemm_mxfp4_w4a4(c[0], c[1], *w[site])
+        return OG.gemm_mxfp4(c[0], s, *w[site])
 
-    # S2: QKV GEMM (E4M3 x MXFP4) from the GPU's h1; its epilogue from the GPU's fp32 values
-    yq = OG.gemm_mxfp4(g["h1"][rows], s1, *w["qkv"])
+    def check_modulate(c, half, s, what):
+        y = OA.layernorm_modulate(x_bits[rows] if half == 0 else g["x1"][rows], mod, half, eps)
+        if a4:
+            p, e = OQ.quant_mxfp4(y)
+            np.testing.assert_array_equal(c[1], e, err_msg=f"{name} {what} E8M0")
+            np.testing.assert_array_equal(c[0], p, err_msg=f"{name} {what} E2M1")
+            return 0
+        codes, _ = OQ.quant_fp8_per_tensor(y, scale_in=s)
+        pre = np.asarray(y, np.float32) * (np.float32(1.0) / s)
+        return assert_codes_equal_except_ties(c[0], codes, pre, "e4m3", name=f"{name} {what}")
+
+    def check_codes_of_bf16(c, bits, s, what):
+        """The GPU's codes of a fused producer equal the oracle's quantizer of its bf16 output."""
+        v = OC.bf16_to_f64(bits)
+        if a4:
+            p, e = OQ.quant_mxfp4(v)
+            np.testing.assert_array_equal(c[1], e, err_msg=f"{name} {what} E8M0")
+            np.testing.assert_array_equal(c[0], p, err_msg=f"{name} {what} E2M1")
+        else:
+            np.testing.assert_array_equal(c[0], OQ.quant_fp8_per_tensor(v.astype(np.float32), scale_in=s)[0],
+                                          err_msg=f"{name} {what}")
+
+    # S1: modulate (attention branch) of the input
+    st["h1_flips"] = check_modulate(sub(g["h1"]), 0, s1, "h1")
+
+    # S2: QKV GEMM from the GPU's h1; its epilogue from the GPU's fp32 values
+    yq = gemm(sub(g["h1"]), s1, "qkv")
     yg = g["y_qkv"].astype(np.float64)
     st["qkv_gemm_err_rel"] = assert_close_rms(yg, yq, 1e-3, name + " QKV GEMM (fp32)")
     yb = OC.f64_to_bf16(yg)
@@ -314,36 +354,33 @@ def check_block_stages_w4a8(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, ro
     np.testing.assert_array_equal(vr[vn], yb[:, 2 * d:][vn], err_msg=name + " V = bf16 of the GEMM output")
 
     # S3: attention from the GPU's Q8, K8, scales and V^T: the bf16 output at the attention bar, and the
-    # block's E4M3 codes of O equal to the static quantizer's on that bf16 output
+    # block's codes of O equal to the oracle's quantizer on that bf16 output
     o_gpu = g["o_bf16"].reshape(L, H, 128)
     for h in range(H):
         for i in tiles:
             r = slice(i * 128, min(L, (i + 1) * 128))
             want = OAT.sparse_attn_tile(g["q8"], g["qs"], g["k8"], g["ks"], v_bits, idx, cnt, h, i, SM_SCALE)
             assert_bf16_close(np.ascontiguousarray(o_gpu[r, h]), want, 1e-2, f"{name} attention ({h}, {i})")
-    o_rows = OC.bf16_to_f64(g["o_bf16"].reshape(L, d)[rows]).astype(np.float32)
-    np.testing.assert_array_equal(g["o8"].reshape(L, d)[rows], static_codes(o_rows, so)[0],
-                                  err_msg=name + " O codes = static quantizer of the bf16 O")
+    o8 = sub(g["o8"])
+    check_codes_of_bf16((o8[0].reshape(len(rows), -1), o8[1]), g["o_bf16"].reshape(L, d)[rows], so,
+                        "O codes = quantizer of the bf16 O")
 
-    # S5: out-projection (E4M3 x MXFP4) + gated residual from the GPU's O codes
-    y1 = OG.gemm_mxfp4(g["o8"].reshape(L, d)[rows], so, *w["o"])
+    # S5: out-projection + gated residual from the GPU's O codes
+    y1 = gemm((o8[0].reshape(len(rows), -1), o8[1]), so, "o")
     assert_bf16_close(g["x1"][rows], OC.bf16_to_f64(x_bits[rows]) + mod64[2][None, :] * y1, 1e-3, name + " x1")
 
-    # S6: modulate (MLP branch) of the GPU's x1 -> E4M3 under s2
-    y = OA.layernorm_modulate(g["x1"][rows], mod, 1, eps)
-    want, pre = static_codes(y, s2)
-    st["h2_flips"] = assert_codes_equal_except_ties(g["h2"][rows], want, pre, "e4m3", name=name + " h2")
+    # S6: modulate (MLP branch) of the GPU's x1
+    st["h2_flips"] = check_modulate(sub(g["h2"]), 1, s2, "h2")
 
     # S7: up-projection from the GPU's h2: fp32 accumulators at the GEMM bar, bf16 GELU of them at the
-    # bf16 bar, and the block's E4M3 codes of g equal to the static quantizer's on that bf16 GELU
-    yu = OG.gemm_mxfp4(g["h2"][rows], s2, *w["up"])
+    # bf16 bar, and the block's codes of g equal to the oracle's quantizer on that bf16 GELU
+    yu = gemm(sub(g["h2"]), s2, "up")
     st["up_gemm_err_rel"] = assert_close_rms(g["y_up"].astype(np.float64), yu, 1e-3, name + " up GEMM (fp32)")
     assert_bf16_close(g["g_bf16"], OG.gelu(g["y_up"].astype(np.float64)), 1e-3, name + " GELU")
-    np.testing.assert_array_equal(g["g8"][rows], static_codes(OC.bf16_to_f64(g["g_bf16"]).astype(np.float32), sg)[0],
-                                  err_msg=name + " g codes = static quantizer of the bf16 GELU")
+    check_codes_of_bf16(sub(g["g8"]), g["g_bf16"], sg, "g codes = quantizer of the bf16 GELU")
 
     # S9: down-projection + gated residual from the GPU's g codes: the block output (the FP8 block's rule)
-    y2 = OG.gemm_mxfp4(g["g8"][rows], sg, *w["down"])
+    y2 = gemm(sub(g["g8"]), sg, "down")
     y2g = g["y_down"].astype(np.float64)
     st["down_gemm_err_rel"] = assert_close_rms(y2g, y2, 1e-3, name + " down GEMM (fp32)")
     x2_f64 = OC.bf16_to_f64(g["x1"][rows]) + mod64[5][None, :] * y2
@@ -356,9 +393,9 @@ def check_block_stages_w4a8(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, ro
     big = err > 1e-2 * rms
     st["x2_max_err_rel"] = float(err.max() / rms)
     st["x2_tie_flips"] = int(np.count_nonzero(big))
-    say(f"{name}: W4A8 stages ok; h1 {st['h1_flips']} / h2 {st['h2_flips']} near-tie code flips; GEMM fp32 "
-        f"max|err| QKV {st['qkv_gemm_err_rel']:.1e} / up {st['up_gemm_err_rel']:.1e} / down "
-        f"{st['down_gemm_err_rel']:.1e} RMS; block output max|err| {st['x2_max_err_rel']:.2e} RMS")
+    say(f"{name}: {'W4A4' if a4 else 'W4A8'} stages ok; h1 {st['h1_flips']} / h2 {st['h2_flips']} near-tie "
+        f"code flips; GEMM fp32 max|err| QKV {st['qkv_gemm_err_rel']:.1e} / up {st['up_gemm_err_rel']:.1e} / "
+        f"down {st['down_gemm_err_rel']:.1e} RMS; block output max|err| {st['x2_max_err_rel']:.2e} RMS")
     assert (~big | (tie & (err <= np.abs(x2_want) * 2.0 ** -7))).all(), \
         f"{name}: block output beyond 1e-2 RMS away from a near-tie"
     assert st["x2_tie_flips"] <= max(8, 1e-3 * err.size), f"{name}: {st['x2_tie_flips']} near-tie flips"
