@@ -47,6 +47,7 @@ struct GroupSmem {
     int8_t k[2][128 * 128];         // 2 x 16 KB: double-buffered K tiles
     uint16_t vt[128 * 128];         // 32 KB, fp16 bit patterns
     int tiles[MAX_KEPT];            // the valid entries of the item's kept-tile list, in order
+    float tks[MAX_KEPT];            // their K scales
 };
 
 struct AttnSmem {
@@ -72,8 +73,21 @@ QVD_DEV u32 pack_f16x2(float lo, float hi) {
     return __builtin_bit_cast(u32, r);
 }
 
-QVD_DEV void dma16(const void* g, void* lds_slot_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_slot_base, 16, 0, 0);
+// The tile DMAs are buffer loads to LDS (MUBUF), not global_load_lds: a FLAT instruction that may
+// write LDS counts, for the compiler, as an LDS access that completes out of order, so with one in
+// flight every wait on an LDS read becomes lgkmcnt(0) and the next step's fragment reads could never
+// stay in flight under the current step's MFMAs.  A buffer load counts on vmcnt only.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// raw buffer (stride 0, no swizzle) over the whole 32-bit offset range at base; every offset the
+// kernel forms lies inside the operand (the launcher keeps V^T below 4 GiB)
+QVD_DEV rsrc_t raw_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
+}
+
+// 16 bytes per lane from byte offset soff + voff of the buffer; lane l's bytes land at slot l
+QVD_DEV void dma16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds_slot_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_slot_base, 16, voff, soff, 0, 0);
 }
 
 // Barriers with explicit waits: this wave's LDS reads are done (and with dma_barrier its DMA has
@@ -117,7 +131,7 @@ QVD_DEV void stage_k(int8_t* kbuf, const int8_t* __restrict__ k, int L, int H, i
         int kr = j * 128 + key_of_row(r);
         kr = kr < L ? kr : L - 1;
         const uint32_t off = ((uint32_t)kr * (uint32_t)H + (uint32_t)h) * 128u + (uint32_t)(16 * c);
-        dma16(k + off, kbuf + blk * 1024);
+        dma16(raw_rsrc(k), off, 0u, kbuf + blk * 1024);
     }
 }
 
@@ -127,18 +141,17 @@ QVD_DEV void stage_k(int8_t* kbuf, const int8_t* __restrict__ k, int L, int H, i
 // (32-bit offsets: H*128*Lp*2 bytes stays far below 2^32 for every L the launcher accepts)
 QVD_DEV void stage_vt(uint16_t* vbuf, const uint16_t* __restrict__ vt, int Lp, int h, int j,
                       int wv, int lane) {
-    const char* base = reinterpret_cast<const char*>(vt) + (size_t)j * 256u;
+    const rsrc_t r = raw_rsrc(vt);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int blk = 8 * wv + u;
         const int d = blk * 4 + (lane >> 4);
         const int c = (lane & 15) ^ (d & 15);
         uint32_t off = ((uint32_t)(h * 128 + d) * (uint32_t)Lp + (uint32_t)(8 * c)) * 2u;
-        // a 32-bit lane offset from a wave-uniform base: the scalar-base form of the DMA, with no
-        // 64-bit address arithmetic per instruction (the empty asm keeps the compiler from hoisting
-        // 64-bit copies of the offsets out of the tile loop)
+        // the lane offset in a VGPR, the tile's in the scalar offset (the empty asm keeps the compiler
+        // from holding eight loop-invariant lane offsets in registers across the tile loop)
         asm volatile("" : "+v"(off));
-        dma16(base + off, vbuf + blk * 512);
+        dma16(r, off, (uint32_t)j * 256u, vbuf + blk * 512);
     }
 }
 
@@ -161,6 +174,8 @@ QVD_DEV void qk_scores(const int8_t* kbuf, const v4i qf[2][2], int fr, int fg, v
 #pragma unroll
             for (int b = 0; b < 4; ++b) knext[b] = kfrag(4 * ((st + 1) & 1) + b, (st + 1) >> 1);
         }
+        // the reads issue before this step's MFMAs, into registers of their own
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -276,12 +291,13 @@ QVD_DEV void tile_numerators(const v4i s[2][8], float c, const float m[2], int k
     }
 }
 
-// The valid entries (0 <= j < T) of the first `cnt` list elements, in list order, into tiles; their
-// number into *n_out.  Returns the largest |K scale| of those tiles (ks_row: the head's K scales).
+// The valid entries (0 <= j < T) of the first `cnt` list elements, in list order, into tiles and their
+// K scales into tks; their number into *n_out.  Returns the largest |K scale| of those tiles (ks_row:
+// the head's K scales).
 // Run by both groups of the workgroup at once (gtid: thread index in the group, wg: wave in the
 // group): the iteration count depends on kmax only, so every wave meets the same barriers.
 // Ballot-based prefix sums keep the order deterministic.
-QVD_DEV float compact_tiles(int* tiles, int* wcount, float* wkmax, int* n_out,
+QVD_DEV float compact_tiles(int* tiles, float* tks, int* wcount, float* wkmax, int* n_out,
                             const int32_t* __restrict__ list, int cnt, int kmax, int T,
                             const float* __restrict__ ks_row, int gtid, int lane, int wg) {
     int total = 0;
@@ -290,7 +306,8 @@ QVD_DEV float compact_tiles(int* tiles, int* wcount, float* wkmax, int* n_out,
         const int t = base + gtid;
         const int j = t < cnt ? list[t] : -1;
         const bool ok = j >= 0 && j < T;
-        if (ok) km = fmaxf(km, fabsf(ks_row[j]));
+        const float kj = ok ? ks_row[j] : 0.0f;
+        km = fmaxf(km, fabsf(kj));
         const unsigned long long mask = __ballot(ok);
         const int pos = __popcll(mask & ((1ull << lane) - 1ull));
         __syncthreads();
@@ -298,7 +315,10 @@ QVD_DEV float compact_tiles(int* tiles, int* wcount, float* wkmax, int* n_out,
         __syncthreads();
         int off = total;
         for (int w = 0; w < wg; ++w) off += wcount[w];
-        if (ok) tiles[off + pos] = j;
+        if (ok) {
+            tiles[off + pos] = j;
+            tks[off + pos] = kj;
+        }
         total += wcount[0] + wcount[1] + wcount[2] + wcount[3];
     }
     km = wave_max(km);
@@ -328,6 +348,7 @@ QVD_DEV void pv_tile(const uint16_t* vbuf, const v8h pb[2][4], int fr, int fg, v
 #pragma unroll
             for (int b = 0; b < 4; ++b) vnext[b] = vfrag(4 * ((st + 1) & 1) + b, (st + 1) >> 1);
         }
+        __builtin_amdgcn_sched_barrier(0);
         if (hf == 0) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
@@ -423,7 +444,7 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     int cnt = valid ? kv_cnt[h * T + i] : 0;
     cnt = cnt < 0 ? 0 : (cnt > kmax ? kmax : cnt);
     const int32_t* list = kv_idx + ((int64_t)h * T + i) * kmax;
-    const float ks_max = compact_tiles(gs.tiles, sm.wcount[g], sm.wkmax[g], &sm.n[g], list, cnt, kmax, T,
+    const float ks_max = compact_tiles(gs.tiles, gs.tks, sm.wcount[g], sm.wkmax[g], &sm.n[g], list, cnt, kmax, T,
                                        k_scale + (int64_t)h * T, tid & 255, lane, wg);
     const ScoreGrid grid(fabsf(qsc) * ks_max);
     const int n = sm.n[g];
@@ -446,9 +467,9 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     // its own loop, so its scores and numerators are live only where it uses them; the loops meet
     // the same barriers (s_barrier counts waves, not program locations), P + 1 of them in all.
     // Before a group's MFMA phase its waves wait for their DMA (K(t) and V^T(t-1)).
-    //   MFMA phase t: index and K scale of tile t; K(t+1) -> LDS (its buffer was last read in MFMA phase t-1);
-    //                 P.V(t-1); S(t).  (The last one, t = n, multiplies a stale K buffer into unused
-    //                 scores, which keeps the loop free of register merges.)
+    //   MFMA phase t: K(t+1) -> LDS (its buffer was last read in MFMA phase t-1); P.V(t-1); S(t);
+    //                 index and K scale of tile t from LDS.  (The last one, t = n, multiplies a stale K
+    //                 buffer into unused scores, which keeps the loop free of register merges.)
     //   VALU phase t: V^T(t) -> LDS (its buffer was last read in MFMA phase t); numerators of tile t.
     //                 No LDS reads: the tile index and its K scale are read in the MFMA phase before,
     //                 so the other group's fragment reads never hold this phase up.
@@ -468,24 +489,34 @@ __global__ void __launch_bounds__(512, 1) k_sparse_attn(
     if (g == 1) lds_barrier();                   // group 1: B_-1 (its phase 0 is idle)
     dma_barrier();                                // group 0: B_-1; group 1: B_0
     int passed = 1 + g;                           // barriers passed
-    // j is made wave-uniform so that the K scale comes through the scalar cache (counted by lgkmcnt,
-    // which the phase barrier waits for): as a vector load it would make the VALU phase wait for
-    // vmcnt, i.e. for the V^T DMA just issued.
+    // The next VALU phase's tile index (made wave-uniform for the DMA addresses) and K scale are read
+    // from the compacted list in LDS at the end of the MFMA phase, under its last MFMAs.  LDS reads
+    // return in order, so the compiler keeps graded waits (lgkmcnt(n)) on the fragment reads, and the
+    // next step's fragments load while this step multiplies.  A scalar load of the K scale in flight
+    // here made it wait for every outstanding LDS read (lgkmcnt(0)) before each MFMA step, since
+    // scalar loads may return out of order; a vector load would make the VALU phase wait for vmcnt,
+    // i.e. for the V^T DMA just issued.
     if (n > 0) {
         j = __builtin_amdgcn_readfirstlane(gs.tiles[0]);
-        ksc = k_scale[h * T + j];
+        ksc = gs.tks[0];
         mfma_qk(0);
         lds_barrier();
         ++passed;
         for (int t = 0; t < n; ++t) {
             valu_phase();
             dma_barrier();
-            if (t + 1 < n) {
-                j = __builtin_amdgcn_readfirstlane(gs.tiles[t + 1]);
-                ksc = k_scale[h * T + j];
-            }
+            // The MFMA phase issues at raised priority: where its instructions and the other group's
+            // VALU instructions compete for a SIMD's issue, the matrix core is served first.  Without
+            // it the older group (waves 0-3) wins in both phases, which stretched the younger group's
+            // MFMA phases by about a fifth and with them every second barrier interval.
+            __builtin_amdgcn_s_setprio(2);
             pv_tile(gs.vt, pb, fr, fg, o, lacc);
             mfma_qk(t + 1);
+            if (t + 1 < n) {
+                j = __builtin_amdgcn_readfirstlane(gs.tiles[t + 1]);
+                ksc = gs.tks[t + 1];
+            }
+            __builtin_amdgcn_s_setprio(0);
             lds_barrier();
             passed += 2;
         }
