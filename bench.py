@@ -572,6 +572,8 @@ def main():
                     help="skip the sampler loop, the MFMA probes and the attention-only / L=4096 block records")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the instrumented pass (per-kernel HIP events, breakdown and roofline)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the timing of the same steps replayed from HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device-to-device copy (calibrates the HBM byte counters)")
     ap.add_argument("--parse-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -646,6 +648,37 @@ def main():
     elapsed, step_ms = timed_steps()
     log(f"timed {args.steps} steps: {elapsed * 1e3 / args.steps:.2f} ms/step")
 
+    # ---- the same steps replayed from HIP graphs: one captured step per timestep ----------------------
+    graph = None
+    if not args.no_graph:
+        graphs = {}
+        for k in range(args.steps):
+            graphs.setdefault(k % len(ts), None)
+        for t in graphs:
+            graphs[t] = Q.capture_graph(lambda t=t: step(t))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record()
+        for k in range(args.steps):
+            graphs[k % len(ts)].replay()
+            ev[k + 1].record()
+        torch.cuda.synchronize()
+        g_elapsed = time.perf_counter() - t0
+        # the last replay's output against the same step run eagerly
+        last = (args.steps - 1) % len(ts)
+        replayed = x.clone()
+        step(last)
+        torch.cuda.synchronize()
+        graph = {"ms_per_step": round(g_elapsed * 1e3 / args.steps, 3),
+                 "step_ms": [round(ev[k].elapsed_time(ev[k + 1]), 3) for k in range(args.steps)],
+                 "matches_eager_bitwise": bool(torch.equal(replayed.view(torch.int16), x.view(torch.int16))),
+                 "note": "the timed steps above replayed from one captured HIP graph per timestep "
+                         "(x <- x0, the AdaLN projection and the 42 block forwards)"}
+        del graphs, replayed
+        log(f"graph replay: {graph['ms_per_step']:.2f} ms/step (eager {elapsed * 1e3 / args.steps:.2f}); "
+            f"matches eager: {graph['matches_eager_bitwise']}")
+
     # ---- the same steps again with the library's per-kernel HIP events (breakdown, roofline) --------
     kernels, elapsed_inst = {}, None
     if not args.no_kernel_timing:
@@ -719,6 +752,7 @@ def main():
         "pct_of_block_roofline": round(100 * t_bound_ms / ms_per_block, 2),
         "step_ms_by_timestep": per_ts,
         "ms_per_step_with_kernel_events": None if elapsed_inst is None else round(elapsed_inst * 1e3 / args.steps, 3),
+        "graph_replay": graph,
         "roofline": roofline,
         "kernels": breakdown,
         "setup_s": round(setup_s, 1),

@@ -12,5 +12,5 @@ from .ops import (  # noqa: F401
     vt_from_bf16, vt_unify,
     gemm_fp8, gemm_mxfp4, gemm_mxfp4_w4a4, gemm_tiles, quant_mxfp4, amax_update, clip_count, BlockWeights,
     quantize_block_weights, block_ws_bytes, dit_block_forward, block_forward_until, block_intermediates, from_bits, to_bits, timing_enable, timing_report,
-    calibrated_scale, Sampler, mfma_probe, layernorm_modulate_f32, inject_launch_failure,
+    calibrated_scale, Sampler, mfma_probe, layernorm_modulate_f32, inject_launch_failure, capture_graph,
 )

@@ -539,8 +539,13 @@ def select_tiles(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor, kept
 # ----------------------------------------------------------------------------------------------
 # per-kernel event timing
 
+_TIMING_ON = False
+
+
 def timing_enable(on: bool = True):
+    global _TIMING_ON
     call("qvd_timing_enable", 1 if on else 0)
+    _TIMING_ON = bool(on)
 
 
 def timing_report() -> dict:
@@ -630,3 +635,30 @@ def inject_launch_failure(after: int):
     """The launch `after` launches from now on this thread reports QVD_EHIP (qvd_inject_launch_failure);
     -1 cancels.  For tests of error handling."""
     call("qvd_inject_launch_failure", int(after))
+
+
+def capture_graph(fn, warmup: int = 1) -> torch.cuda.CUDAGraph:
+    """Record the launches fn() makes on the current stream into a HIP graph (torch's CUDAGraph over
+    stream capture); graph.replay() runs them again on the same buffers.  The library allocates and
+    synchronises nothing inside its calls, so a block forward or a whole stack step captures as it is;
+    tensors fn allocates come from the graph's private pool.  fn should be repeatable (it runs warmup
+    times on a side stream first, so that every kernel has been loaded before capture).  Per-kernel
+    timing must be off (it records events), and the output poisoning of the tests is suspended while
+    capturing (its byte fill could be recorded as a memset node)."""
+    global POISON
+    if _TIMING_ON:
+        raise RuntimeError("capture_graph: per-kernel timing is on; call timing_enable(False) first")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    saved, POISON = POISON, False
+    try:
+        with torch.cuda.graph(g):
+            fn()
+    finally:
+        POISON = saved
+    return g
