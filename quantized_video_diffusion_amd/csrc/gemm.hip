@@ -11,7 +11,7 @@
 // lane ends up holding four consecutive output columns of one token row -- the shape every epilogue
 // wants (8-byte bf16 stores, per-column bias/gate vectors, per-head INT8 quantization).
 //   workgroup tile 256 (tokens) x 256 (outputs), eight waves (two per SIMD) of 128 x 64 outputs;
-//   K in stages of 128: both operands K-contiguous, moved HBM/L2 -> LDS by global_load_lds_dwordx4
+//   K in stages of 128: both operands K-contiguous, moved HBM/L2 -> LDS by buffer_load_dwordx4 ... lds
 //   into two 64 KB stage buffers (stage s+2 lands while stage s is multiplied), 16-byte chunks
 //   XOR-swizzled by row so the 32-row MFMA fragment reads are bank-conflict free;
 //   tile order: contiguous tile ranges per XCD (workgroup b runs on XCD b % 8) and groups of 8 token
@@ -93,6 +93,32 @@ QVD_DEV u32 absmax_bf16x2(u32 m, u32 p) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Operand DMA: buffer loads to LDS (MUBUF, raw resource over the whole 32-bit offset range; the
+// launcher keeps every operand below 4 GiB), the lane's offset in a VGPR and the stage's K offset in
+// the scalar offset.  Not global_load_lds: a FLAT instruction that may write LDS counts, for the
+// compiler, as an LDS access that completes out of order, so with one in flight every wait on a
+// fragment read becomes lgkmcnt(0), including the reads issued for the next step; a buffer load
+// counts on vmcnt only.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// A wait the compiler sees (lgkmcnt(0), no vmcnt or expcnt wait), once before the main loop: no scalar
+// load (the kernel arguments the epilogue reads) is then in flight where the loop is entered, which
+// would otherwise make the first fragment wait of every stage lgkmcnt(0), since scalar loads may
+// return out of order.
+QVD_DEV void lgkm_settle() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+QVD_DEV rsrc_t raw_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
+}
+
+// 16 (4) bytes per lane from byte offset soff + voff of the buffer at base; lane l's bytes land at slot l
+QVD_DEV void dma_lds16(const void* base, uint32_t voff, uint32_t soff, void* lds_slot_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(base), (lds_void*)lds_slot_base, 16, voff, soff, 0, 0);
+}
+QVD_DEV void dma_lds4(const void* base, uint32_t voff, uint32_t soff, void* lds_slot_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(base), (lds_void*)lds_slot_base, 4, voff, soff, 0, 0);
+}
 
 // ---- accumulator layout ----------------------------------------------------------------------------
 // The MFMAs compute C^T = W . A^T, so a lane holds runs of 4 consecutive output columns (n) of one token
@@ -470,7 +496,7 @@ QVD_DEV void gemm_epilogue(const GemmArgs& g, const typename LY::Acc& acc, float
 // E4M3 x E4M3: 256 x 256 tiles, v_mfma_f32_32x32x64_f8f6f4, eight waves (two per SIMD) of 128 x 64
 // outputs each.
 //
-// Operands move HBM/L2 -> LDS by global_load_lds_dwordx4 in stages of 128 K (two LDS buffers of
+// Operands move HBM/L2 -> LDS by buffer loads to LDS in stages of 128 K (two LDS buffers of
 // 64 KB): one DMA instruction fills 8 whole 128-byte rows, so every request is a full cache line.
 // The MFMAs run in K-steps of 64 (half a stage) on fragments already in registers while the next
 // step's 6 fragments are read from LDS.  One s_barrier per stage, at the start of the stage's second
@@ -490,8 +516,8 @@ constexpr int NWAVE8 = 8;
 QVD_DEV void dma_f8(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
                     const uint32_t* w_off, int u) {
     uint8_t* dst = smem + buf * STAGE8 + (u < 4 ? 0 : BM * BKS) + (4 * wv + (u & 3)) * 1024;
-    const uint8_t* src = u < 4 ? g.a + a_off[u & 3] + k0 : g.w + w_off[u & 3] + k0;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+    if (u < 4) dma_lds16(g.a, a_off[u & 3], (uint32_t)k0, dst);
+    else dma_lds16(g.w, w_off[u & 3], (uint32_t)k0, dst);
 }
 
 QVD_DEV void stage_f8(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
@@ -564,6 +590,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_f8(GemmArgs g) {
     for (int i = 0; i < 2; ++i) fr[0][i] = frag32(smem + BM * BKS, w_blk + i, flo0, fhi0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) fr[0][2 + i] = frag32(smem, a_blk + i, flo0, fhi0);
+    lgkm_settle();
 
     // Stage s, half h, on register set h.  Half 0 reads the fragments of half 1 (same buffer).  Half 1
     // first waits for stage s+1: after that barrier every wave has also finished reading stage s (its
@@ -628,8 +655,8 @@ QVD_DEV void dma_scale_slice(const uint8_t* src, int base, int lim, int kb, int 
     row = row < lim ? row : lim - 1;
     int col = SC_ROW * chc + 4 * (lane & 7);
     col = col < kb ? col : 0;
-    __builtin_amdgcn_global_load_lds(src + (uint32_t)row * (uint32_t)kb + (uint32_t)col,
-                                     (lds_void*)(sc + (ch & 1) * stride + (32 * sl + 8 * part) * SC_ROW), 4, 0, 0);
+    dma_lds4(src, (uint32_t)row * (uint32_t)kb + (uint32_t)col, 0u,
+               sc + (ch & 1) * stride + (32 * sl + 8 * part) * SC_ROW);
 }
 
 // the word of stage t of row r from the chunk buffers at sc (stride between the two)
@@ -648,11 +675,8 @@ constexpr int SMEM_MX = MX_MAIN > NWAVE8 * 16384 ? MX_MAIN : NWAVE8 * 16384;
 QVD_DEV void dma_mx(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
                     const uint32_t* w_off, int u) {
     uint8_t* st = smem + buf * STAGE_MX;
-    if (u < 4)
-        __builtin_amdgcn_global_load_lds(g.a + a_off[u] + k0, (lds_void*)(st + (4 * wv + u) * 1024), 16, 0, 0);
-    else
-        __builtin_amdgcn_global_load_lds(g.w + w_off[u - 4] + k0 / 2,
-                                         (lds_void*)(st + W4_OFF + (2 * wv + u - 4) * 1024), 16, 0, 0);
+    if (u < 4) dma_lds16(g.a, a_off[u], (uint32_t)k0, st + (4 * wv + u) * 1024);
+    else dma_lds16(g.w, w_off[u - 4], (uint32_t)(k0 / 2), st + W4_OFF + (2 * wv + u - 4) * 1024);
 }
 
 QVD_DEV void stage_mx(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
@@ -738,6 +762,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(GemmArgs g) {
     for (int i = 0; i < 4; ++i) fa[0][i] = frag32(smem, a_blk + i, alo0, ahi0);
 #pragma unroll
     for (int i = 0; i < 2; ++i) scw[i] = scale_word(sc, SC_BUF, 32 * (w_blk + i) + lr, 0) >> (8 * hl);
+    lgkm_settle();
 
     // The step schedule of k_gemm_f8, with step bodies free of branches: with the refill and the E8M0
     // loads of waves 0..3 behind branches, the compiler moved every MFMA of the loop behind the last
@@ -811,11 +836,8 @@ constexpr int SMEM_W4A4 = W4A4_MAIN > NWAVE8 * 16384 ? W4A4_MAIN : NWAVE8 * 1638
 QVD_DEV void dma_w4a4(const GemmArgs& g, uint8_t* smem, int buf, int k0, int wv, const uint32_t* a_off,
                       const uint32_t* w_off, int u) {
     uint8_t* st = smem + buf * STAGE_W4A4;
-    if (u < 2)
-        __builtin_amdgcn_global_load_lds(g.a + a_off[u] + k0 / 2, (lds_void*)(st + (2 * wv + u) * 1024), 16, 0, 0);
-    else
-        __builtin_amdgcn_global_load_lds(g.w + w_off[u - 2] + k0 / 2,
-                                         (lds_void*)(st + W4A4_W_OFF + (2 * wv + u - 2) * 1024), 16, 0, 0);
+    if (u < 2) dma_lds16(g.a, a_off[u], (uint32_t)(k0 / 2), st + (2 * wv + u) * 1024);
+    else dma_lds16(g.w, w_off[u - 2], (uint32_t)(k0 / 2), st + W4A4_W_OFF + (2 * wv + u - 2) * 1024);
 }
 
 // one wave's part of a scale slice: operand o (waves 0..3 A, 4..7 W), part w % 4
@@ -891,6 +913,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4a4(GemmArgs g) {
     for (int i = 0; i < 2; ++i) scw[i] = sc_word(1, w_blk + i, 0) >> (8 * hl);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sca[i] = sc_word(0, a_blk + i, 0) >> (8 * hl);
+    lgkm_settle();
 
     // the step schedule of k_gemm_mx: step 0 of a stage uses blocks h (byte h of the shifted words),
     // step 1 blocks 2 + h (byte 2); the words of stage s+1 are read at the start of step 1 of stage s
