@@ -183,7 +183,7 @@ COUNTER_KERNELS = [
 N_XCD, N_SIMD = 8, 1024
 
 
-def parse_counters(mfma_dir, fetch_dir, write_dir, trace_dir, blocks=2):
+def parse_counters(mfma_dir, fetch_dir, write_dir, trace_dir, blocks=2, headline_steps=10):
     """Per-kernel MFMA utilisation, clock and HBM bytes from three rocprofv3 counter runs of the same
     command, with durations from a kernel-trace run (the counter runs' own timestamps include the
     collection): GRBM_GUI_ACTIVE (summed over the 8 XCDs) gives the kernel's GPU cycles, so
@@ -197,13 +197,18 @@ def parse_counters(mfma_dir, fetch_dir, write_dir, trace_dir, blocks=2):
             grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
             trace.append((int(r["Dispatch_Id"]), r["Kernel_Name"], grid,
                           (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
-    # the 480p stack's dispatches: from the first step's AdaLN projection (set-up work, the weights'
-    # quantization, is before it) to the 6 kernels that follow the last INT8-score attention (any 768p
-    # blocks come after)
+    # the headline steps of the 480p stack (the default command's 2 warm-up + 8 timed steps): from the
+    # first step's AdaLN projection (set-up work, the weights' quantization, is before it) to the
+    # projection that follows them (the graph replays, the static-scale stack and the 768p blocks come
+    # later; without a later projection, to the 6 kernels after the last INT8-score attention)
     trace.sort()
-    first = min((i for i, k, _, _ in trace if "k_adaln_project" in k), default=0)
-    att = [n for n, (_, k, _, _) in enumerate(trace) if "k_sparse_attn<1>" in k]
-    end = trace[min(att[-1] + 6, len(trace) - 1)][0] if att else 0
+    proj = [i for i, k, _, _ in trace if "k_adaln_project" in k]
+    first = proj[0] if proj else 0
+    if len(proj) > headline_steps:
+        end = proj[headline_steps] - 1
+    else:
+        att = [n for n, (_, k, _, _) in enumerate(trace) if "k_sparse_attn<1>" in k]
+        end = trace[min(att[-1] + 6, len(trace) - 1)][0] if att else 0
     rows = []
     for f in glob.glob(os.path.join(mfma_dir, "**", "*counter_collection.csv"), recursive=True):
         rows += list(csv.DictReader(open(f)))
