@@ -223,34 +223,37 @@ def check_block_stages(name, qw, mod, x_bits, idx, cnt, g, n_heads, rows=None, e
     return st
 
 
-# ---- the MXFP4-weight blocks: static E4M3 activations (W4A8) or MXFP4 activations (W4A4) --------------
-# Stages of dit_block_forward with MXFP4 weights.  W4A8 (QVD_W_MXFP4 with act_scale = (s1, s_O, s2, s_g)):
-# modulate -> E4M3 under s1; QKV GEMM (E4M3 x MXFP4) and its INT8 Q/K / V^T epilogue; the attention
-# writing E4M3(bf16(O)) under s_O (no bf16 O); out-projection + gated residual; modulate -> E4M3 under
-# s2; up-projection with the GELU -> E4M3 epilogue under s_g (no bf16 g); down-projection + gated
-# residual.  W4A4 (QVD_W_MXFP4_A4): the same chain with every GEMM input in MXFP4 per token row and 32
-# channels (E2M1 codes + an E8M0 scale per block) and no per-tensor scale.
+# ---- blocks whose producers write the next GEMM's codes ------------------------------------------------
+# Static E4M3 activation scales act_scale = (s1, s_O, s2, s_g) with FP8 weights (W8A8) or MXFP4 weights
+# (W4A8): modulate -> E4M3 under s1; QKV GEMM and its INT8 Q/K / V^T epilogue; the attention writing
+# E4M3(bf16(O)) under s_O (no bf16 O); out-projection + gated residual; modulate -> E4M3 under s2;
+# up-projection with the GELU -> E4M3 epilogue under s_g (no bf16 g); down-projection + gated residual.
+# W4A4 (QVD_W_MXFP4_A4): the same chain with every GEMM input in MXFP4 per token row and 32 channels
+# (E2M1 codes + an E8M0 scale per block) and no per-tensor scale.
 # Bars as for the FP8 block.  The two fused producers are checked in two parts: the bf16 tensor they
 # encode (the attention's bf16 output from the same inputs, the GELU epilogue's bf16 output from the same
 # accumulators) against the oracle at the bf16 bar, and their codes against the oracle's quantizer
 # applied to that bf16 tensor, bit for bit.  The MXFP4 modulate codes are bit-exact (the kernel rounds
 # the float64 modulation once to fp32, as the oracle does); the E4M3 ones follow the near-tie rule.
 
-def run_stages_4bit(bw, mod_d, x_bits, idx_d, cnt_d, rows):
-    """GPU side of the 4-bit stage check: the block whole and stopped after the stages later ones
+def run_stages_fused(bw, mod_d, x_bits, idx_d, cnt_d, rows):
+    """GPU side of the stage check of a block with fused producers: the block whole and stopped after the stages later ones
     overwrite, plus, on `rows`, the fp32 accumulator outputs of the QKV, up and down GEMMs and the
     bf16 GELU of the up-projection's accumulators; the bf16 attention output from the block's own
     Q8/K8/V^T.  Host copies."""
     L = x_bits.shape[0]
     a4 = bw.fmt == _lib.QVD_W_MXFP4_A4
+    fp8 = bw.fmt == _lib.QVD_W_FP8
     rows_d = torch.from_numpy(np.asarray(rows)).cuda()
     a = bw.act_scale
-    wq = {s: (bw.w[s], bw.e8[s]) for s in ("qkv", "o", "up", "down")}
+    wq = {s: (bw.w[s], bw.s[s] if fp8 else bw.e8[s]) for s in ("qkv", "o", "up", "down")}
 
     def gemm(it, codes, e8_slot, k, site, mode=_lib.QVD_EPI_F32):
         c = it[codes][rows_d].contiguous()
         if a4:
             return Q.gemm_mxfp4_w4a4(c, it[e8_slot][rows_d].contiguous(), *wq[site], mode=mode)
+        if fp8:
+            return Q.gemm_fp8(c, a[k:k + 1], *wq[site], mode=mode)
         return Q.gemm_mxfp4(c, a[k:k + 1], *wq[site], mode=mode)
 
     def acts(it, codes, e8_slot):
@@ -286,10 +289,11 @@ def run_stages_4bit(bw, mod_d, x_bits, idx_d, cnt_d, rows):
     return g
 
 
-def check_block_stages_4bit(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, rows, eps=1e-6):
-    """Every stage of a 4-bit block against the oracle, fed the GPU's own inputs.  wm: the GPU's MXFP4
-    weights on the host ('w_<site>' packed E2M1, 'e8_<site>' E8M0); act: the four static E4M3 scales
-    (W4A8), or None for MXFP4 activations (W4A4)."""
+def check_block_stages_fused(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, rows, eps=1e-6):
+    """Every stage of a block with fused producers against the oracle, fed the GPU's own inputs.  wm:
+    the GPU's weights on the host, MXFP4 ('w_<site>' packed E2M1, 'e8_<site>' E8M0) or FP8 ('w_<site>'
+    E4M3 codes, 's_<site>' the per-tensor scale); act: the four static E4M3 scales (W8A8, W4A8), or
+    None for MXFP4 activations (W4A4)."""
     L, d = x_bits.shape
     H = n_heads
     a4 = act is None
@@ -299,7 +303,9 @@ def check_block_stages_4bit(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, ro
     mod64 = mod.astype(np.float64)
     s1, so, s2, sg = (None,) * 4 if a4 else (np.float32(v) for v in act)
     st = {}
-    w = {s: (wm["w_" + s], wm["e8_" + s]) for s in ("qkv", "o", "up", "down")}
+    fp8 = "s_qkv" in wm
+    w = {s: (wm["w_" + s], wm["s_" + s] if fp8 else wm["e8_" + s]) for s in ("qkv", "o", "up", "down")}
+    kind = "W4A4" if a4 else ("W8A8" if fp8 else "W4A8")
 
     def sub(c):
         """The checked rows of a GPU activation (codes, E8M0 or None)."""
@@ -309,6 +315,8 @@ def check_block_stages_4bit(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, ro
         """The oracle's GEMM of the GPU's activation codes (rows already taken) with the site's weights."""
         if a4:
             return OG.gemm_mxfp4_w4a4(c[0], c[1], *w[site])
+        if fp8:
+            return OG.gemm_fp8(c[0], s, *w[site])
         return OG.gemm_mxfp4(c[0], s, *w[site])
 
     def check_modulate(c, half, s, what):
@@ -393,7 +401,7 @@ def check_block_stages_4bit(name, wm, act, mod, x_bits, idx, cnt, g, n_heads, ro
     big = err > 1e-2 * rms
     st["x2_max_err_rel"] = float(err.max() / rms)
     st["x2_tie_flips"] = int(np.count_nonzero(big))
-    say(f"{name}: {'W4A4' if a4 else 'W4A8'} stages ok; h1 {st['h1_flips']} / h2 {st['h2_flips']} near-tie "
+    say(f"{name}: {kind} stages ok; h1 {st['h1_flips']} / h2 {st['h2_flips']} near-tie "
         f"code flips; GEMM fp32 max|err| QKV {st['qkv_gemm_err_rel']:.1e} / up {st['up_gemm_err_rel']:.1e} / "
         f"down {st['down_gemm_err_rel']:.1e} RMS; block output max|err| {st['x2_max_err_rel']:.2e} RMS")
     assert (~big | (tie & (err <= np.abs(x2_want) * 2.0 ** -7))).all(), \

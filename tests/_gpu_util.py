@@ -87,7 +87,10 @@ def assert_codes_equal_except_ties(got, want, pre, kind: str, max_frac: float = 
     """Codes must be equal, except where the oracle's pre-rounding value sits within 2^-12 of a
     rounding midpoint (or the saturation threshold), or -- when `upstream` (the float64 value
     before an intermediate bf16 rounding) is given -- where that value sits within
-    2^-12 |value| + 1e-4 RMS(values) of a bf16 midpoint; there a neighbouring code is accepted."""
+    2^-12 |value| + 1e-4 RMS(values) of a bf16 midpoint; there a neighbouring code is accepted.
+    E4M3 +0 and -0 are the same value: where both sides round to zero, the sign of the zero follows the
+    sign of a value below the format's resolution, which the two sides' cancellation errors decide;
+    such a difference is accepted and counted with the near-ties."""
     got = np.asarray(got).reshape(-1)
     want = np.asarray(want).reshape(-1)
     pre = np.asarray(pre).reshape(-1)
@@ -101,7 +104,8 @@ def assert_codes_equal_except_ties(got, want, pre, kind: str, max_frac: float = 
     else:
         up_near = np.zeros(bad.size, bool)
     if kind == "e4m3":
-        near = e4m3_near_tie(pre[bad]) | up_near
+        zeros = ((got[bad].astype(np.int64) & 0x7F) == 0) & ((want[bad].astype(np.int64) & 0x7F) == 0)
+        near = e4m3_near_tie(pre[bad]) | up_near | zeros
         gv = OC.e4m3_decode(got[bad].astype(np.uint8))
         wv = OC.e4m3_decode(want[bad].astype(np.uint8))
         adj = np.abs(gv - wv) <= np.maximum(np.abs(wv), np.abs(gv)) * 2.0 ** -3 + 2.0 ** -9
