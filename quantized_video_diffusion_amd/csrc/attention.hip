@@ -147,10 +147,9 @@ QVD_DEV void stage_vt(uint16_t* vbuf, const uint16_t* __restrict__ vt, int Lp, i
         const int blk = 8 * wv + u;
         const int d = blk * 4 + (lane >> 4);
         const int c = (lane & 15) ^ (d & 15);
-        uint32_t off = ((uint32_t)(h * 128 + d) * (uint32_t)Lp + (uint32_t)(8 * c)) * 2u;
-        // the lane offset in a VGPR, the tile's in the scalar offset (the empty asm keeps the compiler
-        // from holding eight loop-invariant lane offsets in registers across the tile loop)
-        asm volatile("" : "+v"(off));
+        // the lane offset in a VGPR (loop-invariant: the compiler keeps the eight in registers across
+        // the tile loop), the tile's in the scalar offset
+        const uint32_t off = ((uint32_t)(h * 128 + d) * (uint32_t)Lp + (uint32_t)(8 * c)) * 2u;
         dma16(r, off, (uint32_t)j * 256u, vbuf + blk * 512);
     }
 }
