@@ -19,7 +19,8 @@ def _codes(M, K, seed, tensor="codes_a"):
     return W.random_e4m3_codes((M, K), seed=seed, tensor=tensor)
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (391, 384, 256), (33, 2688, 2688), (700, 768, 1024)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (391, 384, 256), (33, 2688, 2688), (700, 768, 1024),
+                                   (1, 256, 128)])
 def test_gemm_fp8_f32_epilogue(M, N, K):
     say("gemm f32", M, N, K)
     a, w = _codes(M, K, M), _codes(N, K, N, "codes_b")
@@ -207,7 +208,7 @@ def test_gemm_qkv_epilogue(M, H):
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 128, 128), (391, 384, 256), (300, 2688, 2688), (130, 256, 10752),
-                                   (257, 128, 1152)])
+                                   (257, 128, 1152), (1, 256, 128)])
 def test_gemm_mxfp4_f32_and_bf16(M, N, K):
     say("gemm mxfp4", M, N, K)
     a = _codes(M, K, M + 1)
@@ -275,7 +276,7 @@ def test_qk_int32_accumulators_bit_exact(L, i, j):
 
 
 @pytest.mark.parametrize("L,H,sparse", [(256, 2, False), (391, 2, False), (1290, 2, True),
-                                        (2000, 3, True), (128, 1, False)])
+                                        (2000, 3, True), (128, 1, False), (1, 2, False), (37, 3, False)])
 def test_sparse_attn_vs_oracle(L, H, sparse):
     say("attn", L, H, sparse)
     qb, kb, vb, idx, cnt = _attn_inputs(L, H, L, sparse)
