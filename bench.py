@@ -459,6 +459,16 @@ def run_768p(seed, steps=5, warmup=2):
                             "sites": calib, "seconds": round(calib_s, 1)}}
 
 
+def guarded(name, fn, log):
+    """Run one of the records beside the headline; a Python-level failure becomes {"error": ...} in the
+    line instead of ending the run before the headline is printed."""
+    try:
+        return fn()
+    except Exception as e:                      # noqa: BLE001 - reported in the JSON line
+        log(f"{name} failed: {type(e).__name__}: {e}")
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def static_scales_stack(args, Q, blocks, basis, proj_all, masks, x, x0, ws, ts, block_ops, log):
     """The 480p stack with static E4M3 activation scales, which the block fuses into the producers: the
     modulate passes take the scale (one pass each), the attention writes the E4M3 codes of O and the
@@ -712,8 +722,7 @@ def main():
     log(f"timed {args.steps} steps: {elapsed * 1e3 / args.steps:.2f} ms/step")
 
     # ---- the same steps replayed from HIP graphs: one captured step per timestep ----------------------
-    graph = None
-    if not args.no_graph:
+    def graph_replay():
         graphs = {}
         for k in range(args.steps):
             graphs.setdefault(k % len(ts), None)
@@ -733,14 +742,16 @@ def main():
         replayed = x.clone()
         step(last)
         torch.cuda.synchronize()
-        graph = {"ms_per_step": round(g_elapsed * 1e3 / args.steps, 3),
-                 "step_ms": [round(ev[k].elapsed_time(ev[k + 1]), 3) for k in range(args.steps)],
-                 "matches_eager_bitwise": bool(torch.equal(replayed.view(torch.int16), x.view(torch.int16))),
-                 "note": "the timed steps above replayed from one captured HIP graph per timestep "
-                         "(x <- x0, the AdaLN projection and the 42 block forwards)"}
-        del graphs, replayed
-        log(f"graph replay: {graph['ms_per_step']:.2f} ms/step (eager {elapsed * 1e3 / args.steps:.2f}); "
-            f"matches eager: {graph['matches_eager_bitwise']}")
+        rec = {"ms_per_step": round(g_elapsed * 1e3 / args.steps, 3),
+               "step_ms": [round(ev[k].elapsed_time(ev[k + 1]), 3) for k in range(args.steps)],
+               "matches_eager_bitwise": bool(torch.equal(replayed.view(torch.int16), x.view(torch.int16))),
+               "note": "the timed steps above replayed from one captured HIP graph per timestep "
+                       "(x <- x0, the AdaLN projection and the 42 block forwards)"}
+        log(f"graph replay: {rec['ms_per_step']:.2f} ms/step (eager {elapsed * 1e3 / args.steps:.2f}); "
+            f"matches eager: {rec['matches_eager_bitwise']}")
+        return rec
+
+    graph = None if args.no_graph else guarded("graph replay", graph_replay, log)
 
     # ---- the same steps again with the library's per-kernel HIP events (breakdown, roofline) --------
     kernels, elapsed_inst = {}, None
@@ -821,8 +832,9 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     if not args.no_static:
-        result["static_scales_480p"] = static_scales_stack(args, Q, blocks, basis, proj_all, masks, x, x0, ws, ts,
-                                                           block_ops_total, log)
+        result["static_scales_480p"] = guarded(
+            "static scales", lambda: static_scales_stack(args, Q, blocks, basis, proj_all, masks, x, x0, ws, ts,
+                                                         block_ops_total, log), log)
 
     # the sparse-tile selector at this token count (all heads): what choosing the mask from the block's
     # own Q/K would add per block; the timed steps above use the seeded masks
