@@ -59,28 +59,29 @@ QVD_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
     tn = in / gm;
 }
 
-// GELU(y) = y Phi(y), with Phi(y) = h for y < 0 and 1 - h for y >= 0, h = erfc(z) / 2, z = |y|/sqrt 2.
-// erfc from the Chebyshev fit of W. H. Press et al., Numerical Recipes, section 6.2 (function erfcc):
-// erfc(z) = t exp(-z^2 - 1.26551223 + t (1.00002368 + ... + 0.17087277 t^8)), t = 1/(1 + z/2), with
-// fractional error below 1.2e-7 for every z >= 0 -- also in the tail, where a form built on 1 - erf
-// would lose the small values that a static E4M3 scale can still resolve.  The exponent is evaluated
-// in log2 units (coefficients times log2 e) for exp2, with the halving folded into its constant term
-// (-1.8257482 - 1), and z enters through |y| (t = 1/(1 + |y|/(2 sqrt 2)), z^2 log2 e = |y|^2 log2(e)/2).
+// GELU(y) = y Phi(y) = max(y, 0) - |y| h, h = erfc(z) / 2, z = |y|/sqrt 2 (Phi(y) is h for y < 0 and
+// 1 - h for y >= 0).  erfc in the form of the approximation of W. H. Press et al., Numerical Recipes,
+// section 6.2 (function erfcc): erfc(z) / 2 = t 2^(-z^2 log2 e + P(t)), t = 1/(1 + z/2), with P a
+// degree-7 polynomial refitted (minimax, gelu_erfc_fit.py beside this file) over z in [0, 9.5], past
+// which the output is 0 or y in fp32: relative error 6.3e-7 of erfc, a ratio that holds in the tail too,
+// where a form built on 1 - erf would lose the small values that a static E4M3 scale can still resolve.
+// z enters through |y| (t = 1/(1 + |y|/(2 sqrt 2)), z^2 log2(e) = |y|^2 log2(e)/2).  |y| t < 2 sqrt 2
+// always; the bound keeps GELU(+inf) = +inf (inf * 0 would make a NaN).  max(y, 0) is taken as -0 for
+// y < 0, so that a negative input whose GELU underflows gives -0, the sign that y Phi(y) has (the
+// MXFP4 and E4M3 codes of -0 and +0 differ).
 QVD_DEV float gelu_erf(float y) {
     const float ay = fabsf(y);
     const float t = __builtin_amdgcn_rcpf(fmaf(0.35355339059327373f, ay, 1.0f));
-    float p = fmaf(0.2465173f, t, -1.1861149f);
-    p = fmaf(p, t, 2.1474745f);
-    p = fmaf(p, t, -1.6377531f);
-    p = fmaf(p, t, 0.40232158f);
-    p = fmaf(p, t, -0.26875687f);
-    p = fmaf(p, t, 0.13963005f);
-    p = fmaf(p, t, 0.5397006f);
-    p = fmaf(p, t, 1.4427292f);
-    p = fmaf(p, t, -2.8257482f);
+    float p = fmaf(-0.26331817f, t, 1.05167408f);
+    p = fmaf(p, t, -1.38636225f);
+    p = fmaf(p, t, 0.45005937f);
+    p = fmaf(p, t, -0.0276269704f);
+    p = fmaf(p, t, 0.559243484f);
+    p = fmaf(p, t, 1.44212113f);
+    p = fmaf(p, t, -2.82579158f);
     const float arg = fmaf(-(ay * 0.72134752044448170f), ay, p);
-    const float h = t * __builtin_amdgcn_exp2f(arg);             // erfc(z) / 2
-    return y * (y < 0.0f ? h : 1.0f - h);
+    const float at = fminf(ay * t, 2.8284271247461903f);
+    return fmaf(-at, __builtin_amdgcn_exp2f(arg), y >= 0.0f ? y : -0.0f);
 }
 
 // Running max of |v| over the bf16 halves of packed pairs, kept as two 16-bit magnitudes: for finite
