@@ -357,7 +357,11 @@ size_t qvd_block_ws_bytes(const qvd_block_params* p, int32_t L);
 /* x: bf16 [L][d], read and overwritten with the block output.  mod: fp32 [6][d] of this block at
  * this timestep (qvd_adaln_project).  kv_idx/kv_cnt/kmax: the block's sparse mask as in
  * sparse_attn; or kv_idx = kv_cnt = NULL: the block selects min(kmax, T) key tiles per query tile
- * from its own INT8 Q/K by the qvd_select_tiles rule, in the workspace. */
+ * from its own INT8 Q/K by the qvd_select_tiles rule, in the workspace.  Sizes: head_dim 128,
+ * d = 128 n_heads <= 4096, mlp a positive multiple of 256, kmax 1..1024, and every GEMM input and V^T
+ * below 4 GiB (L max(d, mlp) < 2^32 and 2 d 128 ceil(L/128) < 2^32: L < 399,457 at d = 2,688,
+ * mlp = 10,752); QVD_ESHAPE otherwise, QVD_EINVAL for NULL or inconsistent pointers, QVD_EALIGN,
+ * QVD_EWORKSPACE below qvd_block_ws_bytes. */
 int dit_block_forward(const qvd_block_params* p, const float* mod, uint16_t* x, int32_t L,
                       const int32_t* kv_idx, const int32_t* kv_cnt, int32_t kmax, void* ws,
                       size_t ws_bytes, void* stream);

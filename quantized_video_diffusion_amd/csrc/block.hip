@@ -110,6 +110,10 @@ int validate(const qvd_block_params* p, int L) {
     QVD_REQUIRE(p->mlp >= 128 && p->mlp % 256 == 0, QVD_ESHAPE,
                 "block: mlp = %d (positive multiple of 256)", p->mlp);
     QVD_REQUIRE(L >= 0, QVD_ESHAPE, "block: L = %d", L);
+    // the GEMM operand and V^T DMAs address their buffers with 32-bit offsets
+    const double widest = (double)(p->mlp > p->d ? p->mlp : p->d);
+    QVD_REQUIRE((double)L * widest < 4294967296.0 && 2.0 * p->d * 128.0 * ((L + 127) / 128) < 4294967296.0,
+                QVD_ESHAPE, "block: L = %d too large (every GEMM input and V^T must stay below 4 GiB)", L);
     QVD_REQUIRE(p->weight_format == QVD_W_FP8 || p->weight_format == QVD_W_MXFP4 ||
                     p->weight_format == QVD_W_MXFP4_A4,
                 QVD_EINVAL, "block: weight_format = %d", p->weight_format);

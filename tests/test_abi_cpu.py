@@ -162,6 +162,35 @@ def test_host_validation_errors(lib):
     assert _status(lib, "qvd_clip_count", fake, 5, None, fake, None) == _lib.QVD_EINVAL
 
 
+def test_size_limits_refused_before_launch(lib):
+    """The kernels address GEMM operands and V^T with 32-bit buffer offsets: every entry point refuses
+    sizes that would take an operand to 4 GiB, at the exact boundary, before any device work (the
+    largest accepted size goes on to fail a later check instead)."""
+    P = C.c_void_p
+    fake = P(0x10000)
+    e = _lib.Epilogue()
+    e.mode = _lib.QVD_EPI_F32
+    e.out_f32 = 0x10000
+    # GEMM: M K = 2^32 refused; one row fewer passes the size check and stops at w = NULL
+    assert _status(lib, "qvd_gemm_fp8", fake, fake, fake, fake, None, 1 << 21, 128, 2048, C.byref(e), None) == _lib.QVD_ESHAPE
+    assert b"4 GiB" in lib.qvd_last_error()
+    assert _status(lib, "qvd_gemm_fp8", fake, fake, None, fake, None, (1 << 21) - 1, 128, 2048, C.byref(e), None) == _lib.QVD_EINVAL
+    # attention: V^T of 128 heads x 128 dims x 1,024 tiles x 128 tokens in fp16 is 4 GiB
+    for L, want in ((1024 * 128, _lib.QVD_ESHAPE), (1023 * 128 + 1, _lib.QVD_ESHAPE), (1023 * 128, _lib.QVD_EINVAL)):
+        st = _status(lib, "sparse_attn", fake, fake, fake, fake, fake, L, 128, 128, None, fake, 3,
+                     C.c_float(0.1), fake, None, fake, 1 << 40, None)
+        assert st == want, (L, st, lib.qvd_last_error())
+    # block at the Trim width: the down-projection input L x 10,752 bytes reaches 2^32 at L = 399,458
+    p = _lib.BlockParams()
+    p.version, p.d, p.n_heads, p.head_dim, p.mlp = _lib.ABI_VERSION, 2688, 21, 128, 10752
+    for f in ("w_qkv", "w_o", "w_up", "w_down", "s_qkv", "s_o", "s_up", "s_down"):
+        setattr(p, f, 0x10000)
+    assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 399458, fake, fake, 53, fake, 1 << 40, None) == _lib.QVD_ESHAPE
+    assert b"4 GiB" in lib.qvd_last_error()
+    assert _status(lib, "dit_block_forward", C.byref(p), fake, fake, 399457, fake, fake, 0, fake, 1 << 40, None) == _lib.QVD_ESHAPE
+    assert b"kmax" in lib.qvd_last_error()
+
+
 def test_workspace_sizes_scale_with_tokens(lib):
     p = _lib.BlockParams()
     p.version, p.d, p.n_heads, p.head_dim, p.mlp = _lib.ABI_VERSION, 2688, 21, 128, 10752
