@@ -147,13 +147,13 @@ int adaln_modulate_noalloc(const uint16_t* x, int32_t L, int32_t d, const float*
  * consecutive channels X = 2^(floor(log2 max|y|) - 2) (all-zero block: X = 1), codes E2M1(y / X),
  * round to nearest even, saturating at 6.  packed: uint8 [L][d/2] (channel 2j in the low nibble of
  * byte j); e8m0: uint8 [L][d/32].  One pass; no workspace. */
+int adaln_modulate_mxfp4(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
+                         float eps, uint8_t* packed, uint8_t* e8m0, void* stream);
 /* The values the modulate quantizers encode, for calibration: y fp32 [L][d] =
  * fp32(LN(x)(1 + scale) + shift) with the statistics and the affine map in float64, rounded once
  * (the same y as adaln_modulate).  No workspace. */
 int adaln_layernorm_modulate_f32(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
                                  float eps, float* y, void* stream);
-int adaln_modulate_mxfp4(const uint16_t* x, int32_t L, int32_t d, const float* mod, int32_t half,
-                         float eps, uint8_t* packed, uint8_t* e8m0, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Block-sparse attention with INT8 scores -- "Trim 改变了什么" training bullet (80% sparsity)
