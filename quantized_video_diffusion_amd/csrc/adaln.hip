@@ -146,7 +146,9 @@ QVD_DEV void load_mod_table(float4* tab, const float* __restrict__ mod, int half
 // fp32 as fma(centered(x), fp32(rstd) fp32(1 + scale), shift), which is within 6 * 2^-24 (|y| + |shift|)
 // < 2^-21 (|y| + |shift|) of it; only elements within 2^-19 (max + max|shift|) of the row's fp32
 // maximum can hold the exact maximum, and those (usually one) are evaluated in float64.
-template <int NW>
+// EXACT: d = 128 NW, so every word loop runs whole and the loads carry no branches (the compiler can
+// then count the next row's loads in flight instead of waiting for all of them).
+template <int NW, bool EXACT>
 __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x, int L, int d,
                                                   const float* __restrict__ mod, int half, float eps,
                                                   double2* __restrict__ stats,
@@ -154,46 +156,56 @@ __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x
     __shared__ float4 tab[4096 / 2];
     __shared__ float red[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int nw = d >> 7;
+    const int nw = EXACT ? NW : d >> 7;
     load_mod_table(tab, mod, half, d, false, 1.0f);
     float shmax = 0.0f;
     for (int p = threadIdx.x; p < d / 2; p += 256)
         shmax = fmaxf(shmax, fmaxf(fabsf(tab[p].y), fabsf(tab[p].w)));
     shmax = block_max_nonneg<4>(shmax, red);
     float m = 0.0f;
-    Row<NW> R;
-    for (int row = blockIdx.x * 4 + wv; row < L; row += gridDim.x * 4) {
-        const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)row * d);
+    // the next row's loads are issued before this row is reduced, so their latency is covered
+    auto load_row = [&](Row<NW>& D, int r) {
+        const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)r * d);
 #pragma unroll
         for (int j = 0; j < NW; ++j)
-            if (j < nw) R.x[j] = __builtin_nontemporal_load(xr + lane + 64 * j);
+            if (j < nw) D.x[j] = __builtin_nontemporal_load(xr + lane + 64 * j);
+    };
+    const int stride = gridDim.x * 4;
+    Row<NW> R, Rn;
+    int row = blockIdx.x * 4 + wv;
+    if (row < L) load_row(R, row);
+    for (; row < L; row += stride) {
+        load_row(Rn, row + stride < L ? row + stride : L - 1);     // past the end: a row never used
         double mu, rstd;
         row_stats<NW>(R, nw, d, (double)eps, mu, rstd);
         if (lane == 0) stats[row] = make_double2(mu, rstd);
         const float rs = (float)rstd;
         const float mu_hi = (float)mu, mu_lo = (float)(mu - (double)mu_hi);
-        float ay[2 * NW];
+        float aw[NW];                             // per word: the larger fp32 |y| of its two elements
         float m32 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             if (j < nw) {
                 const float4 c = tab[lane + 64 * j];
-                ay[2 * j] = fabsf(fmaf(centered(bf16lo(R.x[j]), mu_hi, mu_lo), rs * (1.0f + c.x), c.y));
-                ay[2 * j + 1] = fabsf(fmaf(centered(bf16hi(R.x[j]), mu_hi, mu_lo), rs * (1.0f + c.z), c.w));
-                m32 = fmaxf(m32, fmaxf(ay[2 * j], ay[2 * j + 1]));
+                aw[j] = fmaxf(fabsf(fmaf(centered(bf16lo(R.x[j]), mu_hi, mu_lo), rs * (1.0f + c.x), c.y)),
+                              fabsf(fmaf(centered(bf16hi(R.x[j]), mu_hi, mu_lo), rs * (1.0f + c.z), c.w)));
+                m32 = fmaxf(m32, aw[j]);
             }
         }
         m32 = wave_max(m32);
         row_fence<NW>(R);
         const float thr = m32 - 0x1p-19f * (m32 + shmax);
+        // both elements of a candidate word in float64: the maximum over any set of exact |y| that
+        // holds every candidate is the row's exact maximum
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
-            if (j < nw && fmaxf(ay[2 * j], ay[2 * j + 1]) >= thr) {
+            if (j < nw && aw[j] >= thr) {
                 const float4 c = tab[lane + 64 * j];
-                if (ay[2 * j] >= thr) m = fmaxf(m, fabsf(modulate_one(bf16lo(R.x[j]), mu, rstd, c.x, c.y)));
-                if (ay[2 * j + 1] >= thr) m = fmaxf(m, fabsf(modulate_one(bf16hi(R.x[j]), mu, rstd, c.z, c.w)));
+                m = fmaxf(m, fabsf(modulate_one(bf16lo(R.x[j]), mu, rstd, c.x, c.y)));
+                m = fmaxf(m, fabsf(modulate_one(bf16hi(R.x[j]), mu, rstd, c.z, c.w)));
             }
         }
+        R = Rn;
     }
     m = block_max_nonneg<4>(m, red);
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
@@ -203,8 +215,9 @@ __global__ void __launch_bounds__(256) k_ln_stats(const uint16_t* __restrict__ x
 // here and the scale read from scale_in.  The codes are E4M3(y * inv) with y * inv formed in fp32 as
 // fma(centered(x), rstd (1 + scale) inv, shift inv): x - mu keeps its accuracy under cancellation (see
 // centered); the result is within a few fp32 ulps of the float64 modulation, which moves a code only
-// where the value lies that close to a rounding midpoint.
-template <int NW>
+// where the value lies that close to a rounding midpoint.  The next row is loaded while this one is
+// encoded (EXACT as in k_ln_stats).
+template <int NW, bool EXACT>
 __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x, int L, int d,
                                                   const float* __restrict__ mod, int half, float eps,
                                                   const double2* __restrict__ stats,
@@ -215,7 +228,7 @@ __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x
     __shared__ float4 tab[4096 / 2];
     __shared__ float red[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int nw = d >> 7;
+    const int nw = EXACT ? NW : d >> 7;
     float s, inv;
     if (scale_in) {
         s = *scale_in;
@@ -234,12 +247,18 @@ __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
     load_mod_table(tab, mod, half, d, true, inv);
-    Row<NW> R;
-    for (int row = blockIdx.x * 4 + wv; row < L; row += gridDim.x * 4) {
-        const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)row * d);
+    auto load_row = [&](Row<NW>& D, int r) {
+        const u32* xr = reinterpret_cast<const u32*>(x + (int64_t)r * d);
 #pragma unroll
         for (int j = 0; j < NW; ++j)
-            if (j < nw) R.x[j] = __builtin_nontemporal_load(xr + lane + 64 * j);
+            if (j < nw) D.x[j] = __builtin_nontemporal_load(xr + lane + 64 * j);
+    };
+    const int stride = gridDim.x * 4;
+    Row<NW> R, Rn;
+    int row = blockIdx.x * 4 + wv;
+    if (row < L) load_row(R, row);
+    for (; row < L; row += stride) {
+        load_row(Rn, row + stride < L ? row + stride : L - 1);     // past the end: a row never used
         double mu, rstd;
         if (scale_in) {
             row_stats<NW>(R, nw, d, (double)eps, mu, rstd);
@@ -260,6 +279,7 @@ __global__ void __launch_bounds__(256) k_ln_quant(const uint16_t* __restrict__ x
                 qr[lane + 64 * j] = (uint16_t)e4m3_encode2(v0, v1);
             }
         }
+        R = Rn;
     }
 }
 
@@ -393,8 +413,12 @@ static int launch_modulate_nw(const uint16_t* x, int L, int d, const float* mod,
     if (!scale_in) {
         int g = (L + rows_per_pass - 1) / rows_per_pass;
         g = g < 1 ? 1 : (g > LN_GRID_STATS ? LN_GRID_STATS : g);
-        hipLaunchKernelGGL(k_ln_stats<NW>, dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, stats,
-                           partials);
+        if ((d >> 7) == NW)
+            hipLaunchKernelGGL((k_ln_stats<NW, true>), dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, stats,
+                               partials);
+        else
+            hipLaunchKernelGGL((k_ln_stats<NW, false>), dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, stats,
+                               partials);
         np = g;
         int s = launch_status("adaln_modulate stats");
         if (s) return s;
@@ -403,8 +427,12 @@ static int launch_modulate_nw(const uint16_t* x, int L, int d, const float* mod,
     // grid of 4,096 ran the pass about 7% slower
     int g = (L + rows_per_pass - 1) / rows_per_pass;
     g = g < 1 ? 1 : (g > LN_GRID_QUANT ? LN_GRID_QUANT : g);
-    hipLaunchKernelGGL(k_ln_quant<NW>, dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, stats,
-                       partials, np, scale_in, q, scale_out);
+    if ((d >> 7) == NW)
+        hipLaunchKernelGGL((k_ln_quant<NW, true>), dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, stats,
+                           partials, np, scale_in, q, scale_out);
+    else
+        hipLaunchKernelGGL((k_ln_quant<NW, false>), dim3(g), dim3(256), 0, st, x, L, d, mod, half, eps, stats,
+                           partials, np, scale_in, q, scale_out);
     return launch_status("adaln_modulate quant");
 }
 
