@@ -176,8 +176,8 @@ COUNTER_KERNELS = [
     ("k_gemm_f8<4>", "QKV GEMM, INT8 Q/K + V^T epilogue", False),
     ("k_gemm_f8<3>", "up GEMM, GELU epilogue", False),
     ("k_gemm_f8<2>", "out / down GEMM, gated residual (mean of both)", False),
-    ("k_ln_stats<21>", "modulate pass 1", False),
-    ("k_ln_quant<21>", "modulate pass 2", False),
+    ("k_ln_stats<21, true>", "modulate pass 1", False),
+    ("k_ln_quant<21, true>", "modulate pass 2", False),
     ("k_quant_fp8_bf16", "FP8 quantizer of O and GELU (mean of both)", True),
 ]
 N_XCD, N_SIMD = 8, 1024
